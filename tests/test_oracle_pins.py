@@ -1,0 +1,471 @@
+"""Pins for the CPU oracle: values and properties the pages or mathematics fix.
+
+Each test checks the oracle against something other than itself: a worked
+example the pages print, a closed form, a library routine, published
+known-answer vectors, or brute force over tiny inputs.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+from oracle import moe_oracle as M
+from mixture_experts_layer_08_amd.synth import (CONFIGS, MoEConfig, make_inputs,
+                                                f32_to_bf16_bits, bf16_bits_to_f32)
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _tiny_inputs(rng, T, H, I, E, act="swiglu", bias=False, scale=1.0):
+    x = rng.standard_normal((T, H))
+    d = {"x": x, "w_r": rng.standard_normal((H, E)) * scale,
+         "b_r": rng.standard_normal(E) if bias else None}
+    if act == "swiglu":
+        d["w_gate"] = rng.standard_normal((E, H, I)) * 0.3
+        d["w_up"] = rng.standard_normal((E, H, I)) * 0.3
+        d["w_down"] = rng.standard_normal((E, I, H)) * 0.3
+    else:
+        d["w1"] = rng.standard_normal((E, H, I)) * 0.3
+        d["w2"] = rng.standard_normal((E, I, H)) * 0.3
+        d["b1"] = rng.standard_normal((E, I)) * 0.1
+        d["b2"] = rng.standard_normal((E, H)) * 0.1
+    return d
+
+
+def _cfg(T, H, I, E, k, cf, act="swiglu", route="softmax", seed=7, seq=0, alpha=0.01):
+    return MoEConfig("t", "f64", T=T, H=H, I=I, E=E, k=k, cf=cf, act=act,
+                     route=route, seed=seed, seq=seq or T, alpha=alpha)
+
+
+# ------------------------------------------------------------------ P1 ----
+@pytest.mark.parametrize("route", ["softmax", "gumbel"])
+def test_p1_weights_sum_to_one(route):
+    """Renormalised top-k weights sum to 1 (llama-moe essay,
+    coreui.cn/article/2610641, section 3.1)."""
+    rng = np.random.default_rng(1)
+    cfg = _cfg(200, 16, 8, 6, 3, 2.0, route=route)
+    r = M.route(_tiny_inputs(rng, 200, 16, 8, 6), cfg)
+    assert np.all(np.abs(r.w.sum(axis=1) - 1.0) < 1e-15)
+    assert np.all(r.w > 0)
+
+
+def test_p1_renorm_equals_softmax_of_selected_logits():
+    """MoE basics page (dpshk.com/news/6005940, section 3.1) takes a softmax
+    over the selected logits; the llama-moe essay divides the selected
+    probabilities by their sum.  Both are the same number."""
+    rng = np.random.default_rng(2)
+    cfg = _cfg(100, 12, 8, 8, 2, 2.0)
+    r = M.route(_tiny_inputs(rng, 100, 12, 8, 8), cfg)
+    sel = np.take_along_axis(r.logits, r.idx, axis=1)
+    ez = np.exp(sel - sel.max(axis=1, keepdims=True))
+    np.testing.assert_allclose(r.w, ez / ez.sum(axis=1, keepdims=True), rtol=1e-14)
+
+
+# ------------------------------------------------------------------ P2 ----
+def test_p2_worked_example_f1():
+    g = _gold("worked_example_f.json")
+    E, T = g["E"], g["T"]
+    # logits that send each token to the printed expert
+    logits = np.full((T, E), -1.0)
+    for t, e in enumerate(g["tokens_to_expert"]):
+        logits[t, e] = 1.0
+    idx = M.topk_lowest_index(logits, g["k"])
+    a = M.aux_stats(idx, M.softmax_rows(logits), E, 0.01)
+    assert a.counts.tolist() == g["expected_counts"]
+    assert a.f[1] == g["expected_f1"]
+
+
+def test_p2_uniform_case_gives_one():
+    """LLaMA4-MoE guide (dpshk.com/news/5809432, section 3.2): with f_i and
+    P_i both 1/E, E * sum f_i P_i = 1, i.e. L_aux = alpha."""
+    E, T, k = 8, 64, 2
+    idx = np.array([[(2 * t) % E, (2 * t + 1) % E] for t in range(T)])
+    p = np.full((T, E), 1.0 / E)
+    a = M.aux_stats(idx, p, E, 0.01)
+    assert np.all(a.f == 1.0 / E)
+    assert abs(a.l_aux - 0.01) < 1e-17
+
+
+# ------------------------------------------------------------------ P3 ----
+def test_p3_capacity_values():
+    expected = {1: 40, 2: 1280, 3: 4096, 4: 2560, 5: 2560}   # T*k*cf/E exact
+    for c, cfg in CONFIGS.items():
+        assert M.capacity(cfg.T, cfg.k, cfg.E, cfg.cf) == expected[c]
+    assert M.capacity(10, 1, 4, 1.0) == 3
+    # k = 1 is the MoE basics page's ceil(tokens / experts * cf), section 2.4
+    for T, E, cf in [(10, 4, 1.0), (1000, 7, 1.25), (333, 8, 1.5), (5, 3, 1.1)]:
+        assert M.capacity(T, 1, E, cf) == math.ceil(T / E * cf)
+
+
+# ------------------------------------------------------------------ P4 ----
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_p4_single_expert_is_dense_ffn(act):
+    """E = 1, k = 1: the layer reduces to one dense FFN (checked against
+    torch's own silu / exact gelu as the library routine)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(3)
+    T, H, I = 37, 16, 24
+    d = _tiny_inputs(rng, T, H, I, 1, act=act)
+    cfg = _cfg(T, H, I, 1, 1, 1.0, act=act)
+    res = M.forward(d, cfg)
+    assert np.all(res.route.w == 1.0) and np.all(res.route.probs == 1.0)
+    assert res.aux.f[0] == 1.0 and abs(res.aux.l_aux - cfg.alpha) < 1e-18
+    assert res.disp.dropped == 0
+    X = torch.from_numpy(d["x"])
+    F = torch.nn.functional
+    if act == "swiglu":
+        ref = (F.silu(X @ torch.from_numpy(d["w_gate"][0])) *
+               (X @ torch.from_numpy(d["w_up"][0]))) @ torch.from_numpy(d["w_down"][0])
+    else:
+        ref = F.linear(F.gelu(F.linear(X, torch.from_numpy(d["w1"][0]).T,
+                                       torch.from_numpy(d["b1"][0]))),
+                       torch.from_numpy(d["w2"][0]).T, torch.from_numpy(d["b2"][0]))
+    np.testing.assert_allclose(res.y, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ P5 ----
+def test_p5_permutation_equivariance():
+    rng = np.random.default_rng(4)
+    T, H, I, E, k = 40, 12, 10, 5, 2
+    d = _tiny_inputs(rng, T, H, I, E)
+    cfg = _cfg(T, H, I, E, k, float(E) / k)     # C = T: no drops possible
+    a = M.forward(d, cfg)
+    perm = rng.permutation(T)
+    d2 = dict(d, x=d["x"][perm])
+    b = M.forward(d2, cfg)
+    assert a.disp.dropped == 0 and b.disp.dropped == 0
+    np.testing.assert_array_equal(b.route.idx, a.route.idx[perm])
+    np.testing.assert_allclose(b.y, a.y[perm], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(b.aux.P, a.aux.P, rtol=1e-14)
+    np.testing.assert_array_equal(b.aux.counts, a.aux.counts)
+    assert abs(b.aux.l_aux - a.aux.l_aux) < 1e-15
+
+
+def test_p5_equivariance_breaks_under_drops_by_design():
+    """With overflow, the token-major drop rule keeps earlier tokens, so a
+    permutation changes which tokens survive (documents that reading)."""
+    E, T, k, H, I = 2, 6, 1, 4, 4
+    rng = np.random.default_rng(5)
+    d = _tiny_inputs(rng, T, H, I, E)
+    d["w_r"] = np.zeros((H, E))                    # every token picks expert 0
+    cfg = _cfg(T, H, I, E, k, 0.5)                 # C = ceil(6*1*0.5/2) = 2
+    a = M.forward(d, cfg)
+    assert a.disp.kept.tolist() == [2, 0] and a.disp.dropped == 4
+    perm = np.array([5, 4, 3, 2, 1, 0])
+    b = M.forward(dict(d, x=d["x"][perm]), cfg)
+    assert not np.allclose(b.y, a.y[perm])
+
+
+# ------------------------------------------------------------------ P6 ----
+def _brute_select(keys, k):
+    T, E = keys.shape
+    idx = np.zeros((T, k), dtype=np.int64)
+    for t in range(T):
+        for e in range(E):
+            rank = sum(1 for e2 in range(E)
+                       if keys[t, e2] > keys[t, e] or (keys[t, e2] == keys[t, e] and e2 < e))
+            if rank < k:
+                idx[t, rank] = e
+    return idx
+
+
+def _brute_positions(idx):
+    T, k = idx.shape
+    flat = [(t, j, idx[t, j]) for t in range(T) for j in range(k)]
+    pos = np.zeros((T, k), dtype=np.int64)
+    for a, (t, j, e) in enumerate(flat):
+        pos[t, j] = sum(1 for b in range(a) if flat[b][2] == e)
+    return pos
+
+
+def _dense_all_experts(d, cfg, idx, w, pos, C):
+    """Every expert on every token, masked by (selected and kept)."""
+    T, E = cfg.T, cfg.E
+    y = np.zeros((T, cfg.H))
+    for e in range(E):
+        _, ye = M.expert_forward(d, cfg.act, e, d["x"])
+        for t in range(T):
+            for j in range(cfg.k):
+                if idx[t, j] == e and pos[t, j] < C:
+                    y[t] += w[t, j] * ye[t]
+    return y
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_p6_brute_force_tiny(case):
+    rng = np.random.default_rng(100 + case)
+    T = int(rng.integers(1, 13))
+    E = int(rng.integers(1, 7))
+    k = int(rng.integers(1, min(3, E) + 1))
+    H, I = int(rng.integers(1, 9)), int(rng.integers(1, 9))
+    act = "swiglu" if case % 2 == 0 else "gelu"
+    cf = float(rng.choice([0.5, 0.75, 1.0, 1.25, 3.0]))
+    d = _tiny_inputs(rng, T, H, I, E, act=act)
+    if case % 3 == 0:
+        # exact ties: quantise router weights and inputs to a coarse grid
+        d["x"] = np.round(d["x"])
+        d["w_r"] = np.round(d["w_r"])
+    cfg = _cfg(T, H, I, E, k, cf, act=act)
+    res = M.forward(d, cfg)
+    idx = _brute_select(res.route.logits, k)
+    np.testing.assert_array_equal(res.route.idx, idx)
+    pos = _brute_positions(idx)
+    C = res.disp.C
+    for t in range(T):
+        for j in range(k):
+            want = idx[t, j] * C + pos[t, j] if pos[t, j] < C else -1
+            assert res.disp.slot[t, j] == want
+    y = _dense_all_experts(d, cfg, idx, res.route.w, pos, C)
+    np.testing.assert_allclose(res.y, y, rtol=1e-12, atol=1e-12)
+
+
+def test_p6_k_equals_E_is_full_softmax_mixture():
+    rng = np.random.default_rng(9)
+    T, H, I, E = 9, 6, 5, 4
+    d = _tiny_inputs(rng, T, H, I, E)
+    cfg = _cfg(T, H, I, E, E, 1.0)       # C = T: nothing dropped
+    res = M.forward(d, cfg)
+    p = M.softmax_rows(d["x"] @ d["w_r"])
+    y = np.zeros((T, H))
+    for e in range(E):
+        _, ye = M.expert_forward(d, "swiglu", e, d["x"])
+        y += p[:, e:e + 1] * ye
+    np.testing.assert_allclose(res.y, y, rtol=1e-12, atol=1e-13)
+
+
+def test_p6_expert_loop_stack_and_sum():
+    """The expert-loop formulation of the Loop-MoE page (discosf.com/news/
+    5228035, section 2.3): per expert, run the masked tokens, stack, sum."""
+    rng = np.random.default_rng(11)
+    T, H, I, E, k = 20, 8, 6, 5, 2
+    d = _tiny_inputs(rng, T, H, I, E)
+    cfg = _cfg(T, H, I, E, k, float(E))
+    res = M.forward(d, cfg)
+    states = np.zeros((E, T, H))
+    for e in range(E):
+        mask = (res.route.idx == e)
+        rows = mask.any(axis=1)
+        if rows.any():
+            _, ye = M.expert_forward(d, "swiglu", e, d["x"][rows])
+            wt = (res.route.w * mask).sum(axis=1)[rows]
+            states[e][rows] = wt[:, None] * ye
+    np.testing.assert_allclose(res.y, states.sum(axis=0), rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------------ P7 ----
+def test_p7_zero_router_closed_forms():
+    T, H, I, E, k = 30, 6, 4, 5, 2
+    rng = np.random.default_rng(12)
+    d = _tiny_inputs(rng, T, H, I, E)
+    d["w_r"] = np.zeros((H, E))
+    cfg = _cfg(T, H, I, E, k, 1.0)              # C = ceil(60/5) = 12
+    res = M.forward(d, cfg)
+    assert np.allclose(res.aux.P, 1.0 / E, rtol=0, atol=1e-15)
+    assert abs(res.aux.l_aux - cfg.alpha) < 1e-15
+    assert np.all(res.route.idx == np.arange(k)[None, :])     # ties -> low index
+    assert np.all(res.aux.f[:k] == 1.0 / k) and np.all(res.aux.f[k:] == 0)
+    C = res.disp.C
+    assert C == 12
+    for t in range(T):
+        for j in range(k):
+            assert (res.disp.slot[t, j] >= 0) == (t < C)
+    assert res.disp.dropped == k * (T - C)
+
+
+def test_p7_bounds_and_two_expert_sigmoid():
+    rng = np.random.default_rng(13)
+    T, H, E = 500, 10, 7
+    d = _tiny_inputs(rng, T, H, 4, E, scale=3.0)
+    r = M.route(d, _cfg(T, H, 4, E, 2, 1.0))
+    a = M.aux_stats(r.idx, r.probs, E, 0.01)
+    assert a.l_aux <= 0.01 * E + 1e-15
+    top = np.take_along_axis(r.logits, r.idx, axis=1)
+    sig = 1.0 / (1.0 + np.exp(-(top[:, 0] - top[:, 1])))
+    np.testing.assert_allclose(r.w[:, 0], sig, rtol=1e-13)
+    # Gumbel mode: slot-0 weight is sigmoid of the key gap over tau
+    cfg = _cfg(T, H, 4, E, 2, 1.0, route="gumbel", seq=20000, seed=77)
+    g = M.route(d, cfg)
+    tau = M.gumbel_temperature(20000)
+    s = np.take_along_axis(g.keys, g.idx, axis=1)
+    np.testing.assert_allclose(g.w[:, 0], 1.0 / (1.0 + np.exp(-(s[:, 0] - s[:, 1]) / tau)),
+                               rtol=1e-13)
+
+
+# ------------------------------------------------------------------ P8 ----
+def test_p8_philox_known_answers():
+    for v in _gold("philox4x32_10_kat.json")["vectors"]:
+        c = [int(h, 16) for h in v["ctr"]]
+        kk = [int(h, 16) for h in v["key"]]
+        out = O.philox4x32_10(*c, *kk)
+        assert [int(o) for o in out] == [int(h, 16) for h in v["out"]]
+
+
+def test_p8_gumbel_moments_and_temperature():
+    g = O.gumbel_noise(2024, 1000, 1000).ravel()
+    assert abs(g.mean() - 0.5772156649) < 0.004
+    assert abs(g.var() - math.pi ** 2 / 6) < 0.01
+    u = O.gumbel_uniform(5, 64, 64)
+    assert u.min() > 0 and u.max() < 1
+    gold = _gold("gumbel_temperature.json")
+    tau = M.gumbel_temperature(gold["seq_len"])
+    assert abs(tau - gold["expected_tau"]) < 1e-12
+    assert abs(tau - gold["page_rounded_value"]) < gold["page_tolerance"]
+
+
+def test_p8_gumbel_selection_ignores_tau():
+    rng = np.random.default_rng(14)
+    d = _tiny_inputs(rng, 300, 8, 4, 9)
+    a = M.route(d, _cfg(300, 8, 4, 9, 2, 1.0, route="gumbel", seq=1, seed=3))
+    b = M.route(d, _cfg(300, 8, 4, 9, 2, 1.0, route="gumbel", seq=10 ** 7, seed=3))
+    np.testing.assert_array_equal(a.idx, b.idx)
+    assert not np.allclose(a.w, b.w)
+
+
+def test_p8_gumbel_counter_layout():
+    """Noise for (t, e) is word 0 at counter (t, e, 0, 0), key (lo, hi)."""
+    seed = (7 << 32) | 11
+    w = O.gumbel_words(seed, 3, 4)
+    for t in range(3):
+        for e in range(4):
+            assert w[t, e] == int(O.philox4x32_10(t, e, 0, 0, 11, 7)[0])
+
+
+# ------------------------------------------------------------------ P9 ----
+def test_p9_activations_against_math():
+    zs = np.linspace(-9, 9, 37)
+    for z, s, g in zip(zs, M.silu(zs), M.gelu_erf(zs)):
+        assert abs(s - z / (1 + math.exp(-z))) <= 1e-15 * max(1, abs(z))
+        assert abs(g - 0.5 * z * (1 + math.erf(z / math.sqrt(2)))) <= 1e-15 * max(1, abs(z))
+    assert M.silu(np.array([0.0]))[0] == 0 and M.gelu_erf(np.array([0.0]))[0] == 0
+
+
+# ------------------------------------------------------------- P10/P11 ----
+def test_p10_all_dropped_token_is_zero_and_p11_idle_expert():
+    T, H, I, E, k = 10, 6, 4, 3, 2
+    rng = np.random.default_rng(15)
+    d = _tiny_inputs(rng, T, H, I, E)
+    d["w_r"] = np.zeros((H, E))           # all tokens pick experts 0, 1
+    cfg = _cfg(T, H, I, E, k, 0.6)        # C = ceil(20*0.6/3) = 4
+    res = M.forward(d, cfg)
+    assert res.disp.C == 4
+    assert res.disp.kept.tolist() == [4, 4, 0]      # expert 2 idle
+    assert np.all(res.y[4:] == 0.0)                 # tokens 4.. fully dropped
+    assert np.all(res.y_disp[2] == 0.0)
+    assert np.any(res.y[:4] != 0.0)
+
+
+# ------------------------------------------------------------- helpers ----
+def test_bf16_rounding_is_nearest_even():
+    vals = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9,
+                     -2.5, 3.0e38, 1e-40], dtype=np.float32)
+    b = bf16_bits_to_f32(f32_to_bf16_bits(vals))
+    assert b[0] == 1.0
+    assert b[1] == 1.0                       # tie -> even (down)
+    assert b[2] == 1.0 + 4 * 2 ** -8         # tie -> even (up)
+    assert b[3] == 1.0
+    assert b[4] == -2.5
+    rel = np.abs(b[5] - vals[5]) / vals[5]
+    assert rel <= 2 ** -9
+    torch = pytest.importorskip("torch")
+    r = np.random.default_rng(0).standard_normal(10000).astype(np.float32)
+    tb = torch.from_numpy(r).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(tb, f32_to_bf16_bits(r))
+
+
+def test_near_tie_detection():
+    keys = np.array([[1.0, 0.99995, 0.5], [1.0, 0.5, 0.49]])
+    assert O.near_tie_tokens(keys, 1).tolist() == [True, False]
+    assert O.near_tie_tokens(keys, 2).tolist() == [False, False]
+
+
+def test_sampled_forward_matches_full():
+    cfg = CONFIGS[1]
+    inp = make_inputs(cfg)
+    full = M.forward(inp, cfg)
+    sample = np.array([0, 5, 17, 63, 31])
+    part = M.forward(inp, cfg, sample=sample)
+    np.testing.assert_allclose(part.y, full.y[sample], rtol=1e-13, atol=1e-15)
+
+
+# ------------------------------------------------- planted mistakes ------
+def _mutants():
+    def topk_high_index(keys, k):
+        order = np.argsort(-keys[:, ::-1], axis=1, kind="stable")
+        return (keys.shape[1] - 1 - order[:, :k]).astype(np.int64)
+
+    def aux_wrong_norm(idx, probs, E, alpha):
+        r = M.AuxResult.__new__(M.AuxResult)
+        T, k = idx.shape
+        counts = np.bincount(idx.ravel(), minlength=E)
+        f = counts / float(T)
+        P = probs.mean(axis=0)
+        return M.AuxResult(counts, f, P, float(alpha * E * np.sum(f * P)))
+
+    def cap_no_k(T, k, E, cf):
+        return int(math.ceil(T * cf / E))
+
+    def swiglu_swapped(xr, wg, wu, wd):
+        h = silu(xr @ wu) * (xr @ wg)
+        return h, h @ wd
+
+    silu = M.silu
+
+    def gelu_no_b2(xr, w1, b1, w2, b2):
+        h = M.gelu_erf(xr @ w1 + b1[None, :])
+        return h, h @ w2
+
+    def combine_renorm(y_disp, slot, w, H):
+        w2 = np.where(slot >= 0, w, 0.0)
+        s = w2.sum(axis=1, keepdims=True)
+        w2 = np.divide(w2, s, out=np.zeros_like(w2), where=s > 0)
+        T, k = slot.shape
+        y = np.zeros((T, H))
+        flat = y_disp.reshape(-1, H)
+        for j in range(k):
+            m = slot[:, j] >= 0
+            y[m] += w2[m, j][:, None] * flat[slot[m, j]]
+        return y
+
+    def renorm_missing(p, idx):
+        return np.take_along_axis(p, idx, axis=1)
+
+    return {"topk_lowest_index": topk_high_index, "aux_stats": aux_wrong_norm,
+            "capacity": cap_no_k, "expert_swiglu": swiglu_swapped,
+            "expert_gelu": gelu_no_b2, "combine": combine_renorm,
+            "renormalise": renorm_missing}
+
+
+PIN_TESTS = [test_p1_weights_sum_to_one, test_p2_worked_example_f1, test_p3_capacity_values,
+             test_p4_single_expert_is_dense_ffn, test_p6_brute_force_tiny,
+             test_p7_zero_router_closed_forms, test_p10_all_dropped_token_is_zero_and_p11_idle_expert]
+
+
+def _run_pins():
+    for fn in PIN_TESTS:
+        if fn is test_p1_weights_sum_to_one:
+            fn("softmax")
+        elif fn is test_p4_single_expert_is_dense_ffn:
+            fn("swiglu")
+            fn("gelu")
+        elif fn is test_p6_brute_force_tiny:
+            for c in range(12):
+                fn(c)
+        else:
+            fn()
+
+
+@pytest.mark.parametrize("name", sorted(_mutants().keys()))
+def test_planted_mistakes_are_caught(name, monkeypatch):
+    """A plausible slip planted in the oracle (on the CPU) fails some pin."""
+    monkeypatch.setattr(M, name, _mutants()[name])
+    with pytest.raises(AssertionError):
+        _run_pins()
