@@ -1,0 +1,203 @@
+/*
+ * moe.h — C ABI of libmoe_mi355x.so: the forward pass of one sparse
+ * Mixture-of-Experts FFN layer on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer is five calls, issued in this order on one HIP stream:
+ *
+ *   moe_route       router logits x.W_r (+b_r), softmax, top-k with
+ *                   renormalised weights (or Gumbel hard top-k);
+ *   moe_aux_stats   load-balancing statistics f_i, p_i and
+ *                   L_aux = alpha * E * sum_i f_i p_i;
+ *   moe_dispatch    capacity-bounded grouping of the token copies by expert;
+ *   moe_expert_ffn  every expert's FFN over its rows (grouped GEMM);
+ *   moe_combine     weighted sum of each token's expert outputs.
+ *
+ * Sources (cited by page and section):
+ *   [P1] LLaMA4-MoE hand-built guide, dpshk.com/news/5809432
+ *   [P2] MoE basics and minimal PyTorch MoELayer, dpshk.com/news/6005940
+ *   [P3] How to Loop MoE: Flatten the Experts, Untie the Attention,
+ *        discosf.com/news/5228035
+ *   [P4] Long-context MoE training on one A100-80G, 2kiu.com/news/5130654
+ *   [P5] pjlab-sys4nlp/llama-moe architecture essay, coreui.cn/article/2610641
+ *
+ * Conventions shared by every call
+ *   - Every array argument is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees or synchronises, and keeps no state
+ *     between calls, so calls on different streams are independent.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *     enqueued; results are valid once the caller synchronises that stream.
+ *   - Arrays are dense and row-major with the shapes given.  Element type is
+ *     bf16 (stored as its 16-bit pattern) or fp32 as `dtype` says; integer
+ *     outputs are int32; probabilities, weights and statistics are fp32.
+ *   - Arguments are validated on the host BEFORE anything is enqueued; on
+ *     any error nothing is enqueued and a status other than MOE_OK is
+ *     returned.  MOE_ERR_LAUNCH reports a failed kernel launch.  Faults that
+ *     only the device can see surface at the caller's synchronisation.
+ *   - Limits: 1 <= k <= MOE_MAX_TOPK, k <= E <= MOE_MAX_EXPERTS, T >= 0.
+ *     For bf16, H and I must be multiples of 256 and 128 (the grouped GEMM's
+ *     tile sizes) and pointers 16-byte aligned; fp32 needs H, I multiples
+ *     of 4.  T = 0 is a valid empty call.
+ *   - The output of a call depends only on its inputs: there are no
+ *     floating-point atomics, so two runs are bitwise identical.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_MAX_EXPERTS 64
+#define MOE_MAX_TOPK 8
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,        /* a required pointer is NULL                 */
+    MOE_ERR_SHAPE = 2,       /* a size is negative, zero or inconsistent   */
+    MOE_ERR_DTYPE = 3,       /* unknown dtype / mode / activation          */
+    MOE_ERR_UNSUPPORTED = 4, /* legal but beyond this library's limits     */
+    MOE_ERR_ALIGN = 5,       /* size or pointer alignment not met          */
+    MOE_ERR_WORKSPACE = 6,   /* workspace missing or too small             */
+    MOE_ERR_LAUNCH = 7       /* the HIP runtime rejected a kernel launch   */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+typedef enum {
+    MOE_ROUTE_SOFTMAX_TOPK = 0,  /* [P2] 2.1 / 3.1, [P5] 3.1            */
+    MOE_ROUTE_GUMBEL_HARD = 1    /* [P4] 2 and 5.2                      */
+} moe_route_mode_t;
+
+typedef enum {
+    MOE_ACT_SWIGLU = 0,      /* (silu(x W1) * (x W3)) W2, no biases      */
+    MOE_ACT_GELU_BIAS = 1    /* gelu_erf(x W1 + b1) W2 + b2 ([P2] 3.1)   */
+} moe_act_t;
+
+/* Expert capacity C = ceil(T * k * cf / E), evaluated in double in that
+ * order ([P2] section 2.4 gives ceil(tokens / experts * cf); the tokens here
+ * are the T*k router assignments, which agrees for k = 1).  Host-only and
+ * pure.  Returns -1 when an argument is out of range (T < 0, k < 1, E < 1,
+ * cf <= 0 or not finite). */
+int64_t moe_capacity(int64_t T, int k, int E, double cf);
+
+/* Static, NUL-terminated text for a status code (never NULL). */
+const char* moe_status_string(int status);
+
+/* Bytes of workspace moe_aux_stats and moe_dispatch need for T tokens,
+ * E experts and top-k (the larger of the two).  0 if arguments are out of
+ * range. */
+size_t moe_workspace_bytes(int64_t T, int E, int k);
+
+/* Router.  [P2] section 2.1 (score = x . W_r, softmax, keep the top-k);
+ * [P2] section 3.1 and [P5] section 3.1 (renormalise the selected weights);
+ * [P4] sections 2 and 5.2 (Gumbel hard top-k, temperature 1 + 1e-4 seq_len).
+ *
+ *   x        [T, H]  dtype       token activations
+ *   w_r      [H, E]  dtype       router weight (x . w_r gives the logits)
+ *   b_r      [E]     fp32|NULL   optional logit bias
+ *   mode     SOFTMAX_TOPK: key = l = x.w_r + b_r; probs = softmax(l);
+ *            GUMBEL_HARD:  key = s = l + g, g = -log(-log u), u from
+ *                          Philox4x32-10 word 0 at counter (t, e, 0, 0) with
+ *                          key (seed & 0xffffffff, seed >> 32) mapped to
+ *                          (word + 0.5) * 2^-32; probs = softmax(s / tau),
+ *                          tau = 1 + 1e-4 * seq_len (seq_len > 0 required).
+ *   topk_idx [T, k]  int32 out   the k largest keys, slot 0 = largest, equal
+ *                                keys ordered by lower expert index first
+ *   topk_w   [T, k]  fp32  out   probs[t, idx] / sum over the k selected
+ *   probs    [T, E]  fp32  out   the row probabilities defined above
+ *   keys     [T, E]  fp32|NULL   optional output of the selection keys
+ * Logits, softmax and weights are computed in fp32 (bf16 products are
+ * exact in fp32; accumulation is fp32). */
+moe_status_t moe_route(void* stream, moe_dtype_t dtype, const void* x,
+                       const void* w_r, const float* b_r, int64_t T, int64_t H,
+                       int E, int k, moe_route_mode_t mode, uint64_t seed,
+                       int64_t seq_len, int32_t* topk_idx, float* topk_w,
+                       float* probs, float* keys);
+
+/* Load-balancing statistics.  [P2] section 2.3 (f_i, p_i and
+ * L_aux = alpha * N * sum f_i p_i; worked example f_1 = 7/8), [P1] 3.2.
+ *
+ *   topk_idx [T, k] int32, probs [T, E] fp32   (outputs of moe_route)
+ *   counts   [E] int32 out   router assignments per expert (before capacity)
+ *   f        [E] fp32  out   counts / (T * k)
+ *   p        [E] fp32  out   mean over tokens of probs[:, e]
+ *   l_aux    [1] fp32  out   alpha * E * sum_e f[e] * p[e]
+ *   ws       workspace of at least moe_workspace_bytes(T, E, k) bytes
+ * Reductions run in a fixed order (fp64 partial sums): deterministic.
+ * With T = 0 every output is zero. */
+moe_status_t moe_aux_stats(void* stream, const int32_t* topk_idx,
+                           const float* probs, int64_t T, int E, int k,
+                           float alpha, int32_t* counts, float* f, float* p,
+                           float* l_aux, void* ws, size_t ws_bytes);
+
+/* Capacity-bounded dispatch.  [P2] section 2.4 (a per-expert capacity;
+ * overflow tokens are dropped), [P1] section 2.4 (group the token copies by
+ * expert id).  Assignment (t, j) takes the next free row of expert
+ * e = topk_idx[t, j], walking assignments in row-major (t, then j) order;
+ * the row index pos is kept when pos < C.
+ *
+ *   x          [T, H]    dtype         token activations
+ *   topk_idx   [T, k]    int32         expert of each assignment (< E)
+ *   C          rows per expert (normally moe_capacity(T, k, E, cf)), >= 0
+ *   x_disp     [E, C, H] dtype  out    x_disp[e, pos] = x[t]; rows >= kept[e]
+ *                                      are left untouched
+ *   slot       [T, k]    int32  out    e * C + pos, or -1 when dropped
+ *   slot_token [E, C]    int32  out    token in that row, or -1
+ *   kept       [E]       int32  out    min(assignments to e, C)
+ *   dropped    [1]       int32  out    number of dropped assignments
+ *   ws         workspace of at least moe_workspace_bytes(T, E, k) bytes
+ * Expert ids outside [0, E) are a caller error (not checked on device). */
+moe_status_t moe_dispatch(void* stream, moe_dtype_t dtype, const void* x,
+                          const int32_t* topk_idx, int64_t T, int64_t H, int E,
+                          int k, int64_t C, void* x_disp, int32_t* slot,
+                          int32_t* slot_token, int32_t* kept, int32_t* dropped,
+                          void* ws, size_t ws_bytes);
+
+/* Expert FFNs as one grouped GEMM over the dispatched rows.
+ * [P2] sections 2.2 and 3.1 (each expert is an FFN; GELU expert with two
+ * biased Linears), [P5] section 2.1 (SwiGLU), [P2] section 4.4 / [P5] 6.3
+ * (merge each expert's tokens into one large matrix product).
+ *
+ *   x_disp [E, C, H] dtype      rows r < kept[e] are used
+ *   kept   [E]       int32      (device) rows per expert, 0 <= kept <= C
+ *   w1     [E, H, I] dtype      SwiGLU gate / GELU first matrix
+ *   w3     [E, H, I] dtype      SwiGLU up matrix; NULL for GELU
+ *   w2     [E, I, H] dtype      down / second matrix
+ *   b1     [E, I]    dtype      GELU first bias (required for GELU)
+ *   b2     [E, H]    dtype|NULL GELU second bias (optional)
+ *   h_ws   [E, C, I] dtype      caller workspace for the hidden activation
+ *   y_disp [E, C, H] fp32  out  expert outputs (fp32 for both dtypes, so
+ *                               the combine rounds only once); rows >=
+ *                               kept[e] untouched
+ * bf16 runs on the matrix cores with fp32 accumulation; h is rounded to bf16
+ * (nearest-even) between the two products.  An expert with kept = 0 is a
+ * valid no-op. */
+moe_status_t moe_expert_ffn(void* stream, moe_dtype_t dtype, moe_act_t act,
+                            const void* x_disp, const int32_t* kept, int E,
+                            int64_t C, int64_t H, int64_t I, const void* w1,
+                            const void* w3, const void* w2, const void* b1,
+                            const void* b2, void* h_ws, void* y_disp);
+
+/* Weighted combine back to token order.  [P1] section 2.4 and [P2]
+ * section 3.1 (each token's output is the weighted sum of its selected
+ * experts' outputs).  Dropped assignments (slot < 0) add nothing and the
+ * other weights are not renormalised; a token with every copy dropped gets
+ * zeros.
+ *
+ *   y_disp [E*C, H] fp32 (moe_expert_ffn's output), slot [T, k] int32,
+ *   topk_w [T, k] fp32
+ *   y      [T, H]   dtype out   (fp32 accumulation, bf16 rounded once)
+ * H must be a multiple of 8. 
+ * Every slot must be -1 or a row index below E*C (not checked on device). */
+moe_status_t moe_combine(void* stream, moe_dtype_t dtype, const void* y_disp,
+                         const int32_t* slot, const float* topk_w, int64_t T,
+                         int64_t H, int k, void* y);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,88 @@
+// Weighted combine of each token's expert outputs back to token order.
+//
+// [P1] LLaMA4-MoE guide (dpshk.com/news/5809432) section 2.4 and [P2] MoE
+//      basics page (dpshk.com/news/6005940) section 3.1: a token's output is
+//      the weighted sum of the outputs of its selected experts.  A dropped
+//      copy (slot < 0) contributes nothing and the remaining weights are
+//      not renormalised.
+//
+// Bandwidth-bound gather: each workgroup owns a few tokens; each lane owns
+// 8 columns of the row, reads them from the k fp32 expert rows through
+// slot[], accumulates in fp32 and writes the row once (bf16 output is
+// rounded once, to nearest-even).
+#include "moe_common.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr int kCThreads = 256;
+constexpr int kCTok = 4;
+
+// Each lane owns 8 consecutive columns: two 16-byte fp32 reads per expert
+// row, one 16-byte bf16 store (or two fp32 stores) per output row.
+template <bool BF16_OUT>
+__global__ __launch_bounds__(kCThreads) void combine_kernel(const float4* __restrict__ yd,
+                                                           const int32_t* __restrict__ slot,
+                                                           const float* __restrict__ w, int64_t T,
+                                                           int k, int row_oct, void* __restrict__ y) {
+    const int64_t t0 = (int64_t)blockIdx.x * kCTok;
+    for (int v = threadIdx.x; v < row_oct; v += kCThreads) {
+#pragma unroll
+        for (int i = 0; i < kCTok; ++i) {
+            const int64_t t = t0 + i;
+            if (t >= T) break;
+            float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
+            for (int j = 0; j < k; ++j) {
+                const int s = slot[t * k + j];
+                if (s < 0) continue;
+                const float wj = w[t * k + j];
+                const float4 q0 = yd[((int64_t)s * row_oct + v) * 2];
+                const float4 q1 = yd[((int64_t)s * row_oct + v) * 2 + 1];
+                a0.x = fmaf(wj, q0.x, a0.x);
+                a0.y = fmaf(wj, q0.y, a0.y);
+                a0.z = fmaf(wj, q0.z, a0.z);
+                a0.w = fmaf(wj, q0.w, a0.w);
+                a1.x = fmaf(wj, q1.x, a1.x);
+                a1.y = fmaf(wj, q1.y, a1.y);
+                a1.z = fmaf(wj, q1.z, a1.z);
+                a1.w = fmaf(wj, q1.w, a1.w);
+            }
+            if (BF16_OUT) {
+                static_cast<uint4*>(y)[t * row_oct + v] =
+                    make_uint4(pack_bf2(a0.x, a0.y), pack_bf2(a0.z, a0.w), pack_bf2(a1.x, a1.y),
+                               pack_bf2(a1.z, a1.w));
+            } else {
+                float4* yo = static_cast<float4*>(y) + (t * row_oct + v) * 2;
+                yo[0] = a0;
+                yo[1] = a1;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+extern "C" moe_status_t moe_combine(void* stream, moe_dtype_t dtype, const void* y_disp,
+                                    const int32_t* slot, const float* topk_w, int64_t T, int64_t H,
+                                    int k, void* y) {
+    if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_DTYPE;
+    if (T < 0 || H <= 0 || k < 1) return MOE_ERR_SHAPE;
+    if (k > MOE_MAX_TOPK || H > (1 << 22) || T * k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    if (H % 8) return MOE_ERR_ALIGN;
+    if (T == 0) return MOE_OK;
+    if (!slot || !topk_w || !y) return MOE_ERR_NULL;
+    if (y_disp && !moe_aligned16(y_disp)) return MOE_ERR_ALIGN;
+    if (!moe_aligned16(y)) return MOE_ERR_ALIGN;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int row_oct = (int)(H / 8);
+    const int64_t grid = (T + kCTok - 1) / kCTok;
+    if (dtype == MOE_BF16)
+        hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)grid), dim3(kCThreads), 0, st,
+                           static_cast<const float4*>(y_disp), slot, topk_w, T, k, row_oct, y);
+    else
+        hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)grid), dim3(kCThreads), 0, st,
+                           static_cast<const float4*>(y_disp), slot, topk_w, T, k, row_oct, y);
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
+}

@@ -1,0 +1,222 @@
+// Capacity-bounded dispatch of token copies into per-expert row buffers.
+//
+// [P2] MoE basics page (dpshk.com/news/6005940) section 2.4: each expert
+//      accepts at most C = ceil(tokens / experts * cf) rows; the excess is
+//      dropped.
+// [P1] LLaMA4-MoE guide (dpshk.com/news/5809432) section 2.4: group the
+//      flattened [T, k] assignments by expert id (a stable sort), then run
+//      each expert on its contiguous group.
+//
+// The stable sort is a counting sort with a deterministic order, so every
+// integer output is reproducible bit for bit:
+//  1. histogram: per block of 4096 assignments, LDS integer counts;
+//  2. scan: one small block turns the per-block counts into per-block
+//     starting rows for every expert (exclusive scan in block order), and
+//     finishes kept[e] = min(count, C) and the dropped total;
+//  3. rank: each wave walks 64 assignments at a time in (t, j) order; a
+//     ballot per distinct expert in the chunk gives each lane its rank among
+//     same-expert lanes; slot and slot_token follow;
+//  4. copy: token-major gather of x rows into x_disp, one 16-byte vector per
+//     lane, each row read once and written to each of its kept slots
+//     (bandwidth-bound; many blocks so all CUs stream).
+#include "moe_common.h"
+
+namespace {
+
+constexpr int kDChunk = 4096;          // assignments per histogram / rank block
+constexpr int kDThreads = 256;
+constexpr int kDWaveSpan = kDChunk / (kDThreads / 64);  // 1024 assignments per wave
+constexpr int kCopyTok = 8;            // tokens per copy block
+
+__global__ __launch_bounds__(kDThreads) void disp_hist_kernel(const int32_t* __restrict__ idx,
+                                                             int64_t A, int E,
+                                                             int32_t* __restrict__ hist) {
+    __shared__ int cnt[MOE_MAX_EXPERTS];
+    if (threadIdx.x < E) cnt[threadIdx.x] = 0;
+    __syncthreads();
+    const int64_t a0 = (int64_t)blockIdx.x * kDChunk;
+    int64_t a1 = a0 + kDChunk;
+    if (a1 > A) a1 = A;
+    for (int64_t a = a0 + threadIdx.x; a < a1; a += kDThreads) {
+        const unsigned e = (unsigned)idx[a];
+        if (e < (unsigned)E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    if (threadIdx.x < E) hist[(size_t)blockIdx.x * E + threadIdx.x] = cnt[threadIdx.x];
+}
+
+__global__ __launch_bounds__(MOE_MAX_EXPERTS) void disp_scan_kernel(const int32_t* __restrict__ hist,
+                                                                   int nb, int E, int64_t C,
+                                                                   int32_t* __restrict__ off,
+                                                                   int32_t* __restrict__ kept,
+                                                                   int32_t* __restrict__ dropped) {
+    __shared__ int64_t over[MOE_MAX_EXPERTS];
+    const int e = threadIdx.x;
+    if (e < E) {
+        int64_t run = 0;
+        for (int b = 0; b < nb; ++b) {
+            off[(size_t)b * E + e] = (int32_t)run;
+            run += hist[(size_t)b * E + e];
+        }
+        kept[e] = (int32_t)(run < C ? run : C);
+        over[e] = run > C ? run - C : 0;
+    }
+    __syncthreads();
+    if (e == 0) {
+        int64_t d = 0;
+        for (int i = 0; i < E; ++i) d += over[i];
+        *dropped = (int32_t)d;
+    }
+}
+
+__global__ __launch_bounds__(kDThreads) void disp_rank_kernel(
+    const int32_t* __restrict__ idx, int64_t A, int E, int k, int64_t C,
+    const int32_t* __restrict__ off, const int32_t* __restrict__ kept, int32_t* __restrict__ slot,
+    int32_t* __restrict__ slot_token) {
+    __shared__ int tot[kDThreads / 64][MOE_MAX_EXPERTS];
+    __shared__ int wbase[kDThreads / 64][MOE_MAX_EXPERTS];
+    constexpr int kChunks = kDWaveSpan / 64;
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int64_t start = (int64_t)blockIdx.x * kDChunk + (int64_t)wave * kDWaveSpan;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    int run = 0;            // lane e: this wave's running count of expert e
+    int rank[kChunks];
+    int my_e[kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+        const int64_t a = start + c * 64 + lane;
+        const bool valid = a < A;
+        const int e = valid ? idx[a] : -1;
+        my_e[c] = e;
+        int r = 0;
+        uint64_t rem = __ballot(valid);
+        while (rem) {
+            const int leader = __ffsll((unsigned long long)rem) - 1;
+            const int ee = __shfl(e, leader, 64);
+            const uint64_t m = __ballot(e == ee);
+            const int base = __shfl(run, ee, 64);
+            if (e == ee) r = base + __popcll(m & lt_mask);
+            if (lane == ee) run += __popcll(m);
+            rem &= ~m;
+        }
+        rank[c] = r;
+    }
+    if (lane < E) tot[wave][lane] = run;
+    __syncthreads();
+    if (threadIdx.x < E) {
+        int acc = ((int64_t)blockIdx.x * kDChunk < A) ? off[(size_t)blockIdx.x * E + threadIdx.x] : 0;
+        for (int w = 0; w < kDThreads / 64; ++w) {
+            wbase[w][threadIdx.x] = acc;
+            acc += tot[w][threadIdx.x];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+        const int64_t a = start + c * 64 + lane;
+        if (a < A) {
+            const int e = my_e[c];
+            if ((unsigned)e >= (unsigned)E) {  // caller error: treated as dropped
+                slot[a] = -1;
+                continue;
+            }
+            const int64_t pos = (int64_t)wbase[wave][e] + rank[c];
+            if (pos < C) {
+                slot[a] = (int32_t)(e * C + pos);
+                slot_token[e * C + pos] = (int32_t)(a / k);
+            } else {
+                slot[a] = -1;
+            }
+        }
+    }
+    // rows past kept[e] carry no token
+    const int64_t total = (int64_t)E * C;
+    for (int64_t q = (int64_t)blockIdx.x * kDThreads + threadIdx.x; q < total;
+         q += (int64_t)gridDim.x * kDThreads) {
+        const int64_t e = q / C, pos = q % C;
+        if (pos >= kept[e]) slot_token[q] = -1;
+    }
+}
+
+// Copy rows in 16-byte vectors: row_vecs vectors per row.
+__global__ __launch_bounds__(kDThreads) void disp_copy_kernel(const uint4* __restrict__ x,
+                                                             const int32_t* __restrict__ slot,
+                                                             int64_t T, int k, int row_vecs,
+                                                             uint4* __restrict__ x_disp) {
+    const int64_t t0 = (int64_t)blockIdx.x * kCopyTok;
+    int nt = kCopyTok;
+    if (t0 + nt > T) nt = (int)(T - t0);
+    for (int v = threadIdx.x; v < row_vecs; v += kDThreads) {
+        uint4 buf[kCopyTok];
+#pragma unroll
+        for (int i = 0; i < kCopyTok; ++i)
+            if (i < nt) buf[i] = x[(t0 + i) * row_vecs + v];
+#pragma unroll
+        for (int i = 0; i < kCopyTok; ++i) {
+            if (i < nt) {
+                for (int j = 0; j < k; ++j) {
+                    const int s = slot[(t0 + i) * k + j];
+                    if (s >= 0) x_disp[(int64_t)s * row_vecs + v] = buf[i];
+                }
+            }
+        }
+    }
+}
+
+int disp_blocks(int64_t A) { return (int)((A + kDChunk - 1) / kDChunk); }
+
+}  // namespace
+
+size_t moe_dispatch_ws_bytes(int64_t T, int E, int k) {
+    const int nb = disp_blocks(T * k);
+    return (size_t)nb * E * 2 * sizeof(int32_t) + 256;
+}
+
+extern "C" moe_status_t moe_dispatch(void* stream, moe_dtype_t dtype, const void* x,
+                                     const int32_t* topk_idx, int64_t T, int64_t H, int E, int k,
+                                     int64_t C, void* x_disp, int32_t* slot, int32_t* slot_token,
+                                     int32_t* kept, int32_t* dropped, void* ws, size_t ws_bytes) {
+    if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_DTYPE;
+    if (T < 0 || H <= 0 || E < 1 || k < 1 || k > E || C < 0) return MOE_ERR_SHAPE;
+    if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+    if (T * k >= ((int64_t)1 << 31) || (int64_t)E * C >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    const int esz = dtype == MOE_BF16 ? 2 : 4;
+    if ((H * esz) % 16) return MOE_ERR_ALIGN;
+    if (!kept || !dropped) return MOE_ERR_NULL;
+    if (T > 0 && (!x || !topk_idx || !slot)) return MOE_ERR_NULL;
+    if (C > 0 && (!slot_token || !x_disp)) return MOE_ERR_NULL;
+    if ((x && !moe_aligned16(x)) || (x_disp && !moe_aligned16(x_disp))) return MOE_ERR_ALIGN;
+    const int64_t A = T * k;
+    const int nb = disp_blocks(A);
+    if (nb > 0 && (!ws || ws_bytes < moe_dispatch_ws_bytes(T, E, k))) return MOE_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t* hist = static_cast<int32_t*>(ws);
+    int32_t* off = hist + (size_t)nb * E;
+    if (nb > 0) {
+        hipLaunchKernelGGL(disp_hist_kernel, dim3(nb), dim3(kDThreads), 0, st, topk_idx, A, E, hist);
+        MOE_CHECK_LAUNCH();
+    }
+    hipLaunchKernelGGL(disp_scan_kernel, dim3(1), dim3(MOE_MAX_EXPERTS), 0, st, hist, nb, E, C, off,
+                       kept, dropped);
+    MOE_CHECK_LAUNCH();
+    if (nb > 0) {
+        hipLaunchKernelGGL(disp_rank_kernel, dim3(nb), dim3(kDThreads), 0, st, topk_idx, A, E, k, C,
+                           off, kept, slot, slot_token);
+        MOE_CHECK_LAUNCH();
+    } else if (C > 0) {
+        // no assignments: every row is empty
+        hipLaunchKernelGGL(disp_rank_kernel, dim3(1), dim3(kDThreads), 0, st, topk_idx, (int64_t)0,
+                           E, k, C, off, kept, slot, slot_token);
+        MOE_CHECK_LAUNCH();
+    }
+    if (T > 0 && C > 0) {
+        const int row_vecs = (int)(H * esz / 16);
+        const int64_t grid = (T + kCopyTok - 1) / kCopyTok;
+        hipLaunchKernelGGL(disp_copy_kernel, dim3((unsigned)grid), dim3(kDThreads), 0, st,
+                           static_cast<const uint4*>(x), slot, T, k, row_vecs,
+                           static_cast<uint4*>(x_disp));
+        MOE_CHECK_LAUNCH();
+    }
+    return MOE_OK;
+}

@@ -1,0 +1,127 @@
+"""The whole layer forward as the five library calls on one stream.
+
+`MoELayerGPU` owns the device weights and every intermediate buffer of one
+layer shape, allocated once, so a forward call enqueues only kernels: no
+allocation, no host synchronisation.  It mirrors the (out, aux_loss) return
+of the minimal MoELayer of the MoE basics page (dpshk.com/news/6005940,
+section 3.1).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+from . import ops
+from .synth import MoEConfig
+
+
+def _to_dev(a: Optional[np.ndarray], dev, dtype: str) -> Optional[torch.Tensor]:
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(dev)
+
+
+@dataclass
+class Buffers:
+    topk_idx: torch.Tensor
+    topk_w: torch.Tensor
+    probs: torch.Tensor
+    keys: torch.Tensor
+    counts: torch.Tensor
+    f: torch.Tensor
+    p: torch.Tensor
+    l_aux: torch.Tensor
+    x_disp: torch.Tensor
+    slot: torch.Tensor
+    slot_token: torch.Tensor
+    kept: torch.Tensor
+    dropped: torch.Tensor
+    h: torch.Tensor
+    y_disp: torch.Tensor
+    y: torch.Tensor
+    ws: torch.Tensor
+
+
+class MoELayerGPU:
+    """Device-resident weights + buffers for one configuration."""
+
+    def __init__(self, cfg: MoEConfig, inputs: Dict[str, np.ndarray], device="cuda:0"):
+        self.cfg = cfg
+        dev = torch.device(device)
+        self.dev = dev
+        self.tdtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        self.w_r = _to_dev(inputs["w_r"], dev, cfg.dtype)
+        self.b_r = _to_dev(inputs.get("b_r"), dev, cfg.dtype)
+        if cfg.act == "swiglu":
+            self.w1 = _to_dev(inputs["w_gate"], dev, cfg.dtype)
+            self.w3 = _to_dev(inputs["w_up"], dev, cfg.dtype)
+            self.w2 = _to_dev(inputs["w_down"], dev, cfg.dtype)
+            self.b1 = self.b2 = None
+        else:
+            self.w1 = _to_dev(inputs["w1"], dev, cfg.dtype)
+            self.w3 = None
+            self.w2 = _to_dev(inputs["w2"], dev, cfg.dtype)
+            self.b1 = _to_dev(inputs["b1"], dev, cfg.dtype)
+            self.b2 = _to_dev(inputs.get("b2"), dev, cfg.dtype)
+        self.C = ops.moe_capacity(cfg.T, cfg.k, cfg.E, cfg.cf)
+        self.buf = self.alloc(cfg.T)
+
+    def alloc(self, T: int) -> Buffers:
+        cfg, dev, C = self.cfg, self.dev, self.C
+        E, k, H, I = cfg.E, cfg.k, cfg.H, cfg.I
+        i32, f32, td = torch.int32, torch.float32, self.tdtype
+        e = lambda *s, dt=f32: torch.empty(s, dtype=dt, device=dev)  # noqa: E731
+        return Buffers(
+            topk_idx=e(T, k, dt=i32), topk_w=e(T, k), probs=e(T, E), keys=e(T, E),
+            counts=e(E, dt=i32), f=e(E), p=e(E), l_aux=e(1),
+            x_disp=e(E, C, H, dt=td), slot=e(T, k, dt=i32), slot_token=e(E, C, dt=i32),
+            kept=e(E, dt=i32), dropped=e(1, dt=i32), h=e(E, C, I, dt=td),
+            y_disp=e(E, C, H), y=e(T, H, dt=td),
+            ws=e(max(1, ops.moe_workspace_bytes(T, E, k)), dt=torch.uint8))
+
+    # the five steps, each one library call ---------------------------------
+    def route(self, x: torch.Tensor, keys: bool = False):
+        b, cfg = self.buf, self.cfg
+        return ops.moe_route(x, self.w_r, self.b_r, cfg.k, mode=cfg.route, seed=cfg.seed,
+                             seq_len=cfg.seq_len, topk_idx=b.topk_idx, topk_w=b.topk_w,
+                             probs=b.probs, keys=b.keys if keys else None)
+
+    def aux(self):
+        b = self.buf
+        return ops.moe_aux_stats(b.topk_idx, b.probs, self.cfg.E, self.cfg.alpha, ws=b.ws,
+                                 counts=b.counts, f=b.f, p=b.p, l_aux=b.l_aux)
+
+    def dispatch(self, x: torch.Tensor, topk_idx: Optional[torch.Tensor] = None):
+        b = self.buf
+        return ops.moe_dispatch(x, b.topk_idx if topk_idx is None else topk_idx, self.cfg.E,
+                                self.C, ws=b.ws, x_disp=b.x_disp, slot=b.slot,
+                                slot_token=b.slot_token, kept=b.kept, dropped=b.dropped)
+
+    def experts(self):
+        b = self.buf
+        return ops.moe_expert_ffn(b.x_disp, b.kept, self.w1, self.w3, self.w2, self.b1, self.b2,
+                                  act=self.cfg.act, h_ws=b.h, y_disp=b.y_disp)
+
+    def combine(self):
+        b = self.buf
+        return ops.moe_combine(b.y_disp, b.slot, b.topk_w, y=b.y)
+
+    def forward(self, x: torch.Tensor, keys: bool = False):
+        """y [T, H] and L_aux [1]; every intermediate stays in self.buf."""
+        self.route(x, keys=keys)
+        self.aux()
+        self.dispatch(x)
+        self.experts()
+        self.combine()
+        return self.buf.y, self.buf.l_aux
+
+
+def x_to_device(inputs: Dict[str, np.ndarray], cfg: MoEConfig, device="cuda:0") -> torch.Tensor:
+    return _to_dev(inputs["x"], torch.device(device), cfg.dtype)

@@ -1,0 +1,155 @@
+"""Python binding of the C ABI: one function per entry point, same names.
+
+Each function only marshals arguments: it checks tensor dtypes, devices and
+contiguity, allocates missing outputs with torch (device memory is the only
+thing torch supplies), passes raw device pointers and the current HIP
+stream to the library, and turns a non-zero status into MoEError.  All
+arithmetic runs in the library's kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from ._lib import ACTS, MOE_BF16, MOE_F32, ROUTE_MODES, check, lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _want(t: Optional[torch.Tensor], shape, dtype, dev) -> torch.Tensor:
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"output must be {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+    return t
+
+
+def moe_capacity(T: int, k: int, E: int, cf: float) -> int:
+    c = lib().moe_capacity(int(T), int(k), int(E), float(cf))
+    if c < 0:
+        raise ValueError("moe_capacity: argument out of range")
+    return int(c)
+
+
+def moe_workspace_bytes(T: int, E: int, k: int) -> int:
+    return int(lib().moe_workspace_bytes(int(T), int(E), int(k)))
+
+
+def moe_route(x: torch.Tensor, w_r: torch.Tensor, b_r: Optional[torch.Tensor], k: int, *,
+              mode: str = "softmax", seed: int = 0, seq_len: int = 0,
+              topk_idx: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
+              probs: Optional[torch.Tensor] = None, keys: Optional[torch.Tensor] = None,
+              want_keys: bool = False
+              ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
+    T, H = x.shape
+    E = w_r.shape[1]
+    dev = x.device
+    topk_idx = _want(topk_idx, (T, k), torch.int32, dev)
+    topk_w = _want(topk_w, (T, k), torch.float32, dev)
+    probs = _want(probs, (T, E), torch.float32, dev)
+    if want_keys or keys is not None:
+        keys = _want(keys, (T, E), torch.float32, dev)
+    if w_r.dtype != x.dtype or tuple(w_r.shape) != (H, E):
+        raise ValueError("w_r must be [H, E] with x's dtype")
+    if b_r is not None and (b_r.dtype != torch.float32 or tuple(b_r.shape) != (E,)):
+        raise ValueError("b_r must be fp32 [E]")
+    st = lib().moe_route(_stream(dev), _dtype_code(x), _ptr(x), _ptr(w_r), _ptr(b_r), T, H, E, k,
+                         ROUTE_MODES[mode], int(seed) & (2 ** 64 - 1), int(seq_len),
+                         _ptr(topk_idx), _ptr(topk_w), _ptr(probs), _ptr(keys))
+    check("moe_route", st)
+    return topk_idx, topk_w, probs, keys
+
+
+def moe_aux_stats(topk_idx: torch.Tensor, probs: torch.Tensor, E: int, alpha: float, *,
+                  ws: Optional[torch.Tensor] = None, counts=None, f=None, p=None, l_aux=None):
+    T, k = topk_idx.shape
+    dev = probs.device
+    counts = _want(counts, (E,), torch.int32, dev)
+    f = _want(f, (E,), torch.float32, dev)
+    p = _want(p, (E,), torch.float32, dev)
+    l_aux = _want(l_aux, (1,), torch.float32, dev)
+    if ws is None:
+        ws = torch.empty(max(1, moe_workspace_bytes(T, E, k)), dtype=torch.uint8, device=dev)
+    st = lib().moe_aux_stats(_stream(dev), _ptr(topk_idx), _ptr(probs), T, E, k, float(alpha),
+                             _ptr(counts), _ptr(f), _ptr(p), _ptr(l_aux), _ptr(ws), ws.numel())
+    check("moe_aux_stats", st)
+    return counts, f, p, l_aux
+
+
+def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, C: int, *,
+                 ws: Optional[torch.Tensor] = None, x_disp=None, slot=None, slot_token=None,
+                 kept=None, dropped=None):
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    dev = x.device
+    x_disp = _want(x_disp, (E, C, H), x.dtype, dev)
+    slot = _want(slot, (T, k), torch.int32, dev)
+    slot_token = _want(slot_token, (E, C), torch.int32, dev)
+    kept = _want(kept, (E,), torch.int32, dev)
+    dropped = _want(dropped, (1,), torch.int32, dev)
+    if ws is None:
+        ws = torch.empty(max(1, moe_workspace_bytes(T, E, k)), dtype=torch.uint8, device=dev)
+    st = lib().moe_dispatch(_stream(dev), _dtype_code(x), _ptr(x), _ptr(topk_idx), T, H, E, k, C,
+                            _ptr(x_disp), _ptr(slot), _ptr(slot_token), _ptr(kept),
+                            _ptr(dropped), _ptr(ws), ws.numel())
+    check("moe_dispatch", st)
+    return x_disp, slot, slot_token, kept, dropped
+
+
+def moe_expert_ffn(x_disp: torch.Tensor, kept: torch.Tensor, w1: torch.Tensor,
+                   w3: Optional[torch.Tensor], w2: torch.Tensor, b1: Optional[torch.Tensor] = None,
+                   b2: Optional[torch.Tensor] = None, *, act: str = "swiglu",
+                   h_ws: Optional[torch.Tensor] = None, y_disp: Optional[torch.Tensor] = None):
+    E, C, H = x_disp.shape
+    I = w1.shape[2]
+    dev = x_disp.device
+    if tuple(w1.shape) != (E, H, I) or tuple(w2.shape) != (E, I, H):
+        raise ValueError("w1 must be [E, H, I] and w2 [E, I, H]")
+    if w3 is not None and tuple(w3.shape) != (E, H, I):
+        raise ValueError("w3 must be [E, H, I]")
+    for t in (w1, w3, w2, b1, b2):
+        if t is not None and t.dtype != x_disp.dtype:
+            raise ValueError("weights and biases must have x_disp's dtype")
+    h_ws = _want(h_ws, (E, C, I), x_disp.dtype, dev)
+    y_disp = _want(y_disp, (E, C, H), torch.float32, dev)
+    st = lib().moe_expert_ffn(_stream(dev), _dtype_code(x_disp), ACTS[act], _ptr(x_disp),
+                              _ptr(kept), E, C, H, I, _ptr(w1), _ptr(w3), _ptr(w2), _ptr(b1),
+                              _ptr(b2), _ptr(h_ws), _ptr(y_disp))
+    check("moe_expert_ffn", st)
+    return y_disp, h_ws
+
+
+def moe_combine(y_disp: torch.Tensor, slot: torch.Tensor, topk_w: torch.Tensor, *,
+                y: Optional[torch.Tensor] = None,
+                out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    H = y_disp.shape[-1]
+    T, k = slot.shape
+    dev = slot.device
+    if y_disp.dtype != torch.float32:
+        raise ValueError("y_disp must be fp32")
+    y = _want(y, (T, H), out_dtype if y is None else y.dtype, dev)
+    st = lib().moe_combine(_stream(dev), _dtype_code(y), _ptr(y_disp), _ptr(slot),
+                           _ptr(topk_w), T, H, k, _ptr(y))
+    check("moe_combine", st)
+    return y

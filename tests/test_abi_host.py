@@ -1,0 +1,173 @@
+"""Host-side checks of the C ABI: exports, capacity, status text, and every
+argument error the library must report before enqueueing anything.  None of
+these calls reaches the GPU, so they run without one."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_08_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, NULL, SHAPE, DTYPE, UNSUP, ALIGN, WS = 0, 1, 2, 3, 4, 5, 6
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+        assert getattr(L, name) is not None
+
+
+def test_capacity(L):
+    assert L.moe_capacity(64, 2, 4, 1.25) == 40
+    assert L.moe_capacity(4096, 2, 8, 1.25) == 1280
+    assert L.moe_capacity(16384, 2, 8, 1.0) == 4096
+    assert L.moe_capacity(8192, 2, 8, 1.25) == 2560
+    assert L.moe_capacity(32768, 2, 32, 1.25) == 2560
+    assert L.moe_capacity(10, 1, 4, 1.0) == 3
+    assert L.moe_capacity(0, 2, 8, 1.25) == 0
+    assert L.moe_capacity(-1, 2, 8, 1.0) == -1
+    assert L.moe_capacity(10, 0, 8, 1.0) == -1
+    assert L.moe_capacity(10, 1, 0, 1.0) == -1
+    assert L.moe_capacity(10, 1, 4, 0.0) == -1
+    assert L.moe_capacity(10, 1, 4, float("nan")) == -1
+
+
+def test_status_strings(L):
+    for s in range(8):
+        assert L.moe_status_string(s)
+    assert L.moe_status_string(99) == b"unknown status"
+    assert L.moe_status_string(0) == b"ok"
+
+
+def test_workspace_bytes(L):
+    assert L.moe_workspace_bytes(32768, 32, 2) > 0
+    assert L.moe_workspace_bytes(0, 8, 2) > 0
+    assert L.moe_workspace_bytes(-1, 8, 2) == 0
+    assert L.moe_workspace_bytes(10, 65, 2) == 0
+    assert L.moe_workspace_bytes(100000, 8, 2) >= L.moe_workspace_bytes(100, 8, 2)
+
+
+P = 0x10000          # a fake, 16-byte aligned "device pointer": never dereferenced
+MIS = 0x10008        # misaligned
+
+
+def route(L, dtype=1, x=P, w=P, b=None, T=64, H=256, E=8, k=2, mode=0, seq=0, outs=(P, P, P)):
+    return L.moe_route(None, dtype, x, w, b, T, H, E, k, mode, 0, seq, outs[0], outs[1], outs[2],
+                       None)
+
+
+def test_route_argument_errors(L):
+    assert route(L, dtype=7) == DTYPE
+    assert route(L, mode=3) == DTYPE
+    assert route(L, T=-1) == SHAPE
+    assert route(L, H=0) == SHAPE
+    assert route(L, E=0) == SHAPE
+    assert route(L, k=0) == SHAPE
+    assert route(L, k=9, E=8) == SHAPE
+    assert route(L, E=65, k=2) == UNSUP
+    assert route(L, E=16, k=9) == UNSUP
+    assert route(L, mode=1, seq=0) == SHAPE
+    assert route(L, x=None) == NULL
+    assert route(L, outs=(P, None, P)) == NULL
+    assert route(L, H=200) == ALIGN
+    assert route(L, x=MIS) == ALIGN
+    assert route(L, dtype=0, H=6) == ALIGN
+    assert route(L, H=256 * 32) == UNSUP           # more than 16 k-steps per wave
+    assert route(L, T=0, x=None, w=None, outs=(None, None, None)) == OK
+
+
+def test_aux_argument_errors(L):
+    a = lambda **kw: L.moe_aux_stats(None, kw.get("idx", P), kw.get("probs", P), kw.get("T", 64),  # noqa
+                                     kw.get("E", 8), kw.get("k", 2), 0.01, kw.get("c", P), P, P, P,
+                                     kw.get("ws", P), kw.get("wsb", 1 << 20))
+    assert a(T=-1) == SHAPE
+    assert a(E=0) == SHAPE
+    assert a(k=3, E=2) == SHAPE
+    assert a(E=70) == UNSUP
+    assert a(c=None) == NULL
+    assert a(idx=None) == NULL
+    assert a(ws=None) == WS
+    assert a(wsb=8) == WS
+
+
+def test_dispatch_argument_errors(L):
+    def d(**kw):
+        return L.moe_dispatch(None, kw.get("dtype", 1), kw.get("x", P), kw.get("idx", P),
+                              kw.get("T", 64), kw.get("H", 256), kw.get("E", 8), kw.get("k", 2),
+                              kw.get("C", 20), kw.get("xd", P), P, P, kw.get("kept", P), P,
+                              kw.get("ws", P), kw.get("wsb", 1 << 20))
+    assert d(dtype=5) == DTYPE
+    assert d(C=-1) == SHAPE
+    assert d(T=-1) == SHAPE
+    assert d(k=9, E=8) == SHAPE
+    assert d(E=100) == UNSUP
+    assert d(H=4) == ALIGN                 # 8 bytes per bf16 row: not a 16-byte multiple
+    assert d(kept=None) == NULL
+    assert d(x=None) == NULL
+    assert d(xd=None) == NULL
+    assert d(x=MIS) == ALIGN
+    assert d(ws=None) == WS
+    assert d(wsb=4) == WS
+
+
+def test_expert_ffn_argument_errors(L):
+    def f(**kw):
+        return L.moe_expert_ffn(None, kw.get("dtype", 1), kw.get("act", 0), kw.get("xd", P),
+                                kw.get("kept", P), kw.get("E", 8), kw.get("C", 64),
+                                kw.get("H", 256), kw.get("I", 256), kw.get("w1", P),
+                                kw.get("w3", P), kw.get("w2", P), kw.get("b1", None),
+                                kw.get("b2", None), kw.get("h", P), kw.get("y", P))
+    assert f(dtype=2) == DTYPE
+    assert f(act=5) == DTYPE
+    assert f(E=0) == SHAPE
+    assert f(C=-1) == SHAPE
+    assert f(H=0) == SHAPE
+    assert f(E=65) == UNSUP
+    assert f(w3=None) == NULL                 # SwiGLU needs the up matrix
+    assert f(act=1, w3=None) == NULL          # GELU needs b1
+    assert f(kept=None) == NULL
+    assert f(h=None) == NULL
+    assert f(H=200) == ALIGN
+    assert f(I=200) == ALIGN
+    assert f(w1=MIS) == ALIGN
+    assert f(C=0, xd=None, h=None, y=None) == OK
+
+
+def test_combine_argument_errors(L):
+    def c(**kw):
+        return L.moe_combine(None, kw.get("dtype", 1), kw.get("yd", P), kw.get("slot", P), P,
+                             kw.get("T", 64), kw.get("H", 256), kw.get("k", 2), kw.get("y", P))
+    assert c(dtype=9) == DTYPE
+    assert c(T=-1) == SHAPE
+    assert c(k=0) == SHAPE
+    assert c(k=9) == UNSUP
+    assert c(H=4) == ALIGN
+    assert c(slot=None) == NULL
+    assert c(y=MIS) == ALIGN
+    assert c(T=0, slot=None, y=None) == OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.lib()
