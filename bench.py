@@ -1,0 +1,224 @@
+"""Benchmark: one sparse-MoE FFN layer forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 2] [--gpus 1]
+
+A step is one whole layer forward (route, aux statistics, dispatch, grouped
+expert GEMM, combine) over one batch of synthetic input that is already
+resident in HBM.  The default workload is the 2 x 2048-token layer (hidden
+2048, SwiGLU intermediate 4096, 8 experts, top-2, capacity factor 1.25, bf16
+with fp32 accumulation).  Prints one JSON line.
+
+Timing:
+  * the timed region is exactly K steps, bracketed by device synchronisation;
+  * inside it, HIP events on the launch stream bracket every phase, so each
+    phase's average duration over the timed region is reported too (the
+    grouped GEMM phase is the dominant kernel pair and gives `roofline`);
+  * memory-bound phases are also timed in isolation after a 1 GiB write that
+    flushes the 256 MB Infinity Cache, so their bytes come from HBM;
+  * the CPU oracle (float64, the reference implementation) is timed on the
+    host cores on one full layer forward of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer fwd tokens/sec + grouped-GEMM % MFMA peak, dispatch % HBM peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--iso-reps", type=int, default=10)
+    return ap.parse_args()
+
+
+def algorithmic_work(cfg, kept: np.ndarray, dropped: int):
+    """Bytes and FLOP each phase must move / compute at minimum."""
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    esz = 2 if cfg.dtype == "bf16" else 4
+    n_kept = int(kept.sum())
+    mult = 6 if cfg.act == "swiglu" else 4
+    ffn_flop = mult * H * I * n_kept
+    route_bytes = T * H * esz + H * E * esz + T * k * 8 + T * E * 4
+    aux_bytes = T * k * 4 + T * E * 4
+    # x read once, each kept row written once, idx read, slot + slot_token written
+    dispatch_bytes = T * H * esz + n_kept * H * esz + T * k * 4 + T * k * 4 + n_kept * 4
+    # kept expert rows (fp32) read once, y written once, slot + weights read
+    combine_bytes = n_kept * H * 4 + T * H * esz + T * k * 8
+    return dict(n_kept=n_kept, ffn_flop=ffn_flop, route_bytes=route_bytes, aux_bytes=aux_bytes,
+                dispatch_bytes=dispatch_bytes, combine_bytes=combine_bytes, dropped=dropped)
+
+
+def cpu_baseline(cfg, inputs):
+    """The CPU oracle as it stands, timed on one full layer forward."""
+    from oracle import moe_oracle as M
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info()]
+    except Exception:  # pragma: no cover
+        blas = []
+    threads = max([n for _, n in blas if n] or [1])
+    t0 = time.perf_counter()
+    res = M.forward(inputs, cfg)
+    dt = time.perf_counter() - t0
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": round(cfg.T / dt, 3), "unit": "tokens/s", "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"one full layer forward of the same workload ({cfg.T} tokens), float64 numpy "
+                  f"with BLAS products; {dt:.2f} s",
+        "affinity_cores": len(os.sched_getaffinity(0)), "cpu": cpu_model, "blas": blas,
+        "phase_s": {k: round(v, 4) for k, v in res.timings.items()},
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs the layer on one GPU only; --gpus {args.gpus} is not "
+              "supported (see the design notes for how the layer would shard)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from mixture_experts_layer_08_amd.layer import MoELayerGPU, x_to_device
+    from mixture_experts_layer_08_amd.synth import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.config]
+    print(f"[bench] generating inputs for {cfg.name}", file=sys.stderr, flush=True)
+    inputs = make_inputs(cfg)
+    dev = "cuda:0"
+    layer = MoELayerGPU(cfg, inputs, dev)
+    x = x_to_device(inputs, cfg, dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        layer.forward(x)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        e = ev[s]
+        e[0].record(stream)
+        layer.route(x)
+        e[1].record(stream)
+        layer.aux()
+        e[2].record(stream)
+        layer.dispatch(x)
+        e[3].record(stream)
+        layer.experts()
+        e[4].record(stream)
+        layer.combine()
+        e[5].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ["route", "aux", "dispatch", "expert_ffn", "combine"]
+    ph = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)]))
+          for i, n in enumerate(names)}
+    dev_ms = float(np.mean([ev[s][0].elapsed_time(ev[s][5]) for s in range(K)]))
+    ms_per_step = wall * 1e3 / K
+    print(f"[bench] timed {K} steps: {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    kept = layer.buf.kept.cpu().numpy()
+    dropped = int(layer.buf.dropped.cpu()[0])
+    work = algorithmic_work(cfg, kept, dropped)
+
+    # memory-bound phases in isolation, after flushing the Infinity Cache
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    iso = {}
+    for n, fn in (("route", lambda: layer.route(x)), ("dispatch", lambda: layer.dispatch(x)),
+                  ("combine", layer.combine)):
+        ts = []
+        for _ in range(args.iso_reps):
+            flush.fill_(1)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        iso[n] = float(np.median(ts))
+    del flush
+    layer.forward(x)        # leave buffers consistent
+    torch.cuda.synchronize()
+
+    gemm_ms = ph["expert_ffn"]
+    achieved_tflops = work["ffn_flop"] / (gemm_ms * 1e-3) / 1e12
+    phases = {}
+    for n, key in (("route", "route_bytes"), ("dispatch", "dispatch_bytes"),
+                   ("combine", "combine_bytes"), ("aux", "aux_bytes")):
+        gbs = work[key] / (ph[n] * 1e-3) / 1e9
+        phases[n] = {"ms": round(ph[n], 5), "bytes": work[key], "GB/s": round(gbs, 1),
+                     "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+        if n in iso:
+            g2 = work[key] / (iso[n] * 1e-3) / 1e9
+            phases[n].update({"ms_cold": round(iso[n], 5), "GB/s_cold": round(g2, 1),
+                              "hbm_frac_cold": round(g2 / PEAK_HBM_GBS, 4)})
+    phases["expert_ffn"] = {"ms": round(gemm_ms, 5), "flop": work["ffn_flop"],
+                            "TFLOP/s": round(achieved_tflops, 2),
+                            "mfma_frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(cfg.T / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: one MoE FFN layer forward, T={cfg.T} "
+                               f"({cfg.batch}x{cfg.seq_len}), H={cfg.H}, I={cfg.I}, E={cfg.E}, "
+                               f"top-{cfg.k}, cf={cfg.cf}, {cfg.act}, {cfg.route} router",
+                   "tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I, "experts": cfg.E,
+                   "top_k": cfg.k, "capacity_factor": cfg.cf,
+                   "capacity": layer.C, "kept_rows": work["n_kept"], "dropped": dropped},
+        "roofline": {"bound": "mfma", "kernel": "grouped expert GEMM (moe_expert_ffn: gate/up "
+                     "product with SwiGLU epilogue, then down product)",
+                     "achieved": round(achieved_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "avg_ms": round(gemm_ms, 5),
+                     "flop_per_launch": work["ffn_flop"]},
+        "phases": phases,
+        "device_ms_per_step": round(dev_ms, 5),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, inputs)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
