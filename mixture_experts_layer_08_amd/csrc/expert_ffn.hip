@@ -12,26 +12,37 @@
 //
 // Design (gfx950): one persistent kernel per product.  The tile list is
 // rebuilt on the device from kept[e] (no host round trip): expert e has
-// ceil(kept[e] / BM) row tiles times N / BN_out column tiles.  Workgroup b
+// ceil(kept[e] / 256) row tiles times N / BN_OUT column tiles.  Workgroup b
 // sits on XCD b % 8; in round r it takes tile r*G + (b % 8)*(G/8) + b/8, so
 // each XCD works through a contiguous run of tiles; runs are ordered expert
 // by expert, in groups that cover every row tile of an expert across a few
-// column tiles, so the A rows and the B panels a group shares stay in that
+// column tiles, so the A rows and B panels a group shares stay in that
 // XCD's L2.
 //
-// Per tile: 4 waves (2 x 2), BK = 64, v_mfma_f32_16x16x32_bf16 with fp32
-// accumulators.  A rows are k-contiguous already.  B = W[e] is n-contiguous
-// ([K, N] row-major), but an MFMA B operand wants 8 consecutive k per lane,
-// so each thread loads an 8 (k) x 8 (n) block as eight 16-byte vectors and
-// transposes it in registers; LDS then holds B as [n][k].  LDS is double
-// buffered (one barrier per k-step); the next k-step's global loads are in
-// flight during the current step's MFMAs.  Epilogues run on the fp32
-// accumulators in registers:
-//   SwiGLU:  a tile holds matching gate and up columns (its B tile is half
-//            W_gate, half W_up), so h = silu(g) * u needs no extra pass;
+// Per tile: 256 x 256 outputs (of the B tile: for SwiGLU 128 gate + 128 up
+// columns), K in steps of 64, 4 waves in a 2 x 2 grid, each wave 128 x 128
+// with 64 v_mfma_f32_16x16x32_bf16 accumulators (fp32, 256 registers).
+//   * Global -> LDS: global_load_lds_dwordx4 writes each lane's 16 bytes
+//     straight into LDS (no staging registers, no VALU); two LDS stages of
+//     64 KB, the next k-step's loads in flight during the current MFMAs,
+//     one barrier per k-step.
+//   * A = x_disp rows are k-contiguous: LDS rows of 128 bytes with the
+//     16-byte chunk index XOR (row & 7), read with ds_read_b128.
+//   * B = W[e] in its own [K, N] layout (n-contiguous).  gfx950's
+//     ds_read_b64_tr_b16 reads 4 k-values of one column per lane straight
+//     from an n-contiguous tile: inside each 16-lane group, lane L points at
+//     row k0 + L/4, columns 4*(L%4) .. +3, and receives rows k0..k0+3 of
+//     column L.  Two such reads make one MFMA B operand, so the weights
+//     need no repacking.  The chunk index of each 512-byte B row is XORed
+//     with 2*(k & 3) + 8*((k >> 3) & 1) so the four rows one 16-lane group
+//     reads fall in different banks.
+// Epilogues run on the fp32 accumulators in registers:
+//   SwiGLU:  a tile holds matching gate and up columns, so
+//            h = silu(g) * u needs no extra pass;
 //   GELU:    h = gelu_erf(acc + b1);   second product: y = acc (+ b2).
-// Results are rounded to bf16 and staged through LDS for full-row 16-byte
-// stores.  Rows at or beyond kept[e] are read as zeros and never stored.
+// h is rounded to bf16, y stays fp32; both are staged through LDS for
+// full-row 16-byte stores.  A rows at or beyond kept[e] are loaded from row
+// kept[e] - 1 (in bounds; those output rows are never stored).
 #include "moe_common.h"
 
 #include <math.h>
@@ -40,11 +51,51 @@ namespace {
 
 using namespace moe;
 
+constexpr int kBM = 256;
+constexpr int kBN = 256;
 constexpr int kBK = 64;
-constexpr int kLdsRow = kBK + 8;  // bf16 per LDS row: 144 bytes, keeps 16-byte alignment
-constexpr int kGThreads = 256;
+constexpr int kGThreads = 512;   // 8 waves: 4 (rows) x 2 (columns), 64 x 128 each
+constexpr int kStageA = kBM * kBK * 2;  // 32 KB
+constexpr int kStageB = kBK * kBN * 2;  // 32 KB
+constexpr int kStage = kStageA + kStageB;
 
 enum { MODE_SWIGLU = 0, MODE_GELU = 1, MODE_DOWN = 2 };
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
+
+// buffer_load_dwordx4 ... lds: each lane's 16 bytes go to LDS at M0 + 16 * lane.
+// Written as asm so the compiler does not add a wait for these LDS writes
+// before unrelated LDS reads of the other stage; the instruction has no
+// register outputs, and the kernel itself waits (vmcnt(0)) and barriers
+// before any wave reads the stage the loads fill.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; nothing else in these kernels uses it
+__device__ __forceinline__ void lds_dma16(i32x4_t rsrc, const void* lds, int voffset, int soffset) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(const lds_void_t*)lds;
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        :
+        : "s"(m0), "v"(voffset), "s"(rsrc), "s"(soffset)
+        : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Buffer resource: 48-bit base, no stride, num_records bytes; loads past the
+// end return zero.  Every argument must be wave-uniform.
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4_t r;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
+    r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+    r.w = 0x00020000;
+    return r;
+}
 
 struct GemmArgs {
     const uint16_t* A;      // [E, C, K]
@@ -64,56 +115,37 @@ __device__ __forceinline__ float gelu_f(float z) {
     return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
 }
 
-// 8x8 bf16 transpose: r[i] holds row i (8 values, 2 per word); returns the
-// column j as 8 values (k = 0..7).
-__device__ __forceinline__ uint4 transpose_col(const uint4 (&r)[8], int j) {
-    uint32_t o[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const uint32_t* a = reinterpret_cast<const uint32_t*>(&r[2 * w]);
-        const uint32_t* b = reinterpret_cast<const uint32_t*>(&r[2 * w + 1]);
-        const uint32_t x = a[j >> 1], y = b[j >> 1];
-        o[w] = (j & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
-    }
-    return make_uint4(o[0], o[1], o[2], o[3]);
-}
+__device__ __forceinline__ int swz_b(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
 
-template <int BM, int BN, int MODE>
-struct Tile {
-    static constexpr int BN_OUT = (MODE == MODE_SWIGLU) ? BN / 2 : BN;
-    static constexpr int WM = BM / 2, WN = BN / 2;          // per-wave tile
-    static constexpr int TM = WM / 16, TN = WN / 16;        // MFMA tiles per wave
-    static constexpr int A_VECS = BM * kBK / 8;             // 16-byte vectors per A tile
-    static constexpr int A_PER_T = (A_VECS + kGThreads - 1) / kGThreads;
-    static constexpr int B_UNITS = (kBK / 8) * (BN / 8);    // 8x8 blocks per B tile
-    static constexpr int B_PER_T = (B_UNITS + kGThreads - 1) / kGThreads;
-    static constexpr size_t LDS_STAGE = (size_t)(BM + BN) * kLdsRow * 2;
-    // second product keeps fp32 outputs; the first rounds h to bf16
+template <int MODE>
+struct Epi {
+    static constexpr int BN_OUT = (MODE == MODE_SWIGLU) ? kBN / 2 : kBN;
     static constexpr int OUT_BYTES = (MODE == MODE_DOWN) ? 4 : 2;
-    static constexpr int OUT_PAD = 16 / OUT_BYTES;
-    static constexpr size_t LDS_OUT = (size_t)BM * (BN_OUT + OUT_PAD) * OUT_BYTES;
-    static constexpr size_t LDS = (2 * LDS_STAGE > LDS_OUT ? 2 * LDS_STAGE : LDS_OUT);
+    static constexpr int ROWS = (MODE == MODE_DOWN) ? kBM / 2 : kBM;  // rows staged per phase
+    static constexpr int LD_BYTES = BN_OUT * OUT_BYTES + 16;
+    static constexpr size_t LDS_OUT = (size_t)ROWS * LD_BYTES;
+    static constexpr size_t LDS = (2 * (size_t)kStage > LDS_OUT) ? 2 * (size_t)kStage : LDS_OUT;
 };
 
-template <int BM, int BN, int MODE>
+template <int MODE>
 __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
-    using TL = Tile<BM, BN, MODE>;
-    constexpr int TM = TL::TM, TN = TL::TN;
+    using EP = Epi<MODE>;
+    constexpr int TM = 4, TN = 8;
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_pref[MOE_MAX_EXPERTS + 1];
     __shared__ int s_mt[MOE_MAX_EXPERTS];
 
     const int tid = threadIdx.x;
-    const int wave = tid / kWave, lane = tid % kWave;
-    const int wm = wave / 2, wn = wave % 2;
-    const int NT = g.N / TL::BN_OUT;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+    const int wm = wave / 2, wn = wave % 2;   // wave rows wm*64.., columns per wn
+    const int NT = g.N / EP::BN_OUT;
     if (tid == 0) {
         int cum = 0;
         for (int e = 0; e < g.E; ++e) {
             int kp = g.kept[e];
             if (kp < 0) kp = 0;
             if (kp > g.C) kp = (int)g.C;
-            const int mt = (kp + BM - 1) / BM;
+            const int mt = (kp + kBM - 1) / kBM;
             s_mt[e] = mt;
             s_pref[e] = cum;
             cum += mt * NT;
@@ -124,13 +156,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
     const int total = s_pref[g.E];
     const int G = gridDim.x;
     const int xcd = blockIdx.x % 8, slot8 = blockIdx.x / 8;
-
-    uint16_t* As[2];
-    uint16_t* Bs[2];
-    As[0] = reinterpret_cast<uint16_t*>(smem);
-    Bs[0] = As[0] + BM * kLdsRow;
-    As[1] = Bs[0] + BN * kLdsRow;
-    Bs[1] = As[1] + BM * kLdsRow;
+    const int nk = g.K / kBK;
 
     for (int round = 0;; ++round) {
         const int logical = round * G + xcd * (G / 8) + slot8;
@@ -151,68 +177,40 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
 
         int kept = g.kept[e];
         if (kept > g.C) kept = (int)g.C;
-        const int m0 = m_tile * BM;
-        const int n0 = n_tile * TL::BN_OUT;  // output column base
-        const uint16_t* Ab = g.A + ((size_t)e * g.C + m0) * g.K;
-        const uint16_t* B0b = g.B0 + (size_t)e * g.K * g.N;
-        const uint16_t* B1b = (MODE == MODE_SWIGLU) ? g.B1 + (size_t)e * g.K * g.N : nullptr;
+        kept = __builtin_amdgcn_readfirstlane(kept);
+        e = __builtin_amdgcn_readfirstlane(e);
+        const int m0 = __builtin_amdgcn_readfirstlane(m_tile * kBM);
+        const int n0 = __builtin_amdgcn_readfirstlane(n_tile * EP::BN_OUT);
 
-        uint4 ra[TL::A_PER_T];
-        uint4 rb[TL::B_PER_T][8];
-
-        auto load_global = [&](int k0) {
+        // A: rows m0.. of expert e; rows at or past kept read as zero
+        const i32x4_t rsA = make_rsrc(g.A + ((size_t)e * g.C + m0) * g.K,
+                                      (uint32_t)((size_t)(kept - m0) * g.K * 2));
+        // B: two 128-column sub-tiles; waves 0-3 fill sub-tile 0, waves 4-7 sub-tile 1
+        const int sub = wave / 4;
+        const uint16_t* bsrc;
+        if (MODE == MODE_SWIGLU)
+            bsrc = (sub == 0 ? g.B0 : g.B1) + (size_t)e * g.K * g.N + n0;
+        else
+            bsrc = g.B0 + (size_t)e * g.K * g.N + n0 + sub * 128;
+        const size_t coloff = (MODE == MODE_SWIGLU) ? (size_t)n0 : (size_t)n0 + sub * 128;
+        const i32x4_t rsB = make_rsrc(bsrc, (uint32_t)(((size_t)g.K * g.N - coloff) * 2));
+        // A load q of this wave: tile row R = (wave*4 + q)*8 + lane/8, chunk
+        // (lane % 8) ^ (R & 7) = (lane % 8) ^ (lane / 8)
+        const int voffA = ((wave * 32 + lane / 8) * g.K + (((lane % 8) ^ (lane / 8)) * 8)) * 2;
+        // B load q: sub-tile row kr = (wave%4)*16 + q*4 + lane/16, chunk
+        // (lane % 16) ^ swz_b(kr); swz_b(kr) = 2*(lane/16) + 8*((q >> 1) & 1)
+        const int voffB0 = ((lane / 16) * g.N + (((lane % 16) ^ ((lane / 16) << 1)) * 8)) * 2;
+        const int voffB1 = ((lane / 16) * g.N + (((lane % 16) ^ (((lane / 16) << 1) | 8)) * 8)) * 2;
+        auto issue = [&](int kt, int stage) {
+            unsigned char* st = smem + stage * kStage;
 #pragma unroll
-            for (int i = 0; i < TL::A_PER_T; ++i) {
-                const int v = tid + i * kGThreads;
-                if (v < TL::A_VECS) {
-                    const int row = v / (kBK / 8), kc = v % (kBK / 8);
-                    if (m0 + row < kept)
-                        ra[i] = *reinterpret_cast<const uint4*>(Ab + (size_t)row * g.K + k0 + kc * 8);
-                    else
-                        ra[i] = make_uint4(0, 0, 0, 0);
-                }
-            }
+            for (int q = 0; q < 4; ++q)
+                lds_dma16(rsA, st + (wave * 4 + q) * 1024, voffA, (q * 8 * g.K + kt * kBK) * 2);
 #pragma unroll
-            for (int i = 0; i < TL::B_PER_T; ++i) {
-                const int u = tid + i * kGThreads;
-                if (u < TL::B_UNITS) {
-                    const int kb = u / (BN / 8), nb = u % (BN / 8);
-                    const uint16_t* src;
-                    if (MODE == MODE_SWIGLU) {
-                        const int half = BN / 16;  // 8-column groups per half
-                        src = (nb < half) ? B0b + n0 + nb * 8 : B1b + n0 + (nb - half) * 8;
-                    } else {
-                        src = B0b + n0 + nb * 8;
-                    }
-                    src += (size_t)(k0 + kb * 8) * g.N;
-#pragma unroll
-                    for (int r = 0; r < 8; ++r)
-                        rb[i][r] = *reinterpret_cast<const uint4*>(src + (size_t)r * g.N);
-                }
-            }
-        };
-        auto store_lds = [&](int buf) {
-            uint16_t* as = As[buf];
-            uint16_t* bs = Bs[buf];
-#pragma unroll
-            for (int i = 0; i < TL::A_PER_T; ++i) {
-                const int v = tid + i * kGThreads;
-                if (v < TL::A_VECS) {
-                    const int row = v / (kBK / 8), kc = v % (kBK / 8);
-                    *reinterpret_cast<uint4*>(as + row * kLdsRow + kc * 8) = ra[i];
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < TL::B_PER_T; ++i) {
-                const int u = tid + i * kGThreads;
-                if (u < TL::B_UNITS) {
-                    const int kb = u / (BN / 8), nb = u % (BN / 8);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        *reinterpret_cast<uint4*>(bs + (nb * 8 + j) * kLdsRow + kb * 8) =
-                            transpose_col(rb[i], j);
-                }
-            }
+            for (int q = 0; q < 4; ++q)
+                lds_dma16(rsB, st + kStageA + (sub * 16 + (wave % 4) * 4 + q) * 1024,
+                          ((q >> 1) & 1) ? voffB1 : voffB0,
+                          (((wave % 4) * 16 + q * 4 + kt * kBK) * g.N) * 2);
         };
 
         f32x4_t acc[TM][TN];
@@ -221,93 +219,109 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
 #pragma unroll
             for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        // B column (LDS row) of this wave's n-tile j
-        auto bcol = [&](int j) {
-            if (MODE == MODE_SWIGLU) {
-                constexpr int q = BN / 4;  // columns per wave per half
-                return (j < TN / 2) ? wn * q + j * 16 : BN / 2 + wn * q + (j - TN / 2) * 16;
-            }
-            return wn * (BN / 2) + j * 16;
-        };
-
-        const int nk = g.K / kBK;
-        load_global(0);
-        store_lds(0);
-        __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            const int cur = kt & 1;
-            if (kt + 1 < nk) load_global((kt + 1) * kBK);
-            const uint16_t* as = As[cur];
-            const uint16_t* bs = Bs[cur];
+        auto compute = [&](int stage) {
+            const unsigned char* As = smem + stage * kStage;
+            const unsigned char* Bs = As + kStageA;
 #pragma unroll
             for (int kk = 0; kk < kBK / 32; ++kk) {
-                const int koff = kk * 32 + (lane / 16) * 8;
                 bf16x8_t af[TM], bfr[TN];
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
-                    af[i] = as_bf16x8(*reinterpret_cast<const uint4*>(
-                        as + (wm * TL::WM + i * 16 + lane % 16) * kLdsRow + koff));
+                for (int i = 0; i < TM; ++i) {
+                    const int row = wm * 64 + i * 16 + lane % 16;
+                    const int phys = (kk * 4 + lane / 16) ^ (row & 7);
+                    af[i] = as_bf16x8(*reinterpret_cast<const uint4*>(As + row * 128 + phys * 16));
+                }
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    bfr[j] = as_bf16x8(*reinterpret_cast<const uint4*>(
-                        bs + (bcol(j) + lane % 16) * kLdsRow + koff));
+                for (int j = 0; j < TN; ++j) {
+                    int sb, col;  // B sub-tile and column inside it
+                    if (MODE == MODE_SWIGLU) {
+                        sb = (j < TN / 2) ? 0 : 1;
+                        col = wn * 64 + (j % (TN / 2)) * 16;
+                    } else {
+                        sb = wn;
+                        col = j * 16;
+                    }
+                    col += 4 * (lane % 4);
+                    i16x4_t v[2];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int kr = kk * 32 + (lane / 16) * 8 + h * 4 + (lane % 16) / 4;
+                        const int phys = (col >> 3) ^ swz_b(kr);
+                        v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(
+                            Bs + sb * (kStageB / 2) + kr * 256 + phys * 16 + (col & 7) * 2));
+                    }
+                    const uint2 lo = __builtin_bit_cast(uint2, v[0]);
+                    const uint2 hi = __builtin_bit_cast(uint2, v[1]);
+                    bfr[j] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+                }
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j],
+                                                                            0, 0, 0);
             }
-            if (kt + 1 < nk) store_lds(cur ^ 1);
+        };
+        // The next k-step's loads are issued right after the barrier that
+        // frees their stage; the last k-step is peeled so the loop body has no
+        // branch (keeps the accumulators in place across iterations).
+        issue(0, 0);
+        for (int kt = 0; kt + 1 < nk; ++kt) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
+            issue(kt + 1, (kt + 1) & 1);
+            compute(kt & 1);
         }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        compute((nk - 1) & 1);
+        __syncthreads();  // every wave is done with the stages: LDS is reused below
 
-        // epilogue: activation in registers, bf16 tile in LDS, row stores
-        uint16_t* os = reinterpret_cast<uint16_t*>(smem);
-        float* osf = reinterpret_cast<float*>(smem);
-        constexpr int ldo = TL::BN_OUT + TL::OUT_PAD;
+        // epilogue: activation in registers, tile staged in LDS, row stores
         const uint16_t* biasb = g.bias ? g.bias + (size_t)e * g.N + n0 : nullptr;
         constexpr int TNO = (MODE == MODE_SWIGLU) ? TN / 2 : TN;
+        constexpr int PHASES = (MODE == MODE_DOWN) ? 2 : 1;
+        constexpr int vec_per_row = EP::BN_OUT * EP::OUT_BYTES / 16;
+        for (int ph = 0; ph < PHASES; ++ph) {
+            if (PHASES == 1 || wm / 2 == ph) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
+                for (int i = 0; i < TM; ++i) {
 #pragma unroll
-            for (int j = 0; j < TNO; ++j) {
-                int ocol;
-                if (MODE == MODE_SWIGLU)
-                    ocol = wn * (BN / 4) + j * 16 + lane % 16;
-                else
-                    ocol = wn * (BN / 2) + j * 16 + lane % 16;
-                float bv = 0.f;
-                if (MODE != MODE_SWIGLU && biasb) bv = bf2f(biasb[ocol]);
+                    for (int j = 0; j < TNO; ++j) {
+                        const int ocol = (MODE == MODE_SWIGLU ? wn * 64 : wn * 128) + j * 16 + lane % 16;
+                        float bv = 0.f;
+                        if (MODE != MODE_SWIGLU && biasb) bv = bf2f(biasb[ocol]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int orow = wm * TL::WM + i * 16 + (lane / 16) * 4 + r;
-                    float v;
-                    if (MODE == MODE_SWIGLU)
-                        v = silu_f(acc[i][j][r]) * acc[i][j + TN / 2][r];
-                    else if (MODE == MODE_GELU)
-                        v = gelu_f(acc[i][j][r] + bv);
-                    else
-                        v = acc[i][j][r] + bv;
-                    if (MODE == MODE_DOWN)
-                        osf[orow * ldo + ocol] = v;
-                    else
-                        os[orow * ldo + ocol] = (uint16_t)f2bf(v);
+                        for (int r = 0; r < 4; ++r) {
+                            const int orow = (PHASES == 1 ? wm : wm % 2) * 64 + i * 16 + (lane / 16) * 4 + r;
+                            float v;
+                            if (MODE == MODE_SWIGLU)
+                                v = silu_f(acc[i][j][r]) * acc[i][j + TN / 2][r];
+                            else if (MODE == MODE_GELU)
+                                v = gelu_f(acc[i][j][r] + bv);
+                            else
+                                v = acc[i][j][r] + bv;
+                            unsigned char* dst = smem + orow * EP::LD_BYTES + ocol * EP::OUT_BYTES;
+                            if (MODE == MODE_DOWN)
+                                *reinterpret_cast<float*>(dst) = v;
+                            else
+                                *reinterpret_cast<uint16_t*>(dst) = (uint16_t)f2bf(v);
+                        }
+                    }
                 }
             }
+            __syncthreads();
+            const int row0 = m0 + ph * EP::ROWS;
+            unsigned char* ob = static_cast<unsigned char*>(g.out) +
+                                (((size_t)e * g.C + row0) * g.N + n0) * EP::OUT_BYTES;
+            for (int v = tid; v < EP::ROWS * vec_per_row; v += kGThreads) {
+                const int row = v / vec_per_row, c = v % vec_per_row;
+                if (row0 + row < kept)
+                    *reinterpret_cast<uint4*>(ob + (size_t)row * g.N * EP::OUT_BYTES + c * 16) =
+                        *reinterpret_cast<const uint4*>(smem + row * EP::LD_BYTES + c * 16);
+            }
+            __syncthreads();
         }
-        __syncthreads();
-        constexpr int el_per_vec = 16 / TL::OUT_BYTES;
-        constexpr int vec_per_row = TL::BN_OUT / el_per_vec;
-        unsigned char* ob = static_cast<unsigned char*>(g.out) +
-                            (((size_t)e * g.C + m0) * g.N + n0) * TL::OUT_BYTES;
-        for (int v = tid; v < BM * vec_per_row; v += kGThreads) {
-            const int row = v / vec_per_row, c = v % vec_per_row;
-            if (m0 + row < kept)
-                *reinterpret_cast<uint4*>(ob + ((size_t)row * g.N + c * el_per_vec) * TL::OUT_BYTES) =
-                    *reinterpret_cast<const uint4*>(smem + ((size_t)row * ldo + c * el_per_vec) *
-                                                               TL::OUT_BYTES);
-        }
-        __syncthreads();
     }
 }
 
@@ -369,26 +383,22 @@ int num_cus() {
     return n;
 }
 
-template <int BM, int BN, int MODE>
+template <int MODE>
 moe_status_t launch_gemm(const GemmArgs& a, hipStream_t st) {
-    using TL = Tile<BM, BN, MODE>;
-    auto kern = grouped_gemm_kernel<BM, BN, MODE>;
+    using EP = Epi<MODE>;
+    auto kern = grouped_gemm_kernel<MODE>;
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)TL::LDS) != hipSuccess)
+                            (int)EP::LDS) != hipSuccess)
         return MOE_ERR_LAUNCH;
-    const int64_t max_tiles = (int64_t)a.E * ((a.C + BM - 1) / BM) * (a.N / TL::BN_OUT);
-    const int per_cu = TL::LDS <= 80 * 1024 ? 2 : 1;
-    int64_t grid = (int64_t)num_cus() * per_cu;
+    const int64_t max_tiles = (int64_t)a.E * ((a.C + kBM - 1) / kBM) * (a.N / EP::BN_OUT);
+    int64_t grid = num_cus();
     if (grid > max_tiles) grid = (max_tiles + 7) / 8 * 8;
     grid = grid / 8 * 8;
     if (grid < 8) grid = 8;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kGThreads), TL::LDS, st, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kGThreads), EP::LDS, st, a);
     MOE_CHECK_LAUNCH();
     return MOE_OK;
 }
-
-constexpr int kBM = 256;
-constexpr int kBN = 128;
 
 }  // namespace
 
@@ -432,6 +442,7 @@ extern "C" moe_status_t moe_expert_ffn(void* stream, moe_dtype_t dtype, moe_act_
     // bf16: K steps of 64; output tiles of 128 (SwiGLU h) or 256 columns
     if (H % kBN || I % kBK) return MOE_ERR_ALIGN;
     if (act == MOE_ACT_SWIGLU ? (I % (kBN / 2)) : (I % kBN)) return MOE_ERR_ALIGN;
+    if (C > (1 << 30) / 8) return MOE_ERR_UNSUPPORTED;
     const void* ptrs[] = {x_disp, w1, w3, w2, b1, b2, h_ws, y_disp};
     for (const void* q : ptrs)
         if (q && !moe_aligned16(q)) return MOE_ERR_ALIGN;
@@ -446,8 +457,8 @@ extern "C" moe_status_t moe_expert_ffn(void* stream, moe_dtype_t dtype, moe_act_
     a1.C = C;
     a1.K = (int)H;
     a1.N = (int)I;
-    moe_status_t s = act == MOE_ACT_SWIGLU ? launch_gemm<kBM, kBN, MODE_SWIGLU>(a1, st)
-                                           : launch_gemm<kBM, kBN, MODE_GELU>(a1, st);
+    moe_status_t s = act == MOE_ACT_SWIGLU ? launch_gemm<MODE_SWIGLU>(a1, st)
+                                           : launch_gemm<MODE_GELU>(a1, st);
     if (s != MOE_OK) return s;
     GemmArgs a2 = a1;
     a2.A = static_cast<const uint16_t*>(h_ws);
@@ -457,5 +468,5 @@ extern "C" moe_status_t moe_expert_ffn(void* stream, moe_dtype_t dtype, moe_act_
     a2.out = y_disp;
     a2.K = (int)I;
     a2.N = (int)H;
-    return launch_gemm<kBM, kBN, MODE_DOWN>(a2, st);
+    return launch_gemm<MODE_DOWN>(a2, st);
 }
