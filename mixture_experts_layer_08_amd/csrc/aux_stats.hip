@@ -18,7 +18,7 @@
 namespace {
 
 constexpr int kAuxThreads = 256;
-constexpr int kAuxTokPerBlock = 512;
+constexpr int kAuxTokPerBlock = 64;
 
 __global__ __launch_bounds__(kAuxThreads) void aux_partial_kernel(const int32_t* __restrict__ idx,
                                                                  const float* __restrict__ probs,
@@ -61,7 +61,22 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void aux_final_kernel(
     if (e < E) {
         int64_t c = 0;
         double s = 0.0;
-        for (int b = 0; b < nblocks; ++b) {
+        int b = 0;
+        for (; b + 8 <= nblocks; b += 8) {  // eight independent loads in flight, summed in order
+            int cc[8];
+            double ss[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                cc[u] = ws_cnt[(size_t)(b + u) * E + e];
+                ss[u] = ws_sum[(size_t)(b + u) * E + e];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                c += cc[u];
+                s += ss[u];
+            }
+        }
+        for (; b < nblocks; ++b) {
             c += ws_cnt[(size_t)b * E + e];
             s += ws_sum[(size_t)b * E + e];
         }

@@ -26,36 +26,57 @@ __global__ __launch_bounds__(kCThreads) void combine_kernel(const float4* __rest
                                                            const int32_t* __restrict__ slot,
                                                            const float* __restrict__ w, int64_t T,
                                                            int k, int row_oct, void* __restrict__ y) {
+    __shared__ int s_slot[kCTok * MOE_MAX_TOPK];
+    __shared__ float s_w[kCTok * MOE_MAX_TOPK];
     const int64_t t0 = (int64_t)blockIdx.x * kCTok;
+    int nt = kCTok;
+    if (t0 + nt > T) nt = (int)(T - t0);
+    for (int q = threadIdx.x; q < nt * k; q += kCThreads) {
+        s_slot[q] = slot[t0 * k + q];
+        s_w[q] = w[t0 * k + q];
+    }
+    __syncthreads();
     for (int v = threadIdx.x; v < row_oct; v += kCThreads) {
+        float4 a0[kCTok], a1[kCTok];
+#pragma unroll
+        for (int i = 0; i < kCTok; ++i) a0[i] = a1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < k; ++j) {
+            float4 q0[kCTok], q1[kCTok];
+#pragma unroll
+            for (int i = 0; i < kCTok; ++i) {  // the row loads of all tokens are in flight together
+                const int s = i < nt ? s_slot[i * k + j] : -1;
+                if (s >= 0) {
+                    q0[i] = yd[((int64_t)s * row_oct + v) * 2];
+                    q1[i] = yd[((int64_t)s * row_oct + v) * 2 + 1];
+                } else {
+                    q0[i] = q1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kCTok; ++i) {
+                const float wj = i < nt ? s_w[i * k + j] : 0.f;
+                a0[i].x = fmaf(wj, q0[i].x, a0[i].x);
+                a0[i].y = fmaf(wj, q0[i].y, a0[i].y);
+                a0[i].z = fmaf(wj, q0[i].z, a0[i].z);
+                a0[i].w = fmaf(wj, q0[i].w, a0[i].w);
+                a1[i].x = fmaf(wj, q1[i].x, a1[i].x);
+                a1[i].y = fmaf(wj, q1[i].y, a1[i].y);
+                a1[i].z = fmaf(wj, q1[i].z, a1[i].z);
+                a1[i].w = fmaf(wj, q1[i].w, a1[i].w);
+            }
+        }
 #pragma unroll
         for (int i = 0; i < kCTok; ++i) {
+            if (i >= nt) break;
             const int64_t t = t0 + i;
-            if (t >= T) break;
-            float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
-            for (int j = 0; j < k; ++j) {
-                const int s = slot[t * k + j];
-                if (s < 0) continue;
-                const float wj = w[t * k + j];
-                const float4 q0 = yd[((int64_t)s * row_oct + v) * 2];
-                const float4 q1 = yd[((int64_t)s * row_oct + v) * 2 + 1];
-                a0.x = fmaf(wj, q0.x, a0.x);
-                a0.y = fmaf(wj, q0.y, a0.y);
-                a0.z = fmaf(wj, q0.z, a0.z);
-                a0.w = fmaf(wj, q0.w, a0.w);
-                a1.x = fmaf(wj, q1.x, a1.x);
-                a1.y = fmaf(wj, q1.y, a1.y);
-                a1.z = fmaf(wj, q1.z, a1.z);
-                a1.w = fmaf(wj, q1.w, a1.w);
-            }
             if (BF16_OUT) {
                 static_cast<uint4*>(y)[t * row_oct + v] =
-                    make_uint4(pack_bf2(a0.x, a0.y), pack_bf2(a0.z, a0.w), pack_bf2(a1.x, a1.y),
-                               pack_bf2(a1.z, a1.w));
+                    make_uint4(pack_bf2(a0[i].x, a0[i].y), pack_bf2(a0[i].z, a0[i].w),
+                               pack_bf2(a1[i].x, a1[i].y), pack_bf2(a1[i].z, a1[i].w));
             } else {
                 float4* yo = static_cast<float4*>(y) + (t * row_oct + v) * 2;
-                yo[0] = a0;
-                yo[1] = a1;
+                yo[0] = a0[i];
+                yo[1] = a1[i];
             }
         }
     }

@@ -9,7 +9,7 @@
 //
 // The stable sort is a counting sort with a deterministic order, so every
 // integer output is reproducible bit for bit:
-//  1. histogram: per block of 4096 assignments, LDS integer counts;
+//  1. histogram: per block of 256 assignments, LDS integer counts;
 //  2. scan: one small block turns the per-block counts into per-block
 //     starting rows for every expert (exclusive scan in block order), and
 //     finishes kept[e] = min(count, C) and the dropped total;
@@ -23,9 +23,9 @@
 
 namespace {
 
-constexpr int kDChunk = 4096;          // assignments per histogram / rank block
+constexpr int kDChunk = 256;           // assignments per histogram / rank block
 constexpr int kDThreads = 256;
-constexpr int kDWaveSpan = kDChunk / (kDThreads / 64);  // 1024 assignments per wave
+constexpr int kDWaveSpan = kDChunk / (kDThreads / 64);  // 64 assignments per wave
 constexpr int kCopyTok = 8;            // tokens per copy block
 
 __global__ __launch_bounds__(kDThreads) void disp_hist_kernel(const int32_t* __restrict__ idx,
@@ -54,7 +54,18 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void disp_scan_kernel(const int32_
     const int e = threadIdx.x;
     if (e < E) {
         int64_t run = 0;
-        for (int b = 0; b < nb; ++b) {
+        int b = 0;
+        for (; b + 8 <= nb; b += 8) {  // eight independent loads in flight
+            int h[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) h[u] = hist[(size_t)(b + u) * E + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                off[(size_t)(b + u) * E + e] = (int32_t)run;
+                run += h[u];
+            }
+        }
+        for (; b < nb; ++b) {
             off[(size_t)b * E + e] = (int32_t)run;
             run += hist[(size_t)b * E + e];
         }

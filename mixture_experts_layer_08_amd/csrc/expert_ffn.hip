@@ -47,6 +47,10 @@
 
 #include <math.h>
 
+#ifndef GEMM_WAVES
+#define GEMM_WAVES 8
+#endif
+
 namespace {
 
 using namespace moe;
@@ -54,7 +58,8 @@ using namespace moe;
 constexpr int kBM = 256;
 constexpr int kBN = 256;
 constexpr int kBK = 64;
-constexpr int kGThreads = 512;   // 8 waves: 4 (rows) x 2 (columns), 64 x 128 each
+constexpr int kNW = GEMM_WAVES;  // waves per workgroup: 2 column halves x kNW/2 row blocks
+constexpr int kGThreads = kNW * 64;
 constexpr int kStageA = kBM * kBK * 2;  // 32 KB
 constexpr int kStageB = kBK * kBN * 2;  // 32 KB
 constexpr int kStage = kStageA + kStageB;
@@ -62,6 +67,7 @@ constexpr int kStage = kStageA + kStageB;
 enum { MODE_SWIGLU = 0, MODE_GELU = 1, MODE_DOWN = 2 };
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
@@ -130,14 +136,16 @@ struct Epi {
 template <int MODE>
 __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     using EP = Epi<MODE>;
-    constexpr int TM = 4, TN = 8;
+    constexpr int WM_ROWS = kBM / (kNW / 2);  // rows per wave
+    constexpr int TM = WM_ROWS / 32, TN = 4;  // 32 x 32 MFMA tiles per wave (WM_ROWS x 128)
+    constexpr int QA = 32 / kNW;              // 1 KB A (and B) loads per wave per k-step
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_pref[MOE_MAX_EXPERTS + 1];
     __shared__ int s_mt[MOE_MAX_EXPERTS];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
-    const int wm = wave / 2, wn = wave % 2;   // wave rows wm*64.., columns per wn
+    const int wm = wave / 2, wn = wave % 2;   // wave rows wm*WM_ROWS.., columns per wn
     const int NT = g.N / EP::BN_OUT;
     if (tid == 0) {
         int cum = 0;
@@ -185,8 +193,8 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
         // A: rows m0.. of expert e; rows at or past kept read as zero
         const i32x4_t rsA = make_rsrc(g.A + ((size_t)e * g.C + m0) * g.K,
                                       (uint32_t)((size_t)(kept - m0) * g.K * 2));
-        // B: two 128-column sub-tiles; waves 0-3 fill sub-tile 0, waves 4-7 sub-tile 1
-        const int sub = wave / 4;
+        // B: two 128-column sub-tiles; the first half of the waves fills sub-tile 0
+        const int sub = wave / (kNW / 2);
         const uint16_t* bsrc;
         if (MODE == MODE_SWIGLU)
             bsrc = (sub == 0 ? g.B0 : g.B1) + (size_t)e * g.K * g.N + n0;
@@ -194,87 +202,122 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
             bsrc = g.B0 + (size_t)e * g.K * g.N + n0 + sub * 128;
         const size_t coloff = (MODE == MODE_SWIGLU) ? (size_t)n0 : (size_t)n0 + sub * 128;
         const i32x4_t rsB = make_rsrc(bsrc, (uint32_t)(((size_t)g.K * g.N - coloff) * 2));
-        // A load q of this wave: tile row R = (wave*4 + q)*8 + lane/8, chunk
+        // A load q of this wave: tile row R = (wave*QA + q)*8 + lane/8, chunk
         // (lane % 8) ^ (R & 7) = (lane % 8) ^ (lane / 8)
-        const int voffA = ((wave * 32 + lane / 8) * g.K + (((lane % 8) ^ (lane / 8)) * 8)) * 2;
-        // B load q: sub-tile row kr = (wave%4)*16 + q*4 + lane/16, chunk
+        const int voffA = ((wave * QA * 8 + lane / 8) * g.K + (((lane % 8) ^ (lane / 8)) * 8)) * 2;
+        // B load q: sub-tile row kr = ((wave % (kNW/2))*QA + q)*4 + lane/16, chunk
         // (lane % 16) ^ swz_b(kr); swz_b(kr) = 2*(lane/16) + 8*((q >> 1) & 1)
         const int voffB0 = ((lane / 16) * g.N + (((lane % 16) ^ ((lane / 16) << 1)) * 8)) * 2;
         const int voffB1 = ((lane / 16) * g.N + (((lane % 16) ^ (((lane / 16) << 1) | 8)) * 8)) * 2;
         auto issue = [&](int kt, int stage) {
             unsigned char* st = smem + stage * kStage;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                lds_dma16(rsA, st + (wave * 4 + q) * 1024, voffA, (q * 8 * g.K + kt * kBK) * 2);
+            for (int q = 0; q < QA; ++q)
+                lds_dma16(rsA, st + (wave * QA + q) * 1024, voffA, (q * 8 * g.K + kt * kBK) * 2);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                lds_dma16(rsB, st + kStageA + (sub * 16 + (wave % 4) * 4 + q) * 1024,
+            for (int q = 0; q < QA; ++q)
+                lds_dma16(rsB, st + kStageA + (sub * 16 + (wave % (kNW / 2)) * QA + q) * 1024,
                           ((q >> 1) & 1) ? voffB1 : voffB0,
-                          (((wave % 4) * 16 + q * 4 + kt * kBK) * g.N) * 2);
+                          ((((wave % (kNW / 2)) * QA + q) * 4 + kt * kBK) * g.N) * 2);
         };
 
-        f32x4_t acc[TM][TN];
+        f32x16_t acc[TM][TN];
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-        auto compute = [&](int stage) {
+        // Fragments of one 32-wide half of a k-step: two 16-wide MFMA slices,
+        // A (2 x 32 rows) and B (4 x 32 columns) per slice.
+        auto load_frags = [&](int stage, int kk, bf16x8_t (&af)[2][TM], bf16x8_t (&bfr)[2][TN]) {
             const unsigned char* As = smem + stage * kStage;
             const unsigned char* Bs = As + kStageA;
 #pragma unroll
-            for (int kk = 0; kk < kBK / 32; ++kk) {
-                bf16x8_t af[TM], bfr[TN];
+            for (int ss = 0; ss < 2; ++ss) {
+                const int k16 = kk * 2 + ss;
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
-                    const int row = wm * 64 + i * 16 + lane % 16;
-                    const int phys = (kk * 4 + lane / 16) ^ (row & 7);
-                    af[i] = as_bf16x8(*reinterpret_cast<const uint4*>(As + row * 128 + phys * 16));
+                    const int row = wm * WM_ROWS + i * 32 + lane % 32;
+                    const int phys = (k16 * 2 + lane / 32) ^ (row & 7);
+                    af[ss][i] = as_bf16x8(*reinterpret_cast<const uint4*>(As + row * 128 + phys * 16));
                 }
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     int sb, col;  // B sub-tile and column inside it
                     if (MODE == MODE_SWIGLU) {
                         sb = (j < TN / 2) ? 0 : 1;
-                        col = wn * 64 + (j % (TN / 2)) * 16;
+                        col = wn * 64 + (j % (TN / 2)) * 32;
                     } else {
                         sb = wn;
-                        col = j * 16;
+                        col = j * 32;
                     }
-                    col += 4 * (lane % 4);
+                    // lanes 16-31 / 48-63 take the second 16 columns; lanes 32-63 the k rows 8-15
+                    col += ((lane / 16) % 2) * 16 + 4 * (lane % 4);
                     i16x4_t v[2];
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
-                        const int kr = kk * 32 + (lane / 16) * 8 + h * 4 + (lane % 16) / 4;
+                        const int kr = k16 * 16 + (lane / 32) * 8 + h * 4 + (lane % 16) / 4;
                         const int phys = (col >> 3) ^ swz_b(kr);
                         v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(
                             Bs + sb * (kStageB / 2) + kr * 256 + phys * 16 + (col & 7) * 2));
                     }
                     const uint2 lo = __builtin_bit_cast(uint2, v[0]);
                     const uint2 hi = __builtin_bit_cast(uint2, v[1]);
-                    bfr[j] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+                    bfr[ss][j] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
                 }
+            }
+        };
+        auto mma = [&](const bf16x8_t (&af)[2][TM], const bf16x8_t (&bfr)[2][TN]) {
+#pragma unroll
+            for (int ss = 0; ss < 2; ++ss)
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j],
-                                                                            0, 0, 0);
-            }
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ss][i], bfr[ss][j],
+                                                                            acc[i][j], 0, 0, 0);
         };
-        // The next k-step's loads are issued right after the barrier that
-        // frees their stage; the last k-step is peeled so the loop body has no
-        // branch (keeps the accumulators in place across iterations).
+        // Software pipeline over k-steps of 64 (two 32-wide slices):
+        //   slice 1 of step kt is read while slice 0's MFMAs run; then the
+        //   barrier (step kt+1 has landed, nobody reads step kt any more),
+        //   loads of step kt+2 go into the freed stage, and slice 0 of step
+        //   kt+1 is read while slice 1's MFMAs of step kt run.  The last two
+        //   steps are peeled so the loop body has no branch.
+        bf16x8_t a0[2][TM], b0[2][TN], a1[2][TM], b1[2][TN];
         issue(0, 0);
-        for (int kt = 0; kt + 1 < nk; ++kt) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            issue(kt + 1, (kt + 1) & 1);
-            compute(kt & 1);
-        }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        compute((nk - 1) & 1);
+        issue(1, 1);
+        load_frags(0, 0, a0, b0);
+        int kt = 0;
+        // sched_barrier(0) keeps each group of MFMAs on its side of the
+        // workgroup barrier, so the barrier wait overlaps matrix work.
+        for (; kt + 2 < nk; ++kt) {
+            load_frags(kt & 1, 1, a1, b1);
+            mma(a0, b0);
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            issue(kt + 2, kt & 1);
+            load_frags((kt + 1) & 1, 0, a0, b0);
+            mma(a1, b1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // kt = nk - 2
+        load_frags(kt & 1, 1, a1, b1);
+        mma(a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        load_frags((kt + 1) & 1, 0, a0, b0);
+        mma(a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        // kt = nk - 1
+        load_frags((kt + 1) & 1, 1, a1, b1);
+        mma(a0, b0);
+        mma(a1, b1);
         __syncthreads();  // every wave is done with the stages: LDS is reused below
 
         // epilogue: activation in registers, tile staged in LDS, row stores
@@ -283,24 +326,27 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
         constexpr int PHASES = (MODE == MODE_DOWN) ? 2 : 1;
         constexpr int vec_per_row = EP::BN_OUT * EP::OUT_BYTES / 16;
         for (int ph = 0; ph < PHASES; ++ph) {
-            if (PHASES == 1 || wm / 2 == ph) {
+            if (PHASES == 1 || (wm * WM_ROWS) / EP::ROWS == ph) {
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
 #pragma unroll
                     for (int j = 0; j < TNO; ++j) {
-                        const int ocol = (MODE == MODE_SWIGLU ? wn * 64 : wn * 128) + j * 16 + lane % 16;
+                        const int ocol = (MODE == MODE_SWIGLU ? wn * 64 : wn * 128) + j * 32 + lane % 32;
                         float bv = 0.f;
                         if (MODE != MODE_SWIGLU && biasb) bv = bf2f(biasb[ocol]);
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int orow = (PHASES == 1 ? wm : wm % 2) * 64 + i * 16 + (lane / 16) * 4 + r;
+                        for (int q = 0; q < 16; ++q) {
+                            // 32 x 32 accumulator: element q of lane l is row
+                            // 8*(q/4) + 4*(l/32) + q%4, column l%32
+                            const int orow = (wm * WM_ROWS) % EP::ROWS + i * 32 + (q / 4) * 8 +
+                                             (lane / 32) * 4 + (q % 4);
                             float v;
                             if (MODE == MODE_SWIGLU)
-                                v = silu_f(acc[i][j][r]) * acc[i][j + TN / 2][r];
+                                v = silu_f(acc[i][j][q]) * acc[i][j + TN / 2][q];
                             else if (MODE == MODE_GELU)
-                                v = gelu_f(acc[i][j][r] + bv);
+                                v = gelu_f(acc[i][j][q] + bv);
                             else
-                                v = acc[i][j][r] + bv;
+                                v = acc[i][j][q] + bv;
                             unsigned char* dst = smem + orow * EP::LD_BYTES + ocol * EP::OUT_BYTES;
                             if (MODE == MODE_DOWN)
                                 *reinterpret_cast<float*>(dst) = v;
@@ -443,6 +489,7 @@ extern "C" moe_status_t moe_expert_ffn(void* stream, moe_dtype_t dtype, moe_act_
     if (H % kBN || I % kBK) return MOE_ERR_ALIGN;
     if (act == MOE_ACT_SWIGLU ? (I % (kBN / 2)) : (I % kBN)) return MOE_ERR_ALIGN;
     if (C > (1 << 30) / 8) return MOE_ERR_UNSUPPORTED;
+    if (H < 2 * kBK || I < 2 * kBK) return MOE_ERR_ALIGN;  // the k pipeline needs two steps
     const void* ptrs[] = {x_disp, w1, w3, w2, b1, b2, h_ws, y_disp};
     for (const void* q : ptrs)
         if (q && !moe_aligned16(q)) return MOE_ERR_ALIGN;

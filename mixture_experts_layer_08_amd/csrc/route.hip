@@ -12,8 +12,9 @@
 // and lives in L2), but at E = 32 it is 32 FLOP per byte of x, above what
 // fp32 vector FMA sustains at HBM speed, so the product runs on the matrix
 // cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  One workgroup of 8
-// waves stages W_r in LDS once, already laid out as MFMA B fragments (one
-// 16-byte ds_read per lane per fragment), then walks 16-token tiles.  Each
+// waves copies W_r into LDS once, in its own [H, E] layout (16-byte loads),
+// and reads MFMA B operands from it with gfx950's transpose LDS reads; it
+// then walks 16-token tiles.  Each
 // wave owns 1/8 of the hidden dimension and streams its x slice straight
 // from HBM into A-fragment registers (16 rows x 64 contiguous bytes per
 // load); the next tile's loads are issued before the current tile's
@@ -27,6 +28,9 @@
 namespace {
 
 using namespace moe;
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int kTok = 16;          // tokens per tile (MFMA M)
 constexpr int kRWaves = 8;        // waves per router workgroup
@@ -159,7 +163,7 @@ __global__ __launch_bounds__(kRThreads) void route_bf16_kernel(RouteParams p, in
     const int H = p.H;
     const int nks = H / 32;                    // k-steps of 32
     const int ks_per_wave = nks / kRWaves;     // <= kMaxKsPerWave
-    uint4* wfrag = reinterpret_cast<uint4*>(smem);                         // [nks][NTN][64]
+    uint4* wlds = reinterpret_cast<uint4*>(smem);                          // [H][16*NTN] bf16
     f32x4_t* red = reinterpret_cast<f32x4_t*>(smem + (size_t)nks * NTN * 1024);  // [8][NTN][64]
     float* lg = reinterpret_cast<float*>(red + kRWaves * NTN * kWave);     // [16][16*NTN]
     constexpr int ld = 16 * NTN;
@@ -185,25 +189,26 @@ __global__ __launch_bounds__(kRThreads) void route_bf16_kernel(RouteParams p, in
     int tile = blockIdx.x;
     if (tile < ntiles) load_tile(a_cur, tile);
 
-    // Stage W_r [H, E] as B fragments: slot (ks, nt, l) holds
-    // W[ks*32 + (l/16)*8 + i][nt*16 + l%16], i = 0..7 (zero past E).
-    const int nslots = nks * NTN * kWave;
-    for (int s = tid; s < nslots; s += kRThreads) {
-        const int l = s % kWave;
-        const int nt = (s / kWave) % NTN;
-        const int ks = s / (kWave * NTN);
-        const int col = nt * 16 + l % 16;
-        const int r0 = ks * 32 + (l / 16) * 8;
-        uint32_t w[4] = {0, 0, 0, 0};
-        if (col < p.E) {
-#pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-                const uint32_t lo = wr[(size_t)(r0 + i) * p.E + col];
-                const uint32_t hi = wr[(size_t)(r0 + i + 1) * p.E + col];
-                w[i / 2] = lo | (hi << 16);
-            }
+    // Stage W_r [H, E] in LDS as [H][16*NTN] (experts past E are zero),
+    // 16-byte vectors when E is a multiple of 8.
+    constexpr int EP = 16 * NTN;
+    if (p.E % 8 == 0) {
+        const int vpr = p.E / 8;  // vectors per W_r row
+        for (int v = tid; v < H * vpr; v += kRThreads) {
+            const int h = v / vpr, c = v % vpr;
+            wlds[h * EP / 8 + c] = reinterpret_cast<const uint4*>(wr)[(size_t)h * vpr + c];
         }
-        wfrag[s] = make_uint4(w[0], w[1], w[2], w[3]);
+        const int padv = (EP - p.E) / 8;
+        for (int v = tid; v < H * padv; v += kRThreads) {
+            const int h = v / padv, c = v % padv;
+            wlds[h * EP / 8 + vpr + c] = make_uint4(0, 0, 0, 0);
+        }
+    } else {
+        uint16_t* w16 = reinterpret_cast<uint16_t*>(wlds);
+        for (int v = tid; v < H * EP; v += kRThreads) {
+            const int h = v / EP, e = v % EP;
+            w16[v] = e < p.E ? wr[(size_t)h * p.E + e] : (uint16_t)0;
+        }
     }
     __syncthreads();
 
@@ -217,8 +222,21 @@ __global__ __launch_bounds__(kRThreads) void route_bf16_kernel(RouteParams p, in
                 const bf16x8_t a = as_bf16x8(a_cur[i]);
 #pragma unroll
                 for (int n = 0; n < NTN; ++n) {
-                    const uint4 b = wfrag[((ks0 + i) * NTN + n) * kWave + lane];
-                    acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(b), acc[n], 0, 0, 0);
+                    // transpose reads: lane L of each 16-lane group points at
+                    // row k0 + L/4, experts 4*(L%4).., and receives expert L of
+                    // rows k0..k0+3 (two reads give the 8 k of the B operand)
+                    const unsigned char* wb = reinterpret_cast<const unsigned char*>(wlds);
+                    i16x4_t v[2];
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int kr = (ks0 + i) * 32 + (lane / 16) * 8 + hh * 4 + (lane % 16) / 4;
+                        v[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(
+                            wb + (kr * EP + n * 16 + 4 * (lane % 4)) * 2));
+                    }
+                    const uint2 lo = __builtin_bit_cast(uint2, v[0]);
+                    const uint2 hi = __builtin_bit_cast(uint2, v[1]);
+                    const bf16x8_t b = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+                    acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[n], 0, 0, 0);
                 }
             }
         }
@@ -346,7 +364,7 @@ extern "C" moe_status_t moe_route(void* stream, moe_dtype_t dtype, const void* x
     }
     if (H % 256) return MOE_ERR_ALIGN;
     if (H / 32 / kRWaves > kMaxKsPerWave) return MOE_ERR_UNSUPPORTED;
-    if (!moe_aligned16(x)) return MOE_ERR_ALIGN;
+    if (!moe_aligned16(x) || !moe_aligned16(w_r)) return MOE_ERR_ALIGN;
     const int ntn = (E + 15) / 16;
     switch (ntn) {
         case 1: return launch_bf16<1>(p, st);
