@@ -47,8 +47,13 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #ifndef GEMM_WAVES
 #define GEMM_WAVES 8
+#endif
+#ifndef GEMM_WAVES_N
+#define GEMM_WAVES_N 2
 #endif
 
 namespace {
@@ -58,7 +63,9 @@ using namespace moe;
 constexpr int kBM = 256;
 constexpr int kBN = 256;
 constexpr int kBK = 64;
-constexpr int kNW = GEMM_WAVES;  // waves per workgroup: 2 column halves x kNW/2 row blocks
+constexpr int kNW = GEMM_WAVES;      // waves per workgroup
+constexpr int kWN = GEMM_WAVES_N;    // waves across the B columns
+constexpr int kWMn = kNW / kWN;      // waves across the rows
 constexpr int kGThreads = kNW * 64;
 constexpr int kStageA = kBM * kBK * 2;  // 32 KB
 constexpr int kStageB = kBK * kBN * 2;  // 32 KB
@@ -121,7 +128,13 @@ __device__ __forceinline__ float gelu_f(float z) {
     return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
 }
 
-__device__ __forceinline__ int swz_b(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
+// LDS swizzles (16-byte chunk index XOR).  A rows are 128 bytes: XOR with
+// (row >> 1) & 7 puts any 16 consecutive rows of one chunk on distinct banks.
+// B rows (one 128-column sub-tile) are 256 bytes: a transpose read serves 32
+// lanes per pass, lanes 0-15 and 16-31 reading the same 4 rows at columns 16
+// apart; XOR with 4 * (k & 3) sends the two halves to disjoint chunk sets.
+__device__ __forceinline__ int swz_a(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz_b(int k) { return (k & 3) << 2; }
 
 template <int MODE>
 struct Epi {
@@ -136,8 +149,9 @@ struct Epi {
 template <int MODE>
 __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     using EP = Epi<MODE>;
-    constexpr int WM_ROWS = kBM / (kNW / 2);  // rows per wave
-    constexpr int TM = WM_ROWS / 32, TN = 4;  // 32 x 32 MFMA tiles per wave (WM_ROWS x 128)
+    constexpr int WM_ROWS = kBM / kWMn;       // rows per wave
+    constexpr int WN_COLS = kBN / kWN;        // B columns per wave
+    constexpr int TM = WM_ROWS / 32, TN = WN_COLS / 32;  // 32 x 32 MFMA tiles per wave
     constexpr int QA = 32 / kNW;              // 1 KB A (and B) loads per wave per k-step
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_pref[MOE_MAX_EXPERTS + 1];
@@ -145,7 +159,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
-    const int wm = wave / 2, wn = wave % 2;   // wave rows wm*WM_ROWS.., columns per wn
+    const int wm = wave / kWN, wn = wave % kWN;  // wave rows wm*WM_ROWS.., columns per wn
     const int NT = g.N / EP::BN_OUT;
     if (tid == 0) {
         int cum = 0;
@@ -202,23 +216,24 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
             bsrc = g.B0 + (size_t)e * g.K * g.N + n0 + sub * 128;
         const size_t coloff = (MODE == MODE_SWIGLU) ? (size_t)n0 : (size_t)n0 + sub * 128;
         const i32x4_t rsB = make_rsrc(bsrc, (uint32_t)(((size_t)g.K * g.N - coloff) * 2));
-        // A load q of this wave: tile row R = (wave*QA + q)*8 + lane/8, chunk
-        // (lane % 8) ^ (R & 7) = (lane % 8) ^ (lane / 8)
-        const int voffA = ((wave * QA * 8 + lane / 8) * g.K + (((lane % 8) ^ (lane / 8)) * 8)) * 2;
-        // B load q: sub-tile row kr = ((wave % (kNW/2))*QA + q)*4 + lane/16, chunk
-        // (lane % 16) ^ swz_b(kr); swz_b(kr) = 2*(lane/16) + 8*((q >> 1) & 1)
-        const int voffB0 = ((lane / 16) * g.N + (((lane % 16) ^ ((lane / 16) << 1)) * 8)) * 2;
-        const int voffB1 = ((lane / 16) * g.N + (((lane % 16) ^ (((lane / 16) << 1) | 8)) * 8)) * 2;
+        // A load q of this wave: tile row R = (wave*QA + q)*8 + lane/8 holds in
+        // its chunk lane % 8 the logical chunk (lane % 8) ^ swz_a(R), and
+        // swz_a(R) = 4*(q & 1) + lane/16 (QA is even)
+        const int voffA0 = ((wave * QA * 8 + lane / 8) * g.K + (((lane % 8) ^ (lane / 16)) * 8)) * 2;
+        const int voffA1 = ((wave * QA * 8 + lane / 8) * g.K + (((lane % 8) ^ (4 + lane / 16)) * 8)) * 2;
+        // B load q: sub-tile row kr = ((wave % (kNW/2))*QA + q)*4 + lane/16,
+        // chunk (lane % 16) ^ swz_b(kr) with swz_b(kr) = 4*(lane/16)
+        const int voffB = ((lane / 16) * g.N + (((lane % 16) ^ ((lane / 16) << 2)) * 8)) * 2;
         auto issue = [&](int kt, int stage) {
             unsigned char* st = smem + stage * kStage;
 #pragma unroll
             for (int q = 0; q < QA; ++q)
-                lds_dma16(rsA, st + (wave * QA + q) * 1024, voffA, (q * 8 * g.K + kt * kBK) * 2);
+                lds_dma16(rsA, st + (wave * QA + q) * 1024, (q & 1) ? voffA1 : voffA0,
+                          (q * 8 * g.K + kt * kBK) * 2);
 #pragma unroll
             for (int q = 0; q < QA; ++q)
                 lds_dma16(rsB, st + kStageA + (sub * 16 + (wave % (kNW / 2)) * QA + q) * 1024,
-                          ((q >> 1) & 1) ? voffB1 : voffB0,
-                          ((((wave % (kNW / 2)) * QA + q) * 4 + kt * kBK) * g.N) * 2);
+                          voffB, ((((wave % (kNW / 2)) * QA + q) * 4 + kt * kBK) * g.N) * 2);
         };
 
         f32x16_t acc[TM][TN];
@@ -240,18 +255,19 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
                     const int row = wm * WM_ROWS + i * 32 + lane % 32;
-                    const int phys = (k16 * 2 + lane / 32) ^ (row & 7);
+                    const int phys = (k16 * 2 + lane / 32) ^ swz_a(row);
                     af[ss][i] = as_bf16x8(*reinterpret_cast<const uint4*>(As + row * 128 + phys * 16));
                 }
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     int sb, col;  // B sub-tile and column inside it
-                    if (MODE == MODE_SWIGLU) {
+                    if (MODE == MODE_SWIGLU) {  // first half of the wave's tiles gate, second up
                         sb = (j < TN / 2) ? 0 : 1;
-                        col = wn * 64 + (j % (TN / 2)) * 32;
+                        col = wn * (WN_COLS / 2) + (j % (TN / 2)) * 32;
                     } else {
-                        sb = wn;
-                        col = j * 32;
+                        const int c = wn * WN_COLS + j * 32;
+                        sb = c / 128;
+                        col = c % 128;
                     }
                     // lanes 16-31 / 48-63 take the second 16 columns; lanes 32-63 the k rows 8-15
                     col += ((lane / 16) % 2) * 16 + 4 * (lane % 4);
@@ -285,39 +301,58 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
         //   loads of step kt+2 go into the freed stage, and slice 0 of step
         //   kt+1 is read while slice 1's MFMAs of step kt run.  The last two
         //   steps are peeled so the loop body has no branch.
-        bf16x8_t a0[2][TM], b0[2][TN], a1[2][TM], b1[2][TN];
-        issue(0, 0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        issue(1, 1);
-        load_frags(0, 0, a0, b0);
-        int kt = 0;
-        // sched_barrier(0) keeps each group of MFMAs on its side of the
-        // workgroup barrier, so the barrier wait overlaps matrix work.
-        for (; kt + 2 < nk; ++kt) {
-            load_frags(kt & 1, 1, a1, b1);
-            mma(a0, b0);
+        // A wave whose rows all lie at or past kept[e] (the tail of an
+        // expert's last row tile) runs a copy of the k loop without fragment
+        // reads or MFMAs: it still loads its share of every stage and joins
+        // the same barriers (a barrier counts arrivals, so the two loops stay
+        // in step).
+        auto kloop = [&](auto do_math) {
+            constexpr bool M = decltype(do_math)::value;
+            bf16x8_t a0[2][TM], b0[2][TN], a1[2][TM], b1[2][TN];
+            issue(0, 0);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            issue(1, 1);
+            if (M) load_frags(0, 0, a0, b0);
+            int kt = 0;
+            // sched_barrier(0) keeps each group of MFMAs on its side of the
+            // workgroup barrier, so the barrier wait overlaps matrix work.
+            for (; kt + 2 < nk; ++kt) {
+                if (M) {
+                    load_frags(kt & 1, 1, a1, b1);
+                    mma(a0, b0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __syncthreads();
+                issue(kt + 2, kt & 1);
+                if (M) {
+                    load_frags((kt + 1) & 1, 0, a0, b0);
+                    mma(a1, b1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // kt = nk - 2
+            if (M) {
+                load_frags(kt & 1, 1, a1, b1);
+                mma(a0, b0);
+            }
             __builtin_amdgcn_sched_barrier(0);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
-            issue(kt + 2, kt & 1);
-            load_frags((kt + 1) & 1, 0, a0, b0);
-            mma(a1, b1);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // kt = nk - 2
-        load_frags(kt & 1, 1, a1, b1);
-        mma(a0, b0);
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        load_frags((kt + 1) & 1, 0, a0, b0);
-        mma(a1, b1);
-        __builtin_amdgcn_sched_barrier(0);
-        // kt = nk - 1
-        load_frags((kt + 1) & 1, 1, a1, b1);
-        mma(a0, b0);
-        mma(a1, b1);
+            if (M) {
+                load_frags((kt + 1) & 1, 0, a0, b0);
+                mma(a1, b1);
+                // kt = nk - 1
+                load_frags((kt + 1) & 1, 1, a1, b1);
+                mma(a0, b0);
+                mma(a1, b1);
+            }
+        };
+        if (m0 + wm * WM_ROWS < kept)
+            kloop(std::true_type{});
+        else
+            kloop(std::false_type{});
         __syncthreads();  // every wave is done with the stages: LDS is reused below
 
         // epilogue: activation in registers, tile staged in LDS, row stores
@@ -331,7 +366,8 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
                 for (int i = 0; i < TM; ++i) {
 #pragma unroll
                     for (int j = 0; j < TNO; ++j) {
-                        const int ocol = (MODE == MODE_SWIGLU ? wn * 64 : wn * 128) + j * 32 + lane % 32;
+                        const int ocol = (MODE == MODE_SWIGLU ? wn * (WN_COLS / 2) : wn * WN_COLS) + j * 32 +
+                                         lane % 32;
                         float bv = 0.f;
                         if (MODE != MODE_SWIGLU && biasb) bv = bf2f(biasb[ocol]);
 #pragma unroll
