@@ -53,7 +53,7 @@
 #define GEMM_WAVES 8
 #endif
 #ifndef GEMM_WAVES_N
-#define GEMM_WAVES_N 2
+#define GEMM_WAVES_N 4
 #endif
 
 namespace {
@@ -61,15 +61,13 @@ namespace {
 using namespace moe;
 
 constexpr int kBM = 256;
-constexpr int kBN = 256;
+constexpr int kBNMax = 256;  // widest B tile (two 128-column sub-tiles)
 constexpr int kBK = 64;
 constexpr int kNW = GEMM_WAVES;      // waves per workgroup
 constexpr int kWN = GEMM_WAVES_N;    // waves across the B columns
 constexpr int kWMn = kNW / kWN;      // waves across the rows
 constexpr int kGThreads = kNW * 64;
 constexpr int kStageA = kBM * kBK * 2;  // 32 KB
-constexpr int kStageB = kBK * kBN * 2;  // 32 KB
-constexpr int kStage = kStageA + kStageB;
 
 enum { MODE_SWIGLU = 0, MODE_GELU = 1, MODE_DOWN = 2 };
 
@@ -98,8 +96,16 @@ __device__ __forceinline__ void lds_dma16(i32x4_t rsrc, const void* lds, int vof
 }
 #pragma clang diagnostic pop
 
+// Raw buffer stores (the tile epilogue): the descriptor's byte range ends at
+// the last valid row, and the hardware drops stores past it.
+__device__ void buffer_store_i16(short v, i32x4_t rsrc, int voffset, int soffset,
+                                 int aux) __asm("llvm.amdgcn.raw.buffer.store.i16");
+__device__ void buffer_store_f32(float v, i32x4_t rsrc, int voffset, int soffset,
+                                 int aux) __asm("llvm.amdgcn.raw.buffer.store.f32");
+
 // Buffer resource: 48-bit base, no stride, num_records bytes; loads past the
-// end return zero.  Every argument must be wave-uniform.
+// end return zero and stores past it are dropped.  Every argument must be
+// wave-uniform.
 __device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
     i32x4_t r;
@@ -136,23 +142,33 @@ __device__ __forceinline__ float gelu_f(float z) {
 __device__ __forceinline__ int swz_a(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int swz_b(int k) { return (k & 3) << 2; }
 
-template <int MODE>
+template <int MODE, int BN>
 struct Epi {
-    static constexpr int BN_OUT = (MODE == MODE_SWIGLU) ? kBN / 2 : kBN;
+    static_assert(BN == 256 || (BN == 128 && MODE != MODE_SWIGLU), "B tile is 256 or 128 columns");
+    static constexpr int STAGE_B = kBK * BN * 2;            // 32 or 16 KB
+    static constexpr int STAGE = kStageA + STAGE_B;
+    static constexpr int BN_OUT = (MODE == MODE_SWIGLU) ? BN / 2 : BN;
     static constexpr int OUT_BYTES = (MODE == MODE_DOWN) ? 4 : 2;
-    static constexpr int ROWS = (MODE == MODE_DOWN) ? kBM / 2 : kBM;  // rows staged per phase
-    static constexpr int LD_BYTES = BN_OUT * OUT_BYTES + 16;
-    static constexpr size_t LDS_OUT = (size_t)ROWS * LD_BYTES;
-    static constexpr size_t LDS = (2 * (size_t)kStage > LDS_OUT) ? 2 * (size_t)kStage : LDS_OUT;
+    static constexpr size_t LDS = 2 * (size_t)STAGE;
 };
 
-template <int MODE>
+// One tile of work: expert e, rows m0.., output columns n0.., and the buffer
+// descriptors of its A rows and B columns.
+struct TileCtx {
+    bool valid;
+    int e, m0, n0, kept;
+    i32x4_t rsA, rsB;
+};
+
+template <int MODE, int BN>
 __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
-    using EP = Epi<MODE>;
+    using EP = Epi<MODE, BN>;
+    constexpr int kStage = EP::STAGE;
     constexpr int WM_ROWS = kBM / kWMn;       // rows per wave
-    constexpr int WN_COLS = kBN / kWN;        // B columns per wave
+    constexpr int WN_COLS = BN / kWN;         // B columns per wave
     constexpr int TM = WM_ROWS / 32, TN = WN_COLS / 32;  // 32 x 32 MFMA tiles per wave
-    constexpr int QA = 32 / kNW;              // 1 KB A (and B) loads per wave per k-step
+    constexpr int QA = 32 / kNW;              // 1 KB A loads per wave per k-step
+    constexpr int QB = (BN / 128) * 16 / kNW; // 1 KB B loads per wave per k-step
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_pref[MOE_MAX_EXPERTS + 1];
     __shared__ int s_mt[MOE_MAX_EXPERTS];
@@ -175,14 +191,19 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
         s_pref[g.E] = cum;
     }
     __syncthreads();
-    const int total = s_pref[g.E];
+    const int total = __builtin_amdgcn_readfirstlane(s_pref[g.E]);
     const int G = gridDim.x;
     const int xcd = blockIdx.x % 8, slot8 = blockIdx.x / 8;
     const int nk = g.K / kBK;
+    // B sub-tiles are 128 columns (16 KB); wave w fills 1 KB blocks w*QB..,
+    // all inside sub-tile (w*QB)/16
+    const int sub = (wave * QB) / 16;
 
-    for (int round = 0;; ++round) {
+    auto tile_at = [&](int round) {
+        TileCtx c;
         const int logical = round * G + xcd * (G / 8) + slot8;
-        if (logical >= total) break;
+        c.valid = logical < total;
+        if (!c.valid) return c;
         int e = 0;
         while (e + 1 < g.E && s_pref[e + 1] <= logical) ++e;
         const int local = logical - s_pref[e];
@@ -196,46 +217,97 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
         const int rem = local - grp * mt * gn;
         const int m_tile = rem / width;
         const int n_tile = grp * gn + rem % width;
-
         int kept = g.kept[e];
         if (kept > g.C) kept = (int)g.C;
-        kept = __builtin_amdgcn_readfirstlane(kept);
-        e = __builtin_amdgcn_readfirstlane(e);
-        const int m0 = __builtin_amdgcn_readfirstlane(m_tile * kBM);
-        const int n0 = __builtin_amdgcn_readfirstlane(n_tile * EP::BN_OUT);
-
+        c.kept = __builtin_amdgcn_readfirstlane(kept);
+        c.e = __builtin_amdgcn_readfirstlane(e);
+        c.m0 = __builtin_amdgcn_readfirstlane(m_tile * kBM);
+        c.n0 = __builtin_amdgcn_readfirstlane(n_tile * EP::BN_OUT);
         // A: rows m0.. of expert e; rows at or past kept read as zero
-        const i32x4_t rsA = make_rsrc(g.A + ((size_t)e * g.C + m0) * g.K,
-                                      (uint32_t)((size_t)(kept - m0) * g.K * 2));
-        // B: two 128-column sub-tiles; the first half of the waves fills sub-tile 0
-        const int sub = wave / (kNW / 2);
+        c.rsA = make_rsrc(g.A + ((size_t)c.e * g.C + c.m0) * g.K,
+                          (uint32_t)((size_t)(c.kept - c.m0) * g.K * 2));
         const uint16_t* bsrc;
-        if (MODE == MODE_SWIGLU)
-            bsrc = (sub == 0 ? g.B0 : g.B1) + (size_t)e * g.K * g.N + n0;
-        else
-            bsrc = g.B0 + (size_t)e * g.K * g.N + n0 + sub * 128;
-        const size_t coloff = (MODE == MODE_SWIGLU) ? (size_t)n0 : (size_t)n0 + sub * 128;
-        const i32x4_t rsB = make_rsrc(bsrc, (uint32_t)(((size_t)g.K * g.N - coloff) * 2));
-        // A load q of this wave: tile row R = (wave*QA + q)*8 + lane/8 holds in
-        // its chunk lane % 8 the logical chunk (lane % 8) ^ swz_a(R), and
-        // swz_a(R) = 4*(q & 1) + lane/16 (QA is even)
-        const int voffA0 = ((wave * QA * 8 + lane / 8) * g.K + (((lane % 8) ^ (lane / 16)) * 8)) * 2;
-        const int voffA1 = ((wave * QA * 8 + lane / 8) * g.K + (((lane % 8) ^ (4 + lane / 16)) * 8)) * 2;
-        // B load q: sub-tile row kr = ((wave % (kNW/2))*QA + q)*4 + lane/16,
-        // chunk (lane % 16) ^ swz_b(kr) with swz_b(kr) = 4*(lane/16)
-        const int voffB = ((lane / 16) * g.N + (((lane % 16) ^ ((lane / 16) << 2)) * 8)) * 2;
-        auto issue = [&](int kt, int stage) {
-            unsigned char* st = smem + stage * kStage;
-#pragma unroll
-            for (int q = 0; q < QA; ++q)
-                lds_dma16(rsA, st + (wave * QA + q) * 1024, (q & 1) ? voffA1 : voffA0,
-                          (q * 8 * g.K + kt * kBK) * 2);
-#pragma unroll
-            for (int q = 0; q < QA; ++q)
-                lds_dma16(rsB, st + kStageA + (sub * 16 + (wave % (kNW / 2)) * QA + q) * 1024,
-                          voffB, ((((wave % (kNW / 2)) * QA + q) * 4 + kt * kBK) * g.N) * 2);
-        };
+        size_t coloff;
+        if (MODE == MODE_SWIGLU) {
+            bsrc = (sub == 0 ? g.B0 : g.B1) + (size_t)c.e * g.K * g.N + c.n0;
+            coloff = (size_t)c.n0;
+        } else {
+            bsrc = g.B0 + (size_t)c.e * g.K * g.N + c.n0 + sub * 128;
+            coloff = (size_t)c.n0 + sub * 128;
+        }
+        c.rsB = make_rsrc(bsrc, (uint32_t)(((size_t)g.K * g.N - coloff) * 2));
+        return c;
+    };
 
+    // A load q of this wave: tile row R = (wave*QA + q)*8 + lane/8 holds in
+    // its chunk lane % 8 the logical chunk (lane % 8) ^ swz_a(R), and
+    // swz_a(R) = 4*(q & 1) + lane/16 (QA is even)
+    const int voffA0 = ((wave * QA * 8 + lane / 8) * g.K + (((lane % 8) ^ (lane / 16)) * 8)) * 2;
+    const int voffA1 = ((wave * QA * 8 + lane / 8) * g.K + (((lane % 8) ^ (4 + lane / 16)) * 8)) * 2;
+    // B load q: sub-tile row kr = ((wave*QB + q) % 16)*4 + lane/16,
+    // chunk (lane % 16) ^ swz_b(kr) with swz_b(kr) = 4*(lane/16)
+    const int voffB = ((lane / 16) * g.N + (((lane % 16) ^ ((lane / 16) << 2)) * 8)) * 2;
+    auto issue = [&](const TileCtx& c, int kt, int stage) {
+        unsigned char* st = smem + stage * kStage;
+#pragma unroll
+        for (int q = 0; q < QA; ++q)
+            lds_dma16(c.rsA, st + (wave * QA + q) * 1024, (q & 1) ? voffA1 : voffA0,
+                      (q * 8 * g.K + kt * kBK) * 2);
+#pragma unroll
+        for (int q = 0; q < QB; ++q)
+            lds_dma16(c.rsB, st + kStageA + (wave * QB + q) * 1024, voffB,
+                      ((((wave * QB + q) % 16) * 4 + kt * kBK) * g.N) * 2);
+    };
+
+    // Fragments of one 32-wide half of a k-step: two 16-wide MFMA slices,
+    // A (TM x 32 rows) and B (TN x 32 columns) per slice.
+    auto load_frags = [&](int stage, int kk, bf16x8_t (&af)[2][TM], bf16x8_t (&bfr)[2][TN]) {
+        const unsigned char* As = smem + stage * kStage;
+        const unsigned char* Bs = As + kStageA;
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss) {
+            const int k16 = kk * 2 + ss;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int row = wm * WM_ROWS + i * 32 + lane % 32;
+                const int phys = (k16 * 2 + lane / 32) ^ swz_a(row);
+                af[ss][i] = as_bf16x8(*reinterpret_cast<const uint4*>(As + row * 128 + phys * 16));
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                int sb, col;  // B sub-tile and column inside it
+                if (MODE == MODE_SWIGLU) {  // first half of the wave's tiles gate, second up
+                    sb = (j < TN / 2) ? 0 : 1;
+                    col = wn * (WN_COLS / 2) + (j % (TN / 2)) * 32;
+                } else {
+                    const int c = wn * WN_COLS + j * 32;
+                    sb = c / 128;
+                    col = c % 128;
+                }
+                // lanes 16-31 / 48-63 take the second 16 columns; lanes 32-63 the k rows 8-15
+                col += ((lane / 16) % 2) * 16 + 4 * (lane % 4);
+                i16x4_t v[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int kr = k16 * 16 + (lane / 32) * 8 + h * 4 + (lane % 16) / 4;
+                    const int phys = (col >> 3) ^ swz_b(kr);
+                    v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(
+                        Bs + sb * 16384 + kr * 256 + phys * 16 + (col & 7) * 2));
+                }
+                const uint2 lo = __builtin_bit_cast(uint2, v[0]);
+                const uint2 hi = __builtin_bit_cast(uint2, v[1]);
+                bfr[ss][j] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+            }
+        }
+    };
+
+    TileCtx cur = tile_at(0);
+    if (!cur.valid) return;
+    issue(cur, 0, 0);
+    issue(cur, 1, 1);
+    int base = 0;  // stage holding k-step 0 of the current tile
+    for (int round = 0;; ++round) {
+        const TileCtx nxt = tile_at(round + 1);
         f32x16_t acc[TM][TN];
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -243,48 +315,6 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-
-        // Fragments of one 32-wide half of a k-step: two 16-wide MFMA slices,
-        // A (2 x 32 rows) and B (4 x 32 columns) per slice.
-        auto load_frags = [&](int stage, int kk, bf16x8_t (&af)[2][TM], bf16x8_t (&bfr)[2][TN]) {
-            const unsigned char* As = smem + stage * kStage;
-            const unsigned char* Bs = As + kStageA;
-#pragma unroll
-            for (int ss = 0; ss < 2; ++ss) {
-                const int k16 = kk * 2 + ss;
-#pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    const int row = wm * WM_ROWS + i * 32 + lane % 32;
-                    const int phys = (k16 * 2 + lane / 32) ^ swz_a(row);
-                    af[ss][i] = as_bf16x8(*reinterpret_cast<const uint4*>(As + row * 128 + phys * 16));
-                }
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    int sb, col;  // B sub-tile and column inside it
-                    if (MODE == MODE_SWIGLU) {  // first half of the wave's tiles gate, second up
-                        sb = (j < TN / 2) ? 0 : 1;
-                        col = wn * (WN_COLS / 2) + (j % (TN / 2)) * 32;
-                    } else {
-                        const int c = wn * WN_COLS + j * 32;
-                        sb = c / 128;
-                        col = c % 128;
-                    }
-                    // lanes 16-31 / 48-63 take the second 16 columns; lanes 32-63 the k rows 8-15
-                    col += ((lane / 16) % 2) * 16 + 4 * (lane % 4);
-                    i16x4_t v[2];
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int kr = k16 * 16 + (lane / 32) * 8 + h * 4 + (lane % 16) / 4;
-                        const int phys = (col >> 3) ^ swz_b(kr);
-                        v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(
-                            Bs + sb * (kStageB / 2) + kr * 256 + phys * 16 + (col & 7) * 2));
-                    }
-                    const uint2 lo = __builtin_bit_cast(uint2, v[0]);
-                    const uint2 hi = __builtin_bit_cast(uint2, v[1]);
-                    bfr[ss][j] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-                }
-            }
-        };
         auto mma = [&](const bf16x8_t (&af)[2][TM], const bf16x8_t (&bfr)[2][TN]) {
 #pragma unroll
             for (int ss = 0; ss < 2; ++ss)
@@ -295,115 +325,111 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ss][i], bfr[ss][j],
                                                                             acc[i][j], 0, 0, 0);
         };
-        // Software pipeline over k-steps of 64 (two 32-wide slices):
-        //   slice 1 of step kt is read while slice 0's MFMAs run; then the
-        //   barrier (step kt+1 has landed, nobody reads step kt any more),
-        //   loads of step kt+2 go into the freed stage, and slice 0 of step
-        //   kt+1 is read while slice 1's MFMAs of step kt run.  The last two
-        //   steps are peeled so the loop body has no branch.
-        // A wave whose rows all lie at or past kept[e] (the tail of an
-        // expert's last row tile) runs a copy of the k loop without fragment
-        // reads or MFMAs: it still loads its share of every stage and joins
-        // the same barriers (a barrier counts arrivals, so the two loops stay
-        // in step).
+        // Software pipeline over k-steps of 64 (two 32-wide halves): the
+        // second half of step kt is read while the first half's MFMAs run;
+        // then the barrier (step kt+1 has landed, nobody reads step kt any
+        // more), loads of step kt+2 go into the freed stage, and the first
+        // half of step kt+1 is read while the second half's MFMAs of step kt
+        // run.  After the last barrier the next tile's step 0 is loaded, and
+        // after the final MFMAs its step 1, so the next tile starts with both
+        // stages in flight.  A wave whose rows all lie at or past kept[e]
+        // (the tail of an expert's last row tile) runs the same loop without
+        // fragment reads or MFMAs: it issues the same loads and joins the same
+        // barriers (a barrier counts arrivals, so the two loops stay in step).
+        // sched_barrier(0) keeps each MFMA group on its side of a barrier.
         auto kloop = [&](auto do_math) {
             constexpr bool M = decltype(do_math)::value;
             bf16x8_t a0[2][TM], b0[2][TN], a1[2][TM], b1[2][TN];
-            issue(0, 0);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
-            issue(1, 1);
-            if (M) load_frags(0, 0, a0, b0);
+            if (M) load_frags(base, 0, a0, b0);
             int kt = 0;
-            // sched_barrier(0) keeps each group of MFMAs on its side of the
-            // workgroup barrier, so the barrier wait overlaps matrix work.
             for (; kt + 2 < nk; ++kt) {
+                const int s0 = (base + kt) & 1;
                 if (M) {
-                    load_frags(kt & 1, 1, a1, b1);
+                    load_frags(s0, 1, a1, b1);
                     mma(a0, b0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
-                issue(kt + 2, kt & 1);
+                issue(cur, kt + 2, s0);
                 if (M) {
-                    load_frags((kt + 1) & 1, 0, a0, b0);
+                    load_frags(s0 ^ 1, 0, a0, b0);
                     mma(a1, b1);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
             // kt = nk - 2
+            const int s0 = (base + kt) & 1;
             if (M) {
-                load_frags(kt & 1, 1, a1, b1);
+                load_frags(s0, 1, a1, b1);
                 mma(a0, b0);
             }
             __builtin_amdgcn_sched_barrier(0);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
+            if (nxt.valid) issue(nxt, 0, s0);
             if (M) {
-                load_frags((kt + 1) & 1, 0, a0, b0);
+                load_frags(s0 ^ 1, 0, a0, b0);
                 mma(a1, b1);
                 // kt = nk - 1
-                load_frags((kt + 1) & 1, 1, a1, b1);
+                load_frags(s0 ^ 1, 1, a1, b1);
                 mma(a0, b0);
                 mma(a1, b1);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();  // every wave is done with step nk - 1
+            if (nxt.valid) issue(nxt, 1, s0 ^ 1);
         };
-        if (m0 + wm * WM_ROWS < kept)
+        if (cur.m0 + wm * WM_ROWS < cur.kept)
             kloop(std::true_type{});
         else
             kloop(std::false_type{});
-        __syncthreads();  // every wave is done with the stages: LDS is reused below
 
-        // epilogue: activation in registers, tile staged in LDS, row stores
-        const uint16_t* biasb = g.bias ? g.bias + (size_t)e * g.N + n0 : nullptr;
-        constexpr int TNO = (MODE == MODE_SWIGLU) ? TN / 2 : TN;
-        constexpr int PHASES = (MODE == MODE_DOWN) ? 2 : 1;
-        constexpr int vec_per_row = EP::BN_OUT * EP::OUT_BYTES / 16;
-        for (int ph = 0; ph < PHASES; ++ph) {
-            if (PHASES == 1 || (wm * WM_ROWS) / EP::ROWS == ph) {
+        // epilogue: activation on the fp32 accumulators, stored straight from
+        // registers (element q of a 32 x 32 accumulator in lane l is row
+        // 8*(q/4) + 4*(l/32) + q%4, column l%32; one store covers two rows of
+        // 32 consecutive columns).  The output descriptor ends at row kept[e],
+        // so rows past it are dropped by the hardware.
+        {
+            const uint16_t* biasb = g.bias ? g.bias + (size_t)cur.e * g.N + cur.n0 : nullptr;
+            constexpr int TNO = (MODE == MODE_SWIGLU) ? TN / 2 : TN;
+            constexpr int B = EP::OUT_BYTES;
+            const i32x4_t rsO = make_rsrc(
+                static_cast<unsigned char*>(g.out) + (((size_t)cur.e * g.C + cur.m0) * g.N + cur.n0) * B,
+                (uint32_t)(((size_t)(cur.kept - cur.m0) * g.N - cur.n0) * B));
+            const int row_l = wm * WM_ROWS + (lane / 32) * 4;
+#pragma unroll
+            for (int j = 0; j < TNO; ++j) {
+                const int ocol = (MODE == MODE_SWIGLU ? wn * (WN_COLS / 2) : wn * WN_COLS) + j * 32 +
+                                 lane % 32;
+                const int voff = (row_l * g.N + ocol) * B;
+                float bv = 0.f;
+                if (MODE != MODE_SWIGLU && biasb) bv = bf2f(biasb[ocol]);
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
 #pragma unroll
-                    for (int j = 0; j < TNO; ++j) {
-                        const int ocol = (MODE == MODE_SWIGLU ? wn * (WN_COLS / 2) : wn * WN_COLS) + j * 32 +
-                                         lane % 32;
-                        float bv = 0.f;
-                        if (MODE != MODE_SWIGLU && biasb) bv = bf2f(biasb[ocol]);
-#pragma unroll
-                        for (int q = 0; q < 16; ++q) {
-                            // 32 x 32 accumulator: element q of lane l is row
-                            // 8*(q/4) + 4*(l/32) + q%4, column l%32
-                            const int orow = (wm * WM_ROWS) % EP::ROWS + i * 32 + (q / 4) * 8 +
-                                             (lane / 32) * 4 + (q % 4);
-                            float v;
-                            if (MODE == MODE_SWIGLU)
-                                v = silu_f(acc[i][j][q]) * acc[i][j + TN / 2][q];
-                            else if (MODE == MODE_GELU)
-                                v = gelu_f(acc[i][j][q] + bv);
-                            else
-                                v = acc[i][j][q] + bv;
-                            unsigned char* dst = smem + orow * EP::LD_BYTES + ocol * EP::OUT_BYTES;
-                            if (MODE == MODE_DOWN)
-                                *reinterpret_cast<float*>(dst) = v;
-                            else
-                                *reinterpret_cast<uint16_t*>(dst) = (uint16_t)f2bf(v);
-                        }
+                    for (int q = 0; q < 16; ++q) {
+                        const int soff = ((i * 32 + (q / 4) * 8 + (q % 4)) * g.N) * B;
+                        float v;
+                        if (MODE == MODE_SWIGLU)
+                            v = silu_f(acc[i][j][q]) * acc[i][j + TN / 2][q];
+                        else if (MODE == MODE_GELU)
+                            v = gelu_f(acc[i][j][q] + bv);
+                        else
+                            v = acc[i][j][q] + bv;
+                        if (MODE == MODE_DOWN)
+                            buffer_store_f32(v, rsO, voff, soff, 0);
+                        else
+                            buffer_store_i16((short)f2bf(v), rsO, voff, soff, 0);
                     }
                 }
             }
-            __syncthreads();
-            const int row0 = m0 + ph * EP::ROWS;
-            unsigned char* ob = static_cast<unsigned char*>(g.out) +
-                                (((size_t)e * g.C + row0) * g.N + n0) * EP::OUT_BYTES;
-            for (int v = tid; v < EP::ROWS * vec_per_row; v += kGThreads) {
-                const int row = v / vec_per_row, c = v % vec_per_row;
-                if (row0 + row < kept)
-                    *reinterpret_cast<uint4*>(ob + (size_t)row * g.N * EP::OUT_BYTES + c * 16) =
-                        *reinterpret_cast<const uint4*>(smem + row * EP::LD_BYTES + c * 16);
-            }
-            __syncthreads();
         }
+        if (!nxt.valid) break;
+        cur = nxt;
+        base = (base + nk) & 1;
     }
 }
 
@@ -465,10 +491,10 @@ int num_cus() {
     return n;
 }
 
-template <int MODE>
+template <int MODE, int BN>
 moe_status_t launch_gemm(const GemmArgs& a, hipStream_t st) {
-    using EP = Epi<MODE>;
-    auto kern = grouped_gemm_kernel<MODE>;
+    using EP = Epi<MODE, BN>;
+    auto kern = grouped_gemm_kernel<MODE, BN>;
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)EP::LDS) != hipSuccess)
         return MOE_ERR_LAUNCH;
@@ -480,6 +506,28 @@ moe_status_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kGThreads), EP::LDS, st, a);
     MOE_CHECK_LAUNCH();
     return MOE_OK;
+}
+
+// A single-matrix product (GELU first product, down product) can run with
+// 128-column B tiles.  They do half the work of a 256-column tile but run
+// about 35% less efficiently per FLOP on MI355X, so they are used only when
+// they cut the rounds of 256-column tiles (on the largest tile count kept[]
+// allows) by more than 40%: small products whose single round is mostly empty.
+bool use_narrow_tiles(const GemmArgs& a) {
+    if (a.N % 128) return false;
+    const int64_t cus = num_cus();
+    const int64_t mt = (int64_t)a.E * ((a.C + kBM - 1) / kBM);
+    const int64_t t256 = (a.N % 256) ? -1 : mt * (a.N / 256);
+    if (t256 < 0) return true;
+    const int64_t t128 = mt * (a.N / 128);
+    const double c256 = (double)((t256 + cus - 1) / cus);
+    const double c128 = 0.5 * (double)((t128 + cus - 1) / cus);
+    return c128 < 0.6 * c256;
+}
+
+template <int MODE>
+moe_status_t launch_single(const GemmArgs& a, hipStream_t st) {
+    return use_narrow_tiles(a) ? launch_gemm<MODE, 128>(a, st) : launch_gemm<MODE, 256>(a, st);
 }
 
 }  // namespace
@@ -522,8 +570,8 @@ extern "C" moe_status_t moe_expert_ffn(void* stream, moe_dtype_t dtype, moe_act_
         return MOE_OK;
     }
     // bf16: K steps of 64; output tiles of 128 (SwiGLU h) or 256 columns
-    if (H % kBN || I % kBK) return MOE_ERR_ALIGN;
-    if (act == MOE_ACT_SWIGLU ? (I % (kBN / 2)) : (I % kBN)) return MOE_ERR_ALIGN;
+    if (H % kBNMax || I % kBK) return MOE_ERR_ALIGN;
+    if (act == MOE_ACT_SWIGLU ? (I % (kBNMax / 2)) : (I % kBNMax)) return MOE_ERR_ALIGN;
     if (C > (1 << 30) / 8) return MOE_ERR_UNSUPPORTED;
     if (H < 2 * kBK || I < 2 * kBK) return MOE_ERR_ALIGN;  // the k pipeline needs two steps
     const void* ptrs[] = {x_disp, w1, w3, w2, b1, b2, h_ws, y_disp};
@@ -540,8 +588,8 @@ extern "C" moe_status_t moe_expert_ffn(void* stream, moe_dtype_t dtype, moe_act_
     a1.C = C;
     a1.K = (int)H;
     a1.N = (int)I;
-    moe_status_t s = act == MOE_ACT_SWIGLU ? launch_gemm<MODE_SWIGLU>(a1, st)
-                                           : launch_gemm<MODE_GELU>(a1, st);
+    moe_status_t s = act == MOE_ACT_SWIGLU ? launch_gemm<MODE_SWIGLU, 256>(a1, st)
+                                           : launch_single<MODE_GELU>(a1, st);
     if (s != MOE_OK) return s;
     GemmArgs a2 = a1;
     a2.A = static_cast<const uint16_t*>(h_ws);
@@ -551,5 +599,5 @@ extern "C" moe_status_t moe_expert_ffn(void* stream, moe_dtype_t dtype, moe_act_
     a2.out = y_disp;
     a2.K = (int)I;
     a2.N = (int)H;
-    return launch_gemm<MODE_DOWN>(a2, st);
+    return launch_single<MODE_DOWN>(a2, st);
 }
