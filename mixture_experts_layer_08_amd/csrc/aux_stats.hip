@@ -7,7 +7,8 @@
 //      flattened top-k indices and divides by their number (T * k).
 // [P1] LLaMA4-MoE guide (dpshk.com/news/5809432) section 3.2: the same loss.
 //
-// Two launches, both in a fixed order so results are bitwise reproducible:
+// Two launches (one workgroup for up to 65536 probabilities), both in a fixed
+// order so results are bitwise reproducible:
 //  1. each block takes a contiguous token range, sums probs columns (fp32
 //     per thread, fp64 across threads) and counts expert ids with LDS
 //     integer atomics (integer sums are order-independent);
@@ -95,6 +96,65 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void aux_final_kernel(
     }
 }
 
+// Small inputs (T*E <= 65536 probabilities): everything in one workgroup.
+constexpr int kAuxSmallThreads = 1024;
+
+__global__ __launch_bounds__(kAuxSmallThreads) void aux_small_kernel(
+    const int32_t* __restrict__ idx, const float* __restrict__ probs, int64_t T, int E, int k,
+    float alpha, int32_t* counts, float* f, float* p, float* l_aux) {
+    __shared__ int cnt[MOE_MAX_EXPERTS];
+    __shared__ double colsum[kAuxSmallThreads];
+    __shared__ double fp[MOE_MAX_EXPERTS];
+    const int tid = threadIdx.x;
+    if (tid < E) cnt[tid] = 0;
+    __syncthreads();
+    for (int64_t a0 = tid; a0 < T * k; a0 += 8 * kAuxSmallThreads) {
+        int ids[8];  // eight loads in flight
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t a = a0 + (int64_t)u * kAuxSmallThreads;
+            ids[u] = a < T * k ? idx[a] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if ((unsigned)ids[u] < (unsigned)E) atomicAdd(&cnt[ids[u]], 1);
+    }
+    const int rows = kAuxSmallThreads / E;
+    const int r = tid / E, e = tid % E;
+    float s = 0.f;
+    if (r < rows) {
+        // sixteen loads in flight, summed in token order
+        for (int64_t t0 = r; t0 < T; t0 += 16 * (int64_t)rows) {
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int64_t t = t0 + (int64_t)u * rows;
+                v[u] = t < T ? probs[t * E + e] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) s += v[u];
+        }
+    }
+    colsum[tid] = (r < rows) ? (double)s : 0.0;
+    __syncthreads();
+    if (tid < E) {
+        double acc = 0.0;
+        for (int rr = 0; rr < rows; ++rr) acc += colsum[rr * E + tid];
+        const double fe = (double)cnt[tid] / ((double)T * k);
+        const double pe = acc / (double)T;
+        counts[tid] = cnt[tid];
+        f[tid] = (float)fe;
+        p[tid] = (float)pe;
+        fp[tid] = fe * pe;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double acc = 0.0;
+        for (int i = 0; i < E; ++i) acc += fp[i];
+        *l_aux = (float)((double)alpha * E * acc);
+    }
+}
+
 int aux_blocks(int64_t T) { return (int)((T + kAuxTokPerBlock - 1) / kAuxTokPerBlock); }
 
 }  // namespace
@@ -119,6 +179,12 @@ extern "C" moe_status_t moe_aux_stats(void* stream, const int32_t* topk_idx, con
         if (ws_bytes < moe_aux_ws_bytes(T, E)) return MOE_ERR_WORKSPACE;
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (T > 0 && T * E <= 65536) {
+        hipLaunchKernelGGL(aux_small_kernel, dim3(1), dim3(kAuxSmallThreads), 0, st, topk_idx, probs,
+                           T, E, k, alpha, counts, f, p, l_aux);
+        MOE_CHECK_LAUNCH();
+        return MOE_OK;
+    }
     // workspace: [nb][E] double sums (8-byte aligned first), then [nb][E] int32 counts
     double* ws_sum = static_cast<double*>(ws);
     int32_t* ws_cnt = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + (size_t)nb * E * 8);

@@ -80,6 +80,26 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void disp_scan_kernel(const int32_
     }
 }
 
+// Rank of this lane's assignment among the earlier lanes of the wave with the
+// same expert, plus the wave's running count of that expert (held by lane e
+// of `run`, which is updated).  One uniform iteration per distinct expert in
+// the chunk; the leader's expert and the running count are read with
+// readlane, so no step waits on LDS.
+__device__ __forceinline__ int wave_rank(int e, bool ok, int& run, int lane, uint64_t lt_mask) {
+    int r = 0;
+    uint64_t rem = __ballot(ok);
+    while (rem) {
+        const int leader = __builtin_ctzll(rem);
+        const int ee = __builtin_amdgcn_readlane(e, leader);
+        const uint64_t m = __ballot(ok && e == ee);
+        const int base = __builtin_amdgcn_readlane(run, ee);
+        if (ok && e == ee) r = base + __popcll(m & lt_mask);
+        run += (lane == ee) ? __popcll(m) : 0;
+        rem &= ~m;
+    }
+    return r;
+}
+
 __global__ __launch_bounds__(kDThreads) void disp_rank_kernel(
     const int32_t* __restrict__ idx, int64_t A, int E, int k, int64_t C,
     const int32_t* __restrict__ off, const int32_t* __restrict__ kept, int32_t* __restrict__ slot,
@@ -100,18 +120,7 @@ __global__ __launch_bounds__(kDThreads) void disp_rank_kernel(
         const bool valid = a < A;
         const int e = valid ? idx[a] : -1;
         my_e[c] = e;
-        int r = 0;
-        uint64_t rem = __ballot(valid);
-        while (rem) {
-            const int leader = __ffsll((unsigned long long)rem) - 1;
-            const int ee = __shfl(e, leader, 64);
-            const uint64_t m = __ballot(e == ee);
-            const int base = __shfl(run, ee, 64);
-            if (e == ee) r = base + __popcll(m & lt_mask);
-            if (lane == ee) run += __popcll(m);
-            rem &= ~m;
-        }
-        rank[c] = r;
+        rank[c] = wave_rank(e, valid && (unsigned)e < (unsigned)E, run, lane, lt_mask);
     }
     if (lane < E) tot[wave][lane] = run;
     __syncthreads();
@@ -207,19 +216,22 @@ extern "C" moe_status_t moe_dispatch(void* stream, moe_dtype_t dtype, const void
     if (nb > 0) {
         hipLaunchKernelGGL(disp_hist_kernel, dim3(nb), dim3(kDThreads), 0, st, topk_idx, A, E, hist);
         MOE_CHECK_LAUNCH();
-    }
-    hipLaunchKernelGGL(disp_scan_kernel, dim3(1), dim3(MOE_MAX_EXPERTS), 0, st, hist, nb, E, C, off,
-                       kept, dropped);
-    MOE_CHECK_LAUNCH();
-    if (nb > 0) {
+        hipLaunchKernelGGL(disp_scan_kernel, dim3(1), dim3(MOE_MAX_EXPERTS), 0, st, hist, nb, E, C,
+                           off, kept, dropped);
+        MOE_CHECK_LAUNCH();
         hipLaunchKernelGGL(disp_rank_kernel, dim3(nb), dim3(kDThreads), 0, st, topk_idx, A, E, k, C,
                            off, kept, slot, slot_token);
         MOE_CHECK_LAUNCH();
-    } else if (C > 0) {
-        // no assignments: every row is empty
-        hipLaunchKernelGGL(disp_rank_kernel, dim3(1), dim3(kDThreads), 0, st, topk_idx, (int64_t)0,
-                           E, k, C, off, kept, slot, slot_token);
+    } else {
+        // no assignments: kept = 0, dropped = 0, every row is empty
+        hipLaunchKernelGGL(disp_scan_kernel, dim3(1), dim3(MOE_MAX_EXPERTS), 0, st, hist, 0, E, C,
+                           off, kept, dropped);
         MOE_CHECK_LAUNCH();
+        if (C > 0) {
+            hipLaunchKernelGGL(disp_rank_kernel, dim3(1), dim3(kDThreads), 0, st, topk_idx,
+                               (int64_t)0, E, k, C, off, kept, slot, slot_token);
+            MOE_CHECK_LAUNCH();
+        }
     }
     if (T > 0 && C > 0) {
         const int row_vecs = (int)(H * esz / 16);

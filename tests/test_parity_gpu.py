@@ -232,6 +232,42 @@ def test_empty_and_degenerate_calls():
     _check_y(cfg, to_np(y2), ref.y, "zero-router y")
 
 
+@pytest.mark.parametrize("T,E,k,cf", [(8192, 8, 2, 1.25), (8193, 8, 2, 1.25), (5461, 5, 3, 0.8),
+                                       (5462, 5, 3, 0.8), (1024, 64, 8, 1.0), (1025, 64, 8, 1.0),
+                                       (2048, 32, 2, 2.0), (2049, 32, 2, 2.0)])
+def test_dispatch_and_aux_both_sizes(T, E, k, cf):
+    """Dispatch and aux statistics on either side of the size where the aux
+    statistics switch from one workgroup to the multi-block kernels (65536
+    probabilities), with skewed loads so that some experts overflow:
+    bit-exact integers, 1e-5 floats, x_disp rows exact copies."""
+    log(f"[sizes] T={T} E={E} k={k} cf={cf}")
+    rng = np.random.default_rng(T * 131 + E)
+    skew = np.linspace(2.0, 0.0, E)              # uneven load, so some experts overflow
+    keys = rng.standard_normal((T, E)) + skew
+    idx = np.argsort(-keys, axis=1, kind="stable")[:, :k].astype(np.int32)
+    probs = np.exp(keys - keys.max(axis=1, keepdims=True))
+    probs = (probs / probs.sum(axis=1, keepdims=True)).astype(np.float32)
+    C = M.capacity(T, k, E, cf)
+    H = 64
+    x = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(DEV)
+    idx_d, probs_d = to_dev(idx, torch.int32), to_dev(probs, torch.float32)
+    x_disp, slot, slot_token, kept, dropped = ops.moe_dispatch(x, idx_d, E, C)
+    counts, f, p, l_aux = ops.moe_aux_stats(idx_d, probs_d, E, 0.01)
+    torch.cuda.synchronize()
+    d = M.dispatch(idx.astype(np.int64), E, C)
+    _dispatch_compare((to_np(slot), to_np(slot_token), to_np(kept), to_np(dropped)), d,
+                      f"sizes T={T}")
+    a = M.aux_stats(idx.astype(np.int64), probs.astype(np.float64), E, 0.01)
+    np.testing.assert_array_equal(to_np(counts), a.counts)
+    assert_rel(to_np(f), a.f, 1e-5, "f")
+    assert_rel(to_np(p), a.P, 1e-5, "p")
+    assert_rel(to_np(l_aux), [a.l_aux], 1e-5, "L_aux")
+    xd = to_np(x_disp).reshape(E * C, H)
+    st = d.slot_token.reshape(-1)
+    rows = np.where(st >= 0)[0]
+    np.testing.assert_array_equal(xd[rows], to_np(x)[st[rows]])
+
+
 def test_deterministic_bitwise():
     cfg = SMALL["bf16-swiglu-e8"]
     log("[det] two runs bitwise identical")
