@@ -172,14 +172,28 @@ moe_status_t moe_dispatch(void* stream, moe_dtype_t dtype, const void* x,
  *   y_disp [E, C, H] fp32  out  expert outputs (fp32 for both dtypes, so
  *                               the combine rounds only once); rows >=
  *                               kept[e] untouched
+ *   ws     NULL, or a workspace of ws_bytes >= moe_expert_ffn_ws_bytes()
+ *          bytes (16-byte aligned; contents need not be initialised).  With
+ *          it, the second product's last, partly filled round of tiles is
+ *          cut along K and the pieces' fp32 partial tiles are summed in a
+ *          fixed order (results stay bitwise reproducible); without it, or
+ *          when it is too small, that round runs whole.  Two calls that run
+ *          at the same time must not share one ws.
  * bf16 runs on the matrix cores with fp32 accumulation; h is rounded to bf16
  * (nearest-even) between the two products.  An expert with kept = 0 is a
- * valid no-op. */
+ * valid no-op.  bf16 limits: H a multiple of 256, I a multiple of 128
+ * (SwiGLU) or 256 (GELU), H and I >= 128; fp32 has no size limit beyond
+ * int32 indexing. */
 moe_status_t moe_expert_ffn(void* stream, moe_dtype_t dtype, moe_act_t act,
                             const void* x_disp, const int32_t* kept, int E,
                             int64_t C, int64_t H, int64_t I, const void* w1,
                             const void* w3, const void* w2, const void* b1,
-                            const void* b2, void* h_ws, void* y_disp);
+                            const void* b2, void* h_ws, void* y_disp, void* ws,
+                            size_t ws_bytes);
+
+/* Bytes of the optional moe_expert_ffn workspace on the current device:
+ * 4 KiB of counters plus one 256 KiB fp32 tile per compute unit. */
+size_t moe_expert_ffn_ws_bytes(void);
 
 /* Weighted combine back to token order.  [P1] section 2.4 and [P2]
  * section 3.1 (each token's output is the weighted sum of its selected

@@ -55,6 +55,15 @@
 #ifndef GEMM_WAVES_N
 #define GEMM_WAVES_N 4
 #endif
+#ifndef FFN1_SPLIT_MAX
+#define FFN1_SPLIT_MAX 4  // most K pieces of a tail tile, first product
+#endif
+#ifndef FFN2_SPLIT_MAX
+#define FFN2_SPLIT_MAX 4  // and second product
+#endif
+#ifndef GEMM_GROUP
+#define GEMM_GROUP 32  // tiles per L2 group: every row tile of an expert x a few column tiles
+#endif
 
 namespace {
 
@@ -102,6 +111,8 @@ __device__ void buffer_store_i16(short v, i32x4_t rsrc, int voffset, int soffset
                                  int aux) __asm("llvm.amdgcn.raw.buffer.store.i16");
 __device__ void buffer_store_f32(float v, i32x4_t rsrc, int voffset, int soffset,
                                  int aux) __asm("llvm.amdgcn.raw.buffer.store.f32");
+__device__ void buffer_store_f32x4(f32x4_t v, i32x4_t rsrc, int voffset, int soffset,
+                                   int aux) __asm("llvm.amdgcn.raw.buffer.store.v4f32");
 
 // Buffer resource: 48-bit base, no stride, num_records bytes; loads past the
 // end return zero and stores past it are dropped.  Every argument must be
@@ -127,7 +138,64 @@ struct GemmArgs {
     int64_t C;
     int K;
     int N;                  // output columns
+    // split-K of the last, partly filled round of tiles (null part: off)
+    float* part;            // per-piece fp32 partial tiles, kPartBytes each
+    int smax;               // at most this many pieces per tile
 };
+
+constexpr size_t kPartBytes = (size_t)kBM * kBNMax * 4;  // one fp32 tile
+constexpr int kSMax = 4;  // most pieces per split tile
+
+// ---------------------------------------------------------- tile schedule --
+// Expert e owns tiles s_pref[e] .. s_pref[e+1]-1: ceil(kept[e] / kBM) row
+// tiles times NT column tiles.  Run by one thread.
+__device__ void build_prefix(const GemmArgs& g, int NT, int* s_pref, int* s_mt) {
+    int cum = 0;
+    for (int e = 0; e < g.E; ++e) {
+        int kp = g.kept[e];
+        if (kp < 0) kp = 0;
+        if (kp > g.C) kp = (int)g.C;
+        const int mt = (kp + kBM - 1) / kBM;
+        s_mt[e] = mt;
+        s_pref[e] = cum;
+        cum += mt * NT;
+    }
+    s_pref[g.E] = cum;
+}
+
+// Whole tiles fill total / G rounds of a G-workgroup launch.  When the last
+// round would leave at least half of the workgroups idle, its tiles are cut
+// along K into this many pieces (1: no split).
+__device__ __forceinline__ int tail_splits(const GemmArgs& g, int total, int G, int nk) {
+    const int remt = total % G;
+    if (!g.part || remt == 0 || 2 * remt > G) return 1;
+    int sp = G / remt;
+    if (sp > g.smax) sp = g.smax;
+    if (sp > kSMax) sp = kSMax;
+    if (sp > nk / 2) sp = nk / 2;  // each piece keeps at least two k-steps
+    return sp < 1 ? 1 : sp;
+}
+
+// Tile `logical` -> expert and row / column tile.  Inside an expert, tiles
+// run in groups of every row tile times gn column tiles (about GEMM_GROUP
+// tiles), column-fastest, so one XCD's run of tiles shares A rows and B
+// panels in its L2.
+__device__ __forceinline__ void map_tile(int logical, const int* s_pref, const int* s_mt, int E,
+                                         int NT, int& e, int& m_tile, int& n_tile) {
+    e = 0;
+    while (e + 1 < E && s_pref[e + 1] <= logical) ++e;
+    const int local = logical - s_pref[e];
+    const int mt = s_mt[e];
+    int gn = GEMM_GROUP / mt;
+    if (gn < 1) gn = 1;
+    if (gn > NT) gn = NT;
+    const int grp = local / (mt * gn);
+    int width = NT - grp * gn;
+    if (width > gn) width = gn;
+    const int rem = local - grp * mt * gn;
+    m_tile = rem / width;
+    n_tile = grp * gn + rem % width;
+}
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 __device__ __forceinline__ float gelu_f(float z) {
@@ -157,6 +225,8 @@ struct Epi {
 struct TileCtx {
     bool valid;
     int e, m0, n0, kept;
+    int kb, nks;                // k-steps kb .. kb + nks - 1
+    int pslot;                  // piece of a split tail tile: tile * splits + piece; else -1
     i32x4_t rsA, rsB;
 };
 
@@ -177,46 +247,44 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
     const int wm = wave / kWN, wn = wave % kWN;  // wave rows wm*WM_ROWS.., columns per wn
     const int NT = g.N / EP::BN_OUT;
-    if (tid == 0) {
-        int cum = 0;
-        for (int e = 0; e < g.E; ++e) {
-            int kp = g.kept[e];
-            if (kp < 0) kp = 0;
-            if (kp > g.C) kp = (int)g.C;
-            const int mt = (kp + kBM - 1) / kBM;
-            s_mt[e] = mt;
-            s_pref[e] = cum;
-            cum += mt * NT;
-        }
-        s_pref[g.E] = cum;
-    }
+    if (tid == 0) build_prefix(g, NT, s_pref, s_mt);
     __syncthreads();
     const int total = __builtin_amdgcn_readfirstlane(s_pref[g.E]);
     const int G = gridDim.x;
     const int xcd = blockIdx.x % 8, slot8 = blockIdx.x / 8;
     const int nk = g.K / kBK;
+    // Whole tiles fill `full` rounds; the last round's `remt` tiles may be cut
+    // along K into `splits` pieces, one per workgroup.  A piece stores its
+    // fp32 partial tile; tail_reduce_kernel, launched next, sums the pieces
+    // of each tile in piece order and runs the epilogue.
+    const int full = total / G;
+    const int remt = total - full * G;
+    const int splits = __builtin_amdgcn_readfirstlane(tail_splits(g, total, G, nk));
     // B sub-tiles are 128 columns (16 KB); wave w fills 1 KB blocks w*QB..,
     // all inside sub-tile (w*QB)/16
     const int sub = (wave * QB) / 16;
 
     auto tile_at = [&](int round) {
         TileCtx c;
-        const int logical = round * G + xcd * (G / 8) + slot8;
+        // full rounds: each XCD takes a contiguous run of G/8 tiles (shared
+        // A rows and B panels stay in its L2); the last, partial round goes
+        // round-robin over the XCDs so that every XCD's fabric bandwidth works
+        const int pos = round == full ? (int)blockIdx.x : xcd * (G / 8) + slot8;
+        int logical = round * G + pos;
+        c.pslot = -1;
+        c.kb = 0;
+        c.nks = nk;
+        if (splits > 1 && round == full) {
+            const int t = pos / splits, piece = pos - t * splits;
+            logical = pos < remt * splits ? full * G + t : total;
+            c.pslot = pos;
+            c.kb = piece * nk / splits;
+            c.nks = (piece + 1) * nk / splits - c.kb;
+        }
         c.valid = logical < total;
         if (!c.valid) return c;
-        int e = 0;
-        while (e + 1 < g.E && s_pref[e + 1] <= logical) ++e;
-        const int local = logical - s_pref[e];
-        const int mt = s_mt[e];
-        int gn = 32 / mt;
-        if (gn < 1) gn = 1;
-        if (gn > NT) gn = NT;
-        const int grp = local / (mt * gn);
-        int width = NT - grp * gn;
-        if (width > gn) width = gn;
-        const int rem = local - grp * mt * gn;
-        const int m_tile = rem / width;
-        const int n_tile = grp * gn + rem % width;
+        int e, m_tile, n_tile;
+        map_tile(logical, s_pref, s_mt, g.E, NT, e, m_tile, n_tile);
         int kept = g.kept[e];
         if (kept > g.C) kept = (int)g.C;
         c.kept = __builtin_amdgcn_readfirstlane(kept);
@@ -303,8 +371,8 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
 
     TileCtx cur = tile_at(0);
     if (!cur.valid) return;
-    issue(cur, 0, 0);
-    issue(cur, 1, 1);
+    issue(cur, cur.kb, 0);
+    issue(cur, cur.kb + 1, 1);
     int base = 0;  // stage holding k-step 0 of the current tile
     for (int round = 0;; ++round) {
         const TileCtx nxt = tile_at(round + 1);
@@ -343,8 +411,9 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             if (M) load_frags(base, 0, a0, b0);
+            const int nks = cur.nks;
             int kt = 0;
-            for (; kt + 2 < nk; ++kt) {
+            for (; kt + 2 < nks; ++kt) {
                 const int s0 = (base + kt) & 1;
                 if (M) {
                     load_frags(s0, 1, a1, b1);
@@ -353,7 +422,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
                 __builtin_amdgcn_sched_barrier(0);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
-                issue(cur, kt + 2, s0);
+                issue(cur, cur.kb + kt + 2, s0);
                 if (M) {
                     load_frags(s0 ^ 1, 0, a0, b0);
                     mma(a1, b1);
@@ -369,7 +438,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
             __builtin_amdgcn_sched_barrier(0);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
-            if (nxt.valid) issue(nxt, 0, s0);
+            if (nxt.valid) issue(nxt, nxt.kb, s0);
             if (M) {
                 load_frags(s0 ^ 1, 0, a0, b0);
                 mma(a1, b1);
@@ -380,12 +449,32 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
             }
             __builtin_amdgcn_sched_barrier(0);
             __syncthreads();  // every wave is done with step nk - 1
-            if (nxt.valid) issue(nxt, 1, s0 ^ 1);
+            if (nxt.valid) issue(nxt, nxt.kb + 1, s0 ^ 1);
         };
         if (cur.m0 + wm * WM_ROWS < cur.kept)
             kloop(std::true_type{});
         else
             kloop(std::false_type{});
+
+        if (cur.pslot >= 0) {
+            // a piece of a split tail tile: store the fp32 partial, lane-major
+            // (16-byte group gi of thread tid at gi * kGThreads + tid); the
+            // tail reduction finishes the tile.  Pieces are the last round.
+            const i32x4_t rsP = make_rsrc(g.part + (size_t)cur.pslot * (kPartBytes / 4),
+                                          (uint32_t)kPartBytes);
+            constexpr int NG = TM * TN * 4;
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                const int i = gi / (TN * 4), j = (gi / 4) % TN, q4 = gi % 4;
+                f32x4_t v;
+                v.x = acc[i][j][4 * q4];
+                v.y = acc[i][j][4 * q4 + 1];
+                v.z = acc[i][j][4 * q4 + 2];
+                v.w = acc[i][j][4 * q4 + 3];
+                buffer_store_f32x4(v, rsP, (gi * kGThreads + tid) * 16, 0, 0);
+            }
+            break;
+        }
 
         // epilogue: activation on the fp32 accumulators, stored straight from
         // registers (element q of a 32 x 32 accumulator in lane l is row
@@ -428,8 +517,90 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
             }
         }
         if (!nxt.valid) break;
-        cur = nxt;
-        base = (base + nk) & 1;
+        base = (base + cur.nks) & 1;
+        cur = tile_at(round + 1);  // recomputed: only what the prefetch needs stays live
+    }
+}
+
+// ------------------------------------------------------- tail reduction ----
+// Finishes the split tail tiles of one grouped_gemm_kernel<MODE, BN> launch
+// of G workgroups: recomputes the same schedule from kept[], sums each
+// element's partials in piece order (the result does not depend on which
+// piece finished first) and runs the product's epilogue.  A work item is one
+// group of four accumulator values of one product thread, in the product's
+// register layout, so partial reads are 16-byte and coalesced.
+template <int MODE, int BN>
+__global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g, int G) {
+    using EP = Epi<MODE, BN>;
+    constexpr int WM_ROWS = kBM / kWMn, WN_COLS = BN / kWN;
+    constexpr int TM = WM_ROWS / 32, TN = WN_COLS / 32;
+    constexpr int TNO = (MODE == MODE_SWIGLU) ? TN / 2 : TN;
+    constexpr int PER_TILE = kGThreads * TM * TNO * 4;
+    __shared__ int s_pref[MOE_MAX_EXPERTS + 1];
+    __shared__ int s_mt[MOE_MAX_EXPERTS];
+    const int NT = g.N / EP::BN_OUT;
+    if (threadIdx.x == 0) build_prefix(g, NT, s_pref, s_mt);
+    __syncthreads();
+    const int total = s_pref[g.E];
+    const int splits = tail_splits(g, total, G, g.K / kBK);
+    if (splits <= 1) return;
+    const int full = total / G, remt = total - full * G;
+    const float4* part = reinterpret_cast<const float4*>(g.part);
+    constexpr size_t PSTRIDE = kPartBytes / 16;
+    for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < (int64_t)remt * PER_TILE;
+         w += (int64_t)gridDim.x * blockDim.x) {
+        const int t = (int)(w / PER_TILE);
+        int r = (int)(w - (int64_t)t * PER_TILE);
+        const int vt = r % kGThreads;  // the product thread that held these values
+        r /= kGThreads;
+        const int q4 = r % 4;
+        r /= 4;
+        const int jo = r % TNO, i = r / TNO;
+        int e, m_tile, n_tile;
+        map_tile(full * G + t, s_pref, s_mt, g.E, NT, e, m_tile, n_tile);
+        int kept = g.kept[e];
+        if (kept > g.C) kept = (int)g.C;
+        const int vwave = vt / kWave, vlane = vt % kWave;
+        const int wm = vwave / kWN, wn = vwave % kWN;
+        const size_t base = (size_t)t * splits * PSTRIDE + vt;
+        const int gi0 = (i * TN + jo) * 4 + q4;                // gate / only operand
+        const int gi1 = (i * TN + jo + TN / 2) * 4 + q4;       // up (SwiGLU)
+        float4 s0 = part[base + (size_t)gi0 * kGThreads];
+        float4 s1 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (MODE == MODE_SWIGLU) s1 = part[base + (size_t)gi1 * kGThreads];
+        for (int pc = 1; pc < splits; ++pc) {
+            const float4 v0 = part[base + pc * PSTRIDE + (size_t)gi0 * kGThreads];
+            s0.x += v0.x; s0.y += v0.y; s0.z += v0.z; s0.w += v0.w;
+            if (MODE == MODE_SWIGLU) {
+                const float4 v1 = part[base + pc * PSTRIDE + (size_t)gi1 * kGThreads];
+                s1.x += v1.x; s1.y += v1.y; s1.z += v1.z; s1.w += v1.w;
+            }
+        }
+        const int m0 = m_tile * kBM, n0 = n_tile * EP::BN_OUT;
+        const int col = n0 + (MODE == MODE_SWIGLU ? wn * (WN_COLS / 2) : wn * WN_COLS) + jo * 32 +
+                        vlane % 32;
+        const int row0 = m0 + wm * WM_ROWS + i * 32 + q4 * 8 + (vlane / 32) * 4;
+        float bv = 0.f;
+        if (MODE != MODE_SWIGLU && g.bias) bv = bf2f(g.bias[(size_t)e * g.N + col]);
+        const float a0[4] = {s0.x, s0.y, s0.z, s0.w};
+        const float a1[4] = {s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int row = row0 + u;
+            if (row >= kept) break;
+            float v;
+            if (MODE == MODE_SWIGLU)
+                v = silu_f(a0[u]) * a1[u];
+            else if (MODE == MODE_GELU)
+                v = gelu_f(a0[u] + bv);
+            else
+                v = a0[u] + bv;
+            const size_t o = ((size_t)e * g.C + row) * g.N + col;
+            if (MODE == MODE_DOWN)
+                static_cast<float*>(g.out)[o] = v;
+            else
+                static_cast<uint16_t*>(g.out)[o] = f2bf(v);
+        }
     }
 }
 
@@ -499,12 +670,18 @@ moe_status_t launch_gemm(const GemmArgs& a, hipStream_t st) {
                             (int)EP::LDS) != hipSuccess)
         return MOE_ERR_LAUNCH;
     const int64_t max_tiles = (int64_t)a.E * ((a.C + kBM - 1) / kBM) * (a.N / EP::BN_OUT);
+    const int64_t max_units = a.part ? max_tiles * a.smax : max_tiles;
     int64_t grid = num_cus();
-    if (grid > max_tiles) grid = (max_tiles + 7) / 8 * 8;
+    if (grid > max_units) grid = (max_units + 7) / 8 * 8;
     grid = grid / 8 * 8;
     if (grid < 8) grid = 8;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kGThreads), EP::LDS, st, a);
     MOE_CHECK_LAUNCH();
+    if (a.part) {  // finishes the split tail tiles, if the device schedule split any
+        hipLaunchKernelGGL((tail_reduce_kernel<MODE, BN>), dim3((unsigned)(4 * num_cus())), dim3(256),
+                           0, st, a, (int)grid);
+        MOE_CHECK_LAUNCH();
+    }
     return MOE_OK;
 }
 
@@ -532,11 +709,17 @@ moe_status_t launch_single(const GemmArgs& a, hipStream_t st) {
 
 }  // namespace
 
+// Workspace of the split tail round: one fp32 partial tile per workgroup of
+// a full-device launch (the two products use it one after the other).
+static size_t ffn_ws_bytes() { return (size_t)num_cus() * kPartBytes; }
+
+extern "C" size_t moe_expert_ffn_ws_bytes(void) { return ffn_ws_bytes(); }
+
 extern "C" moe_status_t moe_expert_ffn(void* stream, moe_dtype_t dtype, moe_act_t act,
                                        const void* x_disp, const int32_t* kept, int E, int64_t C,
                                        int64_t H, int64_t I, const void* w1, const void* w3,
                                        const void* w2, const void* b1, const void* b2, void* h_ws,
-                                       void* y_disp) {
+                                       void* y_disp, void* ws, size_t ws_bytes) {
     if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_DTYPE;
     if (act != MOE_ACT_SWIGLU && act != MOE_ACT_GELU_BIAS) return MOE_ERR_DTYPE;
     if (E < 1 || C < 0 || H <= 0 || I <= 0) return MOE_ERR_SHAPE;
@@ -574,7 +757,7 @@ extern "C" moe_status_t moe_expert_ffn(void* stream, moe_dtype_t dtype, moe_act_
     if (act == MOE_ACT_SWIGLU ? (I % (kBNMax / 2)) : (I % kBNMax)) return MOE_ERR_ALIGN;
     if (C > (1 << 30) / 8) return MOE_ERR_UNSUPPORTED;
     if (H < 2 * kBK || I < 2 * kBK) return MOE_ERR_ALIGN;  // the k pipeline needs two steps
-    const void* ptrs[] = {x_disp, w1, w3, w2, b1, b2, h_ws, y_disp};
+    const void* ptrs[] = {x_disp, w1, w3, w2, b1, b2, h_ws, y_disp, ws};
     for (const void* q : ptrs)
         if (q && !moe_aligned16(q)) return MOE_ERR_ALIGN;
     GemmArgs a1;
@@ -588,6 +771,10 @@ extern "C" moe_status_t moe_expert_ffn(void* stream, moe_dtype_t dtype, moe_act_
     a1.C = C;
     a1.K = (int)H;
     a1.N = (int)I;
+    // with a workspace, each product may split its last, partly filled round
+    const bool split = ws && ws_bytes >= ffn_ws_bytes();
+    a1.part = split ? static_cast<float*>(ws) : nullptr;
+    a1.smax = FFN1_SPLIT_MAX;
     moe_status_t s = act == MOE_ACT_SWIGLU ? launch_gemm<MODE_SWIGLU, 256>(a1, st)
                                            : launch_single<MODE_GELU>(a1, st);
     if (s != MOE_OK) return s;
@@ -599,5 +786,7 @@ extern "C" moe_status_t moe_expert_ffn(void* stream, moe_dtype_t dtype, moe_act_
     a2.out = y_disp;
     a2.K = (int)I;
     a2.N = (int)H;
+    a2.part = split ? static_cast<float*>(ws) : nullptr;
+    a2.smax = FFN2_SPLIT_MAX;
     return launch_single<MODE_DOWN>(a2, st);
 }

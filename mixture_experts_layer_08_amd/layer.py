@@ -47,6 +47,7 @@ class Buffers:
     y_disp: torch.Tensor
     y: torch.Tensor
     ws: torch.Tensor
+    ffn_ws: torch.Tensor
 
 
 class MoELayerGPU:
@@ -84,7 +85,8 @@ class MoELayerGPU:
             x_disp=e(E, C, H, dt=td), slot=e(T, k, dt=i32), slot_token=e(E, C, dt=i32),
             kept=e(E, dt=i32), dropped=e(1, dt=i32), h=e(E, C, I, dt=td),
             y_disp=e(E, C, H), y=e(T, H, dt=td),
-            ws=e(max(1, ops.moe_workspace_bytes(T, E, k)), dt=torch.uint8))
+            ws=e(max(1, ops.moe_workspace_bytes(T, E, k)), dt=torch.uint8),
+            ffn_ws=e(ops.moe_expert_ffn_ws_bytes(), dt=torch.uint8))
 
     # the five steps, each one library call ---------------------------------
     def route(self, x: torch.Tensor, keys: bool = False):
@@ -107,7 +109,7 @@ class MoELayerGPU:
     def experts(self):
         b = self.buf
         return ops.moe_expert_ffn(b.x_disp, b.kept, self.w1, self.w3, self.w2, self.b1, self.b2,
-                                  act=self.cfg.act, h_ws=b.h, y_disp=b.y_disp)
+                                  act=self.cfg.act, h_ws=b.h, y_disp=b.y_disp, ws=b.ffn_ws)
 
     def combine(self):
         b = self.buf

@@ -117,10 +117,17 @@ def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, C: int, *,
     return x_disp, slot, slot_token, kept, dropped
 
 
+def moe_expert_ffn_ws_bytes() -> int:
+    return int(lib().moe_expert_ffn_ws_bytes())
+
+
 def moe_expert_ffn(x_disp: torch.Tensor, kept: torch.Tensor, w1: torch.Tensor,
                    w3: Optional[torch.Tensor], w2: torch.Tensor, b1: Optional[torch.Tensor] = None,
                    b2: Optional[torch.Tensor] = None, *, act: str = "swiglu",
-                   h_ws: Optional[torch.Tensor] = None, y_disp: Optional[torch.Tensor] = None):
+                   h_ws: Optional[torch.Tensor] = None, y_disp: Optional[torch.Tensor] = None,
+                   ws: Optional[torch.Tensor] = None):
+    """ws: optional uint8 workspace (see moe_expert_ffn_ws_bytes); None runs
+    every round of tiles whole."""
     E, C, H = x_disp.shape
     I = w1.shape[2]
     dev = x_disp.device
@@ -135,7 +142,8 @@ def moe_expert_ffn(x_disp: torch.Tensor, kept: torch.Tensor, w1: torch.Tensor,
     y_disp = _want(y_disp, (E, C, H), torch.float32, dev)
     st = lib().moe_expert_ffn(_stream(dev), _dtype_code(x_disp), ACTS[act], _ptr(x_disp),
                               _ptr(kept), E, C, H, I, _ptr(w1), _ptr(w3), _ptr(w2), _ptr(b1),
-                              _ptr(b2), _ptr(h_ws), _ptr(y_disp))
+                              _ptr(b2), _ptr(h_ws), _ptr(y_disp), _ptr(ws),
+                              0 if ws is None else ws.numel() * ws.element_size())
     check("moe_expert_ffn", st)
     return y_disp, h_ws
 

@@ -135,7 +135,8 @@ def test_expert_ffn_argument_errors(L):
                                 kw.get("kept", P), kw.get("E", 8), kw.get("C", 64),
                                 kw.get("H", 256), kw.get("I", 256), kw.get("w1", P),
                                 kw.get("w3", P), kw.get("w2", P), kw.get("b1", None),
-                                kw.get("b2", None), kw.get("h", P), kw.get("y", P))
+                                kw.get("b2", None), kw.get("h", P), kw.get("y", P),
+                                kw.get("ws", None), kw.get("wsb", 0))
     assert f(dtype=2) == DTYPE
     assert f(act=5) == DTYPE
     assert f(E=0) == SHAPE
@@ -149,7 +150,13 @@ def test_expert_ffn_argument_errors(L):
     assert f(H=200) == ALIGN
     assert f(I=200) == ALIGN
     assert f(w1=MIS) == ALIGN
+    assert f(ws=MIS, wsb=1 << 30) == ALIGN
     assert f(C=0, xd=None, h=None, y=None) == OK
+
+
+def test_expert_ffn_workspace_size(L):
+    n = L.moe_expert_ffn_ws_bytes()
+    assert n > 0 and n % (256 * 256 * 4) == 0
 
 
 def test_combine_argument_errors(L):
