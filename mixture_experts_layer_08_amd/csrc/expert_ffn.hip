@@ -13,36 +13,41 @@
 // Design (gfx950): one persistent kernel per product.  The tile list is
 // rebuilt on the device from kept[e] (no host round trip): expert e has
 // ceil(kept[e] / 256) row tiles times N / BN_OUT column tiles.  Workgroup b
-// sits on XCD b % 8; in round r it takes tile r*G + (b % 8)*(G/8) + b/8, so
-// each XCD works through a contiguous run of tiles; runs are ordered expert
-// by expert, in groups that cover every row tile of an expert across a few
-// column tiles, so the A rows and B panels a group shares stay in that
-// XCD's L2.
+// sits on XCD b % 8; in full rounds it takes tile r*G + (b % 8)*(G/8) + b/8,
+// so each XCD works through a contiguous run of tiles, ordered expert by
+// expert in groups that cover every row tile of an expert across a few
+// column tiles, and the A rows and B panels a group shares stay in that
+// XCD's L2.  The last, partly filled round goes round-robin over the XCDs;
+// when it would leave at least half of the workgroups idle its tiles are cut
+// along K into pieces, and tail_reduce_kernel finishes them.
 //
-// Per tile: 256 x 256 outputs (of the B tile: for SwiGLU 128 gate + 128 up
-// columns), K in steps of 64, 4 waves in a 2 x 2 grid, each wave 128 x 128
-// with 64 v_mfma_f32_16x16x32_bf16 accumulators (fp32, 256 registers).
-//   * Global -> LDS: global_load_lds_dwordx4 writes each lane's 16 bytes
+// Per tile: 256 x 256 outputs of the B tile (for SwiGLU 128 gate + 128 up
+// columns), K in steps of 64, 8 waves in a 2 x 4 grid, each wave 128 rows x
+// 64 columns = 4 x 2 v_mfma_f32_32x32x16_bf16 accumulators (128 fp32
+// registers).
+//   * Global -> LDS: buffer_load_dwordx4 ... lds writes each lane's 16 bytes
 //     straight into LDS (no staging registers, no VALU); two LDS stages of
 //     64 KB, the next k-step's loads in flight during the current MFMAs,
-//     one barrier per k-step.
-//   * A = x_disp rows are k-contiguous: LDS rows of 128 bytes with the
-//     16-byte chunk index XOR (row & 7), read with ds_read_b128.
+//     one barrier per k-step; the next tile's first two k-steps load during
+//     the current tile's last ones.
+//   * A = rows of x_disp or h, k-contiguous: LDS rows of 128 bytes with the
+//     16-byte chunk index XOR ((row >> 1) & 7), read with ds_read_b128.  The
+//     A descriptor's byte range ends at row kept[e]: padding rows read as
+//     zero without touching memory.
 //   * B = W[e] in its own [K, N] layout (n-contiguous).  gfx950's
 //     ds_read_b64_tr_b16 reads 4 k-values of one column per lane straight
 //     from an n-contiguous tile: inside each 16-lane group, lane L points at
 //     row k0 + L/4, columns 4*(L%4) .. +3, and receives rows k0..k0+3 of
 //     column L.  Two such reads make one MFMA B operand, so the weights
-//     need no repacking.  The chunk index of each 512-byte B row is XORed
-//     with 2*(k & 3) + 8*((k >> 3) & 1) so the four rows one 16-lane group
-//     reads fall in different banks.
+//     need no repacking.  The chunk index of each 256-byte B row is XORed
+//     with 4*(k & 3) so the rows one read serves fall in different banks.
 // Epilogues run on the fp32 accumulators in registers:
 //   SwiGLU:  a tile holds matching gate and up columns, so
 //            h = silu(g) * u needs no extra pass;
 //   GELU:    h = gelu_erf(acc + b1);   second product: y = acc (+ b2).
-// h is rounded to bf16, y stays fp32; both are staged through LDS for
-// full-row 16-byte stores.  A rows at or beyond kept[e] are loaded from row
-// kept[e] - 1 (in bounds; those output rows are never stored).
+// h is rounded to bf16, y stays fp32; both are stored straight from the
+// accumulators through a descriptor that ends at row kept[e], so the
+// hardware drops the padding rows' stores.
 #include "moe_common.h"
 
 #include <math.h>
