@@ -176,7 +176,7 @@ def main():
         e[2].record(stream)
         layer.dispatch(x)
         e[3].record(stream)
-        layer.experts()
+        layer.experts(x)
         e[4].record(stream)
         layer.combine()
         e[5].record(stream)

@@ -139,11 +139,14 @@ moe_status_t moe_aux_stats(void* stream, const int32_t* topk_idx,
  * e = topk_idx[t, j], walking assignments in row-major (t, then j) order;
  * the row index pos is kept when pos < C.
  *
- *   x          [T, H]    dtype         token activations
+ *   x          [T, H]    dtype         token activations (may be NULL when
+ *                                      x_disp is NULL)
  *   topk_idx   [T, k]    int32         expert of each assignment (< E)
  *   C          rows per expert (normally moe_capacity(T, k, E, cf)), >= 0
  *   x_disp     [E, C, H] dtype  out    x_disp[e, pos] = x[t]; rows >= kept[e]
- *                                      are left untouched
+ *                                      are left untouched.  NULL: only the
+ *                                      indices below are produced (for
+ *                                      moe_expert_ffn_gather)
  *   slot       [T, k]    int32  out    e * C + pos, or -1 when dropped
  *   slot_token [E, C]    int32  out    token in that row, or -1
  *   kept       [E]       int32  out    min(assignments to e, C)
@@ -190,6 +193,26 @@ moe_status_t moe_expert_ffn(void* stream, moe_dtype_t dtype, moe_act_t act,
                             const void* w3, const void* w2, const void* b1,
                             const void* b2, void* h_ws, void* y_disp, void* ws,
                             size_t ws_bytes);
+
+/* moe_expert_ffn with the row copy fused into the first product's loads:
+ * the A rows come straight from the token activations through slot_token,
+ * so no x_disp is written or read ([P3] section 2.1 gathers each expert's
+ * tokens inside the expert kernel instead of materialising them).
+ *
+ *   x          [T, H]    dtype   token activations (16-byte aligned)
+ *   slot_token [E, C]    int32   moe_dispatch's output: token of each row
+ *                                r < kept[e]; entries past kept[e] unused
+ * Every other argument, output, workspace use and limit is as for
+ * moe_expert_ffn; in addition T * H * sizeof(dtype) must be below 2^31.
+ * The result equals moe_expert_ffn on the dispatched copy. */
+moe_status_t moe_expert_ffn_gather(void* stream, moe_dtype_t dtype, moe_act_t act,
+                                   const void* x, const int32_t* slot_token,
+                                   int64_t T, const int32_t* kept, int E,
+                                   int64_t C, int64_t H, int64_t I,
+                                   const void* w1, const void* w3,
+                                   const void* w2, const void* b1,
+                                   const void* b2, void* h_ws, void* y_disp,
+                                   void* ws, size_t ws_bytes);
 
 /* Bytes of the optional moe_expert_ffn workspace on the current device:
  * 4 KiB of counters plus one 256 KiB fp32 tile per compute unit. */

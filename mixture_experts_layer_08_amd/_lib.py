@@ -24,8 +24,8 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_capacity", "moe_status_string", "moe_workspace_bytes", "moe_route",
-           "moe_aux_stats", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_ws_bytes",
-           "moe_combine")
+           "moe_aux_stats", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_gather",
+           "moe_expert_ffn_ws_bytes", "moe_combine")
 
 _lock = threading.Lock()
 _lib = None
@@ -59,6 +59,9 @@ def _declare(L: ctypes.CDLL) -> None:
     L.moe_expert_ffn.argtypes = [vp, i32, i32, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp, vp,
                                  vp, vp, vp, c.c_size_t]
     L.moe_expert_ffn.restype = i32
+    L.moe_expert_ffn_gather.argtypes = [vp, i32, i32, vp, vp, i64, vp, i32, i64, i64, i64, vp,
+                                        vp, vp, vp, vp, vp, vp, vp, c.c_size_t]
+    L.moe_expert_ffn_gather.restype = i32
     L.moe_expert_ffn_ws_bytes.argtypes = []
     L.moe_expert_ffn_ws_bytes.restype = c.c_size_t
     L.moe_combine.argtypes = [vp, i32, vp, vp, vp, i64, i64, i32, vp]

@@ -204,8 +204,9 @@ extern "C" moe_status_t moe_dispatch(void* stream, moe_dtype_t dtype, const void
     const int esz = dtype == MOE_BF16 ? 2 : 4;
     if ((H * esz) % 16) return MOE_ERR_ALIGN;
     if (!kept || !dropped) return MOE_ERR_NULL;
-    if (T > 0 && (!x || !topk_idx || !slot)) return MOE_ERR_NULL;
-    if (C > 0 && (!slot_token || !x_disp)) return MOE_ERR_NULL;
+    if (T > 0 && (!topk_idx || !slot)) return MOE_ERR_NULL;
+    if (C > 0 && !slot_token) return MOE_ERR_NULL;
+    if (T > 0 && x_disp && !x) return MOE_ERR_NULL;  // x_disp NULL: indices only, no copy
     if ((x && !moe_aligned16(x)) || (x_disp && !moe_aligned16(x_disp))) return MOE_ERR_ALIGN;
     const int64_t A = T * k;
     const int nb = disp_blocks(A);
@@ -233,7 +234,7 @@ extern "C" moe_status_t moe_dispatch(void* stream, moe_dtype_t dtype, const void
             MOE_CHECK_LAUNCH();
         }
     }
-    if (T > 0 && C > 0) {
+    if (T > 0 && C > 0 && x_disp) {
         const int row_vecs = (int)(H * esz / 16);
         const int64_t grid = (T + kCopyTok - 1) / kCopyTok;
         hipLaunchKernelGGL(disp_copy_kernel, dim3((unsigned)grid), dim3(kDThreads), 0, st,

@@ -100,12 +100,17 @@ typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; nothing else in these kernels uses it
 __device__ __forceinline__ void lds_dma16(i32x4_t rsrc, const void* lds, int voffset, int soffset) {
-    const uint32_t m0 = (uint32_t)(uintptr_t)(const lds_void_t*)lds;
+    // every scalar operand is wave-uniform; readfirstlane states it to the compiler
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds);
+    rsrc.x = __builtin_amdgcn_readfirstlane(rsrc.x);
+    rsrc.y = __builtin_amdgcn_readfirstlane(rsrc.y);
+    rsrc.z = __builtin_amdgcn_readfirstlane(rsrc.z);
+    rsrc.w = __builtin_amdgcn_readfirstlane(rsrc.w);
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "buffer_load_dwordx4 %1, %2, %3 offen lds"
         :
-        : "s"(m0), "v"(voffset), "s"(rsrc), "s"(soffset)
+        : "s"(m0), "v"(voffset), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soffset))
         : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -133,7 +138,9 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
 }
 
 struct GemmArgs {
-    const uint16_t* A;      // [E, C, K]
+    const uint16_t* A;      // [E, C, K], or with slot_token the token rows [a_rows, K]
+    const int32_t* slot_token;  // [E, C] token of each row (-1: empty), or null
+    int64_t a_rows;
     const uint16_t* B0;     // [E, K, N] gate / W1 / W2
     const uint16_t* B1;     // [E, K, N] up (SwiGLU)
     const uint16_t* bias;   // [E, N] or null
@@ -233,9 +240,14 @@ struct TileCtx {
     int kb, nks;                // k-steps kb .. kb + nks - 1
     int pslot;                  // piece of a split tail tile: tile * splits + piece; else -1
     i32x4_t rsA, rsB;
+    // gathered A: token of each of this lane's (up to 4) A rows, or -1 (a
+    // vector, not an array, so element access stays in registers)
+    i32x4_t tok;
 };
 
-template <int MODE, int BN>
+// GATHER: the A rows are read from the token rows x[slot_token[e, r]]
+// instead of a dispatched copy (rows with token -1 read as zero).
+template <int MODE, int BN, bool GATHER>
 __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     using EP = Epi<MODE, BN>;
     constexpr int kStage = EP::STAGE;
@@ -244,6 +256,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
     constexpr int TM = WM_ROWS / 32, TN = WN_COLS / 32;  // 32 x 32 MFMA tiles per wave
     constexpr int QA = 32 / kNW;              // 1 KB A loads per wave per k-step
     constexpr int QB = (BN / 128) * 16 / kNW; // 1 KB B loads per wave per k-step
+    static_assert(QA <= 4 && QA % 2 == 0, "A loads per wave");
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_pref[MOE_MAX_EXPERTS + 1];
     __shared__ int s_mt[MOE_MAX_EXPERTS];
@@ -296,9 +309,20 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
         c.e = __builtin_amdgcn_readfirstlane(e);
         c.m0 = __builtin_amdgcn_readfirstlane(m_tile * kBM);
         c.n0 = __builtin_amdgcn_readfirstlane(n_tile * EP::BN_OUT);
-        // A: rows m0.. of expert e; rows at or past kept read as zero
-        c.rsA = make_rsrc(g.A + ((size_t)c.e * g.C + c.m0) * g.K,
-                          (uint32_t)((size_t)(c.kept - c.m0) * g.K * 2));
+        if (GATHER) {
+            // A: token rows; a row past kept (or an empty slot) reads as zero
+            c.rsA = make_rsrc(g.A, (uint32_t)((size_t)g.a_rows * g.K * 2));
+#pragma unroll
+            for (int q = 0; q < QA; ++q) {  // branch-free: clamp, load, then select
+                const int row = c.m0 + (wave * QA + q) * 8 + lane / 8;
+                const int t = g.slot_token[(size_t)c.e * g.C + (row < c.kept ? row : c.kept - 1)];
+                c.tok[q] = row < c.kept ? t : -1;
+            }
+        } else {
+            // A: rows m0.. of expert e; rows at or past kept read as zero
+            c.rsA = make_rsrc(g.A + ((size_t)c.e * g.C + c.m0) * g.K,
+                              (uint32_t)((size_t)(c.kept - c.m0) * g.K * 2));
+        }
         const uint16_t* bsrc;
         size_t coloff;
         if (MODE == MODE_SWIGLU) {
@@ -320,12 +344,23 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
     // B load q: sub-tile row kr = ((wave*QB + q) % 16)*4 + lane/16,
     // chunk (lane % 16) ^ swz_b(kr) with swz_b(kr) = 4*(lane/16)
     const int voffB = ((lane / 16) * g.N + (((lane % 16) ^ ((lane / 16) << 2)) * 8)) * 2;
+    // gathered A: the same chunk positions, row offset from the token; an
+    // empty row gets an offset past the descriptor's range (reads zero)
+    const int chA0 = (((lane % 8) ^ (lane / 16)) * 8) * 2;
+    const int chA1 = (((lane % 8) ^ (4 + lane / 16)) * 8) * 2;
     auto issue = [&](const TileCtx& c, int kt, int stage) {
         unsigned char* st = smem + stage * kStage;
 #pragma unroll
-        for (int q = 0; q < QA; ++q)
-            lds_dma16(c.rsA, st + (wave * QA + q) * 1024, (q & 1) ? voffA1 : voffA0,
-                      (q * 8 * g.K + kt * kBK) * 2);
+        for (int q = 0; q < QA; ++q) {
+            if (GATHER) {
+                const int tk = c.tok[q];
+                const int vo = tk >= 0 ? tk * g.K * 2 + ((q & 1) ? chA1 : chA0) : (int)0x80000000;
+                lds_dma16(c.rsA, st + (wave * QA + q) * 1024, vo, kt * kBK * 2);
+            } else {
+                lds_dma16(c.rsA, st + (wave * QA + q) * 1024, (q & 1) ? voffA1 : voffA0,
+                          (q * 8 * g.K + kt * kBK) * 2);
+            }
+        }
 #pragma unroll
         for (int q = 0; q < QB; ++q)
             lds_dma16(c.rsB, st + kStageA + (wave * QB + q) * 1024, voffB,
@@ -415,6 +450,14 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
             bf16x8_t a0[2][TM], b0[2][TN], a1[2][TM], b1[2][TN];
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
+            if (GATHER) {
+                // The row tokens were loaded by compiler-visible loads; using
+                // them here makes the compiler's own wait for them happen once,
+                // now, instead of before every issue() inside the loop (where
+                // it would also wait for the k-step loads in flight).
+#pragma unroll
+                for (int q = 0; q < QA; ++q) asm volatile("" ::"v"(cur.tok[q]));
+            }
             if (M) load_frags(base, 0, a0, b0);
             const int nks = cur.nks;
             int kt = 0;
@@ -614,6 +657,7 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g, int G) {
 // meant for small fp32 layers.
 template <int MODE>
 __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ A,
+                                                      const int32_t* __restrict__ slot_token,
                                                       const float* __restrict__ B0,
                                                       const float* __restrict__ B1,
                                                       const float* __restrict__ bias,
@@ -627,13 +671,22 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
     const int m0 = blockIdx.y * 16, n0 = blockIdx.x * 16;
     if (m0 >= kept) return;
     const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
-    const float* Ab = A + (size_t)e * C * K;
+    const float* Ab = A + (size_t)e * C * K;  // gathered: rows of A via slot_token
     const float* B0b = B0 + (size_t)e * K * N;
     const float* B1b = (MODE == MODE_SWIGLU) ? B1 + (size_t)e * K * N : nullptr;
     float s0 = 0.f, s1 = 0.f;
     for (int k0 = 0; k0 < K; k0 += 16) {
         const int r = m0 + ty, kk = k0 + tx;
-        as[ty][tx] = (r < kept && kk < K) ? Ab[(size_t)r * K + kk] : 0.f;
+        float av = 0.f;
+        if (r < kept && kk < K) {
+            if (slot_token) {
+                const int tok = slot_token[(size_t)e * C + r];
+                av = tok >= 0 ? A[(size_t)tok * K + kk] : 0.f;
+            } else {
+                av = Ab[(size_t)r * K + kk];
+            }
+        }
+        as[ty][tx] = av;
         const int kr = k0 + ty, c = n0 + tx;
         b0s[ty][tx] = (kr < K && c < N) ? B0b[(size_t)kr * N + c] : 0.f;
         if (MODE == MODE_SWIGLU) b1s[ty][tx] = (kr < K && c < N) ? B1b[(size_t)kr * N + c] : 0.f;
@@ -667,10 +720,10 @@ int num_cus() {
     return n;
 }
 
-template <int MODE, int BN>
+template <int MODE, int BN, bool GATHER = false>
 moe_status_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     using EP = Epi<MODE, BN>;
-    auto kern = grouped_gemm_kernel<MODE, BN>;
+    auto kern = grouped_gemm_kernel<MODE, BN, GATHER>;
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)EP::LDS) != hipSuccess)
         return MOE_ERR_LAUNCH;
@@ -707,9 +760,10 @@ bool use_narrow_tiles(const GemmArgs& a) {
     return c128 < 0.6 * c256;
 }
 
-template <int MODE>
+template <int MODE, bool GATHER = false>
 moe_status_t launch_single(const GemmArgs& a, hipStream_t st) {
-    return use_narrow_tiles(a) ? launch_gemm<MODE, 128>(a, st) : launch_gemm<MODE, 256>(a, st);
+    return use_narrow_tiles(a) ? launch_gemm<MODE, 128, GATHER>(a, st)
+                               : launch_gemm<MODE, 256, GATHER>(a, st);
 }
 
 }  // namespace
@@ -720,40 +774,48 @@ static size_t ffn_ws_bytes() { return (size_t)num_cus() * kPartBytes; }
 
 extern "C" size_t moe_expert_ffn_ws_bytes(void) { return ffn_ws_bytes(); }
 
-extern "C" moe_status_t moe_expert_ffn(void* stream, moe_dtype_t dtype, moe_act_t act,
-                                       const void* x_disp, const int32_t* kept, int E, int64_t C,
-                                       int64_t H, int64_t I, const void* w1, const void* w3,
-                                       const void* w2, const void* b1, const void* b2, void* h_ws,
-                                       void* y_disp, void* ws, size_t ws_bytes) {
+namespace {
+
+// Both entry points: A is x_disp [E, C, H], or with slot_token the token
+// rows x [a_rows, H] gathered through slot_token [E, C].
+moe_status_t ffn_impl(void* stream, moe_dtype_t dtype, moe_act_t act, const void* A,
+                      const int32_t* slot_token, int64_t a_rows, const int32_t* kept, int E,
+                      int64_t C, int64_t H, int64_t I, const void* w1, const void* w3,
+                      const void* w2, const void* b1, const void* b2, void* h_ws, void* y_disp,
+                      void* ws, size_t ws_bytes) {
     if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_DTYPE;
     if (act != MOE_ACT_SWIGLU && act != MOE_ACT_GELU_BIAS) return MOE_ERR_DTYPE;
-    if (E < 1 || C < 0 || H <= 0 || I <= 0) return MOE_ERR_SHAPE;
+    if (E < 1 || C < 0 || H <= 0 || I <= 0 || a_rows < 0) return MOE_ERR_SHAPE;
     if (E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
     if (H > (1 << 20) || I > (1 << 20) || C >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
     if (!kept || !w1 || !w2) return MOE_ERR_NULL;
     if (act == MOE_ACT_SWIGLU && !w3) return MOE_ERR_NULL;
     if (act == MOE_ACT_GELU_BIAS && !b1) return MOE_ERR_NULL;
     if (C == 0) return MOE_OK;
-    if (!x_disp || !h_ws || !y_disp) return MOE_ERR_NULL;
+    if (!A || !h_ws || !y_disp) return MOE_ERR_NULL;
+    const int esz = dtype == MOE_BF16 ? 2 : 4;
+    // gathered rows are addressed with 32-bit byte offsets
+    if (slot_token && a_rows * H * esz >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (dtype == MOE_F32) {
-        const float* X = static_cast<const float*>(x_disp);
+        const float* X = static_cast<const float*>(A);
         float* Hh = static_cast<float*>(h_ws);
         float* Y = static_cast<float*>(y_disp);
         dim3 g1((unsigned)((I + 15) / 16), (unsigned)((C + 15) / 16), (unsigned)E);
         dim3 g2((unsigned)((H + 15) / 16), (unsigned)((C + 15) / 16), (unsigned)E);
         if (act == MOE_ACT_SWIGLU)
-            hipLaunchKernelGGL(ffn_f32_kernel<MODE_SWIGLU>, g1, dim3(256), 0, st, X,
+            hipLaunchKernelGGL(ffn_f32_kernel<MODE_SWIGLU>, g1, dim3(256), 0, st, X, slot_token,
                                static_cast<const float*>(w1), static_cast<const float*>(w3),
                                (const float*)nullptr, Hh, kept, C, (int)H, (int)I);
         else
-            hipLaunchKernelGGL(ffn_f32_kernel<MODE_GELU>, g1, dim3(256), 0, st, X,
+            hipLaunchKernelGGL(ffn_f32_kernel<MODE_GELU>, g1, dim3(256), 0, st, X, slot_token,
                                static_cast<const float*>(w1), (const float*)nullptr,
                                static_cast<const float*>(b1), Hh, kept, C, (int)H, (int)I);
         MOE_CHECK_LAUNCH();
         hipLaunchKernelGGL(ffn_f32_kernel<MODE_DOWN>, g2, dim3(256), 0, st, (const float*)Hh,
-                           static_cast<const float*>(w2), (const float*)nullptr,
-                           static_cast<const float*>(b2), Y, kept, C, (int)I, (int)H);
+                           (const int32_t*)nullptr, static_cast<const float*>(w2),
+                           (const float*)nullptr, static_cast<const float*>(b2), Y, kept, C,
+                           (int)I, (int)H);
         MOE_CHECK_LAUNCH();
         return MOE_OK;
     }
@@ -762,11 +824,13 @@ extern "C" moe_status_t moe_expert_ffn(void* stream, moe_dtype_t dtype, moe_act_
     if (act == MOE_ACT_SWIGLU ? (I % (kBNMax / 2)) : (I % kBNMax)) return MOE_ERR_ALIGN;
     if (C > (1 << 30) / 8) return MOE_ERR_UNSUPPORTED;
     if (H < 2 * kBK || I < 2 * kBK) return MOE_ERR_ALIGN;  // the k pipeline needs two steps
-    const void* ptrs[] = {x_disp, w1, w3, w2, b1, b2, h_ws, y_disp, ws};
+    const void* ptrs[] = {A, w1, w3, w2, b1, b2, h_ws, y_disp, ws};
     for (const void* q : ptrs)
         if (q && !moe_aligned16(q)) return MOE_ERR_ALIGN;
     GemmArgs a1;
-    a1.A = static_cast<const uint16_t*>(x_disp);
+    a1.A = static_cast<const uint16_t*>(A);
+    a1.slot_token = slot_token;
+    a1.a_rows = a_rows;
     a1.B0 = static_cast<const uint16_t*>(w1);
     a1.B1 = static_cast<const uint16_t*>(w3);
     a1.bias = act == MOE_ACT_GELU_BIAS ? static_cast<const uint16_t*>(b1) : nullptr;
@@ -780,11 +844,18 @@ extern "C" moe_status_t moe_expert_ffn(void* stream, moe_dtype_t dtype, moe_act_
     const bool split = ws && ws_bytes >= ffn_ws_bytes();
     a1.part = split ? static_cast<float*>(ws) : nullptr;
     a1.smax = FFN1_SPLIT_MAX;
-    moe_status_t s = act == MOE_ACT_SWIGLU ? launch_gemm<MODE_SWIGLU, 256>(a1, st)
-                                           : launch_single<MODE_GELU>(a1, st);
+    moe_status_t s;
+    if (slot_token)
+        s = act == MOE_ACT_SWIGLU ? launch_gemm<MODE_SWIGLU, 256, true>(a1, st)
+                                  : launch_single<MODE_GELU, true>(a1, st);
+    else
+        s = act == MOE_ACT_SWIGLU ? launch_gemm<MODE_SWIGLU, 256>(a1, st)
+                                  : launch_single<MODE_GELU>(a1, st);
     if (s != MOE_OK) return s;
     GemmArgs a2 = a1;
     a2.A = static_cast<const uint16_t*>(h_ws);
+    a2.slot_token = nullptr;
+    a2.a_rows = 0;
     a2.B0 = static_cast<const uint16_t*>(w2);
     a2.B1 = nullptr;
     a2.bias = static_cast<const uint16_t*>(b2);
@@ -794,4 +865,28 @@ extern "C" moe_status_t moe_expert_ffn(void* stream, moe_dtype_t dtype, moe_act_
     a2.part = split ? static_cast<float*>(ws) : nullptr;
     a2.smax = FFN2_SPLIT_MAX;
     return launch_single<MODE_DOWN>(a2, st);
+}
+
+}  // namespace
+
+extern "C" moe_status_t moe_expert_ffn(void* stream, moe_dtype_t dtype, moe_act_t act,
+                                       const void* x_disp, const int32_t* kept, int E, int64_t C,
+                                       int64_t H, int64_t I, const void* w1, const void* w3,
+                                       const void* w2, const void* b1, const void* b2, void* h_ws,
+                                       void* y_disp, void* ws, size_t ws_bytes) {
+    return ffn_impl(stream, dtype, act, x_disp, nullptr, 0, kept, E, C, H, I, w1, w3, w2, b1, b2,
+                    h_ws, y_disp, ws, ws_bytes);
+}
+
+extern "C" moe_status_t moe_expert_ffn_gather(void* stream, moe_dtype_t dtype, moe_act_t act,
+                                              const void* x, const int32_t* slot_token,
+                                              int64_t T, const int32_t* kept, int E, int64_t C,
+                                              int64_t H, int64_t I, const void* w1,
+                                              const void* w3, const void* w2, const void* b1,
+                                              const void* b2, void* h_ws, void* y_disp, void* ws,
+                                              size_t ws_bytes) {
+    if (C > 0 && !slot_token) return MOE_ERR_NULL;
+    if (T < 0) return MOE_ERR_SHAPE;
+    return ffn_impl(stream, dtype, act, x, slot_token, T, kept, E, C, H, I, w1, w3, w2, b1, b2,
+                    h_ws, y_disp, ws, ws_bytes);
 }

@@ -2,7 +2,10 @@
 
 `MoELayerGPU` owns the device weights and every intermediate buffer of one
 layer shape, allocated once, so a forward call enqueues only kernels: no
-allocation, no host synchronisation.  It mirrors the (out, aux_loss) return
+allocation, no host synchronisation.  With fused_gather (the default) the
+dispatch step produces only the row indices and the first expert product
+reads each expert's rows straight from x (moe_expert_ffn_gather); without
+it, dispatch materialises x_disp and moe_expert_ffn reads that.  It mirrors the (out, aux_loss) return
 of the minimal MoELayer of the MoE basics page (dpshk.com/news/6005940,
 section 3.1).
 """
@@ -38,7 +41,7 @@ class Buffers:
     f: torch.Tensor
     p: torch.Tensor
     l_aux: torch.Tensor
-    x_disp: torch.Tensor
+    x_disp: Optional[torch.Tensor]
     slot: torch.Tensor
     slot_token: torch.Tensor
     kept: torch.Tensor
@@ -53,8 +56,10 @@ class Buffers:
 class MoELayerGPU:
     """Device-resident weights + buffers for one configuration."""
 
-    def __init__(self, cfg: MoEConfig, inputs: Dict[str, np.ndarray], device="cuda:0"):
+    def __init__(self, cfg: MoEConfig, inputs: Dict[str, np.ndarray], device="cuda:0",
+                 fused_gather: bool = True):
         self.cfg = cfg
+        self.fused_gather = fused_gather
         dev = torch.device(device)
         self.dev = dev
         self.tdtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
@@ -82,7 +87,7 @@ class MoELayerGPU:
         return Buffers(
             topk_idx=e(T, k, dt=i32), topk_w=e(T, k), probs=e(T, E), keys=e(T, E),
             counts=e(E, dt=i32), f=e(E), p=e(E), l_aux=e(1),
-            x_disp=e(E, C, H, dt=td), slot=e(T, k, dt=i32), slot_token=e(E, C, dt=i32),
+            x_disp=None if self.fused_gather else e(E, C, H, dt=td), slot=e(T, k, dt=i32), slot_token=e(E, C, dt=i32),
             kept=e(E, dt=i32), dropped=e(1, dt=i32), h=e(E, C, I, dt=td),
             y_disp=e(E, C, H), y=e(T, H, dt=td),
             ws=e(max(1, ops.moe_workspace_bytes(T, E, k)), dt=torch.uint8),
@@ -104,10 +109,18 @@ class MoELayerGPU:
         b = self.buf
         return ops.moe_dispatch(x, b.topk_idx if topk_idx is None else topk_idx, self.cfg.E,
                                 self.C, ws=b.ws, x_disp=b.x_disp, slot=b.slot,
-                                slot_token=b.slot_token, kept=b.kept, dropped=b.dropped)
+                                slot_token=b.slot_token, kept=b.kept, dropped=b.dropped,
+                                copy=not self.fused_gather)
 
-    def experts(self):
+    def experts(self, x: Optional[torch.Tensor] = None):
+        """x (the token activations) is needed with fused_gather."""
         b = self.buf
+        if self.fused_gather:
+            if x is None:
+                raise ValueError("experts(x): the fused-gather layer reads the token rows")
+            return ops.moe_expert_ffn_gather(x, b.slot_token, b.kept, self.w1, self.w3, self.w2,
+                                             self.b1, self.b2, act=self.cfg.act, h_ws=b.h,
+                                             y_disp=b.y_disp, ws=b.ffn_ws)
         return ops.moe_expert_ffn(b.x_disp, b.kept, self.w1, self.w3, self.w2, self.b1, self.b2,
                                   act=self.cfg.act, h_ws=b.h, y_disp=b.y_disp, ws=b.ffn_ws)
 
@@ -120,7 +133,7 @@ class MoELayerGPU:
         self.route(x, keys=keys)
         self.aux()
         self.dispatch(x)
-        self.experts()
+        self.experts(x)
         self.combine()
         return self.buf.y, self.buf.l_aux
 

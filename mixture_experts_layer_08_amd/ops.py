@@ -99,11 +99,13 @@ def moe_aux_stats(topk_idx: torch.Tensor, probs: torch.Tensor, E: int, alpha: fl
 
 def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, C: int, *,
                  ws: Optional[torch.Tensor] = None, x_disp=None, slot=None, slot_token=None,
-                 kept=None, dropped=None):
+                 kept=None, dropped=None, copy: bool = True):
+    """copy=False: indices only (slot, slot_token, kept, dropped); x_disp is
+    then returned as None (for moe_expert_ffn_gather)."""
     T, H = x.shape
     k = topk_idx.shape[1]
     dev = x.device
-    x_disp = _want(x_disp, (E, C, H), x.dtype, dev)
+    x_disp = _want(x_disp, (E, C, H), x.dtype, dev) if copy else None
     slot = _want(slot, (T, k), torch.int32, dev)
     slot_token = _want(slot_token, (E, C), torch.int32, dev)
     kept = _want(kept, (E,), torch.int32, dev)
@@ -145,6 +147,37 @@ def moe_expert_ffn(x_disp: torch.Tensor, kept: torch.Tensor, w1: torch.Tensor,
                               _ptr(b2), _ptr(h_ws), _ptr(y_disp), _ptr(ws),
                               0 if ws is None else ws.numel() * ws.element_size())
     check("moe_expert_ffn", st)
+    return y_disp, h_ws
+
+
+def moe_expert_ffn_gather(x: torch.Tensor, slot_token: torch.Tensor, kept: torch.Tensor,
+                          w1: torch.Tensor, w3: Optional[torch.Tensor], w2: torch.Tensor,
+                          b1: Optional[torch.Tensor] = None, b2: Optional[torch.Tensor] = None, *,
+                          act: str = "swiglu", h_ws: Optional[torch.Tensor] = None,
+                          y_disp: Optional[torch.Tensor] = None,
+                          ws: Optional[torch.Tensor] = None):
+    """moe_expert_ffn reading each expert's rows straight from x via slot_token."""
+    T, H = x.shape
+    E, C = slot_token.shape
+    I = w1.shape[2]
+    dev = x.device
+    if tuple(w1.shape) != (E, H, I) or tuple(w2.shape) != (E, I, H):
+        raise ValueError("w1 must be [E, H, I] and w2 [E, I, H]")
+    if w3 is not None and tuple(w3.shape) != (E, H, I):
+        raise ValueError("w3 must be [E, H, I]")
+    for t in (w1, w3, w2, b1, b2):
+        if t is not None and t.dtype != x.dtype:
+            raise ValueError("weights and biases must have x's dtype")
+    if slot_token.dtype != torch.int32:
+        raise ValueError("slot_token must be int32")
+    h_ws = _want(h_ws, (E, C, I), x.dtype, dev)
+    y_disp = _want(y_disp, (E, C, H), torch.float32, dev)
+    st = lib().moe_expert_ffn_gather(_stream(dev), _dtype_code(x), ACTS[act], _ptr(x),
+                                     _ptr(slot_token), T, _ptr(kept), E, C, H, I, _ptr(w1),
+                                     _ptr(w3), _ptr(w2), _ptr(b1), _ptr(b2), _ptr(h_ws),
+                                     _ptr(y_disp), _ptr(ws),
+                                     0 if ws is None else ws.numel() * ws.element_size())
+    check("moe_expert_ffn_gather", st)
     return y_disp, h_ws
 
 

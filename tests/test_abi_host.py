@@ -122,8 +122,8 @@ def test_dispatch_argument_errors(L):
     assert d(E=100) == UNSUP
     assert d(H=4) == ALIGN                 # 8 bytes per bf16 row: not a 16-byte multiple
     assert d(kept=None) == NULL
-    assert d(x=None) == NULL
-    assert d(xd=None) == NULL
+    assert d(x=None) == NULL                 # x needed when x_disp is written
+    assert d(xd=None, kept=None) == NULL     # indices-only mode still validates
     assert d(x=MIS) == ALIGN
     assert d(ws=None) == WS
     assert d(wsb=4) == WS
@@ -152,6 +152,23 @@ def test_expert_ffn_argument_errors(L):
     assert f(w1=MIS) == ALIGN
     assert f(ws=MIS, wsb=1 << 30) == ALIGN
     assert f(C=0, xd=None, h=None, y=None) == OK
+
+
+def test_expert_ffn_gather_argument_errors(L):
+    def f(**kw):
+        return L.moe_expert_ffn_gather(None, kw.get("dtype", 1), kw.get("act", 0), kw.get("x", P),
+                                       kw.get("st", P), kw.get("T", 100), kw.get("kept", P),
+                                       kw.get("E", 8), kw.get("C", 64), kw.get("H", 256),
+                                       kw.get("I", 256), kw.get("w1", P), kw.get("w3", P),
+                                       kw.get("w2", P), None, None, kw.get("h", P), kw.get("y", P),
+                                       None, 0)
+    assert f(st=None) == NULL
+    assert f(x=None) == NULL
+    assert f(T=-1) == SHAPE
+    assert f(x=MIS) == ALIGN
+    assert f(H=200) == ALIGN
+    assert f(T=1 << 22, H=1 << 10) == UNSUP   # 2^31 bytes of x: past 32-bit row offsets
+    assert f(C=0, x=None, st=None, h=None, y=None) == OK
 
 
 def test_expert_ffn_workspace_size(L):
