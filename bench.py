@@ -2,17 +2,21 @@
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--gpus 1]
 
-A step is one whole layer forward (route, aux statistics, dispatch, grouped
-expert GEMM, combine) over one batch of synthetic input that is already
-resident in HBM.  The default workload is the 2 x 2048-token layer (hidden
-2048, SwiGLU intermediate 4096, 8 experts, top-2, capacity factor 1.25, bf16
-with fp32 accumulation).  Prints one JSON line.
+A step is one whole layer forward (route, aux statistics, dispatch of the
+row maps, the grouped expert GEMM whose first product gathers its rows from x,
+combine) over one batch of synthetic input that is already resident in HBM.
+The default workload is the 2 x 2048-token layer (hidden 2048, SwiGLU
+intermediate 4096, 8 experts, top-2, capacity factor 1.25, bf16 with fp32
+accumulation); --config 6 is the drop-free 64-token decode step on the same
+layer.  Prints one JSON line.
 
 Timing:
   * the timed region is exactly K steps, bracketed by device synchronisation;
   * inside it, HIP events on the launch stream bracket every phase, so each
     phase's average duration over the timed region is reported too (the
-    grouped GEMM phase is the dominant kernel pair and gives `roofline`);
+    expert phase dominates and gives `roofline`, against the matrix-core
+    peak or, when its weights take longer to stream than its FLOP to
+    compute, against HBM);
   * memory-bound phases are also timed in isolation after a 1 GiB write that
     flushes the 256 MB Infinity Cache, so their bytes come from HBM;
   * the CPU oracle (float64, the reference implementation) is timed on the
@@ -58,13 +62,21 @@ def algorithmic_work(cfg, kept: np.ndarray, dropped: int):
     n_kept = int(kept.sum())
     mult = 6 if cfg.act == "swiglu" else 4
     ffn_flop = mult * H * I * n_kept
+    # expert phase: the weights of every expert that has rows (read once),
+    # the gathered x rows, h written and read back, fp32 y_disp written
+    n_mats = 3 if cfg.act == "swiglu" else 2
+    active = int((kept > 0).sum())
+    ffn_bytes = (active * n_mats * H * I * esz + n_kept * H * esz + 2 * n_kept * I * esz
+                 + n_kept * H * 4)
     route_bytes = T * H * esz + H * E * esz + T * k * 8 + T * E * 4
     aux_bytes = T * k * 4 + T * E * 4
-    # x read once, each kept row written once, idx read, slot + slot_token written
-    dispatch_bytes = T * H * esz + n_kept * H * esz + T * k * 4 + T * k * 4 + n_kept * 4
+    # fused-gather layer: dispatch only maps rows (idx read, slot + slot_token
+    # written); the row copy happens inside the first expert product's loads
+    dispatch_bytes = T * k * 4 + T * k * 4 + n_kept * 4
     # kept expert rows (fp32) read once, y written once, slot + weights read
     combine_bytes = n_kept * H * 4 + T * H * esz + T * k * 8
-    return dict(n_kept=n_kept, ffn_flop=ffn_flop, route_bytes=route_bytes, aux_bytes=aux_bytes,
+    return dict(n_kept=n_kept, ffn_flop=ffn_flop, ffn_bytes=ffn_bytes, route_bytes=route_bytes,
+                aux_bytes=aux_bytes,
                 dispatch_bytes=dispatch_bytes, combine_bytes=combine_bytes, dropped=dropped)
 
 
@@ -232,9 +244,33 @@ def main():
             g2 = work[key] / (iso[n] * 1e-3) / 1e9
             phases[n].update({"ms_cold": round(iso[n], 5), "GB/s_cold": round(g2, 1),
                               "hbm_frac_cold": round(g2 / PEAK_HBM_GBS, 4)})
+    ffn_gbs = work["ffn_bytes"] / (gemm_ms * 1e-3) / 1e9
     phases["expert_ffn"] = {"ms": round(gemm_ms, 5), "flop": work["ffn_flop"],
                             "TFLOP/s": round(achieved_tflops, 2),
-                            "mfma_frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4)}
+                            "mfma_frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
+                            "bytes": work["ffn_bytes"], "GB/s": round(ffn_gbs, 1),
+                            "hbm_frac": round(ffn_gbs / PEAK_HBM_GBS, 4)}
+    # the expert phase is bound by whichever peak it would take longer at:
+    # the matrix cores for many rows per expert, HBM (the weights) for few
+    t_mfma = work["ffn_flop"] / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = work["ffn_bytes"] / (PEAK_HBM_GBS * 1e9)
+    kernel = ("grouped expert GEMM (moe_expert_ffn_gather: " +
+              ("gate/up product with SwiGLU epilogue" if cfg.act == "swiglu" else
+               "first product with bias + GELU epilogue") +
+              ", then down product, with their tail reductions)")
+    if t_hbm > t_mfma:
+        roofline = {"bound": "hbm", "kernel": kernel, "achieved": round(ffn_gbs, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ffn_gbs / PEAK_HBM_GBS, 4),
+                    "bytes_per_launch": work["ffn_bytes"]}
+    else:
+        roofline = {"bound": "mfma", "kernel": kernel, "achieved": round(achieved_tflops, 2),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
+                    "flop_per_launch": work["ffn_flop"]}
+    roofline.update({"traffic": measured_traffic(cfg),
+                     "traffic_unit": "HBM bytes per expert phase (rocprofv3 FETCH_SIZE x2.0 + "
+                                     "WRITE_SIZE x1.0, copy-calibrated)",
+                     "avg_ms": round(gemm_ms, 5)})
 
     out = {
         "metric": METRIC,
@@ -254,15 +290,10 @@ def main():
                                f"top-{cfg.k}, cf={cfg.cf}, {cfg.act}, {cfg.route} router",
                    "tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I, "experts": cfg.E,
                    "top_k": cfg.k, "capacity_factor": cfg.cf,
-                   "capacity": layer.C, "kept_rows": work["n_kept"], "dropped": dropped},
-        "roofline": {"bound": "mfma", "kernel": "grouped expert GEMM (moe_expert_ffn: gate/up "
-                     "product with SwiGLU epilogue, then down product)",
-                     "achieved": round(achieved_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(cfg), "traffic_unit": "bytes per launch "
-                     "pair (rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0, copy-calibrated)",
-                     "avg_ms": round(gemm_ms, 5),
-                     "flop_per_launch": work["ffn_flop"]},
+                   "capacity": layer.C, "kept_rows": work["n_kept"], "dropped": dropped,
+                   "path": "route, aux, dispatch (row maps), gather-fused expert products, "
+                           "combine"},
+        "roofline": roofline,
         "phases": phases,
         "device_ms_per_step": round(dev_ms, 5),
     }

@@ -77,7 +77,17 @@ CONFIGS: Dict[int, MoEConfig] = {
     5: MoEConfig("long-gumbel-bf16", "bf16", T=32768, H=2048, I=5632, E=32,
                  k=2, cf=1.25, route=ROUTE_GUMBEL, batch=1, seq=32768,
                  seed=1005),
+    # Drop-free decode step: 64 sequences x 1 new token on the config-2 layer.
+    # cf = E / k makes C = T, the most rows one expert can receive when a
+    # token's k experts are distinct, so nothing is ever dropped.
+    6: MoEConfig("decode-bf16", "bf16", T=64, H=2048, I=4096, E=8, k=2,
+                 cf=4.0, batch=64, seq=1, seed=1006),
 }
+
+
+def drop_free(cfg: MoEConfig) -> MoEConfig:
+    """The same workload with capacity C = T (cf = E / k): no drops."""
+    return cfg.with_(cf=cfg.E / cfg.k)
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:

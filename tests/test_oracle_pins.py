@@ -97,7 +97,8 @@ def test_p2_uniform_case_gives_one():
 
 # ------------------------------------------------------------------ P3 ----
 def test_p3_capacity_values():
-    expected = {1: 40, 2: 1280, 3: 4096, 4: 2560, 5: 2560}   # T*k*cf/E exact
+    # T*k*cf/E exact; the drop-free decode workload 6 has C = T
+    expected = {1: 40, 2: 1280, 3: 4096, 4: 2560, 5: 2560, 6: 64}
     for c, cfg in CONFIGS.items():
         assert M.capacity(cfg.T, cfg.k, cfg.E, cfg.cf) == expected[c]
     assert M.capacity(10, 1, 4, 1.0) == 3

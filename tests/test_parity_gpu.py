@@ -19,7 +19,7 @@ from oracle import moe_oracle as M
 from oracle import near_tie_tokens
 from mixture_experts_layer_08_amd import ops
 from mixture_experts_layer_08_amd.layer import MoELayerGPU, x_to_device
-from mixture_experts_layer_08_amd.synth import CONFIGS, MoEConfig, make_inputs
+from mixture_experts_layer_08_amd.synth import CONFIGS, MoEConfig, drop_free, make_inputs
 
 from parity_util import assert_rel, assert_rows_close, log, to_dev, to_np
 
@@ -278,6 +278,47 @@ def test_dispatch_and_aux_both_sizes(T, E, k, cf):
     st = d.slot_token.reshape(-1)
     rows = np.where(st >= 0)[0]
     np.testing.assert_array_equal(xd[rows], to_np(x)[st[rows]])
+
+
+@pytest.mark.parametrize("T", [1, 16, 64, 256])
+def test_decode_drop_free(T):
+    """Drop-free decode steps (C = T): nothing dropped, every token's output
+    within tolerance; T = 1 gives each selected expert a single row."""
+    cfg = drop_free(MoEConfig("decode", "bf16", T=T, H=512, I=512, E=8, k=2, cf=1.0,
+                              batch=T, seq=1, seed=20 + T))
+    log(f"[decode] T={T} C={M.capacity(T, cfg.k, cfg.E, cfg.cf)}")
+    inp = make_inputs(cfg)
+    ref = M.forward(inp, cfg)
+    layer = MoELayerGPU(cfg, inp, DEV)
+    assert layer.C == T
+    x = x_to_device(inp, cfg, DEV)
+    y, _ = layer.forward(x)
+    torch.cuda.synchronize()
+    b = layer.buf
+    assert int(to_np(b.dropped)[0]) == 0 and ref.disp.dropped == 0
+    same = _route_compare(cfg, to_np(b.topk_idx), to_np(b.topk_w), to_np(b.probs), None,
+                          ref.route, f"decode T={T}")
+    _check_y(cfg, to_np(y)[same], ref.y[same], f"decode T={T}: y")
+
+
+def test_decode_config_full_size():
+    """The 64-token drop-free decode step on the full-size layer (H 2048,
+    I 4096, E 8): the workload `bench.py --config 6` times."""
+    cfg = CONFIGS[6]
+    log(f"[decode] config 6 {cfg.name}")
+    inp = make_inputs(cfg)
+    ref = M.forward(inp, cfg)
+    layer = MoELayerGPU(cfg, inp, DEV)
+    x = x_to_device(inp, cfg, DEV)
+    y, l_aux = layer.forward(x)
+    torch.cuda.synchronize()
+    b = layer.buf
+    assert int(to_np(b.dropped)[0]) == 0
+    same = _route_compare(cfg, to_np(b.topk_idx), to_np(b.topk_w), to_np(b.probs), None,
+                          ref.route, "config 6")
+    assert_rel(to_np(l_aux), [ref.aux.l_aux], 1e-5, "config 6: L_aux")
+    worst = _check_y(cfg, to_np(y)[same], ref.y[same], "config 6: y")
+    log(f"[decode] config 6: worst err/rms {worst:.3e}")
 
 
 def test_deterministic_bitwise():
