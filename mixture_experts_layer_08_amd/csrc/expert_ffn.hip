@@ -369,14 +369,18 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
 
     // Fragments of one 32-wide half of a k-step: two 16-wide MFMA slices,
     // A (TM x 32 rows) and B (TN x 32 columns) per slice.
-    auto load_frags = [&](int stage, int kk, bf16x8_t (&af)[2][TM], bf16x8_t (&bfr)[2][TN]) {
+    // Only the first NI 32-row blocks of the wave's A rows are read (the
+    // others lie past kept[e]).
+    auto load_frags = [&](auto ni, int stage, int kk, bf16x8_t (&af)[2][TM],
+                          bf16x8_t (&bfr)[2][TN]) {
+        constexpr int NI = decltype(ni)::value;
         const unsigned char* As = smem + stage * kStage;
         const unsigned char* Bs = As + kStageA;
 #pragma unroll
         for (int ss = 0; ss < 2; ++ss) {
             const int k16 = kk * 2 + ss;
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
+            for (int i = 0; i < NI; ++i) {
                 const int row = wm * WM_ROWS + i * 32 + lane % 32;
                 const int phys = (k16 * 2 + lane / 32) ^ swz_a(row);
                 af[ss][i] = as_bf16x8(*reinterpret_cast<const uint4*>(As + row * 128 + phys * 16));
@@ -423,11 +427,12 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-        auto mma = [&](const bf16x8_t (&af)[2][TM], const bf16x8_t (&bfr)[2][TN]) {
+        auto mma = [&](auto ni, const bf16x8_t (&af)[2][TM], const bf16x8_t (&bfr)[2][TN]) {
+            constexpr int NI = decltype(ni)::value;
 #pragma unroll
             for (int ss = 0; ss < 2; ++ss)
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
+                for (int i = 0; i < NI; ++i)
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ss][i], bfr[ss][j],
@@ -440,13 +445,14 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
         // half of step kt+1 is read while the second half's MFMAs of step kt
         // run.  After the last barrier the next tile's step 0 is loaded, and
         // after the final MFMAs its step 1, so the next tile starts with both
-        // stages in flight.  A wave whose rows all lie at or past kept[e]
-        // (the tail of an expert's last row tile) runs the same loop without
-        // fragment reads or MFMAs: it issues the same loads and joins the same
-        // barriers (a barrier counts arrivals, so the two loops stay in step).
+        // stages in flight.  A wave with rows at or past kept[e] (the tail of
+        // an expert's last row tile) runs the same loop with fragment reads and
+        // MFMAs for its live 32-row blocks only (none when every row is past
+        // kept): it issues the same loads and joins the same barriers (a
+        // barrier counts arrivals, so the loop variants stay in step).
         // sched_barrier(0) keeps each MFMA group on its side of a barrier.
-        auto kloop = [&](auto do_math) {
-            constexpr bool M = decltype(do_math)::value;
+        auto kloop = [&](auto ni) {
+            constexpr bool M = decltype(ni)::value > 0;
             bf16x8_t a0[2][TM], b0[2][TN], a1[2][TM], b1[2][TN];
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
@@ -458,51 +464,60 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
 #pragma unroll
                 for (int q = 0; q < QA; ++q) asm volatile("" ::"v"(cur.tok[q]));
             }
-            if (M) load_frags(base, 0, a0, b0);
+            if (M) load_frags(ni, base, 0, a0, b0);
             const int nks = cur.nks;
             int kt = 0;
             for (; kt + 2 < nks; ++kt) {
                 const int s0 = (base + kt) & 1;
                 if (M) {
-                    load_frags(s0, 1, a1, b1);
-                    mma(a0, b0);
+                    load_frags(ni, s0, 1, a1, b1);
+                    mma(ni, a0, b0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
                 issue(cur, cur.kb + kt + 2, s0);
                 if (M) {
-                    load_frags(s0 ^ 1, 0, a0, b0);
-                    mma(a1, b1);
+                    load_frags(ni, s0 ^ 1, 0, a0, b0);
+                    mma(ni, a1, b1);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
             // kt = nk - 2
             const int s0 = (base + kt) & 1;
             if (M) {
-                load_frags(s0, 1, a1, b1);
-                mma(a0, b0);
+                load_frags(ni, s0, 1, a1, b1);
+                mma(ni, a0, b0);
             }
             __builtin_amdgcn_sched_barrier(0);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             if (nxt.valid) issue(nxt, nxt.kb, s0);
             if (M) {
-                load_frags(s0 ^ 1, 0, a0, b0);
-                mma(a1, b1);
+                load_frags(ni, s0 ^ 1, 0, a0, b0);
+                mma(ni, a1, b1);
                 // kt = nk - 1
-                load_frags(s0 ^ 1, 1, a1, b1);
-                mma(a0, b0);
-                mma(a1, b1);
+                load_frags(ni, s0 ^ 1, 1, a1, b1);
+                mma(ni, a0, b0);
+                mma(ni, a1, b1);
             }
             __builtin_amdgcn_sched_barrier(0);
             __syncthreads();  // every wave is done with step nk - 1
             if (nxt.valid) issue(nxt, nxt.kb + 1, s0 ^ 1);
         };
-        if (cur.m0 + wm * WM_ROWS < cur.kept)
-            kloop(std::true_type{});
-        else
-            kloop(std::false_type{});
+        // MFMAs only on the wave's 32-row blocks that hold rows below kept[e]
+        // (thin last row tiles of an expert, decode steps)
+        {
+            const int rows = cur.kept - (cur.m0 + wm * WM_ROWS);
+            if (rows > 64)
+                kloop(std::integral_constant<int, TM>{});
+            else if (rows > 32)
+                kloop(std::integral_constant<int, (TM < 2 ? TM : 2)>{});
+            else if (rows > 0)
+                kloop(std::integral_constant<int, 1>{});
+            else
+                kloop(std::integral_constant<int, 0>{});
+        }
 
         if (cur.pslot >= 0) {
             // a piece of a split tail tile: store the fp32 partial, lane-major
