@@ -80,7 +80,10 @@ def algorithmic_work(cfg, kept: np.ndarray, dropped: int):
                 dispatch_bytes=dispatch_bytes, combine_bytes=combine_bytes, dropped=dropped)
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "grouped_gemm_layer_bf16_4096tok_traffic.md")
+TRAFFIC_PROFILES = {
+    "layer-bf16": os.path.join(ROOT, "profiles", "grouped_gemm_layer_bf16_4096tok_traffic.md"),
+    "decode-bf16": os.path.join(ROOT, "profiles", "grouped_gemm_decode_bf16_64tok_traffic.md"),
+}
 GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_08_amd", "csrc", "expert_ffn.hip")
 
 
@@ -88,11 +91,11 @@ def measured_traffic(cfg):
     """HBM bytes per expert phase from the committed rocprofv3 counter summary
     (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when that summary is
     for another workload or for another version of the GEMM source."""
-    import hashlib
     import re
-    if cfg.name != "layer-bf16" or not os.path.exists(TRAFFIC_PROFILE):
+    path = TRAFFIC_PROFILES.get(cfg.name)
+    if path is None or not os.path.exists(path):
         return None
-    text = open(TRAFFIC_PROFILE).read()
+    text = open(path).read()
     m_b = re.search(r"traffic_bytes_per_layer_call:\s*(\d+)", text)
     m_h = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
     if not m_b or not m_h:

@@ -525,10 +525,13 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
             // tail reduction finishes the tile.  Pieces are the last round.
             const i32x4_t rsP = make_rsrc(g.part + (size_t)cur.pslot * (kPartBytes / 4),
                                           (uint32_t)kPartBytes);
+            // (32-row blocks wholly past kept[e] are skipped: the reduction
+            // never reads them)
             constexpr int NG = TM * TN * 4;
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
                 const int i = gi / (TN * 4), j = (gi / 4) % TN, q4 = gi % 4;
+                if (cur.m0 + wm * WM_ROWS + i * 32 >= cur.kept) continue;
                 f32x4_t v;
                 v.x = acc[i][j][4 * q4];
                 v.y = acc[i][j][4 * q4 + 1];
@@ -625,6 +628,9 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g, int G) {
         if (kept > g.C) kept = (int)g.C;
         const int vwave = vt / kWave, vlane = vt % kWave;
         const int wm = vwave / kWN, wn = vwave % kWN;
+        const int m0 = m_tile * kBM, n0 = n_tile * EP::BN_OUT;
+        const int row0 = m0 + wm * WM_ROWS + i * 32 + q4 * 8 + (vlane / 32) * 4;
+        if (m0 + wm * WM_ROWS + i * 32 >= kept) continue;  // block past kept: no partials stored
         const size_t base = (size_t)t * splits * PSTRIDE + vt;
         const int gi0 = (i * TN + jo) * 4 + q4;                // gate / only operand
         const int gi1 = (i * TN + jo + TN / 2) * 4 + q4;       // up (SwiGLU)
@@ -639,10 +645,8 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g, int G) {
                 s1.x += v1.x; s1.y += v1.y; s1.z += v1.z; s1.w += v1.w;
             }
         }
-        const int m0 = m_tile * kBM, n0 = n_tile * EP::BN_OUT;
         const int col = n0 + (MODE == MODE_SWIGLU ? wn * (WN_COLS / 2) : wn * WN_COLS) + jo * 32 +
                         vlane % 32;
-        const int row0 = m0 + wm * WM_ROWS + i * 32 + q4 * 8 + (vlane / 32) * 4;
         float bv = 0.f;
         if (MODE != MODE_SWIGLU && g.bias) bv = bf2f(g.bias[(size_t)e * g.N + col]);
         const float a0[4] = {s0.x, s0.y, s0.z, s0.w};
