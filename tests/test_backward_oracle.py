@@ -1,0 +1,181 @@
+"""Pins of the backward oracle (CPU).
+
+The backward oracle is checked against things other than itself:
+  * central finite differences of the forward oracle's objective
+    sum(dy * y) + dl_aux * L_aux, element by element, on tiny layers with
+    drops, biases, both expert kinds and both routers (the top-k choice and
+    the drops are held fixed: an element whose perturbation would change
+    them is skipped);
+  * the one-expert layer (E = k = 1) is a dense FFN, whose gradients torch
+    autograd computes independently;
+  * planted slips in the backward (wrong activation derivative, a missing
+    softmax or renormalisation term, a missing aux term) fail the
+    finite-difference check.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_backward as B
+from oracle import moe_oracle as M
+from mixture_experts_layer_08_amd.synth import MoEConfig
+
+
+def _inputs(cfg, seed, bias=False, b2=True):
+    g = np.random.default_rng(seed)
+    T, H, I, E = cfg.T, cfg.H, cfg.I, cfg.E
+    inp = {"x": g.standard_normal((T, H)), "w_r": g.standard_normal((H, E)) * 0.7,
+           "b_r": g.standard_normal(E) * 0.5 if bias else None}
+    if cfg.act == "swiglu":
+        inp["w_gate"] = g.standard_normal((E, H, I)) * 0.5
+        inp["w_up"] = g.standard_normal((E, H, I)) * 0.5
+        inp["w_down"] = g.standard_normal((E, I, H)) * 0.5
+    else:
+        inp["w1"] = g.standard_normal((E, H, I)) * 0.5
+        inp["b1"] = g.standard_normal((E, I)) * 0.3
+        inp["w2"] = g.standard_normal((E, I, H)) * 0.5
+        inp["b2"] = g.standard_normal((E, H)) * 0.3 if b2 else None
+    return inp
+
+
+CASES = {
+    "swiglu-softmax-drops-bias": (MoEConfig("fd1", "f32", T=9, H=5, I=6, E=4, k=2, cf=0.75,
+                                            seed=1), dict(bias=True)),
+    "gelu-softmax-b2": (MoEConfig("fd2", "f32", T=7, H=4, I=5, E=3, k=2, cf=1.0, act="gelu",
+                                  seed=2), dict()),
+    "gelu-no-b2-k1": (MoEConfig("fd3", "f32", T=6, H=4, I=3, E=3, k=1, cf=2.0, act="gelu",
+                                seed=3), dict(b2=False)),
+    "swiglu-gumbel": (MoEConfig("fd4", "f32", T=8, H=4, I=5, E=5, k=2, cf=1.0, route="gumbel",
+                                seq=300, seed=4), dict(bias=True)),
+    "swiglu-k3": (MoEConfig("fd5", "f32", T=6, H=3, I=4, E=4, k=3, cf=1.0, seed=5), dict()),
+}
+
+
+def _fd_check(cfg, inp, seed, max_elems=12, eps=1e-6, rtol=2e-6):
+    """Compare every gradient of the backward oracle with central
+    differences of the forward objective; returns the worst relative error."""
+    g = np.random.default_rng(seed + 100)
+    dy = g.standard_normal((cfg.T, cfg.H))
+    dl_aux = 0.7
+    grads = B.backward(inp, cfg, dy, dl_aux)
+    r0 = M.route(inp, cfg)
+    d0 = M.dispatch(r0.idx, cfg.E, M.capacity(cfg.T, cfg.k, cfg.E, cfg.cf))
+    analytic = {"x": grads.dx, "w_r": grads.dw_r}
+    if inp.get("b_r") is not None:
+        analytic["b_r"] = grads.db_r
+    analytic.update(grads.dweights)
+    worst = 0.0
+    checked = 0
+    for name, ga in analytic.items():
+        arr = inp[name]
+        flat_idx = g.choice(arr.size, size=min(max_elems, arr.size), replace=False)
+        for fi in flat_idx:
+            ix = np.unravel_index(fi, arr.shape)
+            vals = []
+            ok = True
+            for sgn in (+1, -1):
+                p = dict(inp)
+                p[name] = arr.copy()
+                p[name][ix] += sgn * eps
+                r = M.route(p, cfg)
+                if not np.array_equal(r.idx, r0.idx):
+                    ok = False
+                    break
+                vals.append(B.objective(p, cfg, dy, dl_aux))
+            if not ok:
+                continue
+            fd = (vals[0] - vals[1]) / (2 * eps)
+            an = ga[ix]
+            err = abs(fd - an) / max(1.0, abs(fd))
+            worst = max(worst, err)
+            checked += 1
+            assert err <= rtol, f"{cfg.name} {name}{ix}: analytic {an} vs finite difference {fd}"
+    assert checked > 20
+    return worst, d0.dropped
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_backward_matches_finite_differences(name):
+    cfg, kw = CASES[name]
+    inp = _inputs(cfg, cfg.seed, **kw)
+    worst, dropped = _fd_check(cfg, inp, cfg.seed)
+    if name.endswith("drops-bias"):
+        assert dropped > 0          # the case does exercise the capacity drop
+
+
+def test_single_expert_is_a_dense_ffn_under_autograd():
+    """E = k = 1: the layer is y = FFN(x) (w = 1, p = 1, no drops), so its
+    gradients are a dense SwiGLU FFN's, computed here by torch autograd."""
+    cfg = MoEConfig("dense", "f32", T=11, H=6, I=7, E=1, k=1, cf=1.0, seed=9)
+    inp = _inputs(cfg, 9)
+    dy = np.random.default_rng(19).standard_normal((cfg.T, cfg.H))
+    grads = B.backward(inp, cfg, dy, dl_aux=0.0)
+    t = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True)
+         for k, v in (("x", inp["x"]), ("w1", inp["w_gate"][0]), ("w3", inp["w_up"][0]),
+                      ("w2", inp["w_down"][0]))}
+    y = (torch.nn.functional.silu(t["x"] @ t["w1"]) * (t["x"] @ t["w3"])) @ t["w2"]
+    (y * torch.tensor(dy)).sum().backward()
+    np.testing.assert_allclose(grads.dx, t["x"].grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(grads.dweights["w_gate"][0], t["w1"].grad.numpy(), rtol=1e-12,
+                               atol=1e-12)
+    np.testing.assert_allclose(grads.dweights["w_up"][0], t["w3"].grad.numpy(), rtol=1e-12,
+                               atol=1e-12)
+    np.testing.assert_allclose(grads.dweights["w_down"][0], t["w2"].grad.numpy(), rtol=1e-12,
+                               atol=1e-12)
+    assert np.all(grads.dlogits == 0.0)     # a one-expert softmax is constant
+
+
+def test_activation_derivatives_against_torch():
+    z = np.linspace(-6, 6, 97)
+    tz = torch.tensor(z, requires_grad=True)
+    torch.nn.functional.silu(tz).sum().backward()
+    np.testing.assert_allclose(B.silu_grad(z), tz.grad.numpy(), rtol=1e-13, atol=1e-15)
+    tz = torch.tensor(z, requires_grad=True)
+    torch.nn.functional.gelu(tz).sum().backward()
+    np.testing.assert_allclose(B.gelu_erf_grad(z), tz.grad.numpy(), rtol=1e-12, atol=1e-14)
+
+
+_MUTANTS = {
+    "silu_grad": lambda z: 1.0 / (1.0 + np.exp(-z)),          # sigmoid only
+    "gelu_erf_grad": lambda z: 0.5 * (1.0 + np.tanh(z)),       # wrong derivative
+    "softmax_backward": lambda p, dp: p * dp,                  # drops the mean term
+}
+
+
+def _without_renormalisation(orig):
+    """A backward that passes dw straight to the selected probabilities
+    (dp_sel = dw / S), forgetting that S depends on them too."""
+    def slip(inputs, c, dy, dl_aux=1.0):
+        gr = orig(inputs, c, dy, dl_aux)
+        r = M.route(inputs, c)
+        S = np.take_along_axis(r.probs, r.idx, axis=1).sum(axis=1, keepdims=True)
+        dprobs = np.zeros_like(gr.dprobs)
+        np.put_along_axis(dprobs, r.idx, gr.dw_topk / S, axis=1)
+        a = M.aux_stats(r.idx, r.probs, c.E, c.alpha)
+        dprobs += dl_aux * c.alpha * c.E * a.f[None, :] / c.T
+        dl = B.softmax_backward(r.probs, dprobs)
+        w_r, x = M.widen(inputs["w_r"]), M.widen(inputs["x"])
+        return B.Grads(gr.dx_experts + dl @ w_r.T, x.T @ dl,
+                       dl.sum(axis=0) if inputs.get("b_r") is not None else None,
+                       gr.dweights, gr.dw_topk, dprobs, dl, gr.dy_disp, gr.dx_disp,
+                       gr.dx_experts, dl @ w_r.T)
+    return slip
+
+
+@pytest.mark.parametrize("mutant", ["silu_grad", "gelu_erf_grad", "softmax_backward", "no_renorm",
+                                    "no_aux"])
+def test_planted_backward_slips_are_caught(mutant, monkeypatch):
+    case = "gelu-softmax-b2" if mutant == "gelu_erf_grad" else "swiglu-softmax-drops-bias"
+    cfg, kw = CASES[case]
+    inp = _inputs(cfg, cfg.seed, **kw)
+    if mutant in _MUTANTS:
+        monkeypatch.setattr(B, mutant, _MUTANTS[mutant])
+    elif mutant == "no_renorm":
+        monkeypatch.setattr(B, "backward", _without_renormalisation(B.backward))
+    else:  # no_aux: forgets the aux-loss path
+        orig = B.backward
+        monkeypatch.setattr(B, "backward", lambda i, c, dy, dl_aux=1.0: orig(i, c, dy, 0.0))
+    with pytest.raises(AssertionError):
+        _fd_check(cfg, inp, cfg.seed)
