@@ -233,6 +233,89 @@ moe_status_t moe_combine(void* stream, moe_dtype_t dtype, const void* y_disp,
                          const int32_t* slot, const float* topk_w, int64_t T,
                          int64_t H, int k, void* y);
 
+/* ------------------------------------------------------------ backward ----
+ * Gradients of  L = sum(dy * y) + dl_aux * L_aux  for a given output
+ * gradient dy.  The top-k choice and the capacity drop are piecewise
+ * constant and pass no gradient; f_i is a count and is held constant.
+ * One backward step, in order:
+ *   moe_combine_bwd     dy_disp, dw (gradient of the combine weights)
+ *   moe_expert_ffn_bwd  dx_disp and every expert weight gradient
+ *   moe_dispatch_bwd    dx = sum over each token's kept copies of dx_disp
+ *   moe_route_bwd       dlogits, dW_r, db_r, and dx += dlogits W_r^T
+ * All gradient outputs are fp32; every sum runs in a fixed order
+ * (bitwise reproducible). */
+
+/* Combine backward.  [P1] section 2.4 (y_t = sum_j w_tj Y[slot_tj]).
+ *   dy      [T, H]   dtype   output gradient
+ *   y_disp  [E*C, H] fp32    the forward's expert outputs
+ *   slot    [T, k]   int32,  topk_w [T, k] fp32  (the forward's)
+ *   dy_disp [E*C, H] dtype out  w_tj * dy_t at row slot_tj for every kept
+ *                               copy; other rows untouched
+ *   dw      [T, k]   fp32  out  <dy_t, Y[slot_tj]>, 0 for a dropped copy
+ * H must be a multiple of 8; pointers 16-byte aligned. */
+moe_status_t moe_combine_bwd(void* stream, moe_dtype_t dtype, const void* dy,
+                             const void* y_disp, const int32_t* slot,
+                             const float* topk_w, int64_t T, int64_t H, int k,
+                             void* dy_disp, float* dw);
+
+/* Expert FFN backward.  [P2] sections 2.2 and 3.1, [P5] section 2.1 (the
+ * expert FFNs being differentiated).  Re-runs the first product to recover
+ * h and its pre-activations (bf16), then
+ *   SwiGLU: dh = dY W_down^T, dg = dh u silu'(g), du = dh silu(g),
+ *           dX = dg W_gate^T + du W_up^T, dW_down = h^T dY,
+ *           dW_gate = X^T dg, dW_up = X^T du
+ *   GELU:   dz = (dY W2^T) gelu'(z), dX = dz W1^T, dW2 = h^T dY,
+ *           dW1 = X^T dz, db1 = sum_rows dz, db2 = sum_rows dY
+ * over each expert's kept rows.
+ *   x_disp  [E, C, H] bf16       the forward's dispatched rows
+ *   kept    [E]       int32      (device)
+ *   w1, w3, w2, b1               as for moe_expert_ffn (w3 SwiGLU only,
+ *                                b1 GELU only)
+ *   dy_disp [E, C, H] bf16       moe_combine_bwd's output
+ *   dx_disp [E, C, H] fp32 out   rows < kept[e] written
+ *   dw1 [E, H, I], dw3 [E, H, I] (SwiGLU), dw2 [E, I, H]   fp32 out
+ *   db1 [E, I] (GELU, required), db2 [E, H] (GELU, may be NULL)  fp32 out
+ *   ws      moe_expert_ffn_bwd_ws_bytes(E, C, I) bytes, 16-byte aligned
+ * bf16 only (MOE_ERR_UNSUPPORTED for fp32); H and I multiples of 256. An
+ * expert with no rows gets zero weight gradients. */
+moe_status_t moe_expert_ffn_bwd(void* stream, moe_dtype_t dtype, moe_act_t act,
+                                const void* x_disp, const int32_t* kept, int E,
+                                int64_t C, int64_t H, int64_t I, const void* w1,
+                                const void* w3, const void* w2, const void* b1,
+                                const void* dy_disp, float* dx_disp, float* dw1,
+                                float* dw3, float* dw2, float* db1, float* db2,
+                                void* ws, size_t ws_bytes);
+
+/* Bytes of moe_expert_ffn_bwd's workspace: five bf16 [E, C, I] planes. */
+size_t moe_expert_ffn_bwd_ws_bytes(int E, int64_t C, int64_t I);
+
+/* Dispatch backward: dx[t] = sum over kept j of dx_disp[slot[t, j]] (fp32;
+ * a token with every copy dropped gets zeros).  [P1] section 2.4 (the
+ * copies are gathered back by token).  H a multiple of 8. */
+moe_status_t moe_dispatch_bwd(void* stream, const float* dx_disp,
+                              const int32_t* slot, int64_t T, int64_t H, int k,
+                              float* dx);
+
+/* Router backward.  [P5] section 3.1 (renormalised top-k of the softmax),
+ * [P2] section 2.3 (L_aux), [P4] section 2 (Gumbel soft path).
+ *   x [T, H], w_r [H, E]  dtype;  probs [T, E] fp32 (the forward's p, or q in
+ *   Gumbel mode);  topk_idx, topk_w [T, k] (the forward's);  dw [T, k] fp32
+ *   (moe_combine_bwd's);  f [E] fp32 (moe_aux_stats');  alpha, dl_aux;
+ *   seq_len (the temperature, Gumbel mode)
+ *   dlogits [T, E] fp32 out   gradient of the router logits
+ *   dx      [T, H] fp32 in/out dx += dlogits W_r^T (NULL: skipped)
+ *   dw_r    [H, E] fp32 out;  db_r [E] fp32 out (NULL when there is no bias)
+ *   ws      moe_route_bwd_ws_bytes(T, H, E) bytes */
+moe_status_t moe_route_bwd(void* stream, moe_dtype_t dtype, moe_route_mode_t mode,
+                           const void* x, const void* w_r, const float* probs,
+                           const int32_t* topk_idx, const float* topk_w,
+                           const float* dw, const float* f, float alpha,
+                           float dl_aux, int64_t T, int64_t H, int E, int k,
+                           int64_t seq_len, float* dlogits, float* dx, float* dw_r,
+                           float* db_r, void* ws, size_t ws_bytes);
+
+size_t moe_route_bwd_ws_bytes(int64_t T, int64_t H, int E);
+
 #ifdef __cplusplus
 }
 #endif

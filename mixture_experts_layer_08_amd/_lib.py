@@ -25,7 +25,9 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_capacity", "moe_status_string", "moe_workspace_bytes", "moe_route",
            "moe_aux_stats", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_gather",
-           "moe_expert_ffn_ws_bytes", "moe_combine")
+           "moe_expert_ffn_ws_bytes", "moe_combine", "moe_combine_bwd", "moe_expert_ffn_bwd",
+           "moe_expert_ffn_bwd_ws_bytes", "moe_dispatch_bwd", "moe_route_bwd",
+           "moe_route_bwd_ws_bytes")
 
 _lock = threading.Lock()
 _lib = None
@@ -66,6 +68,20 @@ def _declare(L: ctypes.CDLL) -> None:
     L.moe_expert_ffn_ws_bytes.restype = c.c_size_t
     L.moe_combine.argtypes = [vp, i32, vp, vp, vp, i64, i64, i32, vp]
     L.moe_combine.restype = i32
+    L.moe_combine_bwd.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i32, vp, vp]
+    L.moe_combine_bwd.restype = i32
+    L.moe_expert_ffn_bwd.argtypes = [vp, i32, i32, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp, vp,
+                                     vp, vp, vp, vp, vp, vp, vp, c.c_size_t]
+    L.moe_expert_ffn_bwd.restype = i32
+    L.moe_expert_ffn_bwd_ws_bytes.argtypes = [i32, i64, i64]
+    L.moe_expert_ffn_bwd_ws_bytes.restype = c.c_size_t
+    L.moe_dispatch_bwd.argtypes = [vp, vp, vp, i64, i64, i32, vp]
+    L.moe_dispatch_bwd.restype = i32
+    L.moe_route_bwd.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, f32, i64, i64, i32,
+                                i32, i64, vp, vp, vp, vp, vp, c.c_size_t]
+    L.moe_route_bwd.restype = i32
+    L.moe_route_bwd_ws_bytes.argtypes = [i64, i64, i32]
+    L.moe_route_bwd_ws_bytes.restype = c.c_size_t
 
 
 def lib() -> ctypes.CDLL:

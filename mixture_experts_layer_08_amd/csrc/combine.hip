@@ -33,7 +33,7 @@ __global__ __launch_bounds__(kCThreads) void combine_kernel(const float4* __rest
     if (t0 + nt > T) nt = (int)(T - t0);
     for (int q = threadIdx.x; q < nt * k; q += kCThreads) {
         s_slot[q] = slot[t0 * k + q];
-        s_w[q] = w[t0 * k + q];
+        s_w[q] = w ? w[t0 * k + q] : 1.0f;  // no weights: the plain sum (dispatch backward)
     }
     __syncthreads();
     for (int v = threadIdx.x; v < row_oct; v += kCThreads) {
@@ -104,6 +104,25 @@ extern "C" moe_status_t moe_combine(void* stream, moe_dtype_t dtype, const void*
     else
         hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)grid), dim3(kCThreads), 0, st,
                            static_cast<const float4*>(y_disp), slot, topk_w, T, k, row_oct, y);
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
+}
+
+// Backward of the row copy: a token's gradient is the sum of the gradients
+// of its kept copies (the combine's gather with unit weights), fp32.
+extern "C" moe_status_t moe_dispatch_bwd(void* stream, const float* dx_disp, const int32_t* slot,
+                                         int64_t T, int64_t H, int k, float* dx) {
+    if (T < 0 || H <= 0 || k < 1) return MOE_ERR_SHAPE;
+    if (k > MOE_MAX_TOPK || H > (1 << 22) || T * k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    if (H % 8) return MOE_ERR_ALIGN;
+    if (T == 0) return MOE_OK;
+    if (!slot || !dx) return MOE_ERR_NULL;
+    if ((dx_disp && !moe_aligned16(dx_disp)) || !moe_aligned16(dx)) return MOE_ERR_ALIGN;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t grid = (T + kCTok - 1) / kCTok;
+    hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)grid), dim3(kCThreads), 0, st,
+                       reinterpret_cast<const float4*>(dx_disp), slot, (const float*)nullptr, T, k,
+                       (int)(H / 8), static_cast<void*>(dx));
     MOE_CHECK_LAUNCH();
     return MOE_OK;
 }

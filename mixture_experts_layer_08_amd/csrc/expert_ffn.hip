@@ -49,93 +49,29 @@
 // accumulators through a descriptor that ends at row kept[e], so the
 // hardware drops the padding rows' stores.
 #include "moe_common.h"
+#include "gemm_common.h"
+#include "internal.h"
 
 #include <math.h>
 
 #include <type_traits>
 
-#ifndef GEMM_WAVES
-#define GEMM_WAVES 8
-#endif
-#ifndef GEMM_WAVES_N
-#define GEMM_WAVES_N 4
-#endif
 #ifndef FFN1_SPLIT_MAX
 #define FFN1_SPLIT_MAX 4  // most K pieces of a tail tile, first product
 #endif
 #ifndef FFN2_SPLIT_MAX
 #define FFN2_SPLIT_MAX 4  // and second product
 #endif
-#ifndef GEMM_GROUP
-#define GEMM_GROUP 32  // tiles per L2 group: every row tile of an expert x a few column tiles
-#endif
 
 namespace {
 
 using namespace moe;
 
-constexpr int kBM = 256;
-constexpr int kBNMax = 256;  // widest B tile (two 128-column sub-tiles)
-constexpr int kBK = 64;
-constexpr int kNW = GEMM_WAVES;      // waves per workgroup
-constexpr int kWN = GEMM_WAVES_N;    // waves across the B columns
-constexpr int kWMn = kNW / kWN;      // waves across the rows
-constexpr int kGThreads = kNW * 64;
-constexpr int kStageA = kBM * kBK * 2;  // 32 KB
-
-enum { MODE_SWIGLU = 0, MODE_GELU = 1, MODE_DOWN = 2 };
-
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
-typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
-
-// buffer_load_dwordx4 ... lds: each lane's 16 bytes go to LDS at M0 + 16 * lane.
-// Written as asm so the compiler does not add a wait for these LDS writes
-// before unrelated LDS reads of the other stage; the instruction has no
-// register outputs, and the kernel itself waits (vmcnt(0)) and barriers
-// before any wave reads the stage the loads fill.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; nothing else in these kernels uses it
-__device__ __forceinline__ void lds_dma16(i32x4_t rsrc, const void* lds, int voffset, int soffset) {
-    // every scalar operand is wave-uniform; readfirstlane states it to the compiler
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds);
-    rsrc.x = __builtin_amdgcn_readfirstlane(rsrc.x);
-    rsrc.y = __builtin_amdgcn_readfirstlane(rsrc.y);
-    rsrc.z = __builtin_amdgcn_readfirstlane(rsrc.z);
-    rsrc.w = __builtin_amdgcn_readfirstlane(rsrc.w);
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "buffer_load_dwordx4 %1, %2, %3 offen lds"
-        :
-        : "s"(m0), "v"(voffset), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soffset))
-        : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// Raw buffer stores (the tile epilogue): the descriptor's byte range ends at
-// the last valid row, and the hardware drops stores past it.
-__device__ void buffer_store_i16(short v, i32x4_t rsrc, int voffset, int soffset,
-                                 int aux) __asm("llvm.amdgcn.raw.buffer.store.i16");
-__device__ void buffer_store_f32(float v, i32x4_t rsrc, int voffset, int soffset,
-                                 int aux) __asm("llvm.amdgcn.raw.buffer.store.f32");
-__device__ void buffer_store_f32x4(f32x4_t v, i32x4_t rsrc, int voffset, int soffset,
-                                   int aux) __asm("llvm.amdgcn.raw.buffer.store.v4f32");
-
-// Buffer resource: 48-bit base, no stride, num_records bytes; loads past the
-// end return zero and stores past it are dropped.  Every argument must be
-// wave-uniform.
-__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    i32x4_t r;
-    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
-    r.z = __builtin_amdgcn_readfirstlane((int)bytes);
-    r.w = 0x00020000;
-    return r;
-}
+// Training variants of the first product: the same epilogue, which also
+// stores the pre-activations the backward needs (SwiGLU: g = X W_gate and
+// u = X W_up; GELU: z = X W1 + b1), rounded to bf16.
+enum { MODE_SWIGLU_SAVE = 3, MODE_GELU_SAVE = 4 };
+constexpr int mode_base(int m) { return m == MODE_SWIGLU_SAVE ? MODE_SWIGLU : m == MODE_GELU_SAVE ? MODE_GELU : m; }
 
 struct GemmArgs {
     const uint16_t* A;      // [E, C, K], or with slot_token the token rows [a_rows, K]
@@ -153,6 +89,8 @@ struct GemmArgs {
     // split-K of the last, partly filled round of tiles (null part: off)
     float* part;            // per-piece fp32 partial tiles, kPartBytes each
     int smax;               // at most this many pieces per tile
+    uint16_t* save0;        // *_SAVE modes: [E, C, N_out] g (or z)
+    uint16_t* save1;        // SwiGLU: [E, C, N_out] u
 };
 
 constexpr size_t kPartBytes = (size_t)kBM * kBNMax * 4;  // one fp32 tile
@@ -188,47 +126,15 @@ __device__ __forceinline__ int tail_splits(const GemmArgs& g, int total, int G, 
     return sp < 1 ? 1 : sp;
 }
 
-// Tile `logical` -> expert and row / column tile.  Inside an expert, tiles
-// run in groups of every row tile times gn column tiles (about GEMM_GROUP
-// tiles), column-fastest, so one XCD's run of tiles shares A rows and B
-// panels in its L2.
-__device__ __forceinline__ void map_tile(int logical, const int* s_pref, const int* s_mt, int E,
-                                         int NT, int& e, int& m_tile, int& n_tile) {
-    e = 0;
-    while (e + 1 < E && s_pref[e + 1] <= logical) ++e;
-    const int local = logical - s_pref[e];
-    const int mt = s_mt[e];
-    int gn = GEMM_GROUP / mt;
-    if (gn < 1) gn = 1;
-    if (gn > NT) gn = NT;
-    const int grp = local / (mt * gn);
-    int width = NT - grp * gn;
-    if (width > gn) width = gn;
-    const int rem = local - grp * mt * gn;
-    m_tile = rem / width;
-    n_tile = grp * gn + rem % width;
-}
-
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
-__device__ __forceinline__ float gelu_f(float z) {
-    return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
-}
-
-// LDS swizzles (16-byte chunk index XOR).  A rows are 128 bytes: XOR with
-// (row >> 1) & 7 puts any 16 consecutive rows of one chunk on distinct banks.
-// B rows (one 128-column sub-tile) are 256 bytes: a transpose read serves 32
-// lanes per pass, lanes 0-15 and 16-31 reading the same 4 rows at columns 16
-// apart; XOR with 4 * (k & 3) sends the two halves to disjoint chunk sets.
-__device__ __forceinline__ int swz_a(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int swz_b(int k) { return (k & 3) << 2; }
 
 template <int MODE, int BN>
 struct Epi {
-    static_assert(BN == 256 || (BN == 128 && MODE != MODE_SWIGLU), "B tile is 256 or 128 columns");
+    static constexpr int MB = mode_base(MODE);
+    static_assert(BN == 256 || (BN == 128 && MB != MODE_SWIGLU), "B tile is 256 or 128 columns");
     static constexpr int STAGE_B = kBK * BN * 2;            // 32 or 16 KB
     static constexpr int STAGE = kStageA + STAGE_B;
-    static constexpr int BN_OUT = (MODE == MODE_SWIGLU) ? BN / 2 : BN;
-    static constexpr int OUT_BYTES = (MODE == MODE_DOWN) ? 4 : 2;
+    static constexpr int BN_OUT = (MB == MODE_SWIGLU) ? BN / 2 : BN;
+    static constexpr int OUT_BYTES = (MB == MODE_DOWN) ? 4 : 2;
     static constexpr size_t LDS = 2 * (size_t)STAGE;
 };
 
@@ -250,6 +156,8 @@ struct TileCtx {
 template <int MODE, int BN, bool GATHER>
 __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     using EP = Epi<MODE, BN>;
+    constexpr int MB = mode_base(MODE);
+    constexpr bool SAVE = MODE != MB;
     constexpr int kStage = EP::STAGE;
     constexpr int WM_ROWS = kBM / kWMn;       // rows per wave
     constexpr int WN_COLS = BN / kWN;         // B columns per wave
@@ -325,7 +233,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
         }
         const uint16_t* bsrc;
         size_t coloff;
-        if (MODE == MODE_SWIGLU) {
+        if (MB == MODE_SWIGLU) {
             bsrc = (sub == 0 ? g.B0 : g.B1) + (size_t)c.e * g.K * g.N + c.n0;
             coloff = (size_t)c.n0;
         } else {
@@ -388,7 +296,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 int sb, col;  // B sub-tile and column inside it
-                if (MODE == MODE_SWIGLU) {  // first half of the wave's tiles gate, second up
+                if (MB == MODE_SWIGLU) {  // first half of the wave's tiles gate, second up
                     sb = (j < TN / 2) ? 0 : 1;
                     col = wn * (WN_COLS / 2) + (j % (TN / 2)) * 32;
                 } else {
@@ -549,35 +457,49 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
         // so rows past it are dropped by the hardware.
         {
             const uint16_t* biasb = g.bias ? g.bias + (size_t)cur.e * g.N + cur.n0 : nullptr;
-            constexpr int TNO = (MODE == MODE_SWIGLU) ? TN / 2 : TN;
+            constexpr int TNO = (MB == MODE_SWIGLU) ? TN / 2 : TN;
             constexpr int B = EP::OUT_BYTES;
             const i32x4_t rsO = make_rsrc(
                 static_cast<unsigned char*>(g.out) + (((size_t)cur.e * g.C + cur.m0) * g.N + cur.n0) * B,
                 (uint32_t)(((size_t)(cur.kept - cur.m0) * g.N - cur.n0) * B));
             const int row_l = wm * WM_ROWS + (lane / 32) * 4;
+            i32x4_t rsS0 = rsO, rsS1 = rsO;  // same layout and row bound as h
+            if (SAVE) {
+                const size_t off = ((size_t)cur.e * g.C + cur.m0) * g.N + cur.n0;
+                rsS0 = make_rsrc(g.save0 + off, (uint32_t)(((size_t)(cur.kept - cur.m0) * g.N - cur.n0) * 2));
+                if (MB == MODE_SWIGLU)
+                    rsS1 = make_rsrc(g.save1 + off,
+                                     (uint32_t)(((size_t)(cur.kept - cur.m0) * g.N - cur.n0) * 2));
+            }
 #pragma unroll
             for (int j = 0; j < TNO; ++j) {
-                const int ocol = (MODE == MODE_SWIGLU ? wn * (WN_COLS / 2) : wn * WN_COLS) + j * 32 +
+                const int ocol = (MB == MODE_SWIGLU ? wn * (WN_COLS / 2) : wn * WN_COLS) + j * 32 +
                                  lane % 32;
                 const int voff = (row_l * g.N + ocol) * B;
                 float bv = 0.f;
-                if (MODE != MODE_SWIGLU && biasb) bv = bf2f(biasb[ocol]);
+                if (MB != MODE_SWIGLU && biasb) bv = bf2f(biasb[ocol]);
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
 #pragma unroll
                     for (int q = 0; q < 16; ++q) {
                         const int soff = ((i * 32 + (q / 4) * 8 + (q % 4)) * g.N) * B;
                         float v;
-                        if (MODE == MODE_SWIGLU)
+                        if (MB == MODE_SWIGLU)
                             v = silu_f(acc[i][j][q]) * acc[i][j + TN / 2][q];
-                        else if (MODE == MODE_GELU)
+                        else if (MB == MODE_GELU)
                             v = gelu_f(acc[i][j][q] + bv);
                         else
                             v = acc[i][j][q] + bv;
-                        if (MODE == MODE_DOWN)
+                        if (MB == MODE_DOWN)
                             buffer_store_f32(v, rsO, voff, soff, 0);
                         else
                             buffer_store_i16((short)f2bf(v), rsO, voff, soff, 0);
+                        if (SAVE && MB == MODE_SWIGLU) {
+                            buffer_store_i16((short)f2bf(acc[i][j][q]), rsS0, voff, soff, 0);
+                            buffer_store_i16((short)f2bf(acc[i][j + TN / 2][q]), rsS1, voff, soff, 0);
+                        } else if (SAVE) {
+                            buffer_store_i16((short)f2bf(acc[i][j][q] + bv), rsS0, voff, soff, 0);
+                        }
                     }
                 }
             }
@@ -598,9 +520,10 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
 template <int MODE, int BN>
 __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g, int G) {
     using EP = Epi<MODE, BN>;
+    constexpr int MB = mode_base(MODE);
     constexpr int WM_ROWS = kBM / kWMn, WN_COLS = BN / kWN;
     constexpr int TM = WM_ROWS / 32, TN = WN_COLS / 32;
-    constexpr int TNO = (MODE == MODE_SWIGLU) ? TN / 2 : TN;
+    constexpr int TNO = (MB == MODE_SWIGLU) ? TN / 2 : TN;
     constexpr int PER_TILE = kGThreads * TM * TNO * 4;
     __shared__ int s_pref[MOE_MAX_EXPERTS + 1];
     __shared__ int s_mt[MOE_MAX_EXPERTS];
@@ -636,19 +559,19 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g, int G) {
         const int gi1 = (i * TN + jo + TN / 2) * 4 + q4;       // up (SwiGLU)
         float4 s0 = part[base + (size_t)gi0 * kGThreads];
         float4 s1 = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (MODE == MODE_SWIGLU) s1 = part[base + (size_t)gi1 * kGThreads];
+        if (MB == MODE_SWIGLU) s1 = part[base + (size_t)gi1 * kGThreads];
         for (int pc = 1; pc < splits; ++pc) {
             const float4 v0 = part[base + pc * PSTRIDE + (size_t)gi0 * kGThreads];
             s0.x += v0.x; s0.y += v0.y; s0.z += v0.z; s0.w += v0.w;
-            if (MODE == MODE_SWIGLU) {
+            if (MB == MODE_SWIGLU) {
                 const float4 v1 = part[base + pc * PSTRIDE + (size_t)gi1 * kGThreads];
                 s1.x += v1.x; s1.y += v1.y; s1.z += v1.z; s1.w += v1.w;
             }
         }
-        const int col = n0 + (MODE == MODE_SWIGLU ? wn * (WN_COLS / 2) : wn * WN_COLS) + jo * 32 +
+        const int col = n0 + (MB == MODE_SWIGLU ? wn * (WN_COLS / 2) : wn * WN_COLS) + jo * 32 +
                         vlane % 32;
         float bv = 0.f;
-        if (MODE != MODE_SWIGLU && g.bias) bv = bf2f(g.bias[(size_t)e * g.N + col]);
+        if (MB != MODE_SWIGLU && g.bias) bv = bf2f(g.bias[(size_t)e * g.N + col]);
         const float a0[4] = {s0.x, s0.y, s0.z, s0.w};
         const float a1[4] = {s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
@@ -656,14 +579,14 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g, int G) {
             const int row = row0 + u;
             if (row >= kept) break;
             float v;
-            if (MODE == MODE_SWIGLU)
+            if (MB == MODE_SWIGLU)
                 v = silu_f(a0[u]) * a1[u];
-            else if (MODE == MODE_GELU)
+            else if (MB == MODE_GELU)
                 v = gelu_f(a0[u] + bv);
             else
                 v = a0[u] + bv;
             const size_t o = ((size_t)e * g.C + row) * g.N + col;
-            if (MODE == MODE_DOWN)
+            if (MB == MODE_DOWN)
                 static_cast<float*>(g.out)[o] = v;
             else
                 static_cast<uint16_t*>(g.out)[o] = f2bf(v);
@@ -731,13 +654,6 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
     }
 }
 
-int num_cus() {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-        return 256;
-    return n;
-}
 
 template <int MODE, int BN, bool GATHER = false>
 moe_status_t launch_gemm(const GemmArgs& a, hipStream_t st) {
@@ -754,10 +670,12 @@ moe_status_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     if (grid < 8) grid = 8;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kGThreads), EP::LDS, st, a);
     MOE_CHECK_LAUNCH();
-    if (a.part) {  // finishes the split tail tiles, if the device schedule split any
-        hipLaunchKernelGGL((tail_reduce_kernel<MODE, BN>), dim3((unsigned)(4 * num_cus())), dim3(256),
-                           0, st, a, (int)grid);
-        MOE_CHECK_LAUNCH();
+    if constexpr (MODE == mode_base(MODE)) {  // training variants never split
+        if (a.part) {  // finishes the split tail tiles, if the device schedule split any
+            hipLaunchKernelGGL((tail_reduce_kernel<MODE, BN>), dim3((unsigned)(4 * num_cus())),
+                               dim3(256), 0, st, a, (int)grid);
+            MOE_CHECK_LAUNCH();
+        }
     }
     return MOE_OK;
 }
@@ -854,6 +772,7 @@ moe_status_t ffn_impl(void* stream, moe_dtype_t dtype, moe_act_t act, const void
     a1.B1 = static_cast<const uint16_t*>(w3);
     a1.bias = act == MOE_ACT_GELU_BIAS ? static_cast<const uint16_t*>(b1) : nullptr;
     a1.out = h_ws;
+    a1.save0 = a1.save1 = nullptr;
     a1.kept = kept;
     a1.E = E;
     a1.C = C;
@@ -887,6 +806,32 @@ moe_status_t ffn_impl(void* stream, moe_dtype_t dtype, moe_act_t act, const void
 }
 
 }  // namespace
+
+// The first product again with its pre-activations saved (the backward's
+// recompute): h [E, C, I] and g, u (SwiGLU) or z (GELU), all bf16.
+moe_status_t moe_ffn1_save(hipStream_t st, moe_act_t act, const void* x_disp, const int32_t* kept,
+                           int E, int64_t C, int64_t H, int64_t I, const void* w1, const void* w3,
+                           const void* b1, void* h, void* save0, void* save1) {
+    GemmArgs a;
+    a.A = static_cast<const uint16_t*>(x_disp);
+    a.slot_token = nullptr;
+    a.a_rows = 0;
+    a.B0 = static_cast<const uint16_t*>(w1);
+    a.B1 = static_cast<const uint16_t*>(w3);
+    a.bias = act == MOE_ACT_GELU_BIAS ? static_cast<const uint16_t*>(b1) : nullptr;
+    a.out = h;
+    a.save0 = static_cast<uint16_t*>(save0);
+    a.save1 = static_cast<uint16_t*>(save1);
+    a.kept = kept;
+    a.E = E;
+    a.C = C;
+    a.K = (int)H;
+    a.N = (int)I;
+    a.part = nullptr;
+    a.smax = 1;
+    return act == MOE_ACT_SWIGLU ? launch_gemm<MODE_SWIGLU_SAVE, 256>(a, st)
+                                 : launch_gemm<MODE_GELU_SAVE, 256>(a, st);
+}
 
 extern "C" moe_status_t moe_expert_ffn(void* stream, moe_dtype_t dtype, moe_act_t act,
                                        const void* x_disp, const int32_t* kept, int E, int64_t C,

@@ -1,0 +1,14 @@
+// Library-internal entry points shared between translation units (not part
+// of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/moe.h"
+
+// The first expert product on x_disp with its pre-activations saved for the
+// backward: h [E, C, I] and, all bf16 with the same layout, g = X W_gate and
+// u = X W_up (SwiGLU) or z = X W1 + b1 in save0 (GELU; save1 unused).
+moe_status_t moe_ffn1_save(hipStream_t st, moe_act_t act, const void* x_disp, const int32_t* kept,
+                           int E, int64_t C, int64_t H, int64_t I, const void* w1, const void* w3,
+                           const void* b1, void* h, void* save0, void* save1);

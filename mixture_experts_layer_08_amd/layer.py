@@ -128,6 +128,31 @@ class MoELayerGPU:
         b = self.buf
         return ops.moe_combine(b.y_disp, b.slot, b.topk_w, y=b.y)
 
+    def backward(self, x: torch.Tensor, dy: torch.Tensor, dl_aux: float = 1.0) -> Dict:
+        """Gradients of sum(dy * y) + dl_aux * L_aux after forward(x) (the
+        forward's buffers are read; the layer must keep x_disp, i.e. be built
+        with fused_gather=False).  Returns fp32 tensors: dx [T, H], dw_r,
+        db_r (or None), and the expert weight gradients under the input names
+        (w_gate, w_up, w_down or w1, b1, w2, b2)."""
+        if self.buf.x_disp is None:
+            raise ValueError("backward needs the dispatched rows: build the layer with "
+                             "fused_gather=False")
+        b, cfg = self.buf, self.cfg
+        dy_disp, dw = ops.moe_combine_bwd(dy, b.y_disp, b.slot, b.topk_w)
+        g = ops.moe_expert_ffn_bwd(b.x_disp, b.kept, self.w1, self.w3, self.w2, self.b1, dy_disp,
+                                   act=cfg.act, has_b2=self.b2 is not None)
+        dx = ops.moe_dispatch_bwd(g["dx_disp"], b.slot)
+        dlogits, dw_r, db_r = ops.moe_route_bwd(
+            x, self.w_r, b.probs, b.topk_idx, b.topk_w, dw, b.f, alpha=cfg.alpha, dl_aux=dl_aux,
+            mode=cfg.route, seq_len=cfg.seq_len, dx=dx, bias=self.b_r is not None)
+        out = {"dx": dx, "dw_r": dw_r, "db_r": db_r, "dw_topk": dw, "dlogits": dlogits,
+               "dy_disp": dy_disp, "dx_disp": g["dx_disp"]}
+        if cfg.act == "swiglu":
+            out.update(w_gate=g["dw1"], w_up=g["dw3"], w_down=g["dw2"])
+        else:
+            out.update(w1=g["dw1"], b1=g["db1"], w2=g["dw2"], b2=g["db2"])
+        return out
+
     def forward(self, x: torch.Tensor, keys: bool = False):
         """y [T, H] and L_aux [1]; every intermediate stays in self.buf."""
         self.route(x, keys=keys)

@@ -194,3 +194,86 @@ def moe_combine(y_disp: torch.Tensor, slot: torch.Tensor, topk_w: torch.Tensor, 
                            _ptr(topk_w), T, H, k, _ptr(y))
     check("moe_combine", st)
     return y
+
+
+# ------------------------------------------------------------- backward ----
+
+def moe_combine_bwd(dy: torch.Tensor, y_disp: torch.Tensor, slot: torch.Tensor,
+                    topk_w: torch.Tensor, *, dy_disp: Optional[torch.Tensor] = None,
+                    dw: Optional[torch.Tensor] = None):
+    """dy_disp [E, C, H] (dy's dtype; rows of kept copies written) and dw [T, k]."""
+    T, H = dy.shape
+    k = slot.shape[1]
+    dev = dy.device
+    if y_disp.dtype != torch.float32 or y_disp.shape[-1] != H:
+        raise ValueError("y_disp must be fp32 [E, C, H]")
+    dy_disp = _want(dy_disp, tuple(y_disp.shape), dy.dtype, dev)
+    dw = _want(dw, (T, k), torch.float32, dev)
+    st = lib().moe_combine_bwd(_stream(dev), _dtype_code(dy), _ptr(dy), _ptr(y_disp), _ptr(slot),
+                               _ptr(topk_w), T, H, k, _ptr(dy_disp), _ptr(dw))
+    check("moe_combine_bwd", st)
+    return dy_disp, dw
+
+
+def moe_expert_ffn_bwd(x_disp: torch.Tensor, kept: torch.Tensor, w1: torch.Tensor,
+                       w3: Optional[torch.Tensor], w2: torch.Tensor, b1: Optional[torch.Tensor],
+                       dy_disp: torch.Tensor, *, act: str = "swiglu", has_b2: bool = True,
+                       ws: Optional[torch.Tensor] = None):
+    """Gradients of the expert FFNs: dict with dx_disp [E, C, H] and the
+    weight (and GELU bias) gradients, all fp32."""
+    E, C, H = x_disp.shape
+    I = w1.shape[2]
+    dev = x_disp.device
+    f32 = torch.float32
+    out = {"dx_disp": torch.empty((E, C, H), dtype=f32, device=dev),
+           "dw1": torch.empty((E, H, I), dtype=f32, device=dev),
+           "dw2": torch.empty((E, I, H), dtype=f32, device=dev),
+           "dw3": torch.empty((E, H, I), dtype=f32, device=dev) if act == "swiglu" else None,
+           "db1": torch.empty((E, I), dtype=f32, device=dev) if act == "gelu" else None,
+           "db2": torch.empty((E, H), dtype=f32, device=dev) if act == "gelu" and has_b2 else None}
+    if ws is None:
+        ws = torch.empty(max(16, int(lib().moe_expert_ffn_bwd_ws_bytes(E, C, I))),
+                         dtype=torch.uint8, device=dev)
+    st = lib().moe_expert_ffn_bwd(_stream(dev), _dtype_code(x_disp), ACTS[act], _ptr(x_disp),
+                                  _ptr(kept), E, C, H, I, _ptr(w1), _ptr(w3), _ptr(w2), _ptr(b1),
+                                  _ptr(dy_disp), _ptr(out["dx_disp"]), _ptr(out["dw1"]),
+                                  _ptr(out["dw3"]), _ptr(out["dw2"]), _ptr(out["db1"]),
+                                  _ptr(out["db2"]), _ptr(ws), ws.numel())
+    check("moe_expert_ffn_bwd", st)
+    return out
+
+
+def moe_dispatch_bwd(dx_disp: torch.Tensor, slot: torch.Tensor, *,
+                     dx: Optional[torch.Tensor] = None) -> torch.Tensor:
+    H = dx_disp.shape[-1]
+    T, k = slot.shape
+    dev = slot.device
+    dx = _want(dx, (T, H), torch.float32, dev)
+    st = lib().moe_dispatch_bwd(_stream(dev), _ptr(dx_disp), _ptr(slot), T, H, k, _ptr(dx))
+    check("moe_dispatch_bwd", st)
+    return dx
+
+
+def moe_route_bwd(x: torch.Tensor, w_r: torch.Tensor, probs: torch.Tensor,
+                  topk_idx: torch.Tensor, topk_w: torch.Tensor, dw: torch.Tensor,
+                  f: torch.Tensor, *, alpha: float, dl_aux: float, mode: str = "softmax",
+                  seq_len: int = 0, dx: Optional[torch.Tensor] = None, bias: bool = False,
+                  ws: Optional[torch.Tensor] = None):
+    """dlogits [T, E], dw_r [H, E], db_r [E] (or None); dx, when given, gets
+    dlogits W_r^T added in place."""
+    T, H = x.shape
+    E = w_r.shape[1]
+    k = topk_idx.shape[1]
+    dev = x.device
+    f32 = torch.float32
+    dlogits = torch.empty((T, E), dtype=f32, device=dev)
+    dw_r = torch.empty((H, E), dtype=f32, device=dev)
+    db_r = torch.empty((E,), dtype=f32, device=dev) if bias else None
+    if ws is None:
+        ws = torch.empty(int(lib().moe_route_bwd_ws_bytes(T, H, E)), dtype=torch.uint8, device=dev)
+    st = lib().moe_route_bwd(_stream(dev), _dtype_code(x), ROUTE_MODES[mode], _ptr(x), _ptr(w_r),
+                             _ptr(probs), _ptr(topk_idx), _ptr(topk_w), _ptr(dw), _ptr(f),
+                             float(alpha), float(dl_aux), T, H, E, k, int(seq_len), _ptr(dlogits),
+                             _ptr(dx), _ptr(dw_r), _ptr(db_r), _ptr(ws), ws.numel())
+    check("moe_route_bwd", st)
+    return dlogits, dw_r, db_r
