@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--iso-reps", type=int, default=10)
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the backward pass (combine, expert FFN, dispatch and router "
+                         "backward) after a forward that keeps the dispatched rows")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run three plain 256 MiB device copies (read 256 MiB, write "
                          "256 MiB each), the reference for HBM traffic counters")
@@ -152,6 +155,60 @@ def cpu_baseline(cfg, inputs):
         "affinity_cores": len(os.sched_getaffinity(0)), "cpu": cpu_model, "blas": blas,
         "phase_s": {k: round(v, 4) for k, v in res.timings.items()},
     }
+
+
+def bench_backward(cfg, inputs, dev, args):
+    """Forward (keeping x_disp) + backward, with per-phase events."""
+    import torch
+    from mixture_experts_layer_08_amd import ops
+    from mixture_experts_layer_08_amd.layer import MoELayerGPU, x_to_device
+    layer = MoELayerGPU(cfg, inputs, dev, fused_gather=False)
+    x = x_to_device(inputs, cfg, dev)
+    g = torch.Generator(device="cpu").manual_seed(cfg.seed)
+    dy = torch.randn((cfg.T, cfg.H), generator=g).to(layer.tdtype).to(dev)
+    b = layer.buf
+    bws = torch.empty(max(16, int(ops.lib().moe_expert_ffn_bwd_ws_bytes(cfg.E, layer.C, cfg.I))),
+                      dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        rec = (lambda i: ev[i].record(stream)) if ev else (lambda i: None)
+        rec(0)
+        layer.forward(x)
+        rec(1)
+        dy_disp, dw = ops.moe_combine_bwd(dy, b.y_disp, b.slot, b.topk_w)
+        rec(2)
+        gr = ops.moe_expert_ffn_bwd(b.x_disp, b.kept, layer.w1, layer.w3, layer.w2, layer.b1,
+                                    dy_disp, act=cfg.act, has_b2=layer.b2 is not None, ws=bws)
+        rec(3)
+        dx = ops.moe_dispatch_bwd(gr["dx_disp"], b.slot)
+        rec(4)
+        ops.moe_route_bwd(x, layer.w_r, b.probs, b.topk_idx, b.topk_w, dw, b.f, alpha=cfg.alpha,
+                          dl_aux=1.0, mode=cfg.route, seq_len=cfg.seq_len, dx=dx,
+                          bias=layer.b_r is not None)
+        rec(5)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    K = max(1, args.steps // 2)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for s_ in range(K):
+        step(evs[s_])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / K
+    names = ["forward", "combine_bwd", "expert_ffn_bwd", "dispatch_bwd", "route_bwd"]
+    ph = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+    n_kept = int(b.kept.cpu().numpy().sum())
+    # recompute of the first product + dh + dX + the weight gradients
+    mult = 16 if cfg.act == "swiglu" else 10
+    bwd_flop = mult * cfg.H * cfg.I * n_kept
+    tf = bwd_flop / (ph["expert_ffn_bwd"] * 1e-3) / 1e12
+    return {"train_step_ms": round(wall * 1e3, 5), "train_tokens_per_s": round(cfg.T / wall, 1),
+            "steps": K, "phases_ms": {k: round(v, 5) for k, v in ph.items()},
+            "expert_ffn_bwd": {"flop": bwd_flop, "TFLOP/s": round(tf, 2),
+                               "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
 
 
 def main():
@@ -300,6 +357,8 @@ def main():
         "phases": phases,
         "device_ms_per_step": round(dev_ms, 5),
     }
+    if args.backward:
+        out["backward"] = bench_backward(cfg, inputs, dev, args)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, inputs)
