@@ -89,66 +89,77 @@ struct RouteBwdParams {
     float* dl;               // [T, E]
 };
 
-// One thread per token.
+// One wave per token, lane e holding expert e (E <= 64); the two sums over
+// experts reduce across the wave in a fixed tree order.
 __global__ __launch_bounds__(256) void route_bwd_logits_kernel(RouteBwdParams p) {
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t t = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
+    const int e = threadIdx.x % 64;
     if (t >= p.T) return;
     const int E = p.E, k = p.k;
-    const float* pr = p.probs + t * E;
+    const bool live = e < E;
+    const float pe = live ? p.probs[t * E + e] : 0.f;
+    // S = sum of the selected probabilities, dot = sum_j dw_j w_j (k <= 8 terms,
+    // read by every lane in the same order)
     float S = 0.f, dot = 0.f;
     for (int j = 0; j < k; ++j) {
-        const int e = p.idx[t * k + j];
-        S += pr[e];
+        const int ej = p.idx[t * k + j];
+        S += p.probs[t * E + ej];
         dot = fmaf(p.dw[t * k + j], p.w[t * k + j], dot);
     }
-    float dpv[MOE_MAX_EXPERTS];
-    for (int e = 0; e < E; ++e) dpv[e] = p.aux_scale * p.f[e];
-    for (int j = 0; j < k; ++j) {
-        const int e = p.idx[t * k + j];
-        dpv[e] += (p.dw[t * k + j] - dot) / S;
-    }
-    float sd = 0.f;
-    for (int e = 0; e < E; ++e) sd = fmaf(dpv[e], pr[e], sd);
-    for (int e = 0; e < E; ++e) p.dl[t * E + e] = pr[e] * (dpv[e] - sd) * p.inv_tau;
+    float dpe = live ? p.aux_scale * p.f[e] : 0.f;  // aux statistics' term
+    for (int j = 0; j < k; ++j)                       // renormalisation's term
+        if (p.idx[t * k + j] == e) dpe += (p.dw[t * k + j] - dot) / S;
+    const float sd = group_sum(dpe * pe, 64);
+    if (live) p.dl[t * E + e] = pe * (dpe - sd) * p.inv_tau;
 }
 
-// dx[t, h] += sum_e dl[t, e] * W_r[h, e]: 4 tokens per block, 8 columns per
-// thread step.
+// dx[t, h] += sum_e dl[t, e] * W_r[h, e].  A block takes 8 tokens; a thread
+// takes 8 consecutive columns, holds their W_r values for 8 experts at a
+// time in registers and applies them to every token of the block (dl staged
+// in LDS), so W_r is read once per 8 tokens.
+constexpr int kDxTok = 8;
 template <bool BF16>
 __global__ __launch_bounds__(256) void route_bwd_dx_kernel(const float* __restrict__ dl,
                                                            const void* __restrict__ w_r,
                                                            int64_t T, int H, int E,
                                                            float* __restrict__ dx) {
-    __shared__ float s_dl[4 * MOE_MAX_EXPERTS];
-    const int64_t t0 = (int64_t)blockIdx.x * 4;
-    int nt = 4;
+    __shared__ float s_dl[kDxTok * MOE_MAX_EXPERTS];
+    const int64_t t0 = (int64_t)blockIdx.x * kDxTok;
+    int nt = kDxTok;
     if (t0 + nt > T) nt = (int)(T - t0);
     for (int q = threadIdx.x; q < nt * E; q += blockDim.x) s_dl[q] = dl[t0 * E + q];
     __syncthreads();
     for (int h0 = threadIdx.x * 8; h0 < H; h0 += blockDim.x * 8) {
-        float acc[4][8];
+        float acc[kDxTok][8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kDxTok; ++i)
 #pragma unroll
             for (int c = 0; c < 8; ++c) acc[i][c] = 0.f;
-        for (int e = 0; e < E; ++e) {
-            float wv[8];
+        for (int e0 = 0; e0 < E; e0 += 8) {
+            const int ne = E - e0 < 8 ? E - e0 : 8;
+            float wv[8][8];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const int64_t o = (int64_t)(h0 + c) * E + e;
-                wv[c] = BF16 ? bf2f(static_cast<const uint16_t*>(w_r)[o])
-                             : static_cast<const float*>(w_r)[o];
-            }
+            for (int c = 0; c < 8; ++c)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float d = i < nt ? s_dl[i * E + e] : 0.f;
+                for (int u = 0; u < 8; ++u) {
+                    const int64_t o = (int64_t)(h0 + c) * E + e0 + u;
+                    wv[c][u] = u < ne ? (BF16 ? bf2f(static_cast<const uint16_t*>(w_r)[o])
+                                              : static_cast<const float*>(w_r)[o])
+                                      : 0.f;
+                }
 #pragma unroll
-                for (int c = 0; c < 8; ++c) acc[i][c] = fmaf(d, wv[c], acc[i][c]);
+            for (int i = 0; i < kDxTok; ++i) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float d = (i < nt && u < ne) ? s_dl[i * E + e0 + u] : 0.f;
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) acc[i][c] = fmaf(d, wv[c][u], acc[i][c]);
+                }
             }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (i >= nt) break;
+        for (int i = 0; i < kDxTok; ++i) {
+            if (i >= nt) continue;
             float4* o = reinterpret_cast<float4*>(dx + (t0 + i) * H + h0);
             float4 v0 = o[0], v1 = o[1];
             v0.x += acc[i][0]; v0.y += acc[i][1]; v0.z += acc[i][2]; v0.w += acc[i][3];
@@ -187,6 +198,7 @@ __global__ __launch_bounds__(256) void route_bwd_wpart_kernel(const void* __rest
             s_dl[q] = c < ne ? dl[(tc + tt) * E + e0 + c] : 0.f;
         }
         __syncthreads();
+#pragma unroll 8
         for (int tt = 0; tt < n; ++tt) {
             const float xv = h < H ? (BF16 ? bf2f(static_cast<const uint16_t*>(x)[(tc + tt) * H + h])
                                            : static_cast<const float*>(x)[(tc + tt) * H + h])
@@ -212,7 +224,15 @@ __global__ __launch_bounds__(256) void route_bwd_wfinal_kernel(const float* __re
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < (int64_t)H * E) {
         float s = 0.f;
-        for (int b = 0; b < nb; ++b) s += part[(int64_t)b * H * E + i];
+        int b = 0;
+        for (; b + 8 <= nb; b += 8) {  // eight loads in flight, summed in chunk order
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(b + u) * H * E + i];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s += v[u];
+        }
+        for (; b < nb; ++b) s += part[(int64_t)b * H * E + i];
         dw_r[i] = s;
     }
     if (db_r && i < E) {
@@ -301,11 +321,10 @@ extern "C" moe_status_t moe_route_bwd(void* stream, moe_dtype_t dtype, moe_route
     p.E = E;
     p.k = k;
     p.dl = dlogits;
-    hipLaunchKernelGGL(route_bwd_logits_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st,
-                       p);
+    hipLaunchKernelGGL(route_bwd_logits_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, p);
     MOE_CHECK_LAUNCH();
     if (dx) {
-        const unsigned g = (unsigned)((T + 3) / 4);
+        const unsigned g = (unsigned)((T + kDxTok - 1) / kDxTok);
         if (bf)
             hipLaunchKernelGGL(route_bwd_dx_kernel<true>, dim3(g), dim3(256), 0, st, dlogits, w_r, T,
                                (int)H, E, dx);

@@ -35,8 +35,11 @@
 
 #include <type_traits>
 
-__device__ short buffer_load_i16(moe_i32x4_t rsrc, int voffset, int soffset,
-                                 int aux) __asm("llvm.amdgcn.raw.buffer.load.i16");
+typedef int moe_i32x2_t __attribute__((ext_vector_type(2)));
+__device__ moe_i32x2_t buffer_load_i32x2(moe_i32x4_t rsrc, int voffset, int soffset,
+                                         int aux) __asm("llvm.amdgcn.raw.buffer.load.v2i32");
+__device__ void buffer_store_i32x2(moe_i32x2_t v, moe_i32x4_t rsrc, int voffset, int soffset,
+                                   int aux) __asm("llvm.amdgcn.raw.buffer.store.v2i32");
 
 namespace {
 
@@ -250,7 +253,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ss][i], bfr[ss][j],
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ss][j], af[ss][i],
                                                                             acc[i][j], 0, 0, 0);
         };
         // The forward's pipeline: one barrier per k-step, the second half of
@@ -307,26 +310,33 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
         else
             kloop(std::false_type{});
 
-        // epilogue (accumulator element q of lane l: row 8*(q/4) + 4*(l/32) +
-        // q%4, column l%32 of its 32 x 32 block); descriptors end at the last
-        // valid row, so padding rows are neither read nor written
+        // epilogue.  The products run with the operands swapped (C^T = B^T
+        // A^T), so accumulator element q of lane l is output row l%32 and
+        // column 8*(q/4) + 4*(l/32) + q%4 of its 32 x 32 block: four
+        // consecutive columns per lane, stored (and, for dh, read) as one
+        // 16- or 8-byte access.  Descriptors end at the last valid row, so
+        // padding rows are neither read nor written.
         {
             const int R = KC ? (int)g.C : g.M;  // rows of the output per expert
             const size_t obase = ((size_t)cur.e * R + cur.m0) * g.N + cur.n0;
             const uint32_t obytes = (uint32_t)(((size_t)cur.rows * g.N - cur.n0));
-            const int row_l = wm * WM_ROWS + (lane / 32) * 4;
+            const int vel = (wm * WM_ROWS + lane % 32) * g.N + wn * WN_COLS + (lane / 32) * 4;
             if (EPI == EPI_F32) {
                 const i32x4_t rsO = make_rsrc(static_cast<float*>(g.out) + obase, obytes * 4);
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int voff = (row_l * g.N + wn * WN_COLS + j * 32 + lane % 32) * 4;
+                for (int i = 0; i < TM; ++i)
 #pragma unroll
-                    for (int i = 0; i < TM; ++i)
+                    for (int j = 0; j < TN; ++j)
 #pragma unroll
-                        for (int q = 0; q < 16; ++q)
-                            buffer_store_f32(acc[i][j][q], rsO, voff,
-                                             ((i * 32 + (q / 4) * 8 + (q % 4)) * g.N) * 4, 0);
-                }
+                        for (int qq = 0; qq < 4; ++qq) {
+                            f32x4_t v;
+                            v.x = acc[i][j][qq * 4 + 0];
+                            v.y = acc[i][j][qq * 4 + 1];
+                            v.z = acc[i][j][qq * 4 + 2];
+                            v.w = acc[i][j][qq * 4 + 3];
+                            buffer_store_f32x4(v, rsO, vel * 4,
+                                               (i * 32 * g.N + j * 32 + qq * 8) * 4, 0);
+                        }
             } else {
                 const i32x4_t rsO = make_rsrc(static_cast<uint16_t*>(g.out) + obase, obytes * 2);
                 const i32x4_t rs0 = make_rsrc(g.side0 + obase, obytes * 2);
@@ -336,29 +346,51 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
                     rs1 = make_rsrc(g.side1 + obase, obytes * 2);
                 }
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int voff = (row_l * g.N + wn * WN_COLS + j * 32 + lane % 32) * 2;
+                for (int i = 0; i < TM; ++i)
 #pragma unroll
-                    for (int i = 0; i < TM; ++i)
+                    for (int j = 0; j < TN; ++j) {
+                        // all side reads of this 32 x 32 block first, then the math
+                        moe_i32x2_t sa[4], su[4];
 #pragma unroll
-                        for (int q = 0; q < 16; ++q) {
-                            const int soff = ((i * 32 + (q / 4) * 8 + (q % 4)) * g.N) * 2;
-                            const float dh = acc[i][j][q];
-                            const float a = bf2f((uint16_t)buffer_load_i16(rs0, voff, soff, 0));
+                        for (int qq = 0; qq < 4; ++qq) {
+                            const int so = (i * 32 * g.N + j * 32 + qq * 8) * 2;
+                            sa[qq] = buffer_load_i32x2(rs0, vel * 2, so, 0);
+                            if (EPI == EPI_DH_SWIGLU) su[qq] = buffer_load_i32x2(rs1, vel * 2, so, 0);
+                        }
+#pragma unroll
+                        for (int qq = 0; qq < 4; ++qq) {
+                            const int so = (i * 32 * g.N + j * 32 + qq * 8) * 2;
+                            float r0[4], r1[4];
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) {
+                                const uint32_t wa = (uint32_t)sa[qq][c / 2];
+                                const float a = (c & 1) ? bf_hi(wa) : bf_lo(wa);
+                                const float dh = acc[i][j][qq * 4 + c];
+                                if (EPI == EPI_DH_SWIGLU) {
+                                    const uint32_t wu = (uint32_t)su[qq][c / 2];
+                                    const float u = (c & 1) ? bf_hi(wu) : bf_lo(wu);
+                                    const float sg = 1.0f / (1.0f + __expf(-a));
+                                    const float dsilu = sg * (1.0f + a * (1.0f - sg));
+                                    r0[c] = dh * u * dsilu;
+                                    r1[c] = dh * a * sg;
+                                } else {
+                                    const float cdf = 0.5f * (1.0f + erff(a * 0.70710678118654752f));
+                                    const float pdf = 0.39894228040143268f * __expf(-0.5f * a * a);
+                                    r0[c] = dh * (cdf + a * pdf);
+                                }
+                            }
+                            moe_i32x2_t o0;
+                            o0.x = (int)pack_bf2(r0[0], r0[1]);
+                            o0.y = (int)pack_bf2(r0[2], r0[3]);
+                            buffer_store_i32x2(o0, rsO, vel * 2, so, 0);
                             if (EPI == EPI_DH_SWIGLU) {
-                                const float u = bf2f((uint16_t)buffer_load_i16(rs1, voff, soff, 0));
-                                const float sg = 1.0f / (1.0f + __expf(-a));
-                                const float dsilu = sg * (1.0f + a * (1.0f - sg));
-                                buffer_store_i16((short)f2bf(dh * u * dsilu), rsO, voff, soff, 0);
-                                buffer_store_i16((short)f2bf(dh * a * sg), rsO1, voff, soff, 0);
-                            } else {
-                                const float cdf = 0.5f * (1.0f + erff(a * 0.70710678118654752f));
-                                const float pdf = 0.39894228040143268f * __expf(-0.5f * a * a);
-                                buffer_store_i16((short)f2bf(dh * (cdf + a * pdf)), rsO, voff,
-                                                 soff, 0);
+                                moe_i32x2_t o1;
+                                o1.x = (int)pack_bf2(r1[0], r1[1]);
+                                o1.y = (int)pack_bf2(r1[2], r1[3]);
+                                buffer_store_i32x2(o1, rsO1, vel * 2, so, 0);
                             }
                         }
-                }
+                    }
             }
         }
         if (!nxt.valid) break;
