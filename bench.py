@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward pass (combine, expert FFN, dispatch and router "
                          "backward) after a forward that keeps the dispatched rows")
+    ap.add_argument("--shared", type=int, default=0, metavar="I_S",
+                    help="also time the layer with a shared expert of intermediate size I_S "
+                         "(every token, weight 1)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run three plain 256 MiB device copies (read 256 MiB, write "
                          "256 MiB each), the reference for HBM traffic counters")
@@ -211,6 +214,43 @@ def bench_backward(cfg, inputs, dev, args):
                                "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
 
 
+def bench_shared(cfg, dev, args):
+    """The layer plus a shared expert of intermediate size args.shared: the
+    whole forward, and the shared expert's own launches alone."""
+    import torch
+    from mixture_experts_layer_08_amd.layer import MoELayerGPU, x_to_device
+    from mixture_experts_layer_08_amd.synth import make_inputs
+    scfg = cfg.with_(shared_I=args.shared)
+    inputs = make_inputs(scfg)
+    layer = MoELayerGPU(scfg, inputs, dev)
+    x = x_to_device(inputs, scfg, dev)
+    stream = torch.cuda.current_stream()
+
+    res = {}
+    for name, fn in (("layer", lambda: layer.forward(x)), ("shared", lambda: layer.shared_expert(x))):
+        for _ in range(max(1, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        K = max(1, args.steps)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(K):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        res[name] = a.elapsed_time(b) / K
+    n_kept = int(layer.buf.kept.cpu().numpy().sum())
+    per_row = (6 if cfg.act == "swiglu" else 4) * cfg.H
+    flop = per_row * (cfg.I * n_kept + args.shared * cfg.T)
+    ms = res["layer"]
+    sh_flop = per_row * args.shared * cfg.T
+    return {"shared_intermediate": args.shared, "ms_per_step": round(ms, 5),
+            "tokens_per_s": round(cfg.T / (ms * 1e-3), 1), "expert_flop": flop,
+            "shared_expert_ms": round(res["shared"], 5),
+            "shared_expert_TFLOP/s": round(sh_flop / (res["shared"] * 1e-3) / 1e12, 2)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -359,6 +399,8 @@ def main():
     }
     if args.backward:
         out["backward"] = bench_backward(cfg, inputs, dev, args)
+    if args.shared:
+        out["shared_expert"] = bench_shared(cfg, dev, args)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, inputs)

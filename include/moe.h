@@ -222,16 +222,20 @@ size_t moe_expert_ffn_ws_bytes(void);
  * section 3.1 (each token's output is the weighted sum of its selected
  * experts' outputs).  Dropped assignments (slot < 0) add nothing and the
  * other weights are not renormalised; a token with every copy dropped gets
- * zeros.
+ * zeros (plus the shared experts' row, if any).
  *
- *   y_disp [E*C, H] fp32 (moe_expert_ffn's output), slot [T, k] int32,
- *   topk_w [T, k] fp32
- *   y      [T, H]   dtype out   (fp32 accumulation, bf16 rounded once)
- * H must be a multiple of 8. 
+ *   y_disp   [E*C, H] fp32 (moe_expert_ffn's output), slot [T, k] int32,
+ *   topk_w   [T, k] fp32
+ *   y_shared [T, H]   fp32 or NULL: the shared experts' output, added to
+ *            every token's sum with weight 1 ([P1] section 5.2: shared
+ *            experts every token passes through; moe_expert_ffn with E = 1,
+ *            C = T, kept = {T} and x itself as x_disp computes it)
+ *   y        [T, H]   dtype out   (fp32 accumulation, bf16 rounded once)
+ * H must be a multiple of 8; y_disp, y_shared and y 16-byte aligned.
  * Every slot must be -1 or a row index below E*C (not checked on device). */
 moe_status_t moe_combine(void* stream, moe_dtype_t dtype, const void* y_disp,
                          const int32_t* slot, const float* topk_w, int64_t T,
-                         int64_t H, int k, void* y);
+                         int64_t H, int k, const float* y_shared, void* y);
 
 /* ------------------------------------------------------------ backward ----
  * Gradients of  L = sum(dy * y) + dl_aux * L_aux  for a given output
@@ -289,12 +293,14 @@ moe_status_t moe_expert_ffn_bwd(void* stream, moe_dtype_t dtype, moe_act_t act,
 /* Bytes of moe_expert_ffn_bwd's workspace: five bf16 [E, C, I] planes. */
 size_t moe_expert_ffn_bwd_ws_bytes(int E, int64_t C, int64_t I);
 
-/* Dispatch backward: dx[t] = sum over kept j of dx_disp[slot[t, j]] (fp32;
- * a token with every copy dropped gets zeros).  [P1] section 2.4 (the
- * copies are gathered back by token).  H a multiple of 8. */
+/* Dispatch backward: dx[t] = dx_add[t] + sum over kept j of
+ * dx_disp[slot[t, j]] (fp32; dx_add may be NULL, then a token with every
+ * copy dropped gets zeros).  [P1] section 2.4 (the copies are gathered back
+ * by token); dx_add carries the shared experts' input gradient ([P1]
+ * section 5.2).  H a multiple of 8; pointers 16-byte aligned. */
 moe_status_t moe_dispatch_bwd(void* stream, const float* dx_disp,
                               const int32_t* slot, int64_t T, int64_t H, int k,
-                              float* dx);
+                              const float* dx_add, float* dx);
 
 /* Router backward.  [P5] section 3.1 (renormalised top-k of the softmax),
  * [P2] section 2.3 (L_aux), [P4] section 2 (Gumbel soft path).

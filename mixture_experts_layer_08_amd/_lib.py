@@ -66,7 +66,7 @@ def _declare(L: ctypes.CDLL) -> None:
     L.moe_expert_ffn_gather.restype = i32
     L.moe_expert_ffn_ws_bytes.argtypes = []
     L.moe_expert_ffn_ws_bytes.restype = c.c_size_t
-    L.moe_combine.argtypes = [vp, i32, vp, vp, vp, i64, i64, i32, vp]
+    L.moe_combine.argtypes = [vp, i32, vp, vp, vp, i64, i64, i32, vp, vp]
     L.moe_combine.restype = i32
     L.moe_combine_bwd.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i32, vp, vp]
     L.moe_combine_bwd.restype = i32
@@ -75,7 +75,7 @@ def _declare(L: ctypes.CDLL) -> None:
     L.moe_expert_ffn_bwd.restype = i32
     L.moe_expert_ffn_bwd_ws_bytes.argtypes = [i32, i64, i64]
     L.moe_expert_ffn_bwd_ws_bytes.restype = c.c_size_t
-    L.moe_dispatch_bwd.argtypes = [vp, vp, vp, i64, i64, i32, vp]
+    L.moe_dispatch_bwd.argtypes = [vp, vp, vp, i64, i64, i32, vp, vp]
     L.moe_dispatch_bwd.restype = i32
     L.moe_route_bwd.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, f32, i64, i64, i32,
                                 i32, i64, vp, vp, vp, vp, vp, c.c_size_t]

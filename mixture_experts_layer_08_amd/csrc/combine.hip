@@ -6,6 +6,10 @@
 //      copy (slot < 0) contributes nothing and the remaining weights are
 //      not renormalised.
 //
+// [P1] section 5.2 adds shared experts that every token passes through; their
+//      output (one fp32 row per token, computed like a routed expert over all
+//      tokens) is the optional addend the sum starts from.
+//
 // Bandwidth-bound gather: each workgroup owns a few tokens; each lane owns
 // 8 columns of the row, reads them from the k fp32 expert rows through
 // slot[], accumulates in fp32 and writes the row once (bf16 output is
@@ -24,7 +28,8 @@ constexpr int kCTok = 4;
 template <bool BF16_OUT>
 __global__ __launch_bounds__(kCThreads) void combine_kernel(const float4* __restrict__ yd,
                                                            const int32_t* __restrict__ slot,
-                                                           const float* __restrict__ w, int64_t T,
+                                                           const float* __restrict__ w,
+                                                           const float4* __restrict__ yadd, int64_t T,
                                                            int k, int row_oct, void* __restrict__ y) {
     __shared__ int s_slot[kCTok * MOE_MAX_TOPK];
     __shared__ float s_w[kCTok * MOE_MAX_TOPK];
@@ -39,7 +44,14 @@ __global__ __launch_bounds__(kCThreads) void combine_kernel(const float4* __rest
     for (int v = threadIdx.x; v < row_oct; v += kCThreads) {
         float4 a0[kCTok], a1[kCTok];
 #pragma unroll
-        for (int i = 0; i < kCTok; ++i) a0[i] = a1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int i = 0; i < kCTok; ++i) {  // the sum starts from the addend row (or zero)
+            if (yadd && i < nt) {
+                a0[i] = yadd[((t0 + i) * row_oct + v) * 2];
+                a1[i] = yadd[((t0 + i) * row_oct + v) * 2 + 1];
+            } else {
+                a0[i] = a1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
         for (int j = 0; j < k; ++j) {
             float4 q0[kCTok], q1[kCTok];
 #pragma unroll
@@ -86,7 +98,7 @@ __global__ __launch_bounds__(kCThreads) void combine_kernel(const float4* __rest
 
 extern "C" moe_status_t moe_combine(void* stream, moe_dtype_t dtype, const void* y_disp,
                                     const int32_t* slot, const float* topk_w, int64_t T, int64_t H,
-                                    int k, void* y) {
+                                    int k, const float* y_shared, void* y) {
     if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_DTYPE;
     if (T < 0 || H <= 0 || k < 1) return MOE_ERR_SHAPE;
     if (k > MOE_MAX_TOPK || H > (1 << 22) || T * k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
@@ -94,35 +106,42 @@ extern "C" moe_status_t moe_combine(void* stream, moe_dtype_t dtype, const void*
     if (T == 0) return MOE_OK;
     if (!slot || !topk_w || !y) return MOE_ERR_NULL;
     if (y_disp && !moe_aligned16(y_disp)) return MOE_ERR_ALIGN;
-    if (!moe_aligned16(y)) return MOE_ERR_ALIGN;
+    if (!moe_aligned16(y) || (y_shared && !moe_aligned16(y_shared))) return MOE_ERR_ALIGN;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int row_oct = (int)(H / 8);
     const int64_t grid = (T + kCTok - 1) / kCTok;
     if (dtype == MOE_BF16)
         hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)grid), dim3(kCThreads), 0, st,
-                           static_cast<const float4*>(y_disp), slot, topk_w, T, k, row_oct, y);
+                           static_cast<const float4*>(y_disp), slot, topk_w,
+                           reinterpret_cast<const float4*>(y_shared), T, k, row_oct, y);
     else
         hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)grid), dim3(kCThreads), 0, st,
-                           static_cast<const float4*>(y_disp), slot, topk_w, T, k, row_oct, y);
+                           static_cast<const float4*>(y_disp), slot, topk_w,
+                           reinterpret_cast<const float4*>(y_shared), T, k, row_oct, y);
     MOE_CHECK_LAUNCH();
     return MOE_OK;
 }
 
 // Backward of the row copy: a token's gradient is the sum of the gradients
-// of its kept copies (the combine's gather with unit weights), fp32.
+// of its kept copies (the combine's gather with unit weights), fp32, plus
+// the optional addend row (the shared experts' input gradient).
 extern "C" moe_status_t moe_dispatch_bwd(void* stream, const float* dx_disp, const int32_t* slot,
-                                         int64_t T, int64_t H, int k, float* dx) {
+                                         int64_t T, int64_t H, int k, const float* dx_add,
+                                         float* dx) {
     if (T < 0 || H <= 0 || k < 1) return MOE_ERR_SHAPE;
     if (k > MOE_MAX_TOPK || H > (1 << 22) || T * k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
     if (H % 8) return MOE_ERR_ALIGN;
     if (T == 0) return MOE_OK;
     if (!slot || !dx) return MOE_ERR_NULL;
-    if ((dx_disp && !moe_aligned16(dx_disp)) || !moe_aligned16(dx)) return MOE_ERR_ALIGN;
+    if ((dx_disp && !moe_aligned16(dx_disp)) || !moe_aligned16(dx) ||
+        (dx_add && !moe_aligned16(dx_add)))
+        return MOE_ERR_ALIGN;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int64_t grid = (T + kCTok - 1) / kCTok;
     hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)grid), dim3(kCThreads), 0, st,
-                       reinterpret_cast<const float4*>(dx_disp), slot, (const float*)nullptr, T, k,
-                       (int)(H / 8), static_cast<void*>(dx));
+                       reinterpret_cast<const float4*>(dx_disp), slot, (const float*)nullptr,
+                       reinterpret_cast<const float4*>(dx_add), T, k, (int)(H / 8),
+                       static_cast<void*>(dx));
     MOE_CHECK_LAUNCH();
     return MOE_OK;
 }

@@ -8,6 +8,14 @@ reads each expert's rows straight from x (moe_expert_ffn_gather); without
 it, dispatch materialises x_disp and moe_expert_ffn reads that.  It mirrors the (out, aux_loss) return
 of the minimal MoELayer of the MoE basics page (dpshk.com/news/6005940,
 section 3.1).
+
+A shared expert (the LLaMA4-MoE guide, dpshk.com/news/5809432, section 5.2:
+an expert every token passes through) is moe_expert_ffn with one expert
+whose C = T rows are x itself, enqueued first on the same stream; the
+combine adds its output.  (It does not depend on the routing, but running it
+on a second stream measured slower: the persistent product kernels fill
+every compute unit's registers, so concurrent kernels only queue behind
+them, and two interleaved products lose each other's L2 locality.)
 """
 from __future__ import annotations
 
@@ -51,6 +59,11 @@ class Buffers:
     y: torch.Tensor
     ws: torch.Tensor
     ffn_ws: torch.Tensor
+    # shared expert (None without one)
+    sh_kept: Optional[torch.Tensor] = None
+    sh_h: Optional[torch.Tensor] = None
+    sh_y: Optional[torch.Tensor] = None
+    sh_ws: Optional[torch.Tensor] = None
 
 
 class MoELayerGPU:
@@ -76,6 +89,16 @@ class MoELayerGPU:
             self.w2 = _to_dev(inputs["w2"], dev, cfg.dtype)
             self.b1 = _to_dev(inputs["b1"], dev, cfg.dtype)
             self.b2 = _to_dev(inputs.get("b2"), dev, cfg.dtype)
+        self.shared = bool(cfg.shared_I)
+        if self.shared:
+            if cfg.act == "swiglu":
+                self.sw1, self.sw3, self.sw2 = (_to_dev(inputs["shared_" + n], dev, cfg.dtype)
+                                                for n in ("w_gate", "w_up", "w_down"))
+                self.sb1 = self.sb2 = None
+            else:
+                self.sw1, self.sb1, self.sw2, self.sb2 = (
+                    _to_dev(inputs["shared_" + n], dev, cfg.dtype) for n in ("w1", "b1", "w2", "b2"))
+                self.sw3 = None
         self.C = ops.moe_capacity(cfg.T, cfg.k, cfg.E, cfg.cf)
         self.buf = self.alloc(cfg.T)
 
@@ -84,7 +107,13 @@ class MoELayerGPU:
         E, k, H, I = cfg.E, cfg.k, cfg.H, cfg.I
         i32, f32, td = torch.int32, torch.float32, self.tdtype
         e = lambda *s, dt=f32: torch.empty(s, dtype=dt, device=dev)  # noqa: E731
+        sh = {}
+        if self.shared:
+            sh = dict(sh_kept=torch.full((1,), T, dtype=i32, device=dev),
+                      sh_h=e(1, T, cfg.shared_I, dt=td), sh_y=e(1, T, H),
+                      sh_ws=e(ops.moe_expert_ffn_ws_bytes(), dt=torch.uint8))
         return Buffers(
+            **sh,
             topk_idx=e(T, k, dt=i32), topk_w=e(T, k), probs=e(T, E), keys=e(T, E),
             counts=e(E, dt=i32), f=e(E), p=e(E), l_aux=e(1),
             x_disp=None if self.fused_gather else e(E, C, H, dt=td), slot=e(T, k, dt=i32), slot_token=e(E, C, dt=i32),
@@ -124,9 +153,18 @@ class MoELayerGPU:
         return ops.moe_expert_ffn(b.x_disp, b.kept, self.w1, self.w3, self.w2, self.b1, self.b2,
                                   act=self.cfg.act, h_ws=b.h, y_disp=b.y_disp, ws=b.ffn_ws)
 
+    def shared_expert(self, x: torch.Tensor):
+        """The shared expert over all T rows of x (one expert, C = T) on the
+        current stream; its output is buf.sh_y [1, T, H] fp32."""
+        b, T, H = self.buf, self.cfg.T, self.cfg.H
+        return ops.moe_expert_ffn(x.view(1, T, H), b.sh_kept, self.sw1, self.sw3, self.sw2,
+                                  self.sb1, self.sb2, act=self.cfg.act, h_ws=b.sh_h,
+                                  y_disp=b.sh_y, ws=b.sh_ws)
+
     def combine(self):
         b = self.buf
-        return ops.moe_combine(b.y_disp, b.slot, b.topk_w, y=b.y)
+        ysh = b.sh_y.view(self.cfg.T, self.cfg.H) if self.shared else None
+        return ops.moe_combine(b.y_disp, b.slot, b.topk_w, y=b.y, y_shared=ysh)
 
     def backward(self, x: torch.Tensor, dy: torch.Tensor, dl_aux: float = 1.0) -> Dict:
         """Gradients of sum(dy * y) + dl_aux * L_aux after forward(x) (the
@@ -141,20 +179,33 @@ class MoELayerGPU:
         dy_disp, dw = ops.moe_combine_bwd(dy, b.y_disp, b.slot, b.topk_w)
         g = ops.moe_expert_ffn_bwd(b.x_disp, b.kept, self.w1, self.w3, self.w2, self.b1, dy_disp,
                                    act=cfg.act, has_b2=self.b2 is not None)
-        dx = ops.moe_dispatch_bwd(g["dx_disp"], b.slot)
+        g_sh = None
+        if self.shared:  # the shared expert's output gradient is dy itself
+            T, H = cfg.T, cfg.H
+            g_sh = ops.moe_expert_ffn_bwd(x.view(1, T, H), b.sh_kept, self.sw1, self.sw3, self.sw2,
+                                          self.sb1, dy.view(1, T, H), act=cfg.act,
+                                          has_b2=self.sb2 is not None)
+        dx = ops.moe_dispatch_bwd(g["dx_disp"], b.slot,
+                                  dx_add=None if g_sh is None else g_sh["dx_disp"].view(cfg.T, cfg.H))
         dlogits, dw_r, db_r = ops.moe_route_bwd(
             x, self.w_r, b.probs, b.topk_idx, b.topk_w, dw, b.f, alpha=cfg.alpha, dl_aux=dl_aux,
             mode=cfg.route, seq_len=cfg.seq_len, dx=dx, bias=self.b_r is not None)
         out = {"dx": dx, "dw_r": dw_r, "db_r": db_r, "dw_topk": dw, "dlogits": dlogits,
                "dy_disp": dy_disp, "dx_disp": g["dx_disp"]}
-        if cfg.act == "swiglu":
-            out.update(w_gate=g["dw1"], w_up=g["dw3"], w_down=g["dw2"])
-        else:
-            out.update(w1=g["dw1"], b1=g["db1"], w2=g["dw2"], b2=g["db2"])
+        names = (("w_gate", "dw1"), ("w_up", "dw3"), ("w_down", "dw2")) if cfg.act == "swiglu" \
+            else (("w1", "dw1"), ("b1", "db1"), ("w2", "dw2"), ("b2", "db2"))
+        for n, gk in names:
+            out[n] = g[gk]
+            if g_sh is not None:
+                out["shared_" + n] = g_sh[gk]
+        if g_sh is not None:
+            out["dx_shared"] = g_sh["dx_disp"].view(cfg.T, cfg.H)
         return out
 
     def forward(self, x: torch.Tensor, keys: bool = False):
         """y [T, H] and L_aux [1]; every intermediate stays in self.buf."""
+        if self.shared:
+            self.shared_expert(x)
         self.route(x, keys=keys)
         self.aux()
         self.dispatch(x)

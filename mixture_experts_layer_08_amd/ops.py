@@ -182,16 +182,21 @@ def moe_expert_ffn_gather(x: torch.Tensor, slot_token: torch.Tensor, kept: torch
 
 
 def moe_combine(y_disp: torch.Tensor, slot: torch.Tensor, topk_w: torch.Tensor, *,
-                y: Optional[torch.Tensor] = None,
+                y: Optional[torch.Tensor] = None, y_shared: Optional[torch.Tensor] = None,
                 out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """y_shared: optional fp32 [T, H] (the shared experts' output) added to
+    every token's weighted sum."""
     H = y_disp.shape[-1]
     T, k = slot.shape
     dev = slot.device
     if y_disp.dtype != torch.float32:
         raise ValueError("y_disp must be fp32")
+    if y_shared is not None and (y_shared.dtype != torch.float32 or y_shared.numel() != T * H
+                                 or not y_shared.is_contiguous()):
+        raise ValueError("y_shared must be a contiguous fp32 [T, H] tensor")
     y = _want(y, (T, H), out_dtype if y is None else y.dtype, dev)
     st = lib().moe_combine(_stream(dev), _dtype_code(y), _ptr(y_disp), _ptr(slot),
-                           _ptr(topk_w), T, H, k, _ptr(y))
+                           _ptr(topk_w), T, H, k, _ptr(y_shared), _ptr(y))
     check("moe_combine", st)
     return y
 
@@ -244,12 +249,19 @@ def moe_expert_ffn_bwd(x_disp: torch.Tensor, kept: torch.Tensor, w1: torch.Tenso
 
 
 def moe_dispatch_bwd(dx_disp: torch.Tensor, slot: torch.Tensor, *,
+                     dx_add: Optional[torch.Tensor] = None,
                      dx: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dx [T, H] fp32 = dx_add (optional fp32 [T, H]) + the sum of each
+    token's kept copies of dx_disp."""
     H = dx_disp.shape[-1]
     T, k = slot.shape
     dev = slot.device
+    if dx_add is not None and (dx_add.dtype != torch.float32 or dx_add.numel() != T * H
+                               or not dx_add.is_contiguous()):
+        raise ValueError("dx_add must be a contiguous fp32 [T, H] tensor")
     dx = _want(dx, (T, H), torch.float32, dev)
-    st = lib().moe_dispatch_bwd(_stream(dev), _ptr(dx_disp), _ptr(slot), T, H, k, _ptr(dx))
+    st = lib().moe_dispatch_bwd(_stream(dev), _ptr(dx_disp), _ptr(slot), T, H, k, _ptr(dx_add),
+                                _ptr(dx))
     check("moe_dispatch_bwd", st)
     return dx
 

@@ -55,6 +55,7 @@ class MoEConfig:
     batch: int = 1
     seq: int = 0        # sequence length (sets the Gumbel temperature)
     seed: int = 0
+    shared_I: int = 0   # intermediate size of the shared expert (0 = none)
 
     @property
     def seq_len(self) -> int:
@@ -119,7 +120,11 @@ def make_inputs(cfg: MoEConfig, seed: Optional[int] = None) -> Dict[str, np.ndar
     Returns a dict with x [T,H], w_r [H,E], b_r [E] (float32, or None),
     and per-expert stacks: SwiGLU -> w_gate [E,H,I], w_up [E,H,I],
     w_down [E,I,H]; GELU -> w1 [E,H,I], w2 [E,I,H], b1 [E,I], b2 [E,H].
-    bf16 arrays are uint16 bit patterns; f32 arrays are float32.
+    With cfg.shared_I > 0, the shared expert's weights follow under the same
+    names prefixed "shared_", as one-expert stacks of intermediate size
+    shared_I (drawn after everything else, so the routed inputs do not
+    depend on it).  bf16 arrays are uint16 bit patterns; f32 arrays are
+    float32.
     """
     seed = cfg.seed if seed is None else seed
     g = np.random.Generator(np.random.PCG64(seed))
@@ -161,6 +166,20 @@ def make_inputs(cfg: MoEConfig, seed: Optional[int] = None) -> Dict[str, np.ndar
         out.update(w1=w1, w2=w2, b1=b1, b2=b2)
     else:
         raise ValueError(f"unknown activation {cfg.act!r}")
+    Is = cfg.shared_I
+    if Is:
+        edt = np.uint16 if dt == "bf16" else np.float32
+        if cfg.act == ACT_SWIGLU:
+            for name, shp in (("w_gate", (H, Is)), ("w_up", (H, Is)), ("w_down", (Is, H))):
+                a = np.empty((1,) + shp, edt)
+                a[0] = _store(g.standard_normal(shp, dtype=np.float32) * sw, dt)
+                out["shared_" + name] = a
+        else:
+            for name, shp, sd in (("w1", (H, Is), sw), ("w2", (Is, H), sw), ("b1", (Is,), sb),
+                                  ("b2", (H,), sb)):
+                a = np.empty((1,) + shp, edt)
+                a[0] = _store(g.standard_normal(shp, dtype=np.float32) * sd, dt)
+                out["shared_" + name] = a
     return out
 
 

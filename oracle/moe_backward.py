@@ -16,6 +16,8 @@ reversed:
             GELU   h = gelu_erf(X W1 + b1),       Y = h W2 + b2
               -> weight gradients X^T (.), h^T dY; input gradient dX
   dispatch  X rows are copies of x rows -> dx_t += sum of its kept copies' dX
+  shared    y_t += S(x_t), the shared expert with weight 1 ([P1] section 5.2)
+              -> the expert backward with X = x and dY = dy; dx += its dX
   router    w_j = p_sel_j / sum(p_sel)  ([P5] section 3.1)
               -> dp_sel_j = (dw_j - sum_i dw_i w_i) / sum(p_sel)
             L_aux = alpha E sum_e f_e P_e, P_e = mean_t p_te, f held constant
@@ -75,6 +77,7 @@ class Grads:
     dx_disp: np.ndarray             # [E, C, H]
     dx_experts: np.ndarray          # [T, H] the experts' part of dx
     dx_router: np.ndarray           # [T, H] the router's part of dx
+    dx_shared: Optional[np.ndarray] = None  # [T, H] the shared expert's part of dx
 
 
 def backward(inputs: Dict[str, np.ndarray], cfg, dy: np.ndarray,
@@ -176,8 +179,35 @@ def backward(inputs: Dict[str, np.ndarray], cfg, dy: np.ndarray,
     dx_router = dlogits @ w_r.T
     dw_r = x.T @ dlogits
     db_r = dlogits.sum(axis=0) if inputs.get("b_r") is not None else None
-    return Grads(dx_experts + dx_router, dw_r, db_r, dweights, dw_topk, dprobs, dlogits,
-                 dy_disp, dx_disp, dx_experts, dx_router)
+
+    # shared expert: every token with weight 1, so its output gradient is dy
+    dx_shared = None
+    if cfg.act == "swiglu" and inputs.get("shared_w_gate") is not None:
+        w1, w3, w2 = (M.widen(inputs["shared_" + kk][0]) for kk in ("w_gate", "w_up", "w_down"))
+        g, u = x @ w1, x @ w3
+        h = M.silu(g) * u
+        dh = dy @ w2.T
+        dg = dh * u * silu_grad(g)
+        du = dh * M.silu(g)
+        dweights["shared_w_down"] = (h.T @ dy)[None]
+        dweights["shared_w_gate"] = (x.T @ dg)[None]
+        dweights["shared_w_up"] = (x.T @ du)[None]
+        dx_shared = dg @ w1.T + du @ w3.T
+    elif cfg.act == "gelu" and inputs.get("shared_w1") is not None:
+        w1, b1, w2 = (M.widen(inputs["shared_" + kk][0]) for kk in ("w1", "b1", "w2"))
+        z = x @ w1 + b1[None, :]
+        h = M.gelu_erf(z)
+        dweights["shared_w2"] = (h.T @ dy)[None]
+        dweights["shared_b2"] = dy.sum(axis=0)[None]
+        dz = (dy @ w2.T) * gelu_erf_grad(z)
+        dweights["shared_w1"] = (x.T @ dz)[None]
+        dweights["shared_b1"] = dz.sum(axis=0)[None]
+        dx_shared = dz @ w1.T
+    dx = dx_experts + dx_router
+    if dx_shared is not None:
+        dx = dx + dx_shared
+    return Grads(dx, dw_r, db_r, dweights, dw_topk, dprobs, dlogits,
+                 dy_disp, dx_disp, dx_experts, dx_router, dx_shared)
 
 
 def objective(inputs: Dict[str, np.ndarray], cfg, dy: np.ndarray, dl_aux: float) -> float:

@@ -31,6 +31,11 @@ the design notes):
     q = softmax(s / tau) gives both the combine weights (renormalised over
     the selected experts) and p_i; tau = 1 + 1e-4 * seq_len ([P4] sections
     2 and 5.2).
+  * shared expert ([P1] section 5.2 names experts that every token passes
+    through, without their form): one always-on FFN of the routed experts'
+    form (its own intermediate size), added to every token's output with
+    weight 1, outside routing, capacity and L_aux.  Several shared experts
+    of one form are the same as one whose intermediate size is their sum.
 
 Parity status: every function here is pinned by a CPU test against what the
 pages or the mathematics fix (worked example, closed forms, brute force,
@@ -250,6 +255,21 @@ def expert_forward(inputs: Dict[str, np.ndarray], act: str, e: int,
     raise ValueError(act)
 
 
+def shared_expert(inputs: Dict[str, np.ndarray], act: str, xr: np.ndarray):
+    """The shared expert on float64 rows ([P1] section 5.2: fixed experts
+    that join every token's computation); returns (h, y), or None when the
+    layer has none.  Same form as a routed expert."""
+    if act == "swiglu":
+        if inputs.get("shared_w_gate") is None:
+            return None
+        return expert_swiglu(xr, widen(inputs["shared_w_gate"][0]),
+                             widen(inputs["shared_w_up"][0]), widen(inputs["shared_w_down"][0]))
+    if inputs.get("shared_w1") is None:
+        return None
+    return expert_gelu(xr, widen(inputs["shared_w1"][0]), widen(inputs["shared_b1"][0]),
+                       widen(inputs["shared_w2"][0]), widen(inputs["shared_b2"][0]))
+
+
 # -------------------------------------------------------------- combine ----
 
 def combine(y_disp: np.ndarray, slot: np.ndarray, w: np.ndarray,
@@ -280,6 +300,7 @@ class OracleResult:
     y: np.ndarray                   # [T, H] or [n_sample, H]
     sample: Optional[np.ndarray]    # token ids of y rows when sampled
     timings: Dict[str, float]
+    y_shared: Optional[np.ndarray] = None   # the shared expert's rows of y (None: no shared expert)
 
 
 def route(inputs: Dict[str, np.ndarray], cfg) -> RouteResult:
@@ -328,7 +349,11 @@ def forward(inputs: Dict[str, np.ndarray], cfg,
         t0 = time.perf_counter()
         y = combine(y_disp, d.slot, r.w, H)
         tm["combine"] = time.perf_counter() - t0
-        return OracleResult(r, a, d, y_disp, h_all, y, None, tm)
+        sh = shared_expert(inputs, cfg.act, widen(x))
+        if sh is not None:
+            y = y + sh[1]
+        return OracleResult(r, a, d, y_disp, h_all, y, None, tm,
+                            None if sh is None else sh[1])
     sample = np.asarray(sample, dtype=np.int64)
     y = np.zeros((sample.size, H), dtype=np.float64)
     for e in range(cfg.E):
@@ -340,8 +365,11 @@ def forward(inputs: Dict[str, np.ndarray], cfg,
         _, ye = expert_forward(inputs, cfg.act, e, rows)
         for n, (i, j) in enumerate(hit):
             y[i] += r.w[sample[i], j] * ye[n]
+    sh = shared_expert(inputs, cfg.act, widen(x[sample]))
+    if sh is not None:
+        y = y + sh[1]
     tm["experts+combine"] = time.perf_counter() - t0
-    return OracleResult(r, a, d, None, None, y, sample, tm)
+    return OracleResult(r, a, d, None, None, y, sample, tm, None if sh is None else sh[1])
 
 
 def near_tie_tokens(keys: np.ndarray, k: int, gap: float = 1e-4) -> np.ndarray:

@@ -179,7 +179,8 @@ def test_expert_ffn_workspace_size(L):
 def test_combine_argument_errors(L):
     def c(**kw):
         return L.moe_combine(None, kw.get("dtype", 1), kw.get("yd", P), kw.get("slot", P), P,
-                             kw.get("T", 64), kw.get("H", 256), kw.get("k", 2), kw.get("y", P))
+                             kw.get("T", 64), kw.get("H", 256), kw.get("k", 2),
+                             kw.get("ys", None), kw.get("y", P))
     assert c(dtype=9) == DTYPE
     assert c(T=-1) == SHAPE
     assert c(k=0) == SHAPE
@@ -187,6 +188,7 @@ def test_combine_argument_errors(L):
     assert c(H=4) == ALIGN
     assert c(slot=None) == NULL
     assert c(y=MIS) == ALIGN
+    assert c(ys=MIS) == ALIGN
     assert c(T=0, slot=None, y=None) == OK
 
 

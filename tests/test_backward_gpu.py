@@ -40,6 +40,10 @@ CASES = {
                             route="gumbel", seq=500, seed=33),
     "swiglu-e5-k3-bias": MoEConfig("b-k3", "bf16", T=333, H=256, I=256, E=5, k=3, cf=1.0,
                                    router_bias0=1.0, seed=34),
+    "swiglu-e8-shared": MoEConfig("b-sh", "bf16", T=600, H=256, I=256, E=8, k=2, cf=1.0,
+                                  shared_I=512, seed=35),
+    "gelu-e4-shared": MoEConfig("b-sh-ge", "bf16", T=400, H=256, I=256, E=4, k=2, cf=1.25,
+                                act="gelu", shared_I=256, seed=36),
 }
 
 
@@ -102,9 +106,9 @@ def test_backward_matches_oracle(name):
     if ref.db_r is not None:
         _close(to_np(gg["db_r"]), ref.db_r, 1e-2, f"{name}: db_r")
     worst = 0.0
-    for key, want in ref.dweights.items():
+    for key, want in ref.dweights.items():   # routed experts and the shared one
         got = to_np(gg[key])
-        for e in range(cfg.E):
+        for e in range(want.shape[0]):
             if np.any(want[e] != 0):
                 worst = max(worst, _close(got[e], want[e], 1e-2, f"{name}: d{key}[{e}]"))
             else:

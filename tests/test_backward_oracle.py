@@ -23,7 +23,7 @@ from oracle import moe_oracle as M
 from mixture_experts_layer_08_amd.synth import MoEConfig
 
 
-def _inputs(cfg, seed, bias=False, b2=True):
+def _inputs(cfg, seed, bias=False, b2=True, shared=0):
     g = np.random.default_rng(seed)
     T, H, I, E = cfg.T, cfg.H, cfg.I, cfg.E
     inp = {"x": g.standard_normal((T, H)), "w_r": g.standard_normal((H, E)) * 0.7,
@@ -37,6 +37,16 @@ def _inputs(cfg, seed, bias=False, b2=True):
         inp["b1"] = g.standard_normal((E, I)) * 0.3
         inp["w2"] = g.standard_normal((E, I, H)) * 0.5
         inp["b2"] = g.standard_normal((E, H)) * 0.3 if b2 else None
+    if shared:  # the shared expert, intermediate size `shared`
+        if cfg.act == "swiglu":
+            inp["shared_w_gate"] = g.standard_normal((1, H, shared)) * 0.5
+            inp["shared_w_up"] = g.standard_normal((1, H, shared)) * 0.5
+            inp["shared_w_down"] = g.standard_normal((1, shared, H)) * 0.5
+        else:
+            inp["shared_w1"] = g.standard_normal((1, H, shared)) * 0.5
+            inp["shared_b1"] = g.standard_normal((1, shared)) * 0.3
+            inp["shared_w2"] = g.standard_normal((1, shared, H)) * 0.5
+            inp["shared_b2"] = g.standard_normal((1, H)) * 0.3
     return inp
 
 
@@ -50,6 +60,10 @@ CASES = {
     "swiglu-gumbel": (MoEConfig("fd4", "f32", T=8, H=4, I=5, E=5, k=2, cf=1.0, route="gumbel",
                                 seq=300, seed=4), dict(bias=True)),
     "swiglu-k3": (MoEConfig("fd5", "f32", T=6, H=3, I=4, E=4, k=3, cf=1.0, seed=5), dict()),
+    "swiglu-shared-drops": (MoEConfig("fd6", "f32", T=9, H=5, I=6, E=4, k=2, cf=0.75, seed=6),
+                            dict(bias=True, shared=7)),
+    "gelu-shared": (MoEConfig("fd7", "f32", T=7, H=4, I=5, E=3, k=2, cf=1.0, act="gelu", seed=7),
+                    dict(shared=6)),
 }
 
 
@@ -101,7 +115,7 @@ def test_backward_matches_finite_differences(name):
     cfg, kw = CASES[name]
     inp = _inputs(cfg, cfg.seed, **kw)
     worst, dropped = _fd_check(cfg, inp, cfg.seed)
-    if name.endswith("drops-bias"):
+    if "drops" in name:
         assert dropped > 0          # the case does exercise the capacity drop
 
 
@@ -165,13 +179,22 @@ def _without_renormalisation(orig):
 
 
 @pytest.mark.parametrize("mutant", ["silu_grad", "gelu_erf_grad", "softmax_backward", "no_renorm",
-                                    "no_aux"])
+                                    "no_aux", "no_shared_dx"])
 def test_planted_backward_slips_are_caught(mutant, monkeypatch):
-    case = "gelu-softmax-b2" if mutant == "gelu_erf_grad" else "swiglu-softmax-drops-bias"
+    case = {"gelu_erf_grad": "gelu-softmax-b2",
+            "no_shared_dx": "swiglu-shared-drops"}.get(mutant, "swiglu-softmax-drops-bias")
     cfg, kw = CASES[case]
     inp = _inputs(cfg, cfg.seed, **kw)
     if mutant in _MUTANTS:
         monkeypatch.setattr(B, mutant, _MUTANTS[mutant])
+    elif mutant == "no_shared_dx":  # forgets the shared expert's part of dx
+        orig = B.backward
+
+        def slip(i, c, dy, dl_aux=1.0):
+            gr = orig(i, c, dy, dl_aux)
+            gr.dx = gr.dx - gr.dx_shared
+            return gr
+        monkeypatch.setattr(B, "backward", slip)
     elif mutant == "no_renorm":
         monkeypatch.setattr(B, "backward", _without_renormalisation(B.backward))
     else:  # no_aux: forgets the aux-loss path

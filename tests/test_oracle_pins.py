@@ -382,6 +382,47 @@ def test_bf16_rounding_is_nearest_even():
     np.testing.assert_array_equal(tb, f32_to_bf16_bits(r))
 
 
+# ----------------------------------------------------------------- P12 ----
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_p12_shared_expert(act):
+    """The LLaMA4-MoE guide's shared experts (section 5.2: fixed experts every
+    token passes through).  The layer with a shared expert equals the layer
+    without it plus the one-expert, top-1 layer whose expert carries the
+    shared weights (a path pinned against torch in test_p4), with dropped
+    tokens included; and the shared part alone equals torch's dense FFN."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(12)
+    T, H, I, E, k, Is = 29, 16, 12, 4, 2, 20
+    d = _tiny_inputs(rng, T, H, I, E, act=act)
+    sh = _tiny_inputs(rng, T, H, Is, 1, act=act)
+    for n in (("w_gate", "w_up", "w_down") if act == "swiglu" else ("w1", "b1", "w2", "b2")):
+        d["shared_" + n] = sh[n]
+    cfg = _cfg(T, H, I, E, k, 0.75, act=act)          # cf < 1: some copies are dropped
+    with_sh = M.forward(d, cfg)
+    assert with_sh.disp.dropped > 0
+    routed = M.forward({n: v for n, v in d.items() if not n.startswith("shared_")}, cfg)
+    one = dict(sh, x=d["x"])
+    dense = M.forward(one, _cfg(T, H, Is, 1, 1, 1.0, act=act))
+    np.testing.assert_allclose(with_sh.y, routed.y + dense.y, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(with_sh.y_shared, dense.y, rtol=1e-12, atol=1e-12)
+    X = torch.from_numpy(d["x"])
+    F = torch.nn.functional
+    if act == "swiglu":
+        ref = (F.silu(X @ torch.from_numpy(sh["w_gate"][0])) *
+               (X @ torch.from_numpy(sh["w_up"][0]))) @ torch.from_numpy(sh["w_down"][0])
+    else:
+        ref = F.linear(F.gelu(F.linear(X, torch.from_numpy(sh["w1"][0]).T,
+                                       torch.from_numpy(sh["b1"][0]))),
+                       torch.from_numpy(sh["w2"][0]).T, torch.from_numpy(sh["b2"][0]))
+    np.testing.assert_allclose(with_sh.y - routed.y, ref.numpy(), rtol=1e-11, atol=1e-11)
+    # routing, statistics and dispatch do not see the shared expert
+    np.testing.assert_array_equal(with_sh.disp.slot, routed.disp.slot)
+    assert with_sh.aux.l_aux == routed.aux.l_aux
+    # sampled rows agree with the full forward
+    part = M.forward(d, cfg, sample=np.array([0, 3, 28]))
+    np.testing.assert_allclose(part.y, with_sh.y[[0, 3, 28]], rtol=1e-13, atol=1e-13)
+
+
 def test_near_tie_detection():
     keys = np.array([[1.0, 0.99995, 0.5], [1.0, 0.5, 0.49]])
     assert O.near_tie_tokens(keys, 1).tolist() == [True, False]
@@ -439,22 +480,29 @@ def _mutants():
     def renorm_missing(p, idx):
         return np.take_along_axis(p, idx, axis=1)
 
+    shared_ok = M.shared_expert
+
+    def shared_half(inputs, act, xr):  # shared output mixed in with weight 1/2
+        r = shared_ok(inputs, act, xr)
+        return None if r is None else (r[0], 0.5 * r[1])
+
     return {"topk_lowest_index": topk_high_index, "aux_stats": aux_wrong_norm,
             "capacity": cap_no_k, "expert_swiglu": swiglu_swapped,
             "expert_gelu": gelu_no_b2, "combine": combine_renorm,
-            "renormalise": renorm_missing}
+            "renormalise": renorm_missing, "shared_expert": shared_half}
 
 
 PIN_TESTS = [test_p1_weights_sum_to_one, test_p2_worked_example_f1, test_p3_capacity_values,
              test_p4_single_expert_is_dense_ffn, test_p6_brute_force_tiny,
-             test_p7_zero_router_closed_forms, test_p10_all_dropped_token_is_zero_and_p11_idle_expert]
+             test_p7_zero_router_closed_forms, test_p10_all_dropped_token_is_zero_and_p11_idle_expert,
+             test_p12_shared_expert]
 
 
 def _run_pins():
     for fn in PIN_TESTS:
         if fn is test_p1_weights_sum_to_one:
             fn("softmax")
-        elif fn is test_p4_single_expert_is_dense_ffn:
+        elif fn in (test_p4_single_expert_is_dense_ffn, test_p12_shared_expert):
             fn("swiglu")
             fn("gelu")
         elif fn is test_p6_brute_force_tiny:

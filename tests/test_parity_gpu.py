@@ -40,6 +40,11 @@ SMALL = {
     "f32-config1": CONFIGS[1],
     "f32-gelu-e3": MoEConfig("s-f32-gelu", "f32", T=130, H=64, I=96, E=3, k=2, cf=1.0,
                              act="gelu", seed=16),
+    # with a shared expert (every token, weight 1), drops on the routed side
+    "bf16-swiglu-e8-shared": MoEConfig("s-sh", "bf16", T=1001, H=256, I=256, E=8, k=2, cf=1.0,
+                                       shared_I=512, seed=18),
+    "bf16-gelu-e4-shared": MoEConfig("s-sh-gelu", "bf16", T=600, H=256, I=512, E=4, k=2,
+                                     cf=1.25, act="gelu", shared_I=256, seed=19),
 }
 
 
@@ -135,9 +140,10 @@ def test_layer_end_to_end_small(name, fused):
     worst = _check_y(cfg, to_np(y)[ok], ref.y[ok], f"{name}: y")
     log(f"[e2e] {name}: dropped {int(to_np(b.dropped)[0])}, compared {int(ok.sum())}/{cfg.T} "
         f"rows, worst err/rms {worst:.3e}")
-    # tokens with every copy dropped are exactly zero
+    # tokens with every copy dropped are exactly zero (without a shared expert)
     all_drop = np.all(ref.disp.slot < 0, axis=1) & ok
-    assert np.all(to_np(y)[all_drop] == 0.0)
+    if not cfg.shared_I:
+        assert np.all(to_np(y)[all_drop] == 0.0)
 
 
 # ------------------------------------------------------------ stage-wise ----
@@ -203,6 +209,22 @@ def test_stages_on_oracle_inputs(name):
                       1e-6 * np.sqrt(np.mean(want * want, axis=1, keepdims=True)))
     else:
         assert np.max(np.abs(got - want)) <= 1e-5
+    if cfg.shared_I:
+        # the shared expert over every token (one expert, C = T, rows = x)
+        layer.shared_expert(x)
+        torch.cuda.synchronize()
+        _check_y(cfg, to_np(layer.buf.sh_y)[0], ref.y_shared, f"{name}: shared expert")
+        # combine adding the (fp32-stored) shared rows
+        ysh = ref.y_shared.astype(np.float32)
+        y2 = ops.moe_combine(to_dev(ydisp_store, torch.float32),
+                             to_dev(ref.disp.slot.astype(np.int32), torch.int32),
+                             to_dev(w32.astype(np.float32), torch.float32),
+                             y_shared=to_dev(ysh, torch.float32), out_dtype=tdt)
+        torch.cuda.synchronize()
+        want2 = want + ysh.astype(np.float64)
+        got2 = to_np(y2)
+        assert np.all(np.abs(got2 - want2) <= 2.0 ** -8 * np.abs(want2) + 1e-30 +
+                      1e-6 * np.sqrt(np.mean(want2 * want2, axis=1, keepdims=True)))
 
 
 # ---------------------------------------------------------- edge cases ----
@@ -338,6 +360,30 @@ def test_deterministic_bitwise():
 
 
 # ---------------------------------------------------- full-size configs ----
+def test_full_config2_with_shared_expert():
+    """The 4096-token layer plus a shared expert of intermediate size 4096
+    (run on its own stream, overlapping the routed path)."""
+    cfg = CONFIGS[2].with_(shared_I=4096)
+    log("[full] config 2 + shared expert (I_s 4096)")
+    inp = make_inputs(cfg)
+    layer = MoELayerGPU(cfg, inp, DEV)
+    x = x_to_device(inp, cfg, DEV)
+    y, _ = layer.forward(x)
+    torch.cuda.synchronize()
+    b = layer.buf
+    r = M.route(inp, cfg)
+    same = np.all(to_np(b.topk_idx) == r.idx, axis=1)
+    d_ref = M.dispatch(r.idx, cfg.E, layer.C)
+    ok = same & np.all(to_np(b.slot) == d_ref.slot, axis=1)
+    rng = np.random.default_rng(22)
+    sample = np.sort(rng.choice(np.where(ok)[0], size=64, replace=False))
+    ref = M.forward(inp, cfg, sample=sample)
+    _check_y(cfg, to_np(b.sh_y)[0][sample], ref.y_shared, "config 2: shared expert (sampled)")
+    worst = _check_y(cfg, to_np(y)[sample], ref.y, "config 2 + shared: y (sampled)")
+    log(f"[full] config 2 + shared: worst err/rms {worst:.3e}")
+
+
+
 @pytest.mark.parametrize("cid", [2, 3, 4, 5])
 def test_full_config(cid):
     cfg = CONFIGS[cid]
