@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward pass (combine, expert FFN, dispatch and router "
                          "backward) after a forward that keeps the dispatched rows")
+    ap.add_argument("--weights", choices=["bf16", "fp8"], default="bf16",
+                    help="expert weight storage: bf16, or 8-bit e4m3 codes with per-expert, "
+                         "per-column scales (quantised on the device before timing)")
     ap.add_argument("--shared", type=int, default=0, metavar="I_S",
                     help="also time the layer with a shared expert of intermediate size I_S "
                          "(every token, weight 1)")
@@ -61,10 +64,11 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_work(cfg, kept: np.ndarray, dropped: int):
+def algorithmic_work(cfg, kept: np.ndarray, dropped: int, weights: str = "bf16"):
     """Bytes and FLOP each phase must move / compute at minimum."""
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
     esz = 2 if cfg.dtype == "bf16" else 4
+    wsz = 1 if weights == "fp8" else esz
     n_kept = int(kept.sum())
     mult = 6 if cfg.act == "swiglu" else 4
     ffn_flop = mult * H * I * n_kept
@@ -72,8 +76,10 @@ def algorithmic_work(cfg, kept: np.ndarray, dropped: int):
     # the gathered x rows, h written and read back, fp32 y_disp written
     n_mats = 3 if cfg.act == "swiglu" else 2
     active = int((kept > 0).sum())
-    ffn_bytes = (active * n_mats * H * I * esz + n_kept * H * esz + 2 * n_kept * I * esz
+    ffn_bytes = (active * n_mats * H * I * wsz + n_kept * H * esz + 2 * n_kept * I * esz
                  + n_kept * H * 4)
+    if weights == "fp8":  # the per-column fp32 scales
+        ffn_bytes += active * ((n_mats - 1) * I + H) * 4
     route_bytes = T * H * esz + H * E * esz + T * k * 8 + T * E * 4
     aux_bytes = T * k * 4 + T * E * 4
     # fused-gather layer: dispatch only maps rows (idx read, slot + slot_token
@@ -265,7 +271,7 @@ def main():
     print(f"[bench] generating inputs for {cfg.name}", file=sys.stderr, flush=True)
     inputs = make_inputs(cfg)
     dev = "cuda:0"
-    layer = MoELayerGPU(cfg, inputs, dev)
+    layer = MoELayerGPU(cfg, inputs, dev, weights=args.weights)
     x = x_to_device(inputs, cfg, dev)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
@@ -303,7 +309,7 @@ def main():
 
     kept = layer.buf.kept.cpu().numpy()
     dropped = int(layer.buf.dropped.cpu()[0])
-    work = algorithmic_work(cfg, kept, dropped)
+    work = algorithmic_work(cfg, kept, dropped, args.weights)
 
     # memory-bound phases in isolation, after flushing the Infinity Cache
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -354,7 +360,8 @@ def main():
     # the matrix cores for many rows per expert, HBM (the weights) for few
     t_mfma = work["ffn_flop"] / (PEAK_BF16_TFLOPS * 1e12)
     t_hbm = work["ffn_bytes"] / (PEAK_HBM_GBS * 1e9)
-    kernel = ("grouped expert GEMM (moe_expert_ffn_gather: " +
+    kernel = ("grouped expert GEMM (moe_expert_ffn_gather" +
+              ("_fp8, e4m3 weights" if args.weights == "fp8" else "") + ": " +
               ("gate/up product with SwiGLU epilogue" if cfg.act == "swiglu" else
                "first product with bias + GELU epilogue") +
               ", then down product, with their tail reductions)")
@@ -367,7 +374,7 @@ def main():
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
                     "flop_per_launch": work["ffn_flop"]}
-    roofline.update({"traffic": measured_traffic(cfg),
+    roofline.update({"traffic": measured_traffic(cfg) if args.weights == "bf16" else None,
                      "traffic_unit": "HBM bytes per expert phase (rocprofv3 FETCH_SIZE x2.0 + "
                                      "WRITE_SIZE x1.0, copy-calibrated)",
                      "avg_ms": round(gemm_ms, 5)})
@@ -387,7 +394,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: one MoE FFN layer forward, T={cfg.T} "
                                f"({cfg.batch}x{cfg.seq_len}), H={cfg.H}, I={cfg.I}, E={cfg.E}, "
-                               f"top-{cfg.k}, cf={cfg.cf}, {cfg.act}, {cfg.route} router",
+                               f"top-{cfg.k}, cf={cfg.cf}, {cfg.act}, {cfg.route} router" +
+                               (", e4m3 expert weights with per-column scales"
+                                if args.weights == "fp8" else ""),
+                   "expert_weights": args.weights,
                    "tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I, "experts": cfg.E,
                    "top_k": cfg.k, "capacity_factor": cfg.cf,
                    "capacity": layer.C, "kept_rows": work["n_kept"], "dropped": dropped,

@@ -214,6 +214,55 @@ moe_status_t moe_expert_ffn_gather(void* stream, moe_dtype_t dtype, moe_act_t ac
                                    const void* b2, void* h_ws, void* y_disp,
                                    void* ws, size_t ws_bytes);
 
+/* ------------------------------------------------------ 8-bit weights ----
+ * [P4] section 3 keeps the expert weights in 8 bits and restores them with
+ * a scale computed per expert and per dimension; [P1] section 5.2 and [P5]
+ * section 5.1 name low-bit expert weights for inference.  Here the 8-bit
+ * code is the OCP float8 e4m3 format (gfx950 turns two codes into two bf16
+ * values in one instruction, and every e4m3 value is exactly a bf16 value),
+ * with one fp32 scale per expert and output column.
+ *
+ * Quantisation of W [E, K, N] (bf16, finite):
+ *   scale [E, N] fp32 out  max_k |W[e, k, n]| / 448 (correctly rounded;
+ *                          1 for an all-zero column)
+ *   q     [E, N, K] u8 out the e4m3 code nearest to W[e, k, n] / scale[e, n]
+ *                          (fp32 quotient, ties to the even code), stored
+ *                          transposed: each column's K codes contiguous
+ * K must be a multiple of 16 (q 16-byte aligned); K < 2^22. */
+moe_status_t moe_quantize_fp8(void* stream, const void* w, int E, int64_t K,
+                              int64_t N, uint8_t* q, float* scale);
+
+/* Dequantisation: w [E, K, N] fp32 out = decode(q[e, n, k]) * scale[e, n],
+ * rounded once to fp32 (NaN codes give NaN).  Same layouts and limits as
+ * moe_quantize_fp8. */
+moe_status_t moe_dequantize_fp8(void* stream, const uint8_t* q, const float* scale,
+                                int E, int64_t K, int64_t N, float* w);
+
+/* Expert FFNs on 8-bit weights: moe_expert_ffn (resp. _gather) with
+ *   w1q [E, I, H], w3q [E, I, H] (SwiGLU), w2q [E, H, I]  e4m3 codes as
+ *       moe_quantize_fp8 writes them (of W1, W3 [E, H, I], W2 [E, I, H])
+ *   s1 [E, I], s3 [E, I], s2 [E, H]                        their scales
+ * in place of w1, w3, w2; activations, biases, h_ws and y_disp are bf16 /
+ * bf16 / bf16 / fp32 as for moe_expert_ffn.  The products run on the codes'
+ * exact values in bf16 and each output column is multiplied by its scale
+ * on the fp32 accumulator, so the result is the layer with the dequantised
+ * weights.  Limits as for moe_expert_ffn; in addition H * I < 2^31. */
+moe_status_t moe_expert_ffn_fp8(void* stream, moe_act_t act, const void* x_disp,
+                                const int32_t* kept, int E, int64_t C, int64_t H,
+                                int64_t I, const uint8_t* w1q, const uint8_t* w3q,
+                                const uint8_t* w2q, const float* s1, const float* s3,
+                                const float* s2, const void* b1, const void* b2,
+                                void* h_ws, void* y_disp, void* ws, size_t ws_bytes);
+moe_status_t moe_expert_ffn_gather_fp8(void* stream, moe_act_t act, const void* x,
+                                       const int32_t* slot_token, int64_t T,
+                                       const int32_t* kept, int E, int64_t C,
+                                       int64_t H, int64_t I, const uint8_t* w1q,
+                                       const uint8_t* w3q, const uint8_t* w2q,
+                                       const float* s1, const float* s3,
+                                       const float* s2, const void* b1,
+                                       const void* b2, void* h_ws, void* y_disp,
+                                       void* ws, size_t ws_bytes);
+
 /* Bytes of the optional moe_expert_ffn workspace on the current device:
  * 4 KiB of counters plus one 256 KiB fp32 tile per compute unit. */
 size_t moe_expert_ffn_ws_bytes(void);

@@ -27,7 +27,8 @@ EXPORTS = ("moe_capacity", "moe_status_string", "moe_workspace_bytes", "moe_rout
            "moe_aux_stats", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_gather",
            "moe_expert_ffn_ws_bytes", "moe_combine", "moe_combine_bwd", "moe_expert_ffn_bwd",
            "moe_expert_ffn_bwd_ws_bytes", "moe_dispatch_bwd", "moe_route_bwd",
-           "moe_route_bwd_ws_bytes")
+           "moe_route_bwd_ws_bytes", "moe_quantize_fp8", "moe_dequantize_fp8",
+           "moe_expert_ffn_fp8", "moe_expert_ffn_gather_fp8")
 
 _lock = threading.Lock()
 _lib = None
@@ -82,6 +83,16 @@ def _declare(L: ctypes.CDLL) -> None:
     L.moe_route_bwd.restype = i32
     L.moe_route_bwd_ws_bytes.argtypes = [i64, i64, i32]
     L.moe_route_bwd_ws_bytes.restype = c.c_size_t
+    L.moe_quantize_fp8.argtypes = [vp, vp, i32, i64, i64, vp, vp]
+    L.moe_quantize_fp8.restype = i32
+    L.moe_dequantize_fp8.argtypes = [vp, vp, vp, i32, i64, i64, vp]
+    L.moe_dequantize_fp8.restype = i32
+    L.moe_expert_ffn_fp8.argtypes = [vp, i32, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp,
+                                     vp, vp, vp, vp, vp, c.c_size_t]
+    L.moe_expert_ffn_fp8.restype = i32
+    L.moe_expert_ffn_gather_fp8.argtypes = [vp, i32, vp, vp, i64, vp, i32, i64, i64, i64, vp, vp,
+                                            vp, vp, vp, vp, vp, vp, vp, vp, vp, c.c_size_t]
+    L.moe_expert_ffn_gather_fp8.restype = i32
 
 
 def lib() -> ctypes.CDLL:

@@ -41,6 +41,15 @@
 //     column L.  Two such reads make one MFMA B operand, so the weights
 //     need no repacking.  The chunk index of each 256-byte B row is XORed
 //     with 4*(k & 3) so the rows one read serves fall in different banks.
+//   * 8-bit weights (F8): B = e4m3 codes stored [E, N, K], each output
+//     column's K codes contiguous, with one fp32 scale per column.  The B
+//     stage is 256 rows x 64 bytes (16-byte chunk index XOR ((row >> 2) & 3),
+//     so the 16 rows one ds_read_b64 pass serves hit distinct banks); a lane
+//     reads the 8 codes of its column for its k-slice and turns them into
+//     the MFMA's 8 bf16 values with four v_cvt_scalef32_pk_bf16_fp8 (exact:
+//     every e4m3 value is a bf16 value).  The column scale multiplies the
+//     fp32 accumulator in the epilogue (sum_k x_k q_kn s_n = s_n sum_k x_k
+//     q_kn), so the products run on the codes' exact values.
 // Epilogues run on the fp32 accumulators in registers:
 //   SwiGLU:  a tile holds matching gate and up columns, so
 //            h = silu(g) * u needs no extra pass;
@@ -91,6 +100,12 @@ struct GemmArgs {
     int smax;               // at most this many pieces per tile
     uint16_t* save0;        // *_SAVE modes: [E, C, N_out] g (or z)
     uint16_t* save1;        // SwiGLU: [E, C, N_out] u
+    // 8-bit weights: e4m3 codes [E, N, K] (in place of B0 / B1) and the
+    // per-column fp32 scales [E, N]; null scales: bf16 weights
+    const uint8_t* Q0;
+    const uint8_t* Q1;
+    const float* scale0;
+    const float* scale1;
 };
 
 constexpr size_t kPartBytes = (size_t)kBM * kBNMax * 4;  // one fp32 tile
@@ -127,11 +142,11 @@ __device__ __forceinline__ int tail_splits(const GemmArgs& g, int total, int G, 
 }
 
 
-template <int MODE, int BN>
+template <int MODE, int BN, bool F8 = false>
 struct Epi {
     static constexpr int MB = mode_base(MODE);
     static_assert(BN == 256 || (BN == 128 && MB != MODE_SWIGLU), "B tile is 256 or 128 columns");
-    static constexpr int STAGE_B = kBK * BN * 2;            // 32 or 16 KB
+    static constexpr int STAGE_B = kBK * BN * (F8 ? 1 : 2);  // 32 or 16 KB (8 or 16 KB for codes)
     static constexpr int STAGE = kStageA + STAGE_B;
     static constexpr int BN_OUT = (MB == MODE_SWIGLU) ? BN / 2 : BN;
     static constexpr int OUT_BYTES = (MB == MODE_DOWN) ? 4 : 2;
@@ -153,17 +168,20 @@ struct TileCtx {
 
 // GATHER: the A rows are read from the token rows x[slot_token[e, r]]
 // instead of a dispatched copy (rows with token -1 read as zero).
-template <int MODE, int BN, bool GATHER>
+template <int MODE, int BN, bool GATHER, bool F8>
 __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
-    using EP = Epi<MODE, BN>;
+    using EP = Epi<MODE, BN, F8>;
+    static_assert(!F8 || MODE == mode_base(MODE), "8-bit weights: inference products only");
     constexpr int MB = mode_base(MODE);
     constexpr bool SAVE = MODE != MB;
     constexpr int kStage = EP::STAGE;
     constexpr int WM_ROWS = kBM / kWMn;       // rows per wave
     constexpr int WN_COLS = BN / kWN;         // B columns per wave
     constexpr int TM = WM_ROWS / 32, TN = WN_COLS / 32;  // 32 x 32 MFMA tiles per wave
+    constexpr int TH = TN / 2 > 0 ? TN / 2 : 1;           // SwiGLU: gate (or up) tiles per wave
     constexpr int QA = 32 / kNW;              // 1 KB A loads per wave per k-step
-    constexpr int QB = (BN / 128) * 16 / kNW; // 1 KB B loads per wave per k-step
+    // 1 KB B loads per wave per k-step (codes: 16 rows of 64 bytes each)
+    constexpr int QB = F8 ? BN / 16 / kNW : (BN / 128) * 16 / kNW;
     static_assert(QA <= 4 && QA % 2 == 0, "A loads per wave");
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_pref[MOE_MAX_EXPERTS + 1];
@@ -187,8 +205,8 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
     const int remt = total - full * G;
     const int splits = __builtin_amdgcn_readfirstlane(tail_splits(g, total, G, nk));
     // B sub-tiles are 128 columns (16 KB); wave w fills 1 KB blocks w*QB..,
-    // all inside sub-tile (w*QB)/16
-    const int sub = (wave * QB) / 16;
+    // all inside sub-tile (w*QB)/16 (codes: 128 rows = 8 blocks per sub-tile)
+    const int sub = F8 ? (wave * QB) / 8 : (wave * QB) / 16;
 
     auto tile_at = [&](int round) {
         TileCtx c;
@@ -231,6 +249,14 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
             c.rsA = make_rsrc(g.A + ((size_t)c.e * g.C + c.m0) * g.K,
                               (uint32_t)((size_t)(c.kept - c.m0) * g.K * 2));
         }
+        if (F8) {
+            // codes: tile row r is weight column n0 + r (SwiGLU: gate rows
+            // 0..127, up rows 128..255, each from its own tensor)
+            const uint8_t* q = (MB == MODE_SWIGLU && sub == 1) ? g.Q1 : g.Q0;
+            c.rsB = make_rsrc(q + ((size_t)c.e * g.N + c.n0) * g.K,
+                              (uint32_t)(((size_t)g.N - c.n0) * g.K));
+            return c;
+        }
         const uint16_t* bsrc;
         size_t coloff;
         if (MB == MODE_SWIGLU) {
@@ -256,6 +282,11 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
     // empty row gets an offset past the descriptor's range (reads zero)
     const int chA0 = (((lane % 8) ^ (lane / 16)) * 8) * 2;
     const int chA1 = (((lane % 8) ^ (4 + lane / 16)) * 8) * 2;
+    // code load q: tile row R = (wave*QB + q)*16 + lane/4 (its weight row
+    // is R, less 128 for SwiGLU's up half), chunk (lane % 4) ^ ((R >> 2) & 3)
+    // = (lane % 4) ^ (lane / 16)
+    const int rowQ = wave * QB * 16 + lane / 4 - ((MB == MODE_SWIGLU) ? sub * 128 : 0);
+    const int voffQ = rowQ * g.K + (((lane % 4) ^ (lane / 16)) * 16);
     auto issue = [&](const TileCtx& c, int kt, int stage) {
         unsigned char* st = smem + stage * kStage;
 #pragma unroll
@@ -270,9 +301,14 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
             }
         }
 #pragma unroll
-        for (int q = 0; q < QB; ++q)
-            lds_dma16(c.rsB, st + kStageA + (wave * QB + q) * 1024, voffB,
-                      ((((wave * QB + q) % 16) * 4 + kt * kBK) * g.N) * 2);
+        for (int q = 0; q < QB; ++q) {
+            if (F8)
+                lds_dma16(c.rsB, st + kStageA + (wave * QB + q) * 1024, voffQ,
+                          q * 16 * g.K + kt * kBK);
+            else
+                lds_dma16(c.rsB, st + kStageA + (wave * QB + q) * 1024, voffB,
+                          ((((wave * QB + q) % 16) * 4 + kt * kBK) * g.N) * 2);
+        }
     };
 
     // Fragments of one 32-wide half of a k-step: two 16-wide MFMA slices,
@@ -295,10 +331,27 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
             }
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
+                if (F8) {
+                    // tile row (= weight column) of this lane; 8 codes of k16's
+                    // k values (lane / 32)*8 .. +7
+                    const int nr = ((MB == MODE_SWIGLU) ? ((j < TN / 2) ? 0 : 128) +
+                                                             wn * (WN_COLS / 2) + (j % TH) * 32
+                                                       : wn * WN_COLS + j * 32) + lane % 32;
+                    const int phys = k16 ^ ((nr >> 2) & 3);
+                    const uint2 v = *reinterpret_cast<const uint2*>(Bs + nr * 64 + phys * 16 +
+                                                                    (lane / 32) * 8);
+                    uint4 w;
+                    w.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false));
+                    w.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true));
+                    w.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false));
+                    w.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true));
+                    bfr[ss][j] = as_bf16x8(w);
+                    continue;
+                }
                 int sb, col;  // B sub-tile and column inside it
                 if (MB == MODE_SWIGLU) {  // first half of the wave's tiles gate, second up
                     sb = (j < TN / 2) ? 0 : 1;
-                    col = wn * (WN_COLS / 2) + (j % (TN / 2)) * 32;
+                    col = wn * (WN_COLS / 2) + (j % TH) * 32;
                 } else {
                     const int c = wn * WN_COLS + j * 32;
                     sb = c / 128;
@@ -478,6 +531,12 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
                 const int voff = (row_l * g.N + ocol) * B;
                 float bv = 0.f;
                 if (MB != MODE_SWIGLU && biasb) bv = bf2f(biasb[ocol]);
+                // 8-bit weights: the column scales of this lane's column
+                float sc0 = 1.f, sc1 = 1.f;
+                if (F8) {
+                    sc0 = g.scale0[(size_t)cur.e * g.N + cur.n0 + ocol];
+                    if (MB == MODE_SWIGLU) sc1 = g.scale1[(size_t)cur.e * g.N + cur.n0 + ocol];
+                }
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -485,11 +544,12 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
                         const int soff = ((i * 32 + (q / 4) * 8 + (q % 4)) * g.N) * B;
                         float v;
                         if (MB == MODE_SWIGLU)
-                            v = silu_f(acc[i][j][q]) * acc[i][j + TN / 2][q];
+                            v = F8 ? silu_f(acc[i][j][q] * sc0) * (acc[i][j + TN / 2][q] * sc1)
+                                   : silu_f(acc[i][j][q]) * acc[i][j + TN / 2][q];
                         else if (MB == MODE_GELU)
-                            v = gelu_f(acc[i][j][q] + bv);
+                            v = gelu_f((F8 ? acc[i][j][q] * sc0 : acc[i][j][q]) + bv);
                         else
-                            v = acc[i][j][q] + bv;
+                            v = (F8 ? acc[i][j][q] * sc0 : acc[i][j][q]) + bv;
                         if (MB == MODE_DOWN)
                             buffer_store_f32(v, rsO, voff, soff, 0);
                         else
@@ -572,6 +632,14 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g, int G) {
                         vlane % 32;
         float bv = 0.f;
         if (MB != MODE_SWIGLU && g.bias) bv = bf2f(g.bias[(size_t)e * g.N + col]);
+        if (g.scale0) {  // 8-bit weights: the column scales
+            const float c0 = g.scale0[(size_t)e * g.N + col];
+            s0.x *= c0; s0.y *= c0; s0.z *= c0; s0.w *= c0;
+            if (MB == MODE_SWIGLU) {
+                const float c1 = g.scale1[(size_t)e * g.N + col];
+                s1.x *= c1; s1.y *= c1; s1.z *= c1; s1.w *= c1;
+            }
+        }
         const float a0[4] = {s0.x, s0.y, s0.z, s0.w};
         const float a1[4] = {s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
@@ -655,10 +723,10 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
 }
 
 
-template <int MODE, int BN, bool GATHER = false>
+template <int MODE, int BN, bool GATHER = false, bool F8 = false>
 moe_status_t launch_gemm(const GemmArgs& a, hipStream_t st) {
-    using EP = Epi<MODE, BN>;
-    auto kern = grouped_gemm_kernel<MODE, BN, GATHER>;
+    using EP = Epi<MODE, BN, F8>;
+    auto kern = grouped_gemm_kernel<MODE, BN, GATHER, F8>;
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)EP::LDS) != hipSuccess)
         return MOE_ERR_LAUNCH;
@@ -697,10 +765,10 @@ bool use_narrow_tiles(const GemmArgs& a) {
     return c128 < 0.6 * c256;
 }
 
-template <int MODE, bool GATHER = false>
+template <int MODE, bool GATHER = false, bool F8 = false>
 moe_status_t launch_single(const GemmArgs& a, hipStream_t st) {
-    return use_narrow_tiles(a) ? launch_gemm<MODE, 128, GATHER>(a, st)
-                               : launch_gemm<MODE, 256, GATHER>(a, st);
+    return use_narrow_tiles(a) ? launch_gemm<MODE, 128, GATHER, F8>(a, st)
+                               : launch_gemm<MODE, 256, GATHER, F8>(a, st);
 }
 
 }  // namespace
@@ -713,13 +781,17 @@ extern "C" size_t moe_expert_ffn_ws_bytes(void) { return ffn_ws_bytes(); }
 
 namespace {
 
-// Both entry points: A is x_disp [E, C, H], or with slot_token the token
-// rows x [a_rows, H] gathered through slot_token [E, C].
+// Every entry point: A is x_disp [E, C, H], or with slot_token the token
+// rows x [a_rows, H] gathered through slot_token [E, C].  With scales
+// (s1 non-null), w1 / w3 / w2 are e4m3 codes [E, N, K] with per-column fp32
+// scales s1 / s3 / s2 [E, N] (bf16 activations only).
 moe_status_t ffn_impl(void* stream, moe_dtype_t dtype, moe_act_t act, const void* A,
                       const int32_t* slot_token, int64_t a_rows, const int32_t* kept, int E,
                       int64_t C, int64_t H, int64_t I, const void* w1, const void* w3,
                       const void* w2, const void* b1, const void* b2, void* h_ws, void* y_disp,
-                      void* ws, size_t ws_bytes) {
+                      void* ws, size_t ws_bytes, const float* s1 = nullptr,
+                      const float* s3 = nullptr, const float* s2 = nullptr) {
+    const bool f8 = s1 != nullptr;
     if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_DTYPE;
     if (act != MOE_ACT_SWIGLU && act != MOE_ACT_GELU_BIAS) return MOE_ERR_DTYPE;
     if (E < 1 || C < 0 || H <= 0 || I <= 0 || a_rows < 0) return MOE_ERR_SHAPE;
@@ -728,6 +800,8 @@ moe_status_t ffn_impl(void* stream, moe_dtype_t dtype, moe_act_t act, const void
     if (!kept || !w1 || !w2) return MOE_ERR_NULL;
     if (act == MOE_ACT_SWIGLU && !w3) return MOE_ERR_NULL;
     if (act == MOE_ACT_GELU_BIAS && !b1) return MOE_ERR_NULL;
+    if (f8 && (!s2 || (act == MOE_ACT_SWIGLU && !s3))) return MOE_ERR_NULL;
+    if (f8 && dtype != MOE_BF16) return MOE_ERR_DTYPE;
     if (C == 0) return MOE_OK;
     if (!A || !h_ws || !y_disp) return MOE_ERR_NULL;
     const int esz = dtype == MOE_BF16 ? 2 : 4;
@@ -761,9 +835,11 @@ moe_status_t ffn_impl(void* stream, moe_dtype_t dtype, moe_act_t act, const void
     if (act == MOE_ACT_SWIGLU ? (I % (kBNMax / 2)) : (I % kBNMax)) return MOE_ERR_ALIGN;
     if (C > (1 << 30) / 8) return MOE_ERR_UNSUPPORTED;
     if (H < 2 * kBK || I < 2 * kBK) return MOE_ERR_ALIGN;  // the k pipeline needs two steps
-    const void* ptrs[] = {A, w1, w3, w2, b1, b2, h_ws, y_disp, ws};
+    const void* ptrs[] = {A, w1, w3, w2, b1, b2, h_ws, y_disp, ws, s1, s3, s2};
     for (const void* q : ptrs)
         if (q && !moe_aligned16(q)) return MOE_ERR_ALIGN;
+    // code rows are addressed with 32-bit offsets from an expert's column
+    if (f8 && (int64_t)H * I >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
     GemmArgs a1;
     a1.A = static_cast<const uint16_t*>(A);
     a1.slot_token = slot_token;
@@ -773,6 +849,10 @@ moe_status_t ffn_impl(void* stream, moe_dtype_t dtype, moe_act_t act, const void
     a1.bias = act == MOE_ACT_GELU_BIAS ? static_cast<const uint16_t*>(b1) : nullptr;
     a1.out = h_ws;
     a1.save0 = a1.save1 = nullptr;
+    a1.Q0 = f8 ? static_cast<const uint8_t*>(w1) : nullptr;
+    a1.Q1 = f8 ? static_cast<const uint8_t*>(w3) : nullptr;
+    a1.scale0 = s1;
+    a1.scale1 = f8 ? s3 : nullptr;
     a1.kept = kept;
     a1.E = E;
     a1.C = C;
@@ -783,12 +863,20 @@ moe_status_t ffn_impl(void* stream, moe_dtype_t dtype, moe_act_t act, const void
     a1.part = split ? static_cast<float*>(ws) : nullptr;
     a1.smax = FFN1_SPLIT_MAX;
     moe_status_t s;
-    if (slot_token)
+    if (f8) {
+        if (slot_token)
+            s = act == MOE_ACT_SWIGLU ? launch_gemm<MODE_SWIGLU, 256, true, true>(a1, st)
+                                      : launch_single<MODE_GELU, true, true>(a1, st);
+        else
+            s = act == MOE_ACT_SWIGLU ? launch_gemm<MODE_SWIGLU, 256, false, true>(a1, st)
+                                      : launch_single<MODE_GELU, false, true>(a1, st);
+    } else if (slot_token) {
         s = act == MOE_ACT_SWIGLU ? launch_gemm<MODE_SWIGLU, 256, true>(a1, st)
                                   : launch_single<MODE_GELU, true>(a1, st);
-    else
+    } else {
         s = act == MOE_ACT_SWIGLU ? launch_gemm<MODE_SWIGLU, 256>(a1, st)
                                   : launch_single<MODE_GELU>(a1, st);
+    }
     if (s != MOE_OK) return s;
     GemmArgs a2 = a1;
     a2.A = static_cast<const uint16_t*>(h_ws);
@@ -802,7 +890,11 @@ moe_status_t ffn_impl(void* stream, moe_dtype_t dtype, moe_act_t act, const void
     a2.N = (int)H;
     a2.part = split ? static_cast<float*>(ws) : nullptr;
     a2.smax = FFN2_SPLIT_MAX;
-    return launch_single<MODE_DOWN>(a2, st);
+    a2.Q0 = f8 ? static_cast<const uint8_t*>(w2) : nullptr;
+    a2.Q1 = nullptr;
+    a2.scale0 = f8 ? s2 : nullptr;
+    a2.scale1 = nullptr;
+    return f8 ? launch_single<MODE_DOWN, false, true>(a2, st) : launch_single<MODE_DOWN>(a2, st);
 }
 
 }  // namespace
@@ -822,6 +914,8 @@ moe_status_t moe_ffn1_save(hipStream_t st, moe_act_t act, const void* x_disp, co
     a.out = h;
     a.save0 = static_cast<uint16_t*>(save0);
     a.save1 = static_cast<uint16_t*>(save1);
+    a.Q0 = a.Q1 = nullptr;
+    a.scale0 = a.scale1 = nullptr;
     a.kept = kept;
     a.E = E;
     a.C = C;
@@ -853,4 +947,31 @@ extern "C" moe_status_t moe_expert_ffn_gather(void* stream, moe_dtype_t dtype, m
     if (T < 0) return MOE_ERR_SHAPE;
     return ffn_impl(stream, dtype, act, x, slot_token, T, kept, E, C, H, I, w1, w3, w2, b1, b2,
                     h_ws, y_disp, ws, ws_bytes);
+}
+
+extern "C" moe_status_t moe_expert_ffn_fp8(void* stream, moe_act_t act, const void* x_disp,
+                                           const int32_t* kept, int E, int64_t C, int64_t H,
+                                           int64_t I, const uint8_t* w1q, const uint8_t* w3q,
+                                           const uint8_t* w2q, const float* s1, const float* s3,
+                                           const float* s2, const void* b1, const void* b2,
+                                           void* h_ws, void* y_disp, void* ws, size_t ws_bytes) {
+    if (!s1) return MOE_ERR_NULL;
+    return ffn_impl(stream, MOE_BF16, act, x_disp, nullptr, 0, kept, E, C, H, I, w1q, w3q, w2q, b1,
+                    b2, h_ws, y_disp, ws, ws_bytes, s1, s3, s2);
+}
+
+extern "C" moe_status_t moe_expert_ffn_gather_fp8(void* stream, moe_act_t act, const void* x,
+                                                  const int32_t* slot_token, int64_t T,
+                                                  const int32_t* kept, int E, int64_t C, int64_t H,
+                                                  int64_t I, const uint8_t* w1q,
+                                                  const uint8_t* w3q, const uint8_t* w2q,
+                                                  const float* s1, const float* s3,
+                                                  const float* s2, const void* b1, const void* b2,
+                                                  void* h_ws, void* y_disp, void* ws,
+                                                  size_t ws_bytes) {
+    if (!s1) return MOE_ERR_NULL;
+    if (C > 0 && !slot_token) return MOE_ERR_NULL;
+    if (T < 0) return MOE_ERR_SHAPE;
+    return ffn_impl(stream, MOE_BF16, act, x, slot_token, T, kept, E, C, H, I, w1q, w3q, w2q, b1,
+                    b2, h_ws, y_disp, ws, ws_bytes, s1, s3, s2);
 }

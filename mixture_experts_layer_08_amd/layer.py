@@ -70,9 +70,15 @@ class MoELayerGPU:
     """Device-resident weights + buffers for one configuration."""
 
     def __init__(self, cfg: MoEConfig, inputs: Dict[str, np.ndarray], device="cuda:0",
-                 fused_gather: bool = True):
+                 fused_gather: bool = True, weights: str = "bf16"):
+        """weights="fp8": the routed experts run on 8-bit (e4m3) weights with
+        per-expert, per-column scales, quantised here on the device from the
+        bf16 weights (moe_quantize_fp8)."""
+        if weights not in ("bf16", "fp8"):
+            raise ValueError("weights must be 'bf16' or 'fp8'")
         self.cfg = cfg
         self.fused_gather = fused_gather
+        self.weights = weights
         dev = torch.device(device)
         self.dev = dev
         self.tdtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
@@ -99,6 +105,16 @@ class MoELayerGPU:
                 self.sw1, self.sb1, self.sw2, self.sb2 = (
                     _to_dev(inputs["shared_" + n], dev, cfg.dtype) for n in ("w1", "b1", "w2", "b2"))
                 self.sw3 = None
+        self.q = None
+        if weights == "fp8":
+            if cfg.dtype != "bf16":
+                raise ValueError("8-bit weights need bf16 activations")
+            self.q = {}
+            for name, w in (("w1", self.w1), ("w3", self.w3), ("w2", self.w2)):
+                if w is not None:
+                    self.q[name + "q"], self.q["s" + name[1]] = ops.moe_quantize_fp8(w)
+                else:
+                    self.q[name + "q"], self.q["s" + name[1]] = None, None
         self.C = ops.moe_capacity(cfg.T, cfg.k, cfg.E, cfg.cf)
         self.buf = self.alloc(cfg.T)
 
@@ -144,6 +160,18 @@ class MoELayerGPU:
     def experts(self, x: Optional[torch.Tensor] = None):
         """x (the token activations) is needed with fused_gather."""
         b = self.buf
+        if self.q is not None:
+            q = self.q
+            if self.fused_gather:
+                if x is None:
+                    raise ValueError("experts(x): the fused-gather layer reads the token rows")
+                return ops.moe_expert_ffn_gather_fp8(
+                    x, b.slot_token, b.kept, q["w1q"], q["w3q"], q["w2q"], q["s1"], q["s3"],
+                    q["s2"], self.b1, self.b2, act=self.cfg.act, h_ws=b.h, y_disp=b.y_disp,
+                    ws=b.ffn_ws)
+            return ops.moe_expert_ffn_fp8(
+                b.x_disp, b.kept, q["w1q"], q["w3q"], q["w2q"], q["s1"], q["s3"], q["s2"],
+                self.b1, self.b2, act=self.cfg.act, h_ws=b.h, y_disp=b.y_disp, ws=b.ffn_ws)
         if self.fused_gather:
             if x is None:
                 raise ValueError("experts(x): the fused-gather layer reads the token rows")

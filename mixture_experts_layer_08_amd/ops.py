@@ -181,6 +181,89 @@ def moe_expert_ffn_gather(x: torch.Tensor, slot_token: torch.Tensor, kept: torch
     return y_disp, h_ws
 
 
+def moe_quantize_fp8(w: torch.Tensor, *, q: Optional[torch.Tensor] = None,
+                     scale: Optional[torch.Tensor] = None):
+    """bf16 weights [E, K, N] -> (e4m3 codes [E, N, K] uint8, fp32 scales
+    [E, N]), one scale per expert and output column."""
+    if w.dtype != torch.bfloat16 or w.dim() != 3:
+        raise ValueError("w must be a bf16 [E, K, N] tensor")
+    E, K, N = w.shape
+    q = _want(q, (E, N, K), torch.uint8, w.device)
+    scale = _want(scale, (E, N), torch.float32, w.device)
+    st = lib().moe_quantize_fp8(_stream(w.device), _ptr(w), E, K, N, _ptr(q), _ptr(scale))
+    check("moe_quantize_fp8", st)
+    return q, scale
+
+
+def moe_dequantize_fp8(q: torch.Tensor, scale: torch.Tensor) -> torch.Tensor:
+    """e4m3 codes [E, N, K] and scales [E, N] -> fp32 weights [E, K, N]."""
+    E, N, K = q.shape
+    if q.dtype != torch.uint8 or scale.dtype != torch.float32 or tuple(scale.shape) != (E, N):
+        raise ValueError("q must be uint8 [E, N, K] and scale fp32 [E, N]")
+    w = torch.empty((E, K, N), dtype=torch.float32, device=q.device)
+    st = lib().moe_dequantize_fp8(_stream(q.device), _ptr(q), _ptr(scale), E, K, N, _ptr(w))
+    check("moe_dequantize_fp8", st)
+    return w
+
+
+def _check_fp8_weights(E, H, I, w1q, w3q, w2q, s1, s3, s2):
+    if tuple(w1q.shape) != (E, I, H) or tuple(w2q.shape) != (E, H, I):
+        raise ValueError("w1q must be [E, I, H] and w2q [E, H, I] (codes, K-contiguous)")
+    if w3q is not None and tuple(w3q.shape) != (E, I, H):
+        raise ValueError("w3q must be [E, I, H]")
+    for t in (w1q, w3q, w2q):
+        if t is not None and t.dtype != torch.uint8:
+            raise ValueError("codes must be uint8")
+    for t, n in ((s1, I), (s3, I), (s2, H)):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (E, n)):
+            raise ValueError("scales must be fp32 [E, N]")
+
+
+def moe_expert_ffn_fp8(x_disp: torch.Tensor, kept: torch.Tensor, w1q: torch.Tensor,
+                       w3q: Optional[torch.Tensor], w2q: torch.Tensor, s1: torch.Tensor,
+                       s3: Optional[torch.Tensor], s2: torch.Tensor,
+                       b1: Optional[torch.Tensor] = None, b2: Optional[torch.Tensor] = None, *,
+                       act: str = "swiglu", h_ws: Optional[torch.Tensor] = None,
+                       y_disp: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """moe_expert_ffn on 8-bit weights (codes and scales from moe_quantize_fp8)."""
+    E, C, H = x_disp.shape
+    I = w1q.shape[1]
+    dev = x_disp.device
+    _check_fp8_weights(E, H, I, w1q, w3q, w2q, s1, s3, s2)
+    h_ws = _want(h_ws, (E, C, I), x_disp.dtype, dev)
+    y_disp = _want(y_disp, (E, C, H), torch.float32, dev)
+    st = lib().moe_expert_ffn_fp8(_stream(dev), ACTS[act], _ptr(x_disp), _ptr(kept), E, C, H, I,
+                                  _ptr(w1q), _ptr(w3q), _ptr(w2q), _ptr(s1), _ptr(s3), _ptr(s2),
+                                  _ptr(b1), _ptr(b2), _ptr(h_ws), _ptr(y_disp), _ptr(ws),
+                                  0 if ws is None else ws.numel() * ws.element_size())
+    check("moe_expert_ffn_fp8", st)
+    return y_disp, h_ws
+
+
+def moe_expert_ffn_gather_fp8(x: torch.Tensor, slot_token: torch.Tensor, kept: torch.Tensor,
+                              w1q: torch.Tensor, w3q: Optional[torch.Tensor], w2q: torch.Tensor,
+                              s1: torch.Tensor, s3: Optional[torch.Tensor], s2: torch.Tensor,
+                              b1: Optional[torch.Tensor] = None, b2: Optional[torch.Tensor] = None,
+                              *, act: str = "swiglu", h_ws: Optional[torch.Tensor] = None,
+                              y_disp: Optional[torch.Tensor] = None,
+                              ws: Optional[torch.Tensor] = None):
+    """moe_expert_ffn_gather on 8-bit weights."""
+    T, H = x.shape
+    E, C = slot_token.shape
+    I = w1q.shape[1]
+    dev = x.device
+    _check_fp8_weights(E, H, I, w1q, w3q, w2q, s1, s3, s2)
+    h_ws = _want(h_ws, (E, C, I), x.dtype, dev)
+    y_disp = _want(y_disp, (E, C, H), torch.float32, dev)
+    st = lib().moe_expert_ffn_gather_fp8(_stream(dev), ACTS[act], _ptr(x), _ptr(slot_token), T,
+                                         _ptr(kept), E, C, H, I, _ptr(w1q), _ptr(w3q), _ptr(w2q),
+                                         _ptr(s1), _ptr(s3), _ptr(s2), _ptr(b1), _ptr(b2),
+                                         _ptr(h_ws), _ptr(y_disp), _ptr(ws),
+                                         0 if ws is None else ws.numel() * ws.element_size())
+    check("moe_expert_ffn_gather_fp8", st)
+    return y_disp, h_ws
+
+
 def moe_combine(y_disp: torch.Tensor, slot: torch.Tensor, topk_w: torch.Tensor, *,
                 y: Optional[torch.Tensor] = None, y_shared: Optional[torch.Tensor] = None,
                 out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:

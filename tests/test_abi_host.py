@@ -23,7 +23,7 @@ def L():
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_and_binding_agree():
@@ -190,6 +190,33 @@ def test_combine_argument_errors(L):
     assert c(y=MIS) == ALIGN
     assert c(ys=MIS) == ALIGN
     assert c(T=0, slot=None, y=None) == OK
+
+
+def test_fp8_argument_errors(L):
+    def qz(**kw):
+        return L.moe_quantize_fp8(None, kw.get("w", P), kw.get("E", 2), kw.get("K", 64),
+                                  kw.get("N", 64), kw.get("q", P), kw.get("s", P))
+    assert qz(E=-1) == SHAPE
+    assert qz(K=1 << 22) == UNSUP
+    assert qz(K=40) == ALIGN
+    assert qz(q=MIS) == ALIGN
+    assert qz(w=None) == NULL
+    assert qz(E=0, w=None) == OK
+    assert L.moe_dequantize_fp8(None, P, None, 2, 64, 64, P) == NULL
+
+    def ffn(**kw):
+        return L.moe_expert_ffn_fp8(None, kw.get("act", 0), P, P, kw.get("E", 2), kw.get("C", 64),
+                                    kw.get("H", 256), kw.get("I", 256), P, kw.get("w3", P), P,
+                                    kw.get("s1", P), kw.get("s3", P), kw.get("s2", P), None, None,
+                                    P, P, None, 0)
+    assert ffn(s1=None) == NULL
+    assert ffn(s2=None) == NULL
+    assert ffn(s3=None) == NULL
+    assert ffn(H=200) == ALIGN
+    assert ffn(s1=MIS) == ALIGN
+    assert ffn(C=0) == OK
+    assert L.moe_expert_ffn_gather_fp8(None, 0, P, None, 64, P, 2, 64, 256, 256, P, P, P, P, P,
+                                       P, None, None, P, P, None, 0) == NULL
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

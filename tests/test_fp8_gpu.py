@@ -1,0 +1,153 @@
+"""GPU parity of the 8-bit weight path through the C ABI.
+
+  * quantisation (moe_quantize_fp8): codes and scales bit-exact against the
+    oracle's (an integer decision both sides take in fp32);
+  * dequantisation (moe_dequantize_fp8) of all 256 codes: bit-exact against
+    the oracle's exact product rounded to fp32 (this also pins the hardware
+    e4m3 -> bf16 conversion the expert products use);
+  * the layer on 8-bit weights against the oracle layer with the dequantised
+    weights: max |err| <= 2e-2 * RMS(row), as for bf16 weights (the products
+    run on the codes' exact values; only the storage points round);
+  * the gathered and the dispatched-copy products bitwise equal;
+  * the drop-free decode workload (64 tokens) and the 4096-token layer at
+    full size.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import fp8 as Q
+from oracle import moe_oracle as M
+from mixture_experts_layer_08_amd import ops
+from mixture_experts_layer_08_amd.layer import MoELayerGPU, x_to_device
+from mixture_experts_layer_08_amd.synth import (CONFIGS, MoEConfig, bf16_bits_to_f32,
+                                                f32_to_bf16_bits, make_inputs)
+
+from parity_util import assert_rows_close, log, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+CASES = {
+    "swiglu-e8-drops": MoEConfig("q-sw", "bf16", T=1500, H=512, I=384, E=8, k=2, cf=1.0,
+                                 seed=41),
+    "gelu-e4": MoEConfig("q-ge", "bf16", T=600, H=256, I=512, E=4, k=2, cf=1.25, act="gelu",
+                         seed=42),
+    # few rows per expert: 128-column tiles and split tails in both products
+    "gelu-e8-thin": MoEConfig("q-thin", "bf16", T=48, H=512, I=256, E=8, k=2, cf=4.0,
+                              act="gelu", seed=43),
+    "swiglu-decode-t16": MoEConfig("q-dec", "bf16", T=16, H=256, I=256, E=8, k=2, cf=4.0,
+                                   seed=44),
+}
+
+
+def _bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def test_quantize_bitexact():
+    rng = np.random.default_rng(45)
+    E, K, N = 3, 320, 384
+    w = rng.standard_normal((E, K, N)) * 0.02 * 10.0 ** rng.uniform(-4, 1, (E, 1, N))
+    w[0, :, 5] = 0.0                                   # all-zero column
+    w[1, 7, :] = -0.0                                  # negative zeros
+    w[2, :, 9] = 1e-30                                 # tiny values beside one large one
+    w[2, 3, 9] = 3.0
+    bits = f32_to_bf16_bits(w.astype(np.float32))
+    q, s = ops.moe_quantize_fp8(_bf16_dev(bits))
+    torch.cuda.synchronize()
+    q_ref, s_ref = Q.quantize_weight(bf16_bits_to_f32(bits))
+    np.testing.assert_array_equal(to_np(s).view(np.uint32), s_ref.view(np.uint32))
+    np.testing.assert_array_equal(to_np(q), q_ref)
+    log(f"[fp8] quantise {E}x{K}x{N}: codes and scales bit-exact")
+
+
+def test_dequantize_every_code():
+    E, N, K = 2, 96, 256
+    n = np.arange(N)[:, None]
+    k = np.arange(K)[None, :]
+    codes = np.stack([((n * 131 + k + 37 * e) % 256).astype(np.uint8) for e in range(E)])
+    rng = np.random.default_rng(46)
+    s = (np.abs(rng.standard_normal((E, N))) * 10.0 ** rng.uniform(-6, 2, (E, N))).astype(np.float32)
+    w = ops.moe_dequantize_fp8(to_dev(codes, torch.uint8), to_dev(s, torch.float32))
+    torch.cuda.synchronize()
+    want = Q.dequantize_weight(codes, s).astype(np.float32)   # exact product, rounded once
+    got = to_np(w)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(want))
+    m = ~np.isnan(want)
+    np.testing.assert_array_equal(got[m].view(np.uint32), want[m].view(np.uint32))
+
+
+def _layer_case(cfg, fused):
+    inp = make_inputs(cfg)
+    qref = Q.quantize_inputs(inp, cfg.act)
+    ref_inp = Q.dequantized_inputs(inp, qref, cfg.act)
+    layer = MoELayerGPU(cfg, inp, DEV, fused_gather=fused, weights="fp8")
+    x = x_to_device(inp, cfg, DEV)
+    y, _ = layer.forward(x)
+    torch.cuda.synchronize()
+    # the device quantisation is the oracle's, bit for bit
+    for name in ("w_gate", "w_up", "w_down") if cfg.act == "swiglu" else ("w1", "w2"):
+        key = {"w_gate": "w1", "w1": "w1", "w_up": "w3", "w_down": "w2", "w2": "w2"}[name]
+        np.testing.assert_array_equal(to_np(layer.q[key + "q"]), qref[name + "_q"])
+    return inp, ref_inp, layer, y
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["gather", "copy"])
+@pytest.mark.parametrize("name", list(CASES))
+def test_fp8_layer_matches_dequantised_oracle(name, fused):
+    cfg = CASES[name]
+    log(f"[fp8] {name} ({'gather' if fused else 'copy'}): T={cfg.T} H={cfg.H} I={cfg.I} "
+        f"E={cfg.E} k={cfg.k} cf={cfg.cf} {cfg.act}")
+    inp, ref_inp, layer, y = _layer_case(cfg, fused)
+    ref = M.forward(ref_inp, cfg)
+    b = layer.buf
+    ok = np.all(to_np(b.topk_idx) == ref.route.idx, axis=1)
+    ok &= np.all(to_np(b.slot) == ref.disp.slot, axis=1)
+    assert ok.mean() > 0.95
+    worst = assert_rows_close(to_np(y)[ok], ref.y[ok], 2e-2, f"{name}: y")
+    log(f"[fp8] {name}: dropped {int(to_np(b.dropped)[0])}, worst err/rms {worst:.3e}")
+
+
+def test_fp8_gather_equals_copy_bitwise():
+    cfg = CASES["swiglu-e8-drops"]
+    inp = make_inputs(cfg)
+    x = x_to_device(inp, cfg, DEV)
+    la = MoELayerGPU(cfg, inp, DEV, fused_gather=True, weights="fp8")
+    lb = MoELayerGPU(cfg, inp, DEV, fused_gather=False, weights="fp8")
+    ya, _ = la.forward(x)
+    yb, _ = lb.forward(x)
+    torch.cuda.synchronize()
+    assert torch.equal(ya, yb)
+    kept = to_np(la.buf.kept)
+    for e, n in enumerate(kept):
+        assert torch.equal(la.buf.h[e, :n], lb.buf.h[e, :n])
+
+
+def test_fp8_decode_config_full_size():
+    cfg = CONFIGS[6]
+    log("[fp8] decode workload (64 tokens) full size")
+    inp, ref_inp, layer, y = _layer_case(cfg, True)
+    ref = M.forward(ref_inp, cfg)
+    b = layer.buf
+    assert int(to_np(b.dropped)[0]) == 0
+    ok = np.all(to_np(b.topk_idx) == ref.route.idx, axis=1)
+    worst = assert_rows_close(to_np(y)[ok], ref.y[ok], 2e-2, "decode fp8: y")
+    log(f"[fp8] decode: {int(ok.sum())}/64 rows, worst err/rms {worst:.3e}")
+
+
+def test_fp8_config2_sampled():
+    cfg = CONFIGS[2]
+    log("[fp8] 4096-token layer full size (sampled rows)")
+    inp, ref_inp, layer, y = _layer_case(cfg, True)
+    b = layer.buf
+    r = M.route(inp, cfg)
+    d = M.dispatch(r.idx, cfg.E, layer.C)
+    ok = np.all(to_np(b.topk_idx) == r.idx, axis=1) & np.all(to_np(b.slot) == d.slot, axis=1)
+    rng = np.random.default_rng(47)
+    sample = np.sort(rng.choice(np.where(ok)[0], size=64, replace=False))
+    ref = M.forward(ref_inp, cfg, sample=sample)
+    worst = assert_rows_close(to_np(y)[sample], ref.y, 2e-2, "config 2 fp8: y (sampled)")
+    log(f"[fp8] config 2: worst err/rms {worst:.3e}")
