@@ -339,7 +339,9 @@ moe_status_t moe_expert_ffn_bwd(void* stream, moe_dtype_t dtype, moe_act_t act,
                                 float* dw3, float* dw2, float* db1, float* db2,
                                 void* ws, size_t ws_bytes);
 
-/* Bytes of moe_expert_ffn_bwd's workspace: five bf16 [E, C, I] planes. */
+/* Bytes of moe_expert_ffn_bwd's workspace on the current device: five bf16
+ * [E, C, I] planes, then one 256 KiB fp32 tile per compute unit (the split
+ * tail rounds of the two input-gradient products). */
 size_t moe_expert_ffn_bwd_ws_bytes(int E, int64_t C, int64_t I);
 
 /* Dispatch backward: dx[t] = dx_add[t] + sum over kept j of

@@ -61,12 +61,48 @@ struct BwdArgs {
     uint16_t* out1;         // EPI_DH_SWIGLU: du (out holds dg)
     const uint16_t* side0;  // EPI_DH_*: g (SwiGLU) or z (GELU), [E][C][N]
     const uint16_t* side1;  // EPI_DH_SWIGLU: u
+    // DGRAD: split-K of the last, partly filled round of tiles (null: off)
+    float* part;            // per-piece fp32 partial tiles, kBwdPartBytes each
+    int smax;               // at most this many pieces per tile
 };
+
+constexpr size_t kBwdPartBytes = (size_t)kBM * kBNMax * 4;  // one fp32 tile
+constexpr int kBwdSMax = 4;
+
+// DGRAD tiles fill total / G rounds of a G-workgroup launch; when the last
+// round would leave at least half of the workgroups idle, its tiles are cut
+// along K into this many pieces (1: no split), each keeping two k-steps.
+__device__ __forceinline__ int bwd_tail_splits(const BwdArgs& g, int total, int G, int nk) {
+    const int remt = total % G;
+    if (!g.part || remt == 0 || 2 * remt > G) return 1;
+    int sp = G / remt;
+    if (sp > g.smax) sp = g.smax;
+    if (sp > kBwdSMax) sp = kBwdSMax;
+    if (sp > nk / 2) sp = nk / 2;
+    return sp < 1 ? 1 : sp;
+}
+
+// The DGRAD schedule's per-expert row tiles and tile prefix (one thread).
+__device__ void bwd_prefix(const BwdArgs& g, bool KC, int NT, int* s_pref, int* s_mt) {
+    int cum = 0;
+    for (int e = 0; e < g.E; ++e) {
+        int kp = g.kept[e];
+        if (kp < 0) kp = 0;
+        if (kp > g.C) kp = (int)g.C;
+        const int mt = KC ? (kp + kBM - 1) / kBM : g.M / kBM;
+        s_mt[e] = mt;
+        s_pref[e] = cum;
+        cum += mt * NT;
+    }
+    s_pref[g.E] = cum;
+}
 
 struct BTile {
     bool valid;
     int e, m0, n0, rows;    // rows: valid output rows from m0 (DGRAD: kept - m0)
-    int nks, kstep_pair;    // k-steps of the tile, and of one (A, B) pair
+    int nks, kstep_pair;    // k-steps of the tile (from kb), and of one (A, B) pair
+    int kb;                 // first k-step (a piece of a split tail tile starts later)
+    int pslot;              // piece of a split tail tile: tile * splits + piece; else -1
     int kept;
     i32x4_t rsA0, rsB0, rsA1, rsB1;
 };
@@ -86,29 +122,31 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
     const int wm = wave / kWN, wn = wave % kWN;
     const int NT = g.N / kBNMax;
-    if (tid == 0) {
-        int cum = 0;
-        for (int e = 0; e < g.E; ++e) {
-            int kp = g.kept[e];
-            if (kp < 0) kp = 0;
-            if (kp > g.C) kp = (int)g.C;
-            const int mt = KC ? (kp + kBM - 1) / kBM : g.M / kBM;
-            s_mt[e] = mt;
-            s_pref[e] = cum;
-            cum += mt * NT;
-        }
-        s_pref[g.E] = cum;
-    }
+    if (tid == 0) bwd_prefix(g, KC, NT, s_pref, s_mt);
     __syncthreads();
     const int total = __builtin_amdgcn_readfirstlane(s_pref[g.E]);
     const int G = gridDim.x;
     const int xcd = blockIdx.x % 8, slot8 = blockIdx.x / 8;
     const int full = total / G;
+    const int remt = total - full * G;
+    // DGRAD k-steps of a whole tile (both chained pairs)
+    const int nk_tile = (g.A1 ? 2 : 1) * (g.K / kBK);
+    const int splits =
+        KC ? __builtin_amdgcn_readfirstlane(bwd_tail_splits(g, total, G, nk_tile)) : 1;
 
     auto tile_at = [&](int round) {
         BTile c;
         const int pos = round == full ? (int)blockIdx.x : xcd * (G / 8) + slot8;
-        const int logical = round * G + pos;
+        int logical = round * G + pos;
+        c.kb = 0;
+        c.pslot = -1;
+        int piece = 0;
+        if (splits > 1 && round == full) {
+            const int t = pos / splits;
+            piece = pos - t * splits;
+            logical = pos < remt * splits ? full * G + t : total;
+            c.pslot = pos;
+        }
         c.valid = logical < total;
         if (!c.valid) return c;
         int e, m_tile, n_tile;
@@ -124,6 +162,10 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
             c.rows = c.kept - c.m0;
             c.kstep_pair = g.K / kBK;
             c.nks = g.A1 ? 2 * c.kstep_pair : c.kstep_pair;
+            if (c.pslot >= 0) {  // a piece: k-steps kb .. kb + nks - 1 of the tile
+                c.kb = piece * c.nks / splits;
+                c.nks = (piece + 1) * c.nks / splits - c.kb;
+            }
             // A: the expert's rows from m0 (rows past kept read as zero);
             // B: weight rows n0.. of length K
             const size_t abytes = (size_t)c.rows * g.K * 2;
@@ -234,8 +276,8 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
 
     BTile cur = tile_at(0);
     if (!cur.valid) return;
-    issue(cur, 0, 0);
-    issue(cur, 1, 1);
+    issue(cur, cur.kb, 0);
+    issue(cur, cur.kb + 1, 1);
     int base = 0;
     for (int round = 0;; ++round) {
         const BTile nxt = tile_at(round + 1);
@@ -278,7 +320,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
                 __builtin_amdgcn_sched_barrier(0);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
-                issue(cur, kt + 2, s0);
+                issue(cur, cur.kb + kt + 2, s0);
                 if (Mth) {
                     load_frags(s0 ^ 1, 0, a0, b0);
                     mma(a1, b1);
@@ -293,7 +335,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
             __builtin_amdgcn_sched_barrier(0);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
-            if (nxt.valid) issue(nxt, 0, s0);
+            if (nxt.valid) issue(nxt, nxt.kb, s0);
             if (Mth) {
                 load_frags(s0 ^ 1, 0, a0, b0);
                 mma(a1, b1);
@@ -303,12 +345,34 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
             }
             __builtin_amdgcn_sched_barrier(0);
             __syncthreads();
-            if (nxt.valid) issue(nxt, 1, s0 ^ 1);
+            if (nxt.valid) issue(nxt, nxt.kb + 1, s0 ^ 1);
         };
         if (wm * WM_ROWS < cur.rows)
             kloop(std::true_type{});
         else
             kloop(std::false_type{});
+
+        if (cur.pslot >= 0) {
+            // a piece of a split tail tile: store the fp32 partial, lane-major
+            // (16-byte group gi of thread tid at gi * kGThreads + tid), skipping
+            // 32-row blocks wholly past the valid rows; bwd_tail_reduce_kernel
+            // finishes the tile.  Pieces are the last round.
+            const i32x4_t rsP = make_rsrc(g.part + (size_t)cur.pslot * (kBwdPartBytes / 4),
+                                          (uint32_t)kBwdPartBytes);
+            constexpr int NG = TM * TN * 4;
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                const int i = gi / (TN * 4), j = (gi / 4) % TN, q4 = gi % 4;
+                if (wm * WM_ROWS + i * 32 >= cur.rows) continue;
+                f32x4_t v;
+                v.x = acc[i][j][4 * q4];
+                v.y = acc[i][j][4 * q4 + 1];
+                v.z = acc[i][j][4 * q4 + 2];
+                v.w = acc[i][j][4 * q4 + 3];
+                buffer_store_f32x4(v, rsP, (gi * kGThreads + tid) * 16, 0, 0);
+            }
+            break;
+        }
 
         // epilogue.  The products run with the operands swapped (C^T = B^T
         // A^T), so accumulator element q of lane l is output row l%32 and
@@ -399,6 +463,86 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
     }
 }
 
+// Finishes the split tail tiles of one DGRAD launch of G workgroups:
+// recomputes the schedule from kept[], sums each element's partials in piece
+// order (the result does not depend on which piece finished first) and runs
+// the product's epilogue.  A work item is one 16-byte group of one product
+// thread (four consecutive output columns of one row).
+template <int EPI>
+__global__ __launch_bounds__(256) void bwd_tail_reduce_kernel(BwdArgs g, int G) {
+    constexpr int WM_ROWS = kBM / kWMn, WN_COLS = kBNMax / kWN;
+    constexpr int TM = WM_ROWS / 32, TN = WN_COLS / 32;
+    constexpr int PER_TILE = kGThreads * TM * TN * 4;
+    __shared__ int s_pref[MOE_MAX_EXPERTS + 1];
+    __shared__ int s_mt[MOE_MAX_EXPERTS];
+    const int NT = g.N / kBNMax;
+    if (threadIdx.x == 0) bwd_prefix(g, true, NT, s_pref, s_mt);
+    __syncthreads();
+    const int total = s_pref[g.E];
+    const int splits = bwd_tail_splits(g, total, G, (g.A1 ? 2 : 1) * (g.K / kBK));
+    if (splits <= 1) return;
+    const int full = total / G, remt = total - full * G;
+    const float4* part = reinterpret_cast<const float4*>(g.part);
+    constexpr size_t PSTRIDE = kBwdPartBytes / 16;
+    for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < (int64_t)remt * PER_TILE;
+         w += (int64_t)gridDim.x * blockDim.x) {
+        const int t = (int)(w / PER_TILE);
+        int r = (int)(w - (int64_t)t * PER_TILE);
+        const int vt = r % kGThreads;  // the product thread that held these values
+        const int gi = r / kGThreads;
+        const int i = gi / (TN * 4), j = (gi / 4) % TN, q4 = gi % 4;
+        int e, m_tile, n_tile;
+        map_tile(full * G + t, s_pref, s_mt, g.E, NT, e, m_tile, n_tile);
+        int kept = g.kept[e];
+        if (kept > g.C) kept = (int)g.C;
+        const int vwave = vt / kWave, vlane = vt % kWave;
+        const int wm = vwave / kWN, wn = vwave % kWN;
+        const int m0 = m_tile * kBM, n0 = n_tile * kBNMax;
+        if (m0 + wm * WM_ROWS + i * 32 >= kept) continue;  // block past kept: no partials stored
+        const int row = m0 + wm * WM_ROWS + i * 32 + vlane % 32;
+        if (row >= kept) continue;                         // not an output row
+        const int col = n0 + wn * WN_COLS + j * 32 + 8 * q4 + 4 * (vlane / 32);
+        const size_t base = (size_t)t * splits * PSTRIDE + (size_t)gi * kGThreads + vt;
+        float4 s = part[base];
+        for (int pc = 1; pc < splits; ++pc) {
+            const float4 v = part[base + pc * PSTRIDE];
+            s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+        }
+        const size_t o = ((size_t)e * g.C + row) * g.N + col;
+        if (EPI == EPI_F32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(g.out) + o) = s;
+        } else {
+            const float dh[4] = {s.x, s.y, s.z, s.w};
+            const uint2 wa = *reinterpret_cast<const uint2*>(g.side0 + o);
+            uint2 wu = make_uint2(0u, 0u);
+            if (EPI == EPI_DH_SWIGLU) wu = *reinterpret_cast<const uint2*>(g.side1 + o);
+            float r0[4], r1[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t xa = c < 2 ? wa.x : wa.y;
+                const float a = (c & 1) ? bf_hi(xa) : bf_lo(xa);
+                if (EPI == EPI_DH_SWIGLU) {
+                    const uint32_t xu = c < 2 ? wu.x : wu.y;
+                    const float u = (c & 1) ? bf_hi(xu) : bf_lo(xu);
+                    const float sg = 1.0f / (1.0f + __expf(-a));
+                    const float dsilu = sg * (1.0f + a * (1.0f - sg));
+                    r0[c] = dh[c] * u * dsilu;
+                    r1[c] = dh[c] * a * sg;
+                } else {
+                    const float cdf = 0.5f * (1.0f + erff(a * 0.70710678118654752f));
+                    const float pdf = 0.39894228040143268f * __expf(-0.5f * a * a);
+                    r0[c] = dh[c] * (cdf + a * pdf);
+                }
+            }
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.out) + o) =
+                make_uint2(pack_bf2(r0[0], r0[1]), pack_bf2(r0[2], r0[3]));
+            if (EPI == EPI_DH_SWIGLU)
+                *reinterpret_cast<uint2*>(g.out1 + o) =
+                    make_uint2(pack_bf2(r1[0], r1[1]), pack_bf2(r1[2], r1[3]));
+        }
+    }
+}
+
 // Column sums over each expert's kept rows (the bias gradients), in row
 // order: out[e][n] = sum_{r < kept[e]} src[e][r][n].
 __global__ __launch_bounds__(256) void colsum_kernel(const uint16_t* __restrict__ src,
@@ -428,17 +572,29 @@ moe_status_t launch_bwd(const BwdArgs& a, int64_t max_tiles, hipStream_t st) {
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) !=
         hipSuccess)
         return MOE_ERR_LAUNCH;
+    // split tail pieces may use more workgroups than there are tiles
+    const int64_t max_units = (SCHED == SCHED_DGRAD && a.part) ? max_tiles * a.smax : max_tiles;
     int64_t grid = num_cus();
-    if (grid > max_tiles) grid = (max_tiles + 7) / 8 * 8;
+    if (grid > max_units) grid = (max_units + 7) / 8 * 8;
     grid = grid / 8 * 8;
     if (grid < 8) grid = 8;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kGThreads), lds, st, a);
     MOE_CHECK_LAUNCH();
+    if (SCHED == SCHED_DGRAD && a.part) {  // finishes the split tail tiles, if any were split
+        hipLaunchKernelGGL(bwd_tail_reduce_kernel<EPI>, dim3((unsigned)(4 * num_cus())), dim3(256),
+                           0, st, a, (int)grid);
+        MOE_CHECK_LAUNCH();
+    }
     return MOE_OK;
 }
 
+// h, g, u, dg, du planes (GELU uses h, z, dz), then the split tails'
+// partial tiles: one per workgroup of a full-device launch
+size_t bwd_planes_bytes(int E, int64_t C, int64_t I) {
+    return ((size_t)5 * E * C * I * 2 + 255) / 256 * 256;
+}
 size_t bwd_ws_bytes(int E, int64_t C, int64_t I) {
-    return (size_t)5 * E * C * I * 2;  // h, g, u, dg, du (GELU uses h, z, dz)
+    return bwd_planes_bytes(E, C, I) + (size_t)num_cus() * kBwdPartBytes;
 }
 
 }  // namespace
@@ -480,6 +636,8 @@ extern "C" moe_status_t moe_expert_ffn_bwd(void* stream, moe_dtype_t dtype, moe_
     uint16_t* s1 = wsb + 2 * plane;    // u
     uint16_t* d0 = wsb + 3 * plane;    // dg or dz
     uint16_t* d1 = wsb + 4 * plane;    // du
+    float* part = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) +
+                                           bwd_planes_bytes(E, C, I));
     if (C > 0) {
         // 1. the first product again, saving h and its pre-activations
         moe_status_t s = moe_ffn1_save(st, act, x_disp, kept, E, C, H, I, w1, w3, b1, h, s0,
@@ -499,6 +657,8 @@ extern "C" moe_status_t moe_expert_ffn_bwd(void* stream, moe_dtype_t dtype, moe_
         a.out1 = d1;
         a.side0 = s0;
         a.side1 = s1;
+        a.part = part;
+        a.smax = kBwdSMax;
         s = sw ? launch_bwd<SCHED_DGRAD, EPI_DH_SWIGLU>(a, E * mt_max * (I / kBNMax), st)
                : launch_bwd<SCHED_DGRAD, EPI_DH_GELU>(a, E * mt_max * (I / kBNMax), st);
         if (s != MOE_OK) return s;
@@ -514,6 +674,8 @@ extern "C" moe_status_t moe_expert_ffn_bwd(void* stream, moe_dtype_t dtype, moe_
         b.N = (int)H;
         b.K = (int)I;
         b.out = dx_disp;
+        b.part = part;
+        b.smax = kBwdSMax;
         s = launch_bwd<SCHED_DGRAD, EPI_F32>(b, E * mt_max * (H / kBNMax), st);
         if (s != MOE_OK) return s;
     }
