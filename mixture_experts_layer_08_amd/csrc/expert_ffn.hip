@@ -114,13 +114,13 @@ constexpr int kSMax = 4;  // most pieces per split tile
 // ---------------------------------------------------------- tile schedule --
 // Expert e owns tiles s_pref[e] .. s_pref[e+1]-1: ceil(kept[e] / kBM) row
 // tiles times NT column tiles.  Run by one thread.
-__device__ void build_prefix(const GemmArgs& g, int NT, int* s_pref, int* s_mt) {
+__device__ void build_prefix(const GemmArgs& g, int NT, int BM, int* s_pref, int* s_mt) {
     int cum = 0;
     for (int e = 0; e < g.E; ++e) {
         int kp = g.kept[e];
         if (kp < 0) kp = 0;
         if (kp > g.C) kp = (int)g.C;
-        const int mt = (kp + kBM - 1) / kBM;
+        const int mt = (kp + BM - 1) / BM;
         s_mt[e] = mt;
         s_pref[e] = cum;
         cum += mt * NT;
@@ -142,15 +142,22 @@ __device__ __forceinline__ int tail_splits(const GemmArgs& g, int total, int G, 
 }
 
 
-template <int MODE, int BN, bool F8 = false>
+// THIN: 64-row tiles (every expert has at most 64 rows, as in a decode step)
+// with three LDS stages, so two k-steps of loads are in flight while one is
+// read: a thin tile does little MFMA work per k-step, and with two stages
+// each k-step would wait a whole load round trip.
+template <int MODE, int BN, bool F8 = false, bool THIN = false>
 struct Epi {
     static constexpr int MB = mode_base(MODE);
     static_assert(BN == 256 || (BN == 128 && MB != MODE_SWIGLU), "B tile is 256 or 128 columns");
+    static constexpr int BM = THIN ? 64 : kBM;
+    static constexpr int NSTAGE = THIN ? 3 : 2;
+    static constexpr int STAGE_A = BM * kBK * 2;            // 32 KB (8 KB thin)
     static constexpr int STAGE_B = kBK * BN * (F8 ? 1 : 2);  // 32 or 16 KB (8 or 16 KB for codes)
-    static constexpr int STAGE = kStageA + STAGE_B;
+    static constexpr int STAGE = STAGE_A + STAGE_B;
     static constexpr int BN_OUT = (MB == MODE_SWIGLU) ? BN / 2 : BN;
     static constexpr int OUT_BYTES = (MB == MODE_DOWN) ? 4 : 2;
-    static constexpr size_t LDS = 2 * (size_t)STAGE;
+    static constexpr size_t LDS = NSTAGE * (size_t)STAGE;
 };
 
 // One tile of work: expert e, rows m0.., output columns n0.., and the buffer
@@ -168,21 +175,21 @@ struct TileCtx {
 
 // GATHER: the A rows are read from the token rows x[slot_token[e, r]]
 // instead of a dispatched copy (rows with token -1 read as zero).
-template <int MODE, int BN, bool GATHER, bool F8>
+template <int MODE, int BN, bool GATHER, bool F8, bool THIN>
 __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
-    using EP = Epi<MODE, BN, F8>;
+    using EP = Epi<MODE, BN, F8, THIN>;
     static_assert(!F8 || MODE == mode_base(MODE), "8-bit weights: inference products only");
     constexpr int MB = mode_base(MODE);
     constexpr bool SAVE = MODE != MB;
     constexpr int kStage = EP::STAGE;
-    constexpr int WM_ROWS = kBM / kWMn;       // rows per wave
+    constexpr int WM_ROWS = EP::BM / kWMn;    // rows per wave
     constexpr int WN_COLS = BN / kWN;         // B columns per wave
     constexpr int TM = WM_ROWS / 32, TN = WN_COLS / 32;  // 32 x 32 MFMA tiles per wave
     constexpr int TH = TN / 2 > 0 ? TN / 2 : 1;           // SwiGLU: gate (or up) tiles per wave
-    constexpr int QA = 32 / kNW;              // 1 KB A loads per wave per k-step
+    constexpr int QA = EP::STAGE_A / 1024 / kNW;  // 1 KB A loads per wave per k-step
     // 1 KB B loads per wave per k-step (codes: 16 rows of 64 bytes each)
     constexpr int QB = F8 ? BN / 16 / kNW : (BN / 128) * 16 / kNW;
-    static_assert(QA <= 4 && QA % 2 == 0, "A loads per wave");
+    static_assert(QA == 1 || (QA <= 4 && QA % 2 == 0), "A loads per wave");
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_pref[MOE_MAX_EXPERTS + 1];
     __shared__ int s_mt[MOE_MAX_EXPERTS];
@@ -191,7 +198,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
     const int wm = wave / kWN, wn = wave % kWN;  // wave rows wm*WM_ROWS.., columns per wn
     const int NT = g.N / EP::BN_OUT;
-    if (tid == 0) build_prefix(g, NT, s_pref, s_mt);
+    if (tid == 0) build_prefix(g, NT, EP::BM, s_pref, s_mt);
     __syncthreads();
     const int total = __builtin_amdgcn_readfirstlane(s_pref[g.E]);
     const int G = gridDim.x;
@@ -233,7 +240,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
         if (kept > g.C) kept = (int)g.C;
         c.kept = __builtin_amdgcn_readfirstlane(kept);
         c.e = __builtin_amdgcn_readfirstlane(e);
-        c.m0 = __builtin_amdgcn_readfirstlane(m_tile * kBM);
+        c.m0 = __builtin_amdgcn_readfirstlane(m_tile * EP::BM);
         c.n0 = __builtin_amdgcn_readfirstlane(n_tile * EP::BN_OUT);
         if (GATHER) {
             // A: token rows; a row past kept (or an empty slot) reads as zero
@@ -272,7 +279,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
 
     // A load q of this wave: tile row R = (wave*QA + q)*8 + lane/8 holds in
     // its chunk lane % 8 the logical chunk (lane % 8) ^ swz_a(R), and
-    // swz_a(R) = 4*(q & 1) + lane/16 (QA is even)
+    // swz_a(R) = 4*((wave*QA + q) & 1) + lane/16
     const int voffA0 = ((wave * QA * 8 + lane / 8) * g.K + (((lane % 8) ^ (lane / 16)) * 8)) * 2;
     const int voffA1 = ((wave * QA * 8 + lane / 8) * g.K + (((lane % 8) ^ (4 + lane / 16)) * 8)) * 2;
     // B load q: sub-tile row kr = ((wave*QB + q) % 16)*4 + lane/16,
@@ -293,20 +300,21 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
         for (int q = 0; q < QA; ++q) {
             if (GATHER) {
                 const int tk = c.tok[q];
-                const int vo = tk >= 0 ? tk * g.K * 2 + ((q & 1) ? chA1 : chA0) : (int)0x80000000;
+                const int vo = tk >= 0 ? tk * g.K * 2 + (((wave * QA + q) & 1) ? chA1 : chA0)
+                                       : (int)0x80000000;
                 lds_dma16(c.rsA, st + (wave * QA + q) * 1024, vo, kt * kBK * 2);
             } else {
-                lds_dma16(c.rsA, st + (wave * QA + q) * 1024, (q & 1) ? voffA1 : voffA0,
+                lds_dma16(c.rsA, st + (wave * QA + q) * 1024, ((wave * QA + q) & 1) ? voffA1 : voffA0,
                           (q * 8 * g.K + kt * kBK) * 2);
             }
         }
 #pragma unroll
         for (int q = 0; q < QB; ++q) {
             if (F8)
-                lds_dma16(c.rsB, st + kStageA + (wave * QB + q) * 1024, voffQ,
+                lds_dma16(c.rsB, st + EP::STAGE_A + (wave * QB + q) * 1024, voffQ,
                           q * 16 * g.K + kt * kBK);
             else
-                lds_dma16(c.rsB, st + kStageA + (wave * QB + q) * 1024, voffB,
+                lds_dma16(c.rsB, st + EP::STAGE_A + (wave * QB + q) * 1024, voffB,
                           ((((wave * QB + q) % 16) * 4 + kt * kBK) * g.N) * 2);
         }
     };
@@ -319,7 +327,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
                           bf16x8_t (&bfr)[2][TN]) {
         constexpr int NI = decltype(ni)::value;
         const unsigned char* As = smem + stage * kStage;
-        const unsigned char* Bs = As + kStageA;
+        const unsigned char* Bs = As + EP::STAGE_A;
 #pragma unroll
         for (int ss = 0; ss < 2; ++ss) {
             const int k16 = kk * 2 + ss;
@@ -466,9 +474,55 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
             __syncthreads();  // every wave is done with step nk - 1
             if (nxt.valid) issue(nxt, nxt.kb + 1, s0 ^ 1);
         };
+        // THIN: three stages, one barrier per k-step.  Step kt+2 is loaded
+        // into the stage step kt-1 used (free once every wave has passed this
+        // step's barrier) while step kt is read, so two k-steps of loads are in
+        // flight; the wait before the barrier lets the newest step's loads (NL
+        // buffer loads per wave) stay outstanding, since loads complete in
+        // issue order.  The first step of a tile waits for everything (the
+        // previous tile's epilogue stores included).  The last two iterations
+        // load the next tile's first two steps.
+        auto kloop_thin = [&](auto ni) {
+            constexpr bool M = decltype(ni)::value > 0;
+            constexpr int NL = QA + QB;
+            bf16x8_t af[2][TM], bfr[2][TN];
+            const int nks = cur.nks;
+            for (int kt = 0; kt < nks; ++kt) {
+                if (kt == 0) {
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                } else if (kt + 1 < nks || nxt.valid) {
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NL) : "memory");
+                } else {
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                }
+                __syncthreads();
+                if (GATHER && kt == 0) {
+#pragma unroll
+                    for (int q = 0; q < QA; ++q) asm volatile("" ::"v"(cur.tok[q]));
+                }
+                const int s2 = (base + kt + 2) % 3;
+                if (kt + 2 < nks)
+                    issue(cur, cur.kb + kt + 2, s2);
+                else if (nxt.valid)
+                    issue(nxt, nxt.kb + (kt + 2 - nks), s2);
+                if (M) {
+                    const int sc = (base + kt) % 3;
+                    load_frags(ni, sc, 0, af, bfr);
+                    mma(ni, af, bfr);
+                    load_frags(ni, sc, 1, af, bfr);
+                    mma(ni, af, bfr);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
         // MFMAs only on the wave's 32-row blocks that hold rows below kept[e]
         // (thin last row tiles of an expert, decode steps)
-        {
+        if constexpr (THIN) {
+            if (cur.kept - (cur.m0 + wm * WM_ROWS) > 0)
+                kloop_thin(std::integral_constant<int, 1>{});
+            else
+                kloop_thin(std::integral_constant<int, 0>{});
+        } else {
             const int rows = cur.kept - (cur.m0 + wm * WM_ROWS);
             if (rows > 64)
                 kloop(std::integral_constant<int, TM>{});
@@ -565,7 +619,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
             }
         }
         if (!nxt.valid) break;
-        base = (base + cur.nks) & 1;
+        base = THIN ? (base + cur.nks) % 3 : (base + cur.nks) & 1;
         cur = tile_at(round + 1);  // recomputed: only what the prefetch needs stays live
     }
 }
@@ -577,18 +631,18 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
 // piece finished first) and runs the product's epilogue.  A work item is one
 // group of four accumulator values of one product thread, in the product's
 // register layout, so partial reads are 16-byte and coalesced.
-template <int MODE, int BN>
+template <int MODE, int BN, bool THIN>
 __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g, int G) {
-    using EP = Epi<MODE, BN>;
+    using EP = Epi<MODE, BN, false, THIN>;
     constexpr int MB = mode_base(MODE);
-    constexpr int WM_ROWS = kBM / kWMn, WN_COLS = BN / kWN;
+    constexpr int WM_ROWS = EP::BM / kWMn, WN_COLS = BN / kWN;
     constexpr int TM = WM_ROWS / 32, TN = WN_COLS / 32;
     constexpr int TNO = (MB == MODE_SWIGLU) ? TN / 2 : TN;
     constexpr int PER_TILE = kGThreads * TM * TNO * 4;
     __shared__ int s_pref[MOE_MAX_EXPERTS + 1];
     __shared__ int s_mt[MOE_MAX_EXPERTS];
     const int NT = g.N / EP::BN_OUT;
-    if (threadIdx.x == 0) build_prefix(g, NT, s_pref, s_mt);
+    if (threadIdx.x == 0) build_prefix(g, NT, EP::BM, s_pref, s_mt);
     __syncthreads();
     const int total = s_pref[g.E];
     const int splits = tail_splits(g, total, G, g.K / kBK);
@@ -611,7 +665,7 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g, int G) {
         if (kept > g.C) kept = (int)g.C;
         const int vwave = vt / kWave, vlane = vt % kWave;
         const int wm = vwave / kWN, wn = vwave % kWN;
-        const int m0 = m_tile * kBM, n0 = n_tile * EP::BN_OUT;
+        const int m0 = m_tile * EP::BM, n0 = n_tile * EP::BN_OUT;
         const int row0 = m0 + wm * WM_ROWS + i * 32 + q4 * 8 + (vlane / 32) * 4;
         if (m0 + wm * WM_ROWS + i * 32 >= kept) continue;  // block past kept: no partials stored
         const size_t base = (size_t)t * splits * PSTRIDE + vt;
@@ -723,14 +777,14 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
 }
 
 
-template <int MODE, int BN, bool GATHER = false, bool F8 = false>
+template <int MODE, int BN, bool GATHER = false, bool F8 = false, bool THIN = false>
 moe_status_t launch_gemm(const GemmArgs& a, hipStream_t st) {
-    using EP = Epi<MODE, BN, F8>;
-    auto kern = grouped_gemm_kernel<MODE, BN, GATHER, F8>;
+    using EP = Epi<MODE, BN, F8, THIN>;
+    auto kern = grouped_gemm_kernel<MODE, BN, GATHER, F8, THIN>;
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)EP::LDS) != hipSuccess)
         return MOE_ERR_LAUNCH;
-    const int64_t max_tiles = (int64_t)a.E * ((a.C + kBM - 1) / kBM) * (a.N / EP::BN_OUT);
+    const int64_t max_tiles = (int64_t)a.E * ((a.C + EP::BM - 1) / EP::BM) * (a.N / EP::BN_OUT);
     const int64_t max_units = a.part ? max_tiles * a.smax : max_tiles;
     int64_t grid = num_cus();
     if (grid > max_units) grid = (max_units + 7) / 8 * 8;
@@ -740,7 +794,7 @@ moe_status_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     MOE_CHECK_LAUNCH();
     if constexpr (MODE == mode_base(MODE)) {  // training variants never split
         if (a.part) {  // finishes the split tail tiles, if the device schedule split any
-            hipLaunchKernelGGL((tail_reduce_kernel<MODE, BN>), dim3((unsigned)(4 * num_cus())),
+            hipLaunchKernelGGL((tail_reduce_kernel<MODE, BN, THIN>), dim3((unsigned)(4 * num_cus())),
                                dim3(256), 0, st, a, (int)grid);
             MOE_CHECK_LAUNCH();
         }
@@ -753,10 +807,10 @@ moe_status_t launch_gemm(const GemmArgs& a, hipStream_t st) {
 // about 35% less efficiently per FLOP on MI355X, so they are used only when
 // they cut the rounds of 256-column tiles (on the largest tile count kept[]
 // allows) by more than 40%: small products whose single round is mostly empty.
-bool use_narrow_tiles(const GemmArgs& a) {
+bool use_narrow_tiles(const GemmArgs& a, int bm) {
     if (a.N % 128) return false;
     const int64_t cus = num_cus();
-    const int64_t mt = (int64_t)a.E * ((a.C + kBM - 1) / kBM);
+    const int64_t mt = (int64_t)a.E * ((a.C + bm - 1) / bm);
     const int64_t t256 = (a.N % 256) ? -1 : mt * (a.N / 256);
     if (t256 < 0) return true;
     const int64_t t128 = mt * (a.N / 128);
@@ -765,10 +819,20 @@ bool use_narrow_tiles(const GemmArgs& a) {
     return c128 < 0.6 * c256;
 }
 
-template <int MODE, bool GATHER = false, bool F8 = false>
+template <int MODE, bool GATHER = false, bool F8 = false, bool THIN = false>
 moe_status_t launch_single(const GemmArgs& a, hipStream_t st) {
-    return use_narrow_tiles(a) ? launch_gemm<MODE, 128, GATHER, F8>(a, st)
-                               : launch_gemm<MODE, 256, GATHER, F8>(a, st);
+    return use_narrow_tiles(a, THIN ? 64 : kBM) ? launch_gemm<MODE, 128, GATHER, F8, THIN>(a, st)
+                                               : launch_gemm<MODE, 256, GATHER, F8, THIN>(a, st);
+}
+
+// Every expert has at most kThinRows rows (C <= kThinRows): 64-row tiles with
+// a three-stage pipeline (decode steps).
+constexpr int64_t kThinRows = 64;
+
+template <bool GATHER, bool F8, bool THIN>
+moe_status_t launch_first(moe_act_t act, const GemmArgs& a, hipStream_t st) {
+    return act == MOE_ACT_SWIGLU ? launch_gemm<MODE_SWIGLU, 256, GATHER, F8, THIN>(a, st)
+                                 : launch_single<MODE_GELU, GATHER, F8, THIN>(a, st);
 }
 
 }  // namespace
@@ -862,20 +926,18 @@ moe_status_t ffn_impl(void* stream, moe_dtype_t dtype, moe_act_t act, const void
     const bool split = ws && ws_bytes >= ffn_ws_bytes();
     a1.part = split ? static_cast<float*>(ws) : nullptr;
     a1.smax = FFN1_SPLIT_MAX;
+    const bool thin = C <= kThinRows;
+    const int sel = (slot_token ? 4 : 0) + (f8 ? 2 : 0) + (thin ? 1 : 0);
     moe_status_t s;
-    if (f8) {
-        if (slot_token)
-            s = act == MOE_ACT_SWIGLU ? launch_gemm<MODE_SWIGLU, 256, true, true>(a1, st)
-                                      : launch_single<MODE_GELU, true, true>(a1, st);
-        else
-            s = act == MOE_ACT_SWIGLU ? launch_gemm<MODE_SWIGLU, 256, false, true>(a1, st)
-                                      : launch_single<MODE_GELU, false, true>(a1, st);
-    } else if (slot_token) {
-        s = act == MOE_ACT_SWIGLU ? launch_gemm<MODE_SWIGLU, 256, true>(a1, st)
-                                  : launch_single<MODE_GELU, true>(a1, st);
-    } else {
-        s = act == MOE_ACT_SWIGLU ? launch_gemm<MODE_SWIGLU, 256>(a1, st)
-                                  : launch_single<MODE_GELU>(a1, st);
+    switch (sel) {
+        case 0: s = launch_first<false, false, false>(act, a1, st); break;
+        case 1: s = launch_first<false, false, true>(act, a1, st); break;
+        case 2: s = launch_first<false, true, false>(act, a1, st); break;
+        case 3: s = launch_first<false, true, true>(act, a1, st); break;
+        case 4: s = launch_first<true, false, false>(act, a1, st); break;
+        case 5: s = launch_first<true, false, true>(act, a1, st); break;
+        case 6: s = launch_first<true, true, false>(act, a1, st); break;
+        default: s = launch_first<true, true, true>(act, a1, st); break;
     }
     if (s != MOE_OK) return s;
     GemmArgs a2 = a1;
@@ -894,6 +956,9 @@ moe_status_t ffn_impl(void* stream, moe_dtype_t dtype, moe_act_t act, const void
     a2.Q1 = nullptr;
     a2.scale0 = f8 ? s2 : nullptr;
     a2.scale1 = nullptr;
+    if (thin)
+        return f8 ? launch_single<MODE_DOWN, false, true, true>(a2, st)
+                  : launch_single<MODE_DOWN, false, false, true>(a2, st);
     return f8 ? launch_single<MODE_DOWN, false, true>(a2, st) : launch_single<MODE_DOWN>(a2, st);
 }
 
