@@ -11,16 +11,25 @@ accumulation); --config 6 is the drop-free 64-token decode step on the same
 layer.  Prints one JSON line.
 
 Timing:
-  * the timed region is exactly K steps, bracketed by device synchronisation;
-  * inside it, HIP events on the launch stream bracket every phase, so each
-    phase's average duration over the timed region is reported too (the
-    expert phase dominates and gives `roofline`, against the matrix-core
-    peak or, when its weights take longer to stream than its FLOP to
-    compute, against HBM);
+  * the timed region is exactly K whole-layer forwards, bracketed by device
+    synchronisation, with nothing else enqueued (it sets ms_per_step and
+    value);
+  * K more steps follow with HIP events on the launch stream between the
+    phases, so each phase's average duration is reported too (the expert
+    phase dominates and gives `roofline`, against the matrix-core peak or,
+    when its weights take longer to stream than its FLOP to compute, against
+    HBM);
   * memory-bound phases are also timed in isolation after a 1 GiB write that
     flushes the 256 MB Infinity Cache, so their bytes come from HBM;
   * the CPU oracle (float64, the reference implementation) is timed on the
     host cores on one full layer forward of the same workload.
+
+Further measurements, each added to the same JSON line: --backward (a
+training step: forward keeping the dispatched rows, then the combine, expert,
+dispatch and router backward, per phase), --weights fp8 (the layer on 8-bit
+e4m3 expert weights), --shared I_S (the layer plus a shared expert of
+intermediate size I_S), --copy-calibration (three plain 256 MiB device
+copies, the reference for the HBM traffic counters).
 """
 from __future__ import annotations
 
@@ -282,9 +291,18 @@ def main():
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    # the timed region: K whole-layer forwards, nothing else enqueued
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(K):
+        layer.forward(x)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # the same K steps again with HIP events between the phases (on the launch
+    # stream) for the per-phase times; the events add a little time per step,
+    # so this loop does not set ms_per_step
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    torch.cuda.synchronize()
     for s in range(K):
         e = ev[s]
         e[0].record(stream)
@@ -299,7 +317,6 @@ def main():
         layer.combine()
         e[5].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     names = ["route", "aux", "dispatch", "expert_ffn", "combine"]
     ph = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)]))
           for i, n in enumerate(names)}
