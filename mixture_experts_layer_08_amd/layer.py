@@ -197,9 +197,12 @@ class MoELayerGPU:
     def backward(self, x: torch.Tensor, dy: torch.Tensor, dl_aux: float = 1.0) -> Dict:
         """Gradients of sum(dy * y) + dl_aux * L_aux after forward(x) (the
         forward's buffers are read; the layer must keep x_disp, i.e. be built
-        with fused_gather=False).  Returns fp32 tensors: dx [T, H], dw_r,
-        db_r (or None), and the expert weight gradients under the input names
-        (w_gate, w_up, w_down or w1, b1, w2, b2)."""
+        with fused_gather=False, with bf16 weights).  Returns fp32 tensors:
+        dx [T, H], dw_r, db_r (or None), and the expert weight gradients under
+        the input names (w_gate, w_up, w_down or w1, b1, w2, b2; with a shared
+        expert also shared_<name> and its part of dx, dx_shared)."""
+        if self.q is not None:
+            raise ValueError("backward runs on bf16 expert weights (8-bit weights serve inference)")
         if self.buf.x_disp is None:
             raise ValueError("backward needs the dispatched rows: build the layer with "
                              "fused_gather=False")
