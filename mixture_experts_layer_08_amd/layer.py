@@ -5,9 +5,10 @@ layer shape, allocated once, so a forward call enqueues only kernels: no
 allocation, no host synchronisation.  With fused_gather (the default) the
 dispatch step produces only the row indices and the first expert product
 reads each expert's rows straight from x (moe_expert_ffn_gather); without
-it, dispatch materialises x_disp and moe_expert_ffn reads that.  It mirrors the (out, aux_loss) return
-of the minimal MoELayer of the MoE basics page (dpshk.com/news/6005940,
-section 3.1).
+it, dispatch materialises x_disp and moe_expert_ffn reads that.  With
+weights="fp8" the routed experts run on 8-bit e4m3 weights quantised on the
+device.  It mirrors the (out, aux_loss) return of the minimal MoELayer of the
+MoE basics page (dpshk.com/news/6005940, section 3.1).
 
 A shared expert (the LLaMA4-MoE guide, dpshk.com/news/5809432, section 5.2:
 an expert every token passes through) is moe_expert_ffn with one expert
@@ -132,7 +133,8 @@ class MoELayerGPU:
             **sh,
             topk_idx=e(T, k, dt=i32), topk_w=e(T, k), probs=e(T, E), keys=e(T, E),
             counts=e(E, dt=i32), f=e(E), p=e(E), l_aux=e(1),
-            x_disp=None if self.fused_gather else e(E, C, H, dt=td), slot=e(T, k, dt=i32), slot_token=e(E, C, dt=i32),
+            x_disp=None if self.fused_gather else e(E, C, H, dt=td), slot=e(T, k, dt=i32),
+            slot_token=e(E, C, dt=i32),
             kept=e(E, dt=i32), dropped=e(1, dt=i32), h=e(E, C, I, dt=td),
             y_disp=e(E, C, H), y=e(T, H, dt=td),
             ws=e(max(1, ops.moe_workspace_bytes(T, E, k)), dt=torch.uint8),
