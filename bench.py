@@ -176,7 +176,8 @@ def cpu_baseline(cfg, inputs):
 
 
 def bench_backward(cfg, inputs, dev, args):
-    """Forward (keeping x_disp) + backward, with per-phase events."""
+    """Training step: the training forward (dispatched rows and the first
+    expert product's planes kept) + backward, with per-phase events."""
     import torch
     from mixture_experts_layer_08_amd import ops
     from mixture_experts_layer_08_amd.layer import MoELayerGPU, x_to_device
@@ -185,19 +186,18 @@ def bench_backward(cfg, inputs, dev, args):
     g = torch.Generator(device="cpu").manual_seed(cfg.seed)
     dy = torch.randn((cfg.T, cfg.H), generator=g).to(layer.tdtype).to(dev)
     b = layer.buf
-    bws = torch.empty(max(16, int(ops.lib().moe_expert_ffn_bwd_ws_bytes(cfg.E, layer.C, cfg.I))),
-                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
         rec = (lambda i: ev[i].record(stream)) if ev else (lambda i: None)
         rec(0)
-        layer.forward(x)
+        layer.forward_train(x)
         rec(1)
         dy_disp, dw = ops.moe_combine_bwd(dy, b.y_disp, b.slot, b.topk_w)
         rec(2)
         gr = ops.moe_expert_ffn_bwd(b.x_disp, b.kept, layer.w1, layer.w3, layer.w2, layer.b1,
-                                    dy_disp, act=cfg.act, has_b2=layer.b2 is not None, ws=bws)
+                                    dy_disp, act=cfg.act, has_b2=layer.b2 is not None,
+                                    ws=layer.bws, saved=True)
         rec(3)
         dx = ops.moe_dispatch_bwd(gr["dx_disp"], b.slot)
         rec(4)
@@ -219,8 +219,9 @@ def bench_backward(cfg, inputs, dev, args):
     names = ["forward", "combine_bwd", "expert_ffn_bwd", "dispatch_bwd", "route_bwd"]
     ph = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
     n_kept = int(b.kept.cpu().numpy().sum())
-    # recompute of the first product + dh + dX + the weight gradients
-    mult = 16 if cfg.act == "swiglu" else 10
+    # dh + dX + the weight gradients (the first product's planes come from
+    # the training forward, so the backward does not recompute them)
+    mult = 12 if cfg.act == "swiglu" else 8
     bwd_flop = mult * cfg.H * cfg.I * n_kept
     tf = bwd_flop / (ph["expert_ffn_bwd"] * 1e-3) / 1e12
     return {"train_step_ms": round(wall * 1e3, 5), "train_tokens_per_s": round(cfg.T / wall, 1),

@@ -313,7 +313,8 @@ moe_status_t moe_combine_bwd(void* stream, moe_dtype_t dtype, const void* dy,
 
 /* Expert FFN backward.  [P2] sections 2.2 and 3.1, [P5] section 2.1 (the
  * expert FFNs being differentiated).  Re-runs the first product to recover
- * h and its pre-activations (bf16), then
+ * h and its pre-activations (bf16) — or, with saved != 0, takes them from
+ * ws, where moe_expert_ffn_fwd_save left them for the same inputs — then
  *   SwiGLU: dh = dY W_down^T, dg = dh u silu'(g), du = dh silu(g),
  *           dX = dg W_gate^T + du W_up^T, dW_down = h^T dY,
  *           dW_gate = X^T dg, dW_up = X^T du
@@ -329,6 +330,7 @@ moe_status_t moe_combine_bwd(void* stream, moe_dtype_t dtype, const void* dy,
  *   dw1 [E, H, I], dw3 [E, H, I] (SwiGLU), dw2 [E, I, H]   fp32 out
  *   db1 [E, I] (GELU, required), db2 [E, H] (GELU, may be NULL)  fp32 out
  *   ws      moe_expert_ffn_bwd_ws_bytes(E, C, I) bytes, 16-byte aligned
+ *   saved   0: recompute the first product; else ws holds its saved planes
  * bf16 only (MOE_ERR_UNSUPPORTED for fp32); H and I multiples of 256. An
  * expert with no rows gets zero weight gradients. */
 moe_status_t moe_expert_ffn_bwd(void* stream, moe_dtype_t dtype, moe_act_t act,
@@ -337,12 +339,26 @@ moe_status_t moe_expert_ffn_bwd(void* stream, moe_dtype_t dtype, moe_act_t act,
                                 const void* w3, const void* w2, const void* b1,
                                 const void* dy_disp, float* dx_disp, float* dw1,
                                 float* dw3, float* dw2, float* db1, float* db2,
-                                void* ws, size_t ws_bytes);
+                                void* ws, size_t ws_bytes, int saved);
 
 /* Bytes of moe_expert_ffn_bwd's workspace on the current device: five bf16
  * [E, C, I] planes, then one 256 KiB fp32 tile per compute unit (the split
  * tail rounds of the two input-gradient products). */
 size_t moe_expert_ffn_bwd_ws_bytes(int E, int64_t C, int64_t I);
+
+/* Training forward of the expert FFNs: the result of moe_expert_ffn
+ * (y_disp [E, C, H] fp32; same products, same bounds), with h and the first
+ * product's pre-activations written into ws (moe_expert_ffn_bwd_ws_bytes
+ * bytes) for a later moe_expert_ffn_bwd(..., saved = 1) on the same x_disp,
+ * kept and weights, which then skips its recompute (P3 section 3.3 trades
+ * that recompute against memory; here the memory is five bf16 [E, C, I]
+ * planes).  bf16 only; H and I multiples of 256. */
+moe_status_t moe_expert_ffn_fwd_save(void* stream, moe_dtype_t dtype, moe_act_t act,
+                                     const void* x_disp, const int32_t* kept, int E,
+                                     int64_t C, int64_t H, int64_t I, const void* w1,
+                                     const void* w3, const void* w2, const void* b1,
+                                     const void* b2, void* y_disp, void* ws,
+                                     size_t ws_bytes);
 
 /* Dispatch backward: dx[t] = dx_add[t] + sum over kept j of
  * dx_disp[slot[t, j]] (fp32; dx_add may be NULL, then a token with every

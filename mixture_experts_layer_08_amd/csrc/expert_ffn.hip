@@ -992,6 +992,30 @@ moe_status_t moe_ffn1_save(hipStream_t st, moe_act_t act, const void* x_disp, co
                                  : launch_gemm<MODE_GELU_SAVE, 256>(a, st);
 }
 
+moe_status_t moe_ffn2(hipStream_t st, const void* h, const int32_t* kept, int E, int64_t C,
+                      int64_t H, int64_t I, const void* w2, const void* b2, void* y_disp,
+                      void* part, size_t part_bytes) {
+    GemmArgs a{};
+    a.A = static_cast<const uint16_t*>(h);
+    a.slot_token = nullptr;
+    a.a_rows = 0;
+    a.B0 = static_cast<const uint16_t*>(w2);
+    a.B1 = nullptr;
+    a.bias = static_cast<const uint16_t*>(b2);
+    a.out = y_disp;
+    a.save0 = a.save1 = nullptr;
+    a.Q0 = a.Q1 = nullptr;
+    a.scale0 = a.scale1 = nullptr;
+    a.kept = kept;
+    a.E = E;
+    a.C = C;
+    a.K = (int)I;
+    a.N = (int)H;
+    a.part = (part && part_bytes >= ffn_ws_bytes()) ? static_cast<float*>(part) : nullptr;
+    a.smax = FFN2_SPLIT_MAX;
+    return launch_single<MODE_DOWN>(a, st);
+}
+
 extern "C" moe_status_t moe_expert_ffn(void* stream, moe_dtype_t dtype, moe_act_t act,
                                        const void* x_disp, const int32_t* kept, int E, int64_t C,
                                        int64_t H, int64_t I, const void* w1, const void* w3,

@@ -610,7 +610,7 @@ extern "C" moe_status_t moe_expert_ffn_bwd(void* stream, moe_dtype_t dtype, moe_
                                            const void* w3, const void* w2, const void* b1,
                                            const void* dy_disp, float* dx_disp, float* dw1,
                                            float* dw3, float* dw2, float* db1, float* db2,
-                                           void* ws, size_t ws_bytes) {
+                                           void* ws, size_t ws_bytes, int saved) {
     if (dtype != MOE_BF16) return dtype == MOE_F32 ? MOE_ERR_UNSUPPORTED : MOE_ERR_DTYPE;
     if (act != MOE_ACT_SWIGLU && act != MOE_ACT_GELU_BIAS) return MOE_ERR_DTYPE;
     if (E < 1 || C < 0 || H <= 0 || I <= 0) return MOE_ERR_SHAPE;
@@ -640,9 +640,13 @@ extern "C" moe_status_t moe_expert_ffn_bwd(void* stream, moe_dtype_t dtype, moe_
                                            bwd_planes_bytes(E, C, I));
     if (C > 0) {
         // 1. the first product again, saving h and its pre-activations
-        moe_status_t s = moe_ffn1_save(st, act, x_disp, kept, E, C, H, I, w1, w3, b1, h, s0,
-                                       sw ? s1 : nullptr);
-        if (s != MOE_OK) return s;
+        // (unless moe_expert_ffn_fwd_save left them in the workspace)
+        moe_status_t s = MOE_OK;
+        if (!saved) {
+            s = moe_ffn1_save(st, act, x_disp, kept, E, C, H, I, w1, w3, b1, h, s0,
+                              sw ? s1 : nullptr);
+            if (s != MOE_OK) return s;
+        }
         const int64_t mt_max = (C + kBM - 1) / kBM;
         // 2. dh = dY W2^T, then the activation's derivative in the epilogue
         BwdArgs a{};
@@ -729,4 +733,43 @@ extern "C" moe_status_t moe_expert_ffn_bwd(void* stream, moe_dtype_t dtype, moe_
         }
     }
     return MOE_OK;
+}
+
+// Training forward: the expert products with the first product's
+// pre-activations kept in the backward workspace (h, g, u or h, z planes),
+// so moe_expert_ffn_bwd(..., saved = 1) skips its recompute.
+extern "C" moe_status_t moe_expert_ffn_fwd_save(void* stream, moe_dtype_t dtype, moe_act_t act,
+                                                const void* x_disp, const int32_t* kept, int E,
+                                                int64_t C, int64_t H, int64_t I, const void* w1,
+                                                const void* w3, const void* w2, const void* b1,
+                                                const void* b2, void* y_disp, void* ws,
+                                                size_t ws_bytes) {
+    if (dtype != MOE_BF16) return dtype == MOE_F32 ? MOE_ERR_UNSUPPORTED : MOE_ERR_DTYPE;
+    if (act != MOE_ACT_SWIGLU && act != MOE_ACT_GELU_BIAS) return MOE_ERR_DTYPE;
+    if (E < 1 || C < 0 || H <= 0 || I <= 0) return MOE_ERR_SHAPE;
+    if (E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+    if (H % kBNMax || I % kBNMax || H < 2 * kBK || I < 2 * kBK) return MOE_ERR_ALIGN;
+    if (C > (1 << 30) / 8 || H > (1 << 16) || I > (1 << 16)) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)E * C * I >= ((int64_t)1 << 31) || (int64_t)E * C * H >= ((int64_t)1 << 31))
+        return MOE_ERR_UNSUPPORTED;
+    if (!kept || !w1 || !w2) return MOE_ERR_NULL;
+    if (act == MOE_ACT_SWIGLU && !w3) return MOE_ERR_NULL;
+    if (act == MOE_ACT_GELU_BIAS && !b1) return MOE_ERR_NULL;
+    if (C == 0) return MOE_OK;
+    if (!x_disp || !y_disp) return MOE_ERR_NULL;
+    const void* ptrs[] = {x_disp, w1, w3, w2, b1, b2, y_disp, ws};
+    for (const void* q : ptrs)
+        if (q && !moe_aligned16(q)) return MOE_ERR_ALIGN;
+    if (!ws || ws_bytes < bwd_ws_bytes(E, C, I)) return MOE_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool sw = act == MOE_ACT_SWIGLU;
+    const size_t plane = (size_t)E * C * I;
+    uint16_t* wsb = static_cast<uint16_t*>(ws);
+    uint16_t* h = wsb;
+    moe_status_t s = moe_ffn1_save(st, act, x_disp, kept, E, C, H, I, w1, w3, b1, h, wsb + plane,
+                                   sw ? wsb + 2 * plane : nullptr);
+    if (s != MOE_OK) return s;
+    void* part = static_cast<unsigned char*>(ws) + bwd_planes_bytes(E, C, I);
+    return moe_ffn2(st, h, kept, E, C, H, I, w2, b2, y_disp, part,
+                    (size_t)num_cus() * kBwdPartBytes);
 }

@@ -118,6 +118,12 @@ class MoELayerGPU:
                     self.q[name + "q"], self.q["s" + name[1]] = None, None
         self.C = ops.moe_capacity(cfg.T, cfg.k, cfg.E, cfg.cf)
         self.buf = self.alloc(cfg.T)
+        # training: backward workspaces holding the first products' planes
+        # from forward_train (routed experts, shared expert), and whether
+        # they belong to the last forward
+        self.bws = None
+        self.sh_bws = None
+        self._saved = False
 
     def alloc(self, T: int) -> Buffers:
         cfg, dev, C = self.cfg, self.dev, self.C
@@ -209,15 +215,18 @@ class MoELayerGPU:
             raise ValueError("backward needs the dispatched rows: build the layer with "
                              "fused_gather=False")
         b, cfg = self.buf, self.cfg
+        saved = self._saved  # forward_train kept the first products' planes
         dy_disp, dw = ops.moe_combine_bwd(dy, b.y_disp, b.slot, b.topk_w)
         g = ops.moe_expert_ffn_bwd(b.x_disp, b.kept, self.w1, self.w3, self.w2, self.b1, dy_disp,
-                                   act=cfg.act, has_b2=self.b2 is not None)
+                                   act=cfg.act, has_b2=self.b2 is not None,
+                                   ws=self.bws if saved else None, saved=saved)
         g_sh = None
         if self.shared:  # the shared expert's output gradient is dy itself
             T, H = cfg.T, cfg.H
             g_sh = ops.moe_expert_ffn_bwd(x.view(1, T, H), b.sh_kept, self.sw1, self.sw3, self.sw2,
                                           self.sb1, dy.view(1, T, H), act=cfg.act,
-                                          has_b2=self.sb2 is not None)
+                                          has_b2=self.sb2 is not None,
+                                          ws=self.sh_bws if saved else None, saved=saved)
         dx = ops.moe_dispatch_bwd(g["dx_disp"], b.slot,
                                   dx_add=None if g_sh is None else g_sh["dx_disp"].view(cfg.T, cfg.H))
         dlogits, dw_r, db_r = ops.moe_route_bwd(
@@ -235,8 +244,38 @@ class MoELayerGPU:
             out["dx_shared"] = g_sh["dx_disp"].view(cfg.T, cfg.H)
         return out
 
+    def forward_train(self, x: torch.Tensor):
+        """The forward of a training step: as forward (dispatched-copy path),
+        but the expert products keep their first product's planes (h and the
+        pre-activations) in the backward workspaces, so the backward that
+        follows does not recompute them."""
+        b, cfg = self.buf, self.cfg
+        if b.x_disp is None:
+            raise ValueError("forward_train needs the dispatched rows: build the layer with "
+                             "fused_gather=False")
+        if self.q is not None:
+            raise ValueError("training runs on bf16 expert weights")
+        T, H = cfg.T, cfg.H
+        if self.bws is None:
+            self.bws = ops.moe_expert_ffn_bwd_ws(b.x_disp, cfg.I)
+            if self.shared:
+                self.sh_bws = ops.moe_expert_ffn_bwd_ws(x.view(1, T, H), cfg.shared_I)
+        if self.shared:
+            ops.moe_expert_ffn_fwd_save(x.view(1, T, H), b.sh_kept, self.sw1, self.sw3, self.sw2,
+                                        self.sb1, self.sb2, self.sh_bws, act=cfg.act,
+                                        y_disp=b.sh_y)
+        self.route(x)
+        self.aux()
+        self.dispatch(x)
+        ops.moe_expert_ffn_fwd_save(b.x_disp, b.kept, self.w1, self.w3, self.w2, self.b1, self.b2,
+                                    self.bws, act=cfg.act, y_disp=b.y_disp)
+        self.combine()
+        self._saved = True
+        return b.y, b.l_aux
+
     def forward(self, x: torch.Tensor, keys: bool = False):
         """y [T, H] and L_aux [1]; every intermediate stays in self.buf."""
+        self._saved = False
         if self.shared:
             self.shared_expert(x)
         self.route(x, keys=keys)

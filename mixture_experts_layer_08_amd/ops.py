@@ -306,9 +306,12 @@ def moe_combine_bwd(dy: torch.Tensor, y_disp: torch.Tensor, slot: torch.Tensor,
 def moe_expert_ffn_bwd(x_disp: torch.Tensor, kept: torch.Tensor, w1: torch.Tensor,
                        w3: Optional[torch.Tensor], w2: torch.Tensor, b1: Optional[torch.Tensor],
                        dy_disp: torch.Tensor, *, act: str = "swiglu", has_b2: bool = True,
-                       ws: Optional[torch.Tensor] = None):
+                       ws: Optional[torch.Tensor] = None, saved: bool = False):
     """Gradients of the expert FFNs: dict with dx_disp [E, C, H] and the
-    weight (and GELU bias) gradients, all fp32."""
+    weight (and GELU bias) gradients, all fp32.  saved: ws holds the first
+    product's planes from moe_expert_ffn_fwd_save (no recompute)."""
+    if saved and ws is None:
+        raise ValueError("saved=True needs the workspace moe_expert_ffn_fwd_save filled")
     E, C, H = x_disp.shape
     I = w1.shape[2]
     dev = x_disp.device
@@ -326,9 +329,35 @@ def moe_expert_ffn_bwd(x_disp: torch.Tensor, kept: torch.Tensor, w1: torch.Tenso
                                   _ptr(kept), E, C, H, I, _ptr(w1), _ptr(w3), _ptr(w2), _ptr(b1),
                                   _ptr(dy_disp), _ptr(out["dx_disp"]), _ptr(out["dw1"]),
                                   _ptr(out["dw3"]), _ptr(out["dw2"]), _ptr(out["db1"]),
-                                  _ptr(out["db2"]), _ptr(ws), ws.numel())
+                                  _ptr(out["db2"]), _ptr(ws), ws.numel(), 1 if saved else 0)
     check("moe_expert_ffn_bwd", st)
     return out
+
+
+def moe_expert_ffn_bwd_ws(x_disp: torch.Tensor, I: int) -> torch.Tensor:
+    """A workspace for moe_expert_ffn_fwd_save / moe_expert_ffn_bwd."""
+    E, C, _ = x_disp.shape
+    return torch.empty(max(16, int(lib().moe_expert_ffn_bwd_ws_bytes(E, C, I))),
+                       dtype=torch.uint8, device=x_disp.device)
+
+
+def moe_expert_ffn_fwd_save(x_disp: torch.Tensor, kept: torch.Tensor, w1: torch.Tensor,
+                            w3: Optional[torch.Tensor], w2: torch.Tensor,
+                            b1: Optional[torch.Tensor], b2: Optional[torch.Tensor],
+                            ws: torch.Tensor, *, act: str = "swiglu",
+                            y_disp: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Training forward of the expert FFNs: y_disp [E, C, H] fp32, with the
+    first product's planes kept in ws for moe_expert_ffn_bwd(saved=True)."""
+    E, C, H = x_disp.shape
+    I = w1.shape[2]
+    dev = x_disp.device
+    y_disp = _want(y_disp, (E, C, H), torch.float32, dev)
+    st = lib().moe_expert_ffn_fwd_save(_stream(dev), _dtype_code(x_disp), ACTS[act],
+                                       _ptr(x_disp), _ptr(kept), E, C, H, I, _ptr(w1), _ptr(w3),
+                                       _ptr(w2), _ptr(b1), _ptr(b2), _ptr(y_disp), _ptr(ws),
+                                       ws.numel())
+    check("moe_expert_ffn_fwd_save", st)
+    return y_disp
 
 
 def moe_dispatch_bwd(dx_disp: torch.Tensor, slot: torch.Tensor, *,

@@ -12,7 +12,10 @@ block's RMS.  The bounds are relative to that RMS:
   * the combine weights' gradient dw, the router logits' gradient (whose
     renormalisation term cancels when a token's dw are close, so rows are
     measured against the whole matrix), dW_r and db_r: as the weights;
-plus bitwise reproducibility of two backward passes.  The routing of the
+plus bitwise reproducibility of two backward passes, and the training
+forward (forward_train: the first products' planes kept for the backward)
+giving bitwise the same expert weight gradients as the recomputing backward.
+The routing of the
 chosen seeds has no near tie, so the GPU and the oracle differentiate the
 same top-k choice (asserted).
 """
@@ -70,26 +73,31 @@ def _rows_close(got, want, rel, what):
     assert not bad.any(), f"{what}: {int(bad.sum())} rows out of tolerance (worst row {int(np.argmax(err / np.maximum(rms, 1e-30)))})"
 
 
-def _run(cfg, dl_aux=0.5):
+def _run(cfg, dl_aux=0.5, train=False):
     inp = make_inputs(cfg)
     g = np.random.default_rng(cfg.seed + 7)
     dy_bits = f32_to_bf16_bits(g.standard_normal((cfg.T, cfg.H), dtype=np.float32))
     dy64 = bf16_bits_to_f32(dy_bits).astype(np.float64)
     layer = MoELayerGPU(cfg, inp, DEV, fused_gather=False)
     x = x_to_device(inp, cfg, DEV)
-    layer.forward(x)
+    if train:
+        layer.forward_train(x)
+    else:
+        layer.forward(x)
     dy = torch.from_numpy(dy_bits.view(np.int16)).view(torch.bfloat16).to(DEV)
     grads = layer.backward(x, dy, dl_aux)
     torch.cuda.synchronize()
     return inp, layer, x, dy, dy64, grads
 
 
+@pytest.mark.parametrize("train", [False, True], ids=["recompute", "saved"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_backward_matches_oracle(name):
+def test_backward_matches_oracle(name, train):
     cfg = CASES[name]
-    log(f"[bwd] {name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} {cfg.act} {cfg.route}")
+    log(f"[bwd] {name} ({'saved' if train else 'recompute'}): T={cfg.T} H={cfg.H} I={cfg.I} "
+        f"E={cfg.E} k={cfg.k} {cfg.act} {cfg.route}")
     dl_aux = 0.5
-    inp, layer, x, dy, dy64, gg = _run(cfg, dl_aux)
+    inp, layer, x, dy, dy64, gg = _run(cfg, dl_aux, train)
     ref = B.backward(inp, cfg, dy64, dl_aux)
     r = M.route(inp, cfg)
     np.testing.assert_array_equal(np.sort(to_np(layer.buf.topk_idx), axis=1),
@@ -161,13 +169,29 @@ def test_backward_deterministic_bitwise():
             assert torch.equal(v, g2[k]), k
 
 
+@pytest.mark.parametrize("name", ["swiglu-e8-drops", "gelu-e4-shared"])
+def test_saved_planes_equal_recompute(name):
+    """forward_train keeps the same first-product planes the backward would
+    recompute (the same kernel on the same rows), so every expert weight
+    gradient is bitwise the one of the recomputing backward."""
+    cfg = CASES[name]
+    _, la, x, dy, _, g_re = _run(cfg, 0.5, train=False)
+    _, lb, _, _, _, g_sv = _run(cfg, 0.5, train=True)
+    np.testing.assert_array_equal(to_np(la.buf.kept), to_np(lb.buf.kept))
+    keys = [k for k in g_re if k.startswith(("w_", "w1", "w2", "b1", "b2", "shared_"))
+            and g_re[k] is not None]
+    assert keys
+    for k in keys:
+        assert torch.equal(g_re[k], g_sv[k]), k
+
+
 def test_backward_full_size_config2():
     """The 4096-token layer (H 2048, I 4096, E 8) at full size, every
     gradient against the float64 backward oracle."""
     from mixture_experts_layer_08_amd.synth import CONFIGS
     cfg = CONFIGS[2]
-    log("[bwd] config 2 full size")
-    inp, layer, x, dy, dy64, gg = _run(cfg, 0.5)
+    log("[bwd] config 2 full size (training forward, saved planes)")
+    inp, layer, x, dy, dy64, gg = _run(cfg, 0.5, train=True)
     r = M.route(inp, cfg)
     near = M.near_tie_tokens(r.keys, cfg.k)
     same = np.all(to_np(layer.buf.topk_idx) == r.idx, axis=1)
