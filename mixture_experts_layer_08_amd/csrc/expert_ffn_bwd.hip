@@ -35,11 +35,6 @@
 
 #include <type_traits>
 
-typedef int moe_i32x2_t __attribute__((ext_vector_type(2)));
-__device__ moe_i32x2_t buffer_load_i32x2(moe_i32x4_t rsrc, int voffset, int soffset,
-                                         int aux) __asm("llvm.amdgcn.raw.buffer.load.v2i32");
-__device__ void buffer_store_i32x2(moe_i32x2_t v, moe_i32x4_t rsrc, int voffset, int soffset,
-                                   int aux) __asm("llvm.amdgcn.raw.buffer.store.v2i32");
 
 namespace {
 

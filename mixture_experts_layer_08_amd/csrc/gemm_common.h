@@ -29,6 +29,11 @@ __device__ void buffer_store_f32(float v, moe_i32x4_t rsrc, int voffset, int sof
                                  int aux) __asm("llvm.amdgcn.raw.buffer.store.f32");
 __device__ void buffer_store_f32x4(moe::f32x4_t v, moe_i32x4_t rsrc, int voffset, int soffset,
                                    int aux) __asm("llvm.amdgcn.raw.buffer.store.v4f32");
+typedef int moe_i32x2_t __attribute__((ext_vector_type(2)));
+__device__ void buffer_store_i32x2(moe_i32x2_t v, moe_i32x4_t rsrc, int voffset, int soffset,
+                                   int aux) __asm("llvm.amdgcn.raw.buffer.store.v2i32");
+__device__ moe_i32x2_t buffer_load_i32x2(moe_i32x4_t rsrc, int voffset, int soffset,
+                                         int aux) __asm("llvm.amdgcn.raw.buffer.load.v2i32");
 
 namespace {
 
