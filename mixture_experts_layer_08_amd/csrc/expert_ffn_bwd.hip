@@ -105,6 +105,10 @@ struct BTile {
 template <int SCHED, int EPI>
 __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs g) {
     constexpr bool KC = SCHED == SCHED_DGRAD;   // both operands k-contiguous
+    // dh epilogues run with the operands swapped (four consecutive columns
+    // per lane: vector side reads); fp32 outputs keep the plain layout, whose
+    // stores cover 128 contiguous bytes of a row per half-wave
+    constexpr bool SWAP = EPI != EPI_F32;
     constexpr int kStage = 2 * kStageA;         // A 32 KB + B 32 KB
     constexpr int WM_ROWS = kBM / kWMn, WN_COLS = kBNMax / kWN;
     constexpr int TM = WM_ROWS / 32, TN = WN_COLS / 32;
@@ -290,8 +294,10 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ss][j], af[ss][i],
-                                                                            acc[i][j], 0, 0, 0);
+                        acc[i][j] = SWAP ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                               bfr[ss][j], af[ss][i], acc[i][j], 0, 0, 0)
+                                         : __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                               af[ss][i], bfr[ss][j], acc[i][j], 0, 0, 0);
         };
         // The forward's pipeline: one barrier per k-step, the second half of
         // step kt read while the first half's MFMAs run, step kt+2's loads
@@ -369,33 +375,33 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
             break;
         }
 
-        // epilogue.  The products run with the operands swapped (C^T = B^T
-        // A^T), so accumulator element q of lane l is output row l%32 and
+        // epilogue.  The dh products run with the operands swapped (C^T =
+        // B^T A^T), so accumulator element q of lane l is output row l%32 and
         // column 8*(q/4) + 4*(l/32) + q%4 of its 32 x 32 block: four
-        // consecutive columns per lane, stored (and, for dh, read) as one
-        // 16- or 8-byte access.  Descriptors end at the last valid row, so
-        // padding rows are neither read nor written.
+        // consecutive columns per lane, read (g, u or z) and written (dg, du
+        // or dz) as one 8-byte access each.  fp32 outputs use the plain
+        // layout.  Descriptors end at the last valid row, so padding rows are
+        // neither read nor written.
         {
             const int R = KC ? (int)g.C : g.M;  // rows of the output per expert
             const size_t obase = ((size_t)cur.e * R + cur.m0) * g.N + cur.n0;
             const uint32_t obytes = (uint32_t)(((size_t)cur.rows * g.N - cur.n0));
             const int vel = (wm * WM_ROWS + lane % 32) * g.N + wn * WN_COLS + (lane / 32) * 4;
             if (EPI == EPI_F32) {
+                // plain layout: element q of lane l is row 8*(q/4) + 4*(l/32) +
+                // q%4, column l%32 of its 32 x 32 block
                 const i32x4_t rsO = make_rsrc(static_cast<float*>(g.out) + obase, obytes * 4);
+                const int row_l = wm * WM_ROWS + (lane / 32) * 4;
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
+                for (int j = 0; j < TN; ++j) {
+                    const int voff = (row_l * g.N + wn * WN_COLS + j * 32 + lane % 32) * 4;
 #pragma unroll
-                    for (int j = 0; j < TN; ++j)
+                    for (int i = 0; i < TM; ++i)
 #pragma unroll
-                        for (int qq = 0; qq < 4; ++qq) {
-                            f32x4_t v;
-                            v.x = acc[i][j][qq * 4 + 0];
-                            v.y = acc[i][j][qq * 4 + 1];
-                            v.z = acc[i][j][qq * 4 + 2];
-                            v.w = acc[i][j][qq * 4 + 3];
-                            buffer_store_f32x4(v, rsO, vel * 4,
-                                               (i * 32 * g.N + j * 32 + qq * 8) * 4, 0);
-                        }
+                        for (int q = 0; q < 16; ++q)
+                            buffer_store_f32(acc[i][j][q], rsO, voff,
+                                             ((i * 32 + (q / 4) * 8 + (q % 4)) * g.N) * 4, 0);
+                }
             } else {
                 const i32x4_t rsO = make_rsrc(static_cast<uint16_t*>(g.out) + obase, obytes * 2);
                 const i32x4_t rs0 = make_rsrc(g.side0 + obase, obytes * 2);
@@ -494,19 +500,30 @@ __global__ __launch_bounds__(256) void bwd_tail_reduce_kernel(BwdArgs g, int G) 
         const int wm = vwave / kWN, wn = vwave % kWN;
         const int m0 = m_tile * kBM, n0 = n_tile * kBNMax;
         if (m0 + wm * WM_ROWS + i * 32 >= kept) continue;  // block past kept: no partials stored
-        const int row = m0 + wm * WM_ROWS + i * 32 + vlane % 32;
-        if (row >= kept) continue;                         // not an output row
-        const int col = n0 + wn * WN_COLS + j * 32 + 8 * q4 + 4 * (vlane / 32);
         const size_t base = (size_t)t * splits * PSTRIDE + (size_t)gi * kGThreads + vt;
         float4 s = part[base];
         for (int pc = 1; pc < splits; ++pc) {
             const float4 v = part[base + pc * PSTRIDE];
             s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
         }
-        const size_t o = ((size_t)e * g.C + row) * g.N + col;
         if (EPI == EPI_F32) {
-            *reinterpret_cast<float4*>(static_cast<float*>(g.out) + o) = s;
-        } else {
+            // plain layout: the group holds rows row0 .. row0+3 of one column
+            const int row0 = m0 + wm * WM_ROWS + i * 32 + 8 * q4 + 4 * (vlane / 32);
+            const int col = n0 + wn * WN_COLS + j * 32 + vlane % 32;
+            const float v4[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (row0 + u >= kept) break;                // not an output row
+                static_cast<float*>(g.out)[((size_t)e * g.C + row0 + u) * g.N + col] = v4[u];
+            }
+            continue;
+        }
+        // swapped layout: the group holds four consecutive columns of one row
+        const int row = m0 + wm * WM_ROWS + i * 32 + vlane % 32;
+        if (row >= kept) continue;                         // not an output row
+        const int col = n0 + wn * WN_COLS + j * 32 + 8 * q4 + 4 * (vlane / 32);
+        const size_t o = ((size_t)e * g.C + row) * g.N + col;
+        {
             const float dh[4] = {s.x, s.y, s.z, s.w};
             const uint2 wa = *reinterpret_cast<const uint2*>(g.side0 + o);
             uint2 wu = make_uint2(0u, 0u);
