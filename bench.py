@@ -2,9 +2,10 @@
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--gpus 1]
 
-A step is one whole layer forward (route, aux statistics, dispatch of the
-row maps, the grouped expert GEMM whose first product gathers its rows from x,
-combine) over one batch of synthetic input that is already resident in HBM.
+A step is one whole layer forward (route, dispatch of the row maps with the
+aux statistics in the same pass, the grouped expert GEMM whose first product
+gathers its rows from x, combine) over one batch of synthetic input that is
+already resident in HBM.
 The default workload is the 2 x 2048-token layer (hidden 2048, SwiGLU
 intermediate 4096, 8 experts, top-2, capacity factor 1.25, bf16 with fp32
 accumulation); --config 6 is the drop-free 64-token decode step on the same
@@ -90,14 +91,13 @@ def algorithmic_work(cfg, kept: np.ndarray, dropped: int, weights: str = "bf16")
     if weights == "fp8":  # the per-column fp32 scales
         ffn_bytes += active * ((n_mats - 1) * I + H) * 4
     route_bytes = T * H * esz + H * E * esz + T * k * 8 + T * E * 4
-    aux_bytes = T * k * 4 + T * E * 4
     # fused-gather layer: dispatch only maps rows (idx read, slot + slot_token
-    # written); the row copy happens inside the first expert product's loads
-    dispatch_bytes = T * k * 4 + T * k * 4 + n_kept * 4
+    # written; the row copy happens inside the first expert product's loads),
+    # and it computes the aux statistics in the same pass (probs read once)
+    dispatch_bytes = T * k * 4 + T * k * 4 + n_kept * 4 + T * E * 4
     # kept expert rows (fp32) read once, y written once, slot + weights read
     combine_bytes = n_kept * H * 4 + T * H * esz + T * k * 8
     return dict(n_kept=n_kept, ffn_flop=ffn_flop, ffn_bytes=ffn_bytes, route_bytes=route_bytes,
-                aux_bytes=aux_bytes,
                 dispatch_bytes=dispatch_bytes, combine_bytes=combine_bytes, dropped=dropped)
 
 
@@ -302,26 +302,24 @@ def main():
     # the same K steps again with HIP events between the phases (on the launch
     # stream) for the per-phase times; the events add a little time per step,
     # so this loop does not set ms_per_step
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     torch.cuda.synchronize()
     for s in range(K):
         e = ev[s]
         e[0].record(stream)
         layer.route(x)
         e[1].record(stream)
-        layer.aux()
+        layer.dispatch_aux(x)
         e[2].record(stream)
-        layer.dispatch(x)
-        e[3].record(stream)
         layer.experts(x)
-        e[4].record(stream)
+        e[3].record(stream)
         layer.combine()
-        e[5].record(stream)
+        e[4].record(stream)
     torch.cuda.synchronize()
-    names = ["route", "aux", "dispatch", "expert_ffn", "combine"]
+    names = ["route", "dispatch", "expert_ffn", "combine"]
     ph = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)]))
           for i, n in enumerate(names)}
-    dev_ms = float(np.mean([ev[s][0].elapsed_time(ev[s][5]) for s in range(K)]))
+    dev_ms = float(np.mean([ev[s][0].elapsed_time(ev[s][4]) for s in range(K)]))
     ms_per_step = wall * 1e3 / K
     print(f"[bench] timed {K} steps: {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
 
@@ -332,7 +330,7 @@ def main():
     # memory-bound phases in isolation, after flushing the Infinity Cache
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     iso = {}
-    for n, fn in (("route", lambda: layer.route(x)), ("dispatch", lambda: layer.dispatch(x)),
+    for n, fn in (("route", lambda: layer.route(x)), ("dispatch", lambda: layer.dispatch_aux(x)),
                   ("combine", layer.combine)):
         ts = []
         for _ in range(args.iso_reps):
@@ -360,7 +358,7 @@ def main():
     achieved_tflops = work["ffn_flop"] / (gemm_ms * 1e-3) / 1e12
     phases = {}
     for n, key in (("route", "route_bytes"), ("dispatch", "dispatch_bytes"),
-                   ("combine", "combine_bytes"), ("aux", "aux_bytes")):
+                   ("combine", "combine_bytes")):
         gbs = work[key] / (ph[n] * 1e-3) / 1e9
         phases[n] = {"ms": round(ph[n], 5), "bytes": work[key], "GB/s": round(gbs, 1),
                      "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
@@ -419,7 +417,7 @@ def main():
                    "tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I, "experts": cfg.E,
                    "top_k": cfg.k, "capacity_factor": cfg.cf,
                    "capacity": layer.C, "kept_rows": work["n_kept"], "dropped": dropped,
-                   "path": "route, aux, dispatch (row maps), gather-fused expert products, "
+                   "path": "route, dispatch (row maps) with aux statistics, gather-fused expert products, "
                            "combine"},
         "roofline": roofline,
         "phases": phases,

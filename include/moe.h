@@ -159,6 +159,23 @@ moe_status_t moe_dispatch(void* stream, moe_dtype_t dtype, const void* x,
                           int32_t* slot_token, int32_t* kept, int32_t* dropped,
                           void* ws, size_t ws_bytes);
 
+/* Dispatch and aux statistics in one pass: the outputs of moe_dispatch and of
+ * moe_aux_stats (same arguments, same meanings: probs [T, E] fp32 and alpha
+ * as for moe_aux_stats; counts, f, p, l_aux out) from the same launches —
+ * the histogram blocks also sum their tokens' probabilities and the scan
+ * block finishes the statistics, both in a fixed order (fp64 partial sums).
+ * [P2] sections 2.3 and 2.4, [P1] sections 2.4 and 3.2.
+ *   ws  workspace of at least moe_workspace_bytes(T, E, k) bytes, 16-byte
+ *       aligned
+ * In addition T * E must be below 2^31. */
+moe_status_t moe_dispatch_aux(void* stream, moe_dtype_t dtype, const void* x,
+                              const int32_t* topk_idx, const float* probs,
+                              int64_t T, int64_t H, int E, int k, int64_t C,
+                              float alpha, void* x_disp, int32_t* slot,
+                              int32_t* slot_token, int32_t* kept, int32_t* dropped,
+                              int32_t* counts, float* f, float* p, float* l_aux,
+                              void* ws, size_t ws_bytes);
+
 /* Expert FFNs as one grouped GEMM over the dispatched rows.
  * [P2] sections 2.2 and 3.1 (each expert is an FFN; GELU expert with two
  * biased Linears), [P5] section 2.1 (SwiGLU), [P2] section 4.4 / [P5] 6.3

@@ -19,6 +19,11 @@
 //  4. copy: token-major gather of x rows into x_disp, one 16-byte vector per
 //     lane, each row read once and written to each of its kept slots
 //     (bandwidth-bound; many blocks so all CUs stream).
+// moe_dispatch_aux also produces the load-balancing statistics ([P2]
+// section 2.3, [P1] section 3.2) in the same launches: the histogram blocks
+// sum their tokens' router probabilities per expert as well, and the scan
+// block, which already totals each expert's assignments, finishes f, P and
+// L_aux from those totals and partial sums (both in block order).
 #include "moe_common.h"
 
 namespace {
@@ -43,6 +48,98 @@ __global__ __launch_bounds__(kDThreads) void disp_hist_kernel(const int32_t* __r
     }
     __syncthreads();
     if (threadIdx.x < E) hist[(size_t)blockIdx.x * E + threadIdx.x] = cnt[threadIdx.x];
+}
+
+// The histogram of disp_hist_kernel plus, per block, the column sums of the
+// router probabilities of its tokens (token t belongs to the block holding
+// its first assignment t*k), in double.
+__global__ __launch_bounds__(kDThreads) void disp_hist_aux_kernel(
+    const int32_t* __restrict__ idx, const float* __restrict__ probs, int64_t A, int E, int k,
+    int32_t* __restrict__ hist, double* __restrict__ psum) {
+    __shared__ int cnt[MOE_MAX_EXPERTS];
+    __shared__ double colsum[kDThreads];
+    const int tid = threadIdx.x;
+    if (tid < E) cnt[tid] = 0;
+    __syncthreads();
+    const int64_t a0 = (int64_t)blockIdx.x * kDChunk;
+    int64_t a1 = a0 + kDChunk;
+    if (a1 > A) a1 = A;
+    for (int64_t a = a0 + tid; a < a1; a += kDThreads) {
+        const unsigned e = (unsigned)idx[a];
+        if (e < (unsigned)E) atomicAdd(&cnt[e], 1);
+    }
+    // tokens ceil(a0/k) .. ceil(a1/k)-1; thread (r, e) strides over them
+    const int64_t t0 = (a0 + k - 1) / k, t1 = (a1 + k - 1) / k;
+    const int rows = kDThreads / E;
+    const int r = tid / E, e = tid % E;
+    double sacc = 0.0;
+    if (r < rows)
+        for (int64_t t = t0 + r; t < t1; t += rows) sacc += (double)probs[t * E + e];
+    colsum[tid] = sacc;
+    __syncthreads();
+    if (tid < E) {
+        double acc = 0.0;
+        for (int rr = 0; rr < rows; ++rr) acc += colsum[rr * E + tid];
+        psum[(size_t)blockIdx.x * E + tid] = acc;
+        hist[(size_t)blockIdx.x * E + tid] = cnt[tid];
+    }
+}
+
+// The scan of disp_scan_kernel plus the statistics: counts[e] = the
+// expert's assignments before the drop, f = counts/(T k), P = (sum of the
+// block partials)/T, L_aux = alpha E sum_e f P.
+__global__ __launch_bounds__(MOE_MAX_EXPERTS) void disp_scan_aux_kernel(
+    const int32_t* __restrict__ hist, const double* __restrict__ psum, int nb, int E, int64_t C,
+    int64_t T, int k, float alpha, int32_t* __restrict__ off, int32_t* __restrict__ kept,
+    int32_t* __restrict__ dropped, int32_t* __restrict__ counts, float* __restrict__ f,
+    float* __restrict__ p, float* __restrict__ l_aux) {
+    __shared__ int64_t over[MOE_MAX_EXPERTS];
+    __shared__ double fp[MOE_MAX_EXPERTS];
+    const int e = threadIdx.x;
+    if (e < E) {
+        int64_t run = 0;
+        double ps = 0.0;
+        int b = 0;
+        for (; b + 8 <= nb; b += 8) {  // eight independent loads in flight, used in block order
+            int h[8];
+            double q[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                h[u] = hist[(size_t)(b + u) * E + e];
+                q[u] = psum[(size_t)(b + u) * E + e];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                off[(size_t)(b + u) * E + e] = (int32_t)run;
+                run += h[u];
+                ps += q[u];
+            }
+        }
+        for (; b < nb; ++b) {
+            off[(size_t)b * E + e] = (int32_t)run;
+            run += hist[(size_t)b * E + e];
+            ps += psum[(size_t)b * E + e];
+        }
+        kept[e] = (int32_t)(run < C ? run : C);
+        over[e] = run > C ? run - C : 0;
+        const double fe = T > 0 ? (double)run / ((double)T * k) : 0.0;
+        const double pe = T > 0 ? ps / (double)T : 0.0;
+        counts[e] = (int32_t)run;
+        f[e] = (float)fe;
+        p[e] = (float)pe;
+        fp[e] = fe * pe;
+    }
+    __syncthreads();
+    if (e == 0) {
+        int64_t d = 0;
+        double acc = 0.0;
+        for (int i = 0; i < E; ++i) {
+            d += over[i];
+            acc += fp[i];
+        }
+        *dropped = (int32_t)d;
+        *l_aux = (float)((double)alpha * E * acc);
+    }
 }
 
 __global__ __launch_bounds__(MOE_MAX_EXPERTS) void disp_scan_kernel(const int32_t* __restrict__ hist,
@@ -193,6 +290,13 @@ size_t moe_dispatch_ws_bytes(int64_t T, int E, int k) {
     return (size_t)nb * E * 2 * sizeof(int32_t) + 256;
 }
 
+// moe_dispatch_aux: the dispatch workspace, then nb * E double partial sums
+size_t moe_dispatch_aux_ws_bytes(int64_t T, int E, int k) {
+    const int nb = disp_blocks(T * k);
+    return ((size_t)nb * E * 2 * sizeof(int32_t) + 255) / 256 * 256 + (size_t)nb * E * sizeof(double) +
+           256;
+}
+
 extern "C" moe_status_t moe_dispatch(void* stream, moe_dtype_t dtype, const void* x,
                                      const int32_t* topk_idx, int64_t T, int64_t H, int E, int k,
                                      int64_t C, void* x_disp, int32_t* slot, int32_t* slot_token,
@@ -233,6 +337,60 @@ extern "C" moe_status_t moe_dispatch(void* stream, moe_dtype_t dtype, const void
                                (int64_t)0, E, k, C, off, kept, slot, slot_token);
             MOE_CHECK_LAUNCH();
         }
+    }
+    if (T > 0 && C > 0 && x_disp) {
+        const int row_vecs = (int)(H * esz / 16);
+        const int64_t grid = (T + kCopyTok - 1) / kCopyTok;
+        hipLaunchKernelGGL(disp_copy_kernel, dim3((unsigned)grid), dim3(kDThreads), 0, st,
+                           static_cast<const uint4*>(x), slot, T, k, row_vecs,
+                           static_cast<uint4*>(x_disp));
+        MOE_CHECK_LAUNCH();
+    }
+    return MOE_OK;
+}
+
+// Dispatch and the load-balancing statistics in one pass over the routing.
+extern "C" moe_status_t moe_dispatch_aux(void* stream, moe_dtype_t dtype, const void* x,
+                                         const int32_t* topk_idx, const float* probs, int64_t T,
+                                         int64_t H, int E, int k, int64_t C, float alpha,
+                                         void* x_disp, int32_t* slot, int32_t* slot_token,
+                                         int32_t* kept, int32_t* dropped, int32_t* counts,
+                                         float* f, float* p, float* l_aux, void* ws,
+                                         size_t ws_bytes) {
+    if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_DTYPE;
+    if (T < 0 || H <= 0 || E < 1 || k < 1 || k > E || C < 0) return MOE_ERR_SHAPE;
+    if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+    if (T * k >= ((int64_t)1 << 31) || (int64_t)E * C >= ((int64_t)1 << 31) ||
+        T * E >= ((int64_t)1 << 31))
+        return MOE_ERR_UNSUPPORTED;
+    const int esz = dtype == MOE_BF16 ? 2 : 4;
+    if ((H * esz) % 16) return MOE_ERR_ALIGN;
+    if (!kept || !dropped || !counts || !f || !p || !l_aux) return MOE_ERR_NULL;
+    if (T > 0 && (!topk_idx || !slot || !probs)) return MOE_ERR_NULL;
+    if (C > 0 && !slot_token) return MOE_ERR_NULL;
+    if (T > 0 && x_disp && !x) return MOE_ERR_NULL;  // x_disp NULL: indices only, no copy
+    if ((x && !moe_aligned16(x)) || (x_disp && !moe_aligned16(x_disp))) return MOE_ERR_ALIGN;
+    if (!ws || ws_bytes < moe_dispatch_aux_ws_bytes(T, E, k)) return MOE_ERR_WORKSPACE;
+    if (!moe_aligned16(ws)) return MOE_ERR_ALIGN;
+    const int64_t A = T * k;
+    const int nb = disp_blocks(A);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t* hist = static_cast<int32_t*>(ws);
+    int32_t* off = hist + (size_t)nb * E;
+    double* psum = reinterpret_cast<double*>(static_cast<unsigned char*>(ws) +
+                                             ((size_t)nb * E * 2 * sizeof(int32_t) + 255) / 256 * 256);
+    if (nb > 0) {
+        hipLaunchKernelGGL(disp_hist_aux_kernel, dim3(nb), dim3(kDThreads), 0, st, topk_idx, probs,
+                           A, E, k, hist, psum);
+        MOE_CHECK_LAUNCH();
+    }
+    hipLaunchKernelGGL(disp_scan_aux_kernel, dim3(1), dim3(MOE_MAX_EXPERTS), 0, st, hist, psum, nb, E,
+                       C, T, k, alpha, off, kept, dropped, counts, f, p, l_aux);
+    MOE_CHECK_LAUNCH();
+    if (nb > 0 || C > 0) {
+        hipLaunchKernelGGL(disp_rank_kernel, dim3(nb > 0 ? nb : 1), dim3(kDThreads), 0, st,
+                           topk_idx, A, E, k, C, off, kept, slot, slot_token);
+        MOE_CHECK_LAUNCH();
     }
     if (T > 0 && C > 0 && x_disp) {
         const int row_vecs = (int)(H * esz / 16);

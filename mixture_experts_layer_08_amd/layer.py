@@ -1,4 +1,6 @@
-"""The whole layer forward as the five library calls on one stream.
+"""The whole layer forward as library calls on one stream: route,
+dispatch with the aux statistics (moe_dispatch_aux), the expert products,
+combine.
 
 `MoELayerGPU` owns the device weights and every intermediate buffer of one
 layer shape, allocated once, so a forward call enqueues only kernels: no
@@ -165,6 +167,15 @@ class MoELayerGPU:
                                 slot_token=b.slot_token, kept=b.kept, dropped=b.dropped,
                                 copy=not self.fused_gather)
 
+    def dispatch_aux(self, x: torch.Tensor):
+        """dispatch() and aux() in one pass over the routing (the forward's
+        path: the statistics come out of the dispatch launches)."""
+        b, cfg = self.buf, self.cfg
+        return ops.moe_dispatch_aux(x, b.topk_idx, b.probs, cfg.E, self.C, cfg.alpha, ws=b.ws,
+                                    x_disp=b.x_disp, slot=b.slot, slot_token=b.slot_token,
+                                    kept=b.kept, dropped=b.dropped, counts=b.counts, f=b.f, p=b.p,
+                                    l_aux=b.l_aux, copy=not self.fused_gather)
+
     def experts(self, x: Optional[torch.Tensor] = None):
         """x (the token activations) is needed with fused_gather."""
         b = self.buf
@@ -265,8 +276,7 @@ class MoELayerGPU:
                                         self.sb1, self.sb2, self.sh_bws, act=cfg.act,
                                         y_disp=b.sh_y)
         self.route(x)
-        self.aux()
-        self.dispatch(x)
+        self.dispatch_aux(x)
         ops.moe_expert_ffn_fwd_save(b.x_disp, b.kept, self.w1, self.w3, self.w2, self.b1, self.b2,
                                     self.bws, act=cfg.act, y_disp=b.y_disp)
         self.combine()
@@ -279,8 +289,7 @@ class MoELayerGPU:
         if self.shared:
             self.shared_expert(x)
         self.route(x, keys=keys)
-        self.aux()
-        self.dispatch(x)
+        self.dispatch_aux(x)
         self.experts(x)
         self.combine()
         return self.buf.y, self.buf.l_aux

@@ -119,6 +119,34 @@ def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, C: int, *,
     return x_disp, slot, slot_token, kept, dropped
 
 
+def moe_dispatch_aux(x: torch.Tensor, topk_idx: torch.Tensor, probs: torch.Tensor, E: int, C: int,
+                     alpha: float, *, ws: Optional[torch.Tensor] = None, x_disp=None, slot=None,
+                     slot_token=None, kept=None, dropped=None, counts=None, f=None, p=None,
+                     l_aux=None, copy: bool = True):
+    """moe_dispatch and moe_aux_stats in one pass: (x_disp, slot, slot_token,
+    kept, dropped, counts, f, p, l_aux)."""
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    dev = x.device
+    x_disp = _want(x_disp, (E, C, H), x.dtype, dev) if copy else None
+    slot = _want(slot, (T, k), torch.int32, dev)
+    slot_token = _want(slot_token, (E, C), torch.int32, dev)
+    kept = _want(kept, (E,), torch.int32, dev)
+    dropped = _want(dropped, (1,), torch.int32, dev)
+    counts = _want(counts, (E,), torch.int32, dev)
+    f = _want(f, (E,), torch.float32, dev)
+    p = _want(p, (E,), torch.float32, dev)
+    l_aux = _want(l_aux, (1,), torch.float32, dev)
+    if ws is None:
+        ws = torch.empty(max(16, moe_workspace_bytes(T, E, k)), dtype=torch.uint8, device=dev)
+    st = lib().moe_dispatch_aux(_stream(dev), _dtype_code(x), _ptr(x), _ptr(topk_idx), _ptr(probs),
+                                T, H, E, k, C, float(alpha), _ptr(x_disp), _ptr(slot),
+                                _ptr(slot_token), _ptr(kept), _ptr(dropped), _ptr(counts), _ptr(f),
+                                _ptr(p), _ptr(l_aux), _ptr(ws), ws.numel())
+    check("moe_dispatch_aux", st)
+    return x_disp, slot, slot_token, kept, dropped, counts, f, p, l_aux
+
+
 def moe_expert_ffn_ws_bytes() -> int:
     return int(lib().moe_expert_ffn_ws_bytes())
 

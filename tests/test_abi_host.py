@@ -219,6 +219,27 @@ def test_fp8_argument_errors(L):
                                        P, None, None, P, P, None, 0) == NULL
 
 
+def test_dispatch_aux_argument_errors(L):
+    ws_ok = L.moe_workspace_bytes(64, 8, 2)
+
+    def d(**kw):
+        return L.moe_dispatch_aux(None, kw.get("dtype", 1), kw.get("x", P), kw.get("idx", P),
+                                  kw.get("probs", P), kw.get("T", 64), kw.get("H", 256),
+                                  kw.get("E", 8), kw.get("k", 2), kw.get("C", 20), 0.01,
+                                  kw.get("xd", P), P, P, P, P, kw.get("counts", P), P, P, P,
+                                  kw.get("ws", P), kw.get("wsb", ws_ok))
+    assert d(dtype=7) == DTYPE
+    assert d(k=9) == SHAPE
+    assert d(E=65, k=2) == UNSUP
+    assert d(H=4) == ALIGN
+    assert d(probs=None) == NULL
+    assert d(counts=None) == NULL
+    assert d(ws=None) == WS
+    assert d(wsb=16) == WS
+    assert d(ws=MIS) == ALIGN
+    assert d(xd=MIS) == ALIGN
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))

@@ -237,11 +237,16 @@ def test_empty_and_degenerate_calls():
     counts, f, pp, l_aux = ops.moe_aux_stats(idx, p, E, 0.01)
     x_disp, slot, slot_token, kept, dropped = ops.moe_dispatch(x, idx, E, 3)
     y = ops.moe_combine(torch.zeros((0, H), dtype=torch.float32, device=DEV), slot, w)
+    fused = ops.moe_dispatch_aux(x, idx, p, E, 3, 0.01)
     torch.cuda.synchronize()
     assert y.shape == (0, H)
     assert to_np(counts).tolist() == [0] * E and float(to_np(l_aux)[0]) == 0.0
     assert to_np(kept).tolist() == [0] * E and int(to_np(dropped)[0]) == 0
     assert np.all(to_np(slot_token) == -1)
+    _, _, st_f, kept_f, drop_f, cnt_f, f_f, p_f, la_f = fused
+    assert np.all(to_np(st_f) == -1) and to_np(kept_f).tolist() == [0] * E
+    assert int(to_np(drop_f)[0]) == 0 and to_np(cnt_f).tolist() == [0] * E
+    assert np.all(to_np(f_f) == 0) and np.all(to_np(p_f) == 0) and float(to_np(la_f)[0]) == 0.0
     # C = 0: everything dropped, outputs exactly zero
     cfg = MoEConfig("c0", "bf16", T=40, H=256, I=128, E=4, k=2, cf=1.0, seed=3)
     inp = make_inputs(cfg)
@@ -300,6 +305,15 @@ def test_dispatch_and_aux_both_sizes(T, E, k, cf):
     st = d.slot_token.reshape(-1)
     rows = np.where(st >= 0)[0]
     np.testing.assert_array_equal(xd[rows], to_np(x)[st[rows]])
+    # the fused pass (dispatch and statistics from the same launches)
+    xf, slf, stf, kf, df, cf_, ff, pf, lf = ops.moe_dispatch_aux(x, idx_d, probs_d, E, C, 0.01)
+    torch.cuda.synchronize()
+    _dispatch_compare((to_np(slf), to_np(stf), to_np(kf), to_np(df)), d, f"fused T={T}")
+    np.testing.assert_array_equal(to_np(cf_), a.counts)
+    np.testing.assert_array_equal(to_np(ff), to_np(f))   # the same count / (T k)
+    assert_rel(to_np(pf), a.P, 1e-5, "fused p")
+    assert_rel(to_np(lf), [a.l_aux], 1e-5, "fused L_aux")
+    np.testing.assert_array_equal(to_np(xf).reshape(E * C, H)[rows], to_np(x)[st[rows]])
 
 
 @pytest.mark.parametrize("T", [1, 16, 64, 256])
