@@ -98,6 +98,7 @@ struct GemmArgs {
     // split-K of the last, partly filled round of tiles (null part: off)
     float* part;            // per-piece fp32 partial tiles, kPartBytes each
     int smax;               // at most this many pieces per tile
+    int minsteps;           // each piece keeps at least this many k-steps (set at launch)
     uint16_t* save0;        // *_SAVE modes: [E, C, N_out] g (or z)
     uint16_t* save1;        // SwiGLU: [E, C, N_out] u
     // 8-bit weights: e4m3 codes [E, N, K] (in place of B0 / B1) and the
@@ -112,20 +113,79 @@ constexpr size_t kPartBytes = (size_t)kBM * kBNMax * 4;  // one fp32 tile
 constexpr int kSMax = 4;  // most pieces per split tile
 
 // ---------------------------------------------------------- tile schedule --
-// Expert e owns tiles s_pref[e] .. s_pref[e+1]-1: ceil(kept[e] / kBM) row
-// tiles times NT column tiles.  Run by one thread.
-__device__ void build_prefix(const GemmArgs& g, int NT, int BM, int* s_pref, int* s_mt) {
-    int cum = 0;
-    for (int e = 0; e < g.E; ++e) {
-        int kp = g.kept[e];
-        if (kp < 0) kp = 0;
-        if (kp > g.C) kp = (int)g.C;
-        const int mt = (kp + BM - 1) / BM;
-        s_mt[e] = mt;
-        s_pref[e] = cum;
-        cum += mt * NT;
+// Expert e has ceil(kept[e] / BM) row tiles times NT column tiles.  A last
+// row tile with at most thin_rows rows (thin) costs nearly a whole tile's
+// loads for little MFMA work, so the schedule puts every expert's other tiles
+// first (the main run, expert by expert) and the thin tiles after them (the
+// thin run, expert by expert, columns in order): the thin tiles then fall in
+// the last, partly filled round, which is cut along K.  The schedule is held
+// in registers by every wave of a workgroup: lane e < E holds expert e's
+// values and the ends of its two runs (inclusive prefix sums over the lanes).
+struct WaveSched {
+    int kp;          // kept[e], clamped to [0, C]
+    int mt;          // row tiles in the main run
+    int end;         // end of expert e's main run
+    int tend;        // end of expert e's part of the thin run
+    int main_total;  // tiles of the main run (wave-uniform)
+    int total;       // all tiles (wave-uniform)
+};
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(v, d, 64);
+        if (lane >= d) v += u;
     }
-    s_pref[g.E] = cum;
+    return v;
+}
+__device__ __forceinline__ WaveSched wave_sched(const GemmArgs& g, int NT, int BM, int thin_rows,
+                                                int lane) {
+    WaveSched w;
+    int kp = lane < g.E ? g.kept[lane] : 0;
+    if (kp < 0) kp = 0;
+    if (kp > g.C) kp = (int)g.C;
+    w.kp = kp;
+    const int mt_all = (kp + BM - 1) / BM;
+    const int thin = (mt_all > 0 && kp - (mt_all - 1) * BM <= thin_rows) ? 1 : 0;
+    w.mt = mt_all - thin;
+    w.end = wave_incl_scan(w.mt * NT, lane);
+    w.tend = wave_incl_scan(thin * NT, lane);
+    w.main_total = __builtin_amdgcn_readlane(w.end, 63);
+    w.total = w.main_total + __builtin_amdgcn_readlane(w.tend, 63);
+    return w;
+}
+
+// Tile `logical` -> expert and row / column tile.  In the main run, inside
+// an expert, tiles run in groups of every row tile times gn column tiles
+// (about GEMM_GROUP tiles), column-fastest, so one XCD's run of tiles shares
+// A rows and B panels in its L2.  The expert is the number of experts whose
+// run ends at or before the tile.  Every lane of the wave must be active.
+__device__ __forceinline__ void map_tile_w(int logical, const WaveSched& w, int E, int NT, int lane,
+                                           int& e, int& m_tile, int& n_tile) {
+    if (logical < w.main_total) {
+        e = (int)__popcll(__ballot(lane < E && w.end <= logical));
+        if (e > E - 1) e = E - 1;
+        e = __builtin_amdgcn_readfirstlane(e);
+        const int start = e > 0 ? __builtin_amdgcn_readlane(w.end, e - 1) : 0;
+        const int mt = __builtin_amdgcn_readlane(w.mt, e);
+        const int local = logical - start;
+        int gn = GEMM_GROUP / mt;
+        if (gn < 1) gn = 1;
+        if (gn > NT) gn = NT;
+        const int grp = local / (mt * gn);
+        int width = NT - grp * gn;
+        if (width > gn) width = gn;
+        const int rem = local - grp * mt * gn;
+        m_tile = rem / width;
+        n_tile = grp * gn + rem % width;
+    } else {
+        const int t = logical - w.main_total;
+        e = (int)__popcll(__ballot(lane < E && w.tend <= t));
+        if (e > E - 1) e = E - 1;
+        e = __builtin_amdgcn_readfirstlane(e);
+        const int start = e > 0 ? __builtin_amdgcn_readlane(w.tend, e - 1) : 0;
+        m_tile = __builtin_amdgcn_readlane(w.mt, e);  // the thin tile follows the main ones
+        n_tile = t - start;
+    }
 }
 
 // Whole tiles fill total / G rounds of a G-workgroup launch.  When the last
@@ -137,27 +197,40 @@ __device__ __forceinline__ int tail_splits(const GemmArgs& g, int total, int G, 
     int sp = G / remt;
     if (sp > g.smax) sp = g.smax;
     if (sp > kSMax) sp = kSMax;
-    if (sp > nk / 2) sp = nk / 2;  // each piece keeps at least two k-steps
+    if (sp > nk / g.minsteps) sp = nk / g.minsteps;  // the k pipeline's lookahead
     return sp < 1 ? 1 : sp;
 }
 
-
-// THIN: 64-row tiles (every expert has at most 64 rows, as in a decode step)
-// with three LDS stages, so two k-steps of loads are in flight while one is
-// read: a thin tile does little MFMA work per k-step, and with two stages
-// each k-step would wait a whole load round trip.
-template <int MODE, int BN, bool F8 = false, bool THIN = false>
+// LDS holds NA slots of A k-steps, then NB slots of B k-steps; stream step
+// p of a workgroup (its tiles' k-steps one after another) uses A slot p % NA
+// and B slot p % NB.
+//   * default: two slots each; the loads of step p+2 are issued once every
+//     wave is done with step p, so one k-step of loads is in flight while
+//     one is read.
+//   * DEEP (K of at least three steps): a third B slot, and the B loads of
+//     step p+3 are issued with the A loads of step p+2: the weights, which
+//     the tiles of one L2 share less than the rows, get two k-steps of
+//     lead.  2 x 32 KB + 3 x 32 KB fills the 160 KB of LDS.
+//   * THIN: 64-row tiles (every expert has at most 64 rows, as in a decode
+//     step) with three slots each, two k-steps of loads in flight: a thin
+//     tile does little MFMA work per k-step, and with two slots each k-step
+//     would wait a whole load round trip.
+template <int MODE, int BN, bool F8 = false, bool THIN = false, bool DEEP = false>
 struct Epi {
     static constexpr int MB = mode_base(MODE);
     static_assert(BN == 256 || (BN == 128 && MB != MODE_SWIGLU), "B tile is 256 or 128 columns");
+    static_assert(!(THIN && DEEP), "thin tiles keep their own pipeline");
     static constexpr int BM = THIN ? 64 : kBM;
-    static constexpr int NSTAGE = THIN ? 3 : 2;
+    // last row tiles of at most this many rows go to the end of the schedule
+    static constexpr int THIN_ROWS = THIN ? 0 : 64;
+    static constexpr int NA = THIN ? 3 : 2;
+    static constexpr int NB = (THIN || DEEP) ? 3 : 2;
     static constexpr int STAGE_A = BM * kBK * 2;            // 32 KB (8 KB thin)
     static constexpr int STAGE_B = kBK * BN * (F8 ? 1 : 2);  // 32 or 16 KB (8 or 16 KB for codes)
-    static constexpr int STAGE = STAGE_A + STAGE_B;
     static constexpr int BN_OUT = (MB == MODE_SWIGLU) ? BN / 2 : BN;
     static constexpr int OUT_BYTES = (MB == MODE_DOWN) ? 4 : 2;
-    static constexpr size_t LDS = NSTAGE * (size_t)STAGE;
+    static constexpr size_t LDS = (size_t)NA * STAGE_A + (size_t)NB * STAGE_B;
+    static_assert(LDS <= 160 * 1024, "LDS of one compute unit");
 };
 
 // One tile of work: expert e, rows m0.., output columns n0.., and the buffer
@@ -175,13 +248,12 @@ struct TileCtx {
 
 // GATHER: the A rows are read from the token rows x[slot_token[e, r]]
 // instead of a dispatched copy (rows with token -1 read as zero).
-template <int MODE, int BN, bool GATHER, bool F8, bool THIN>
+template <int MODE, int BN, bool GATHER, bool F8, bool THIN, bool DEEP>
 __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
-    using EP = Epi<MODE, BN, F8, THIN>;
+    using EP = Epi<MODE, BN, F8, THIN, DEEP>;
     static_assert(!F8 || MODE == mode_base(MODE), "8-bit weights: inference products only");
     constexpr int MB = mode_base(MODE);
     constexpr bool SAVE = MODE != MB;
-    constexpr int kStage = EP::STAGE;
     constexpr int WM_ROWS = EP::BM / kWMn;    // rows per wave
     constexpr int WN_COLS = BN / kWN;         // B columns per wave
     constexpr int TM = WM_ROWS / 32, TN = WN_COLS / 32;  // 32 x 32 MFMA tiles per wave
@@ -191,16 +263,13 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
     constexpr int QB = F8 ? BN / 16 / kNW : (BN / 128) * 16 / kNW;
     static_assert(QA == 1 || (QA <= 4 && QA % 2 == 0), "A loads per wave");
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ int s_pref[MOE_MAX_EXPERTS + 1];
-    __shared__ int s_mt[MOE_MAX_EXPERTS];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
     const int wm = wave / kWN, wn = wave % kWN;  // wave rows wm*WM_ROWS.., columns per wn
     const int NT = g.N / EP::BN_OUT;
-    if (tid == 0) build_prefix(g, NT, EP::BM, s_pref, s_mt);
-    __syncthreads();
-    const int total = __builtin_amdgcn_readfirstlane(s_pref[g.E]);
+    const WaveSched ws = wave_sched(g, NT, EP::BM, EP::THIN_ROWS, lane);
+    const int total = ws.total;
     const int G = gridDim.x;
     const int xcd = blockIdx.x % 8, slot8 = blockIdx.x / 8;
     const int nk = g.K / kBK;
@@ -235,10 +304,8 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
         c.valid = logical < total;
         if (!c.valid) return c;
         int e, m_tile, n_tile;
-        map_tile(logical, s_pref, s_mt, g.E, NT, e, m_tile, n_tile);
-        int kept = g.kept[e];
-        if (kept > g.C) kept = (int)g.C;
-        c.kept = __builtin_amdgcn_readfirstlane(kept);
+        map_tile_w(logical, ws, g.E, NT, lane, e, m_tile, n_tile);
+        c.kept = __builtin_amdgcn_readlane(ws.kp, e);
         c.e = __builtin_amdgcn_readfirstlane(e);
         c.m0 = __builtin_amdgcn_readfirstlane(m_tile * EP::BM);
         c.n0 = __builtin_amdgcn_readfirstlane(n_tile * EP::BN_OUT);
@@ -294,28 +361,35 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
     // = (lane % 4) ^ (lane / 16)
     const int rowQ = wave * QB * 16 + lane / 4 - ((MB == MODE_SWIGLU) ? sub * 128 : 0);
     const int voffQ = rowQ * g.K + (((lane % 4) ^ (lane / 16)) * 16);
-    auto issue = [&](const TileCtx& c, int kt, int stage) {
-        unsigned char* st = smem + stage * kStage;
+    // LDS slots (A slots first, then B slots) as 32-bit LDS addresses and
+    // as pointers for the fragment reads
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(const lds_void_t*)smem;
+    auto a_at = [&](int slot) { return smem + slot * EP::STAGE_A; };
+    auto b_at = [&](int slot) { return smem + EP::NA * EP::STAGE_A + slot * EP::STAGE_B; };
+    auto issue_a = [&](const TileCtx& c, int kt, int slot) {
+        const uint32_t st = lds_base + slot * EP::STAGE_A;
 #pragma unroll
         for (int q = 0; q < QA; ++q) {
             if (GATHER) {
                 const int tk = c.tok[q];
                 const int vo = tk >= 0 ? tk * g.K * 2 + (((wave * QA + q) & 1) ? chA1 : chA0)
                                        : (int)0x80000000;
-                lds_dma16(c.rsA, st + (wave * QA + q) * 1024, vo, kt * kBK * 2);
+                lds_dma16_at(c.rsA, st + (wave * QA + q) * 1024, vo, kt * kBK * 2);
             } else {
-                lds_dma16(c.rsA, st + (wave * QA + q) * 1024, ((wave * QA + q) & 1) ? voffA1 : voffA0,
-                          (q * 8 * g.K + kt * kBK) * 2);
+                lds_dma16_at(c.rsA, st + (wave * QA + q) * 1024, ((wave * QA + q) & 1) ? voffA1 : voffA0,
+                             (q * 8 * g.K + kt * kBK) * 2);
             }
         }
+    };
+    auto issue_b = [&](const TileCtx& c, int kt, int slot) {
+        const uint32_t st = lds_base + EP::NA * EP::STAGE_A + slot * EP::STAGE_B;
 #pragma unroll
         for (int q = 0; q < QB; ++q) {
             if (F8)
-                lds_dma16(c.rsB, st + EP::STAGE_A + (wave * QB + q) * 1024, voffQ,
-                          q * 16 * g.K + kt * kBK);
+                lds_dma16_at(c.rsB, st + (wave * QB + q) * 1024, voffQ, q * 16 * g.K + kt * kBK);
             else
-                lds_dma16(c.rsB, st + EP::STAGE_A + (wave * QB + q) * 1024, voffB,
-                          ((((wave * QB + q) % 16) * 4 + kt * kBK) * g.N) * 2);
+                lds_dma16_at(c.rsB, st + (wave * QB + q) * 1024, voffB,
+                             ((((wave * QB + q) % 16) * 4 + kt * kBK) * g.N) * 2);
         }
     };
 
@@ -323,11 +397,11 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
     // A (TM x 32 rows) and B (TN x 32 columns) per slice.
     // Only the first NI 32-row blocks of the wave's A rows are read (the
     // others lie past kept[e]).
-    auto load_frags = [&](auto ni, int stage, int kk, bf16x8_t (&af)[2][TM],
+    auto load_frags = [&](auto ni, int aslot, int bslot, int kk, bf16x8_t (&af)[2][TM],
                           bf16x8_t (&bfr)[2][TN]) {
         constexpr int NI = decltype(ni)::value;
-        const unsigned char* As = smem + stage * kStage;
-        const unsigned char* Bs = As + EP::STAGE_A;
+        const unsigned char* As = a_at(aslot);
+        const unsigned char* Bs = b_at(bslot);
 #pragma unroll
         for (int ss = 0; ss < 2; ++ss) {
             const int k16 = kk * 2 + ss;
@@ -384,11 +458,35 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
 
     TileCtx cur = tile_at(0);
     if (!cur.valid) return;
-    issue(cur, cur.kb, 0);
-    issue(cur, cur.kb + 1, 1);
-    int base = 0;  // stage holding k-step 0 of the current tile
+    // The first steps of the stream, in the order the loop issues them (the
+    // partial waits below count on it): A and B of steps 0 and 1, and with
+    // DEEP the B loads of step 2.
+    issue_a(cur, cur.kb, 0);
+    issue_b(cur, cur.kb, 0);
+    if (DEEP) issue_b(cur, cur.kb + 1, 1);
+    issue_a(cur, cur.kb + 1, 1);
+    if (DEEP)
+        issue_b(cur, cur.kb + 2, 2);
+    else
+        issue_b(cur, cur.kb + 1, 1);
+    int p0 = 0;  // stream index of the current tile's first k-step
     for (int round = 0;; ++round) {
         const TileCtx nxt = tile_at(round + 1);
+        // loads of stream step p: the current tile or, past its end, the next
+        auto stream_a = [&](int p) {
+            const int r = p - p0;
+            if (r < cur.nks)
+                issue_a(cur, cur.kb + r, p % EP::NA);
+            else if (nxt.valid)
+                issue_a(nxt, nxt.kb + r - cur.nks, p % EP::NA);
+        };
+        auto stream_b = [&](int p) {
+            const int r = p - p0;
+            if (r < cur.nks)
+                issue_b(cur, cur.kb + r, p % EP::NB);
+            else if (nxt.valid)
+                issue_b(nxt, nxt.kb + r - cur.nks, p % EP::NB);
+        };
         f32x16_t acc[TM][TN];
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -407,76 +505,80 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ss][i], bfr[ss][j],
                                                                             acc[i][j], 0, 0, 0);
         };
-        // Software pipeline over k-steps of 64 (two 32-wide halves): the
-        // second half of step kt is read while the first half's MFMAs run;
-        // then the barrier (step kt+1 has landed, nobody reads step kt any
-        // more), loads of step kt+2 go into the freed stage, and the first
-        // half of step kt+1 is read while the second half's MFMAs of step kt
-        // run.  After the last barrier the next tile's step 0 is loaded, and
-        // after the final MFMAs its step 1, so the next tile starts with both
-        // stages in flight.  A wave with rows at or past kept[e] (the tail of
-        // an expert's last row tile) runs the same loop with fragment reads and
-        // MFMAs for its live 32-row blocks only (none when every row is past
-        // kept): it issues the same loads and joins the same barriers (a
-        // barrier counts arrivals, so the loop variants stay in step).
-        // sched_barrier(0) keeps each MFMA group on its side of a barrier.
+        // Software pipeline over k-steps of 64 (two 32-wide halves), stream
+        // step p = p0 + kt: the second half of step p is read while the first
+        // half's MFMAs run; then the barrier (step p+1 has landed, nobody
+        // reads step p any more), the loads of step p+2 (DEEP: A of p+2, B of
+        // p+3) go into the slots step p freed, and the first half of step p+1
+        // is read while the second half's MFMAs of step p run.  The tile's
+        // last step has no mid-step barrier; after its MFMAs a barrier frees
+        // its slots for the next tile's loads, so the next tile starts with
+        // its first steps in flight.  Waits are partial where the newest loads
+        // may stay outstanding (loads complete in issue order; any newer
+        // stores only make a wait longer): at the tile's start step p0 must
+        // have landed, with the loads issued after it (DEEP: B of p0+1, A of
+        // p0+1, B of p0+2; else A and B of p0+1) still in flight; at a
+        // mid-step barrier, with DEEP, the B loads of step p+2.  A wave with
+        // rows at or past kept[e] (the tail of an expert's last row tile) runs
+        // the same loop with fragment reads and MFMAs for its live 32-row
+        // blocks only (none when every row is past kept): it issues the same
+        // loads and joins the same barriers (a barrier counts arrivals, so
+        // the loop variants stay in step).  sched_barrier(0) keeps each MFMA
+        // group on its side of a barrier.
         auto kloop = [&](auto ni) {
             constexpr bool M = decltype(ni)::value > 0;
             bf16x8_t a0[2][TM], b0[2][TN], a1[2][TM], b1[2][TN];
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (DEEP)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * QB + QA) : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(QA + QB) : "memory");
             __syncthreads();
             if (GATHER) {
                 // The row tokens were loaded by compiler-visible loads; using
                 // them here makes the compiler's own wait for them happen once,
-                // now, instead of before every issue() inside the loop (where
+                // now, instead of before every load issue inside the loop (where
                 // it would also wait for the k-step loads in flight).
 #pragma unroll
                 for (int q = 0; q < QA; ++q) asm volatile("" ::"v"(cur.tok[q]));
             }
-            if (M) load_frags(ni, base, 0, a0, b0);
+            if (M) load_frags(ni, p0 % EP::NA, p0 % EP::NB, 0, a0, b0);
             const int nks = cur.nks;
             int kt = 0;
-            for (; kt + 2 < nks; ++kt) {
-                const int s0 = (base + kt) & 1;
+            for (; kt + 1 < nks; ++kt) {
+                const int p = p0 + kt;
                 if (M) {
-                    load_frags(ni, s0, 1, a1, b1);
+                    load_frags(ni, p % EP::NA, p % EP::NB, 1, a1, b1);
                     mma(ni, a0, b0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                if (DEEP && (kt + 2 < nks || nxt.valid))
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(QB) : "memory");
+                else
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
-                issue(cur, cur.kb + kt + 2, s0);
+                stream_a(p + 2);
+                stream_b(DEEP ? p + 3 : p + 2);
                 if (M) {
-                    load_frags(ni, s0 ^ 1, 0, a0, b0);
+                    load_frags(ni, (p + 1) % EP::NA, (p + 1) % EP::NB, 0, a0, b0);
                     mma(ni, a1, b1);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // kt = nk - 2
-            const int s0 = (base + kt) & 1;
+            // the tile's last step
+            const int p = p0 + kt;
             if (M) {
-                load_frags(ni, s0, 1, a1, b1);
-                mma(ni, a0, b0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            if (nxt.valid) issue(nxt, nxt.kb, s0);
-            if (M) {
-                load_frags(ni, s0 ^ 1, 0, a0, b0);
-                mma(ni, a1, b1);
-                // kt = nk - 1
-                load_frags(ni, s0 ^ 1, 1, a1, b1);
+                load_frags(ni, p % EP::NA, p % EP::NB, 1, a1, b1);
                 mma(ni, a0, b0);
                 mma(ni, a1, b1);
             }
             __builtin_amdgcn_sched_barrier(0);
-            __syncthreads();  // every wave is done with step nk - 1
-            if (nxt.valid) issue(nxt, nxt.kb + 1, s0 ^ 1);
+            __syncthreads();  // every wave is done with step p
+            stream_a(p + 2);
+            stream_b(DEEP ? p + 3 : p + 2);
         };
-        // THIN: three stages, one barrier per k-step.  Step kt+2 is loaded
-        // into the stage step kt-1 used (free once every wave has passed this
-        // step's barrier) while step kt is read, so two k-steps of loads are in
+        // THIN: three slots, one barrier per k-step.  Step p+2 is loaded
+        // into the slots step p-1 used (free once every wave has passed this
+        // step's barrier) while step p is read, so two k-steps of loads are in
         // flight; the wait before the barrier lets the newest step's loads (NL
         // buffer loads per wave) stay outstanding, since loads complete in
         // issue order.  The first step of a tile waits for everything (the
@@ -500,16 +602,13 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
 #pragma unroll
                     for (int q = 0; q < QA; ++q) asm volatile("" ::"v"(cur.tok[q]));
                 }
-                const int s2 = (base + kt + 2) % 3;
-                if (kt + 2 < nks)
-                    issue(cur, cur.kb + kt + 2, s2);
-                else if (nxt.valid)
-                    issue(nxt, nxt.kb + (kt + 2 - nks), s2);
+                stream_a(p0 + kt + 2);
+                stream_b(p0 + kt + 2);
                 if (M) {
-                    const int sc = (base + kt) % 3;
-                    load_frags(ni, sc, 0, af, bfr);
+                    const int sc = (p0 + kt) % 3;
+                    load_frags(ni, sc, sc, 0, af, bfr);
                     mma(ni, af, bfr);
-                    load_frags(ni, sc, 1, af, bfr);
+                    load_frags(ni, sc, sc, 1, af, bfr);
                     mma(ni, af, bfr);
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -558,18 +657,21 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
         }
 
         // epilogue: activation on the fp32 accumulators, stored straight from
-        // registers (element q of a 32 x 32 accumulator in lane l is row
-        // 8*(q/4) + 4*(l/32) + q%4, column l%32; one store covers two rows of
-        // 32 consecutive columns).  The output descriptor ends at row kept[e],
-        // so rows past it are dropped by the hardware.
+        // registers.  Element q of a 32 x 32 accumulator in lane l is row
+        // 8*(q/4) + 4*(l/32) + q%4, column l%32; a quad transpose over each
+        // four rows (q%4) and four lanes leaves lane l with row
+        // 8*(q/4) + 4*(l/32) + l%4, columns (l%32 & ~3) .. +3, stored with one
+        // 8-byte (bf16) or 16-byte (fp32) store.  The output descriptor ends
+        // at row kept[e], so rows past it are dropped by the hardware.
         {
             const uint16_t* biasb = g.bias ? g.bias + (size_t)cur.e * g.N + cur.n0 : nullptr;
             constexpr int TNO = (MB == MODE_SWIGLU) ? TN / 2 : TN;
             constexpr int B = EP::OUT_BYTES;
+            static_assert(!SAVE || B == 2, "saved planes share h's layout");
             const i32x4_t rsO = make_rsrc(
                 static_cast<unsigned char*>(g.out) + (((size_t)cur.e * g.C + cur.m0) * g.N + cur.n0) * B,
                 (uint32_t)(((size_t)(cur.kept - cur.m0) * g.N - cur.n0) * B));
-            const int row_l = wm * WM_ROWS + (lane / 32) * 4;
+            const int row_t = wm * WM_ROWS + (lane / 32) * 4 + (lane & 3);
             i32x4_t rsS0 = rsO, rsS1 = rsO;  // same layout and row bound as h
             if (SAVE) {
                 const size_t off = ((size_t)cur.e * g.C + cur.m0) * g.N + cur.n0;
@@ -580,9 +682,9 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
             }
 #pragma unroll
             for (int j = 0; j < TNO; ++j) {
-                const int ocol = (MB == MODE_SWIGLU ? wn * (WN_COLS / 2) : wn * WN_COLS) + j * 32 +
-                                 lane % 32;
-                const int voff = (row_l * g.N + ocol) * B;
+                const int cbase = (MB == MODE_SWIGLU ? wn * (WN_COLS / 2) : wn * WN_COLS) + j * 32;
+                const int ocol = cbase + lane % 32;  // this lane's column before the transpose
+                const int voff = (row_t * g.N + cbase + ((lane % 32) & ~3)) * B;
                 float bv = 0.f;
                 if (MB != MODE_SWIGLU && biasb) bv = bf2f(biasb[ocol]);
                 // 8-bit weights: the column scales of this lane's column
@@ -594,32 +696,40 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
 #pragma unroll
-                    for (int q = 0; q < 16; ++q) {
-                        const int soff = ((i * 32 + (q / 4) * 8 + (q % 4)) * g.N) * B;
-                        float v;
-                        if (MB == MODE_SWIGLU)
-                            v = F8 ? silu_f(acc[i][j][q] * sc0) * (acc[i][j + TN / 2][q] * sc1)
-                                   : silu_f(acc[i][j][q]) * acc[i][j + TN / 2][q];
-                        else if (MB == MODE_GELU)
-                            v = gelu_f((F8 ? acc[i][j][q] * sc0 : acc[i][j][q]) + bv);
-                        else
-                            v = (F8 ? acc[i][j][q] * sc0 : acc[i][j][q]) + bv;
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int soff = ((i * 32 + q4 * 8) * g.N) * B;
+                        float v[4], s0v[4], s1v[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int q = 4 * q4 + r;
+                            if (MB == MODE_SWIGLU)
+                                v[r] = F8 ? silu_f(acc[i][j][q] * sc0) * (acc[i][j + TN / 2][q] * sc1)
+                                          : silu_f(acc[i][j][q]) * acc[i][j + TN / 2][q];
+                            else if (MB == MODE_GELU)
+                                v[r] = gelu_f((F8 ? acc[i][j][q] * sc0 : acc[i][j][q]) + bv);
+                            else
+                                v[r] = (F8 ? acc[i][j][q] * sc0 : acc[i][j][q]) + bv;
+                            if (SAVE && MB == MODE_SWIGLU) {
+                                s0v[r] = acc[i][j][q];
+                                s1v[r] = acc[i][j + TN / 2][q];
+                            } else if (SAVE) {
+                                s0v[r] = acc[i][j][q] + bv;
+                            }
+                        }
                         if (MB == MODE_DOWN)
-                            buffer_store_f32(v, rsO, voff, soff, 0);
+                            store_rows4_f32(v, rsO, voff, soff, lane);
                         else
-                            buffer_store_i16((short)f2bf(v), rsO, voff, soff, 0);
-                        if (SAVE && MB == MODE_SWIGLU) {
-                            buffer_store_i16((short)f2bf(acc[i][j][q]), rsS0, voff, soff, 0);
-                            buffer_store_i16((short)f2bf(acc[i][j + TN / 2][q]), rsS1, voff, soff, 0);
-                        } else if (SAVE) {
-                            buffer_store_i16((short)f2bf(acc[i][j][q] + bv), rsS0, voff, soff, 0);
+                            store_rows4_bf16(v, rsO, voff, soff, lane);
+                        if (SAVE) {
+                            store_rows4_bf16(s0v, rsS0, voff, soff, lane);
+                            if (MB == MODE_SWIGLU) store_rows4_bf16(s1v, rsS1, voff, soff, lane);
                         }
                     }
                 }
             }
         }
         if (!nxt.valid) break;
-        base = THIN ? (base + cur.nks) % 3 : (base + cur.nks) & 1;
+        p0 += cur.nks;
         cur = tile_at(round + 1);  // recomputed: only what the prefetch needs stays live
     }
 }
@@ -639,12 +749,10 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g, int G) {
     constexpr int TM = WM_ROWS / 32, TN = WN_COLS / 32;
     constexpr int TNO = (MB == MODE_SWIGLU) ? TN / 2 : TN;
     constexpr int PER_TILE = kGThreads * TM * TNO * 4;
-    __shared__ int s_pref[MOE_MAX_EXPERTS + 1];
-    __shared__ int s_mt[MOE_MAX_EXPERTS];
     const int NT = g.N / EP::BN_OUT;
-    if (threadIdx.x == 0) build_prefix(g, NT, EP::BM, s_pref, s_mt);
-    __syncthreads();
-    const int total = s_pref[g.E];
+    const int lane = threadIdx.x % kWave;
+    const WaveSched ws = wave_sched(g, NT, EP::BM, EP::THIN_ROWS, lane);
+    const int total = ws.total;
     const int splits = tail_splits(g, total, G, g.K / kBK);
     if (splits <= 1) return;
     const int full = total / G, remt = total - full * G;
@@ -660,9 +768,8 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g, int G) {
         r /= 4;
         const int jo = r % TNO, i = r / TNO;
         int e, m_tile, n_tile;
-        map_tile(full * G + t, s_pref, s_mt, g.E, NT, e, m_tile, n_tile);
-        int kept = g.kept[e];
-        if (kept > g.C) kept = (int)g.C;
+        map_tile_w(full * G + t, ws, g.E, NT, lane, e, m_tile, n_tile);  // t is wave-uniform
+        const int kept = __builtin_amdgcn_readlane(ws.kp, e);
         const int vwave = vt / kWave, vlane = vt % kWave;
         const int wm = vwave / kWN, wn = vwave % kWN;
         const int m0 = m_tile * EP::BM, n0 = n_tile * EP::BN_OUT;
@@ -711,7 +818,7 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g, int G) {
             if (MB == MODE_DOWN)
                 static_cast<float*>(g.out)[o] = v;
             else
-                static_cast<uint16_t*>(g.out)[o] = f2bf(v);
+                static_cast<uint16_t*>(g.out)[o] = bf16_rn(v);
         }
     }
 }
@@ -777,10 +884,12 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
 }
 
 
-template <int MODE, int BN, bool GATHER = false, bool F8 = false, bool THIN = false>
-moe_status_t launch_gemm(const GemmArgs& a, hipStream_t st) {
-    using EP = Epi<MODE, BN, F8, THIN>;
-    auto kern = grouped_gemm_kernel<MODE, BN, GATHER, F8, THIN>;
+template <int MODE, int BN, bool GATHER, bool F8, bool THIN, bool DEEP>
+moe_status_t launch_gemm_k(const GemmArgs& args, hipStream_t st) {
+    using EP = Epi<MODE, BN, F8, THIN, DEEP>;
+    GemmArgs a = args;
+    a.minsteps = DEEP ? 3 : 2;  // the product and its tail reduction agree on the split
+    auto kern = grouped_gemm_kernel<MODE, BN, GATHER, F8, THIN, DEEP>;
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)EP::LDS) != hipSuccess)
         return MOE_ERR_LAUNCH;
@@ -800,6 +909,18 @@ moe_status_t launch_gemm(const GemmArgs& a, hipStream_t st) {
         }
     }
     return MOE_OK;
+}
+
+// Full-size tiles take the deeper weight prefetch when K has at least three
+// k-steps (every split piece then keeps three).
+template <int MODE, int BN, bool GATHER = false, bool F8 = false, bool THIN = false>
+moe_status_t launch_gemm(const GemmArgs& a, hipStream_t st) {
+    if constexpr (THIN) {
+        return launch_gemm_k<MODE, BN, GATHER, F8, true, false>(a, st);
+    } else {
+        if (a.K / kBK >= 3) return launch_gemm_k<MODE, BN, GATHER, F8, false, true>(a, st);
+        return launch_gemm_k<MODE, BN, GATHER, F8, false, false>(a, st);
+    }
 }
 
 // A single-matrix product (GELU first product, down product) can run with

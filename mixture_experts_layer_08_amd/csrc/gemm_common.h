@@ -78,6 +78,21 @@ __device__ __forceinline__ void lds_dma16(i32x4_t rsrc, const void* lds, int vof
         : "s"(m0), "v"(voffset), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soffset))
         : "memory", "m0");
 }
+// The same with the LDS destination as a 32-bit LDS address (computed once
+// per kernel from the shared array, so no generic-pointer conversion per load).
+__device__ __forceinline__ void lds_dma16_at(i32x4_t rsrc, uint32_t lds_addr, int voffset, int soffset) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+    rsrc.x = __builtin_amdgcn_readfirstlane(rsrc.x);
+    rsrc.y = __builtin_amdgcn_readfirstlane(rsrc.y);
+    rsrc.z = __builtin_amdgcn_readfirstlane(rsrc.z);
+    rsrc.w = __builtin_amdgcn_readfirstlane(rsrc.w);
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        :
+        : "s"(m0), "v"(voffset), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soffset))
+        : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Buffer resource: 48-bit base, no stride, num_records bytes; loads past the
@@ -93,9 +108,78 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
     return r;
 }
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g * sigmoid(g), the reciprocal from v_rcp_f32 (1 ulp): the
+// products' outputs are rounded to bf16 or feed fp32 sums, where an IEEE
+// division's last bit does not show.
+__device__ __forceinline__ float silu_f(float g) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
 __device__ __forceinline__ float gelu_f(float z) {
     return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+}
+
+// Round to nearest even bf16 (v_cvt_pk_bf16_f32), two values per word, lo
+// in the low half.
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const bf16x2_v v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t bf16_rn(float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Exchange inside lane pairs (CTRL 0xB1: lanes XOR 1) or pairs of pairs
+// (CTRL 0x4E: lanes XOR 2) by DPP quad permutes: the lower lane of a pair
+// keeps a and receives the partner's a into b; the upper lane keeps b and
+// receives the partner's b into a.
+template <int CTRL>
+__device__ __forceinline__ void quad_xchg(uint32_t& a, uint32_t& b, bool upper) {
+    const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)(upper ? a : b), CTRL, 0xF, 0xF, false);
+    if (upper)
+        a = got;
+    else
+        b = got;
+}
+
+// Stores of four rows of an MFMA 32 x 32 accumulator: in lanes 4m .. 4m+3,
+// v[0..3] hold rows r .. r+3 of column c0 + (lane & 3).  Two exchange rounds
+// (lane bit 0 with row bit 0, then lane bit 1 with row bit 1) leave lane
+// 4m + j with row r + j, columns c0 .. c0+3, written with one 8-byte (bf16)
+// or 16-byte (fp32) store.  Every lane of each quad must be active.
+__device__ __forceinline__ void store_rows4_bf16(const float (&v)[4], i32x4_t rs, int voff,
+                                                 int soff, int lane) {
+    uint32_t w0 = __float_as_uint(v[0]), w1 = __float_as_uint(v[1]);
+    uint32_t w2 = __float_as_uint(v[2]), w3 = __float_as_uint(v[3]);
+    quad_xchg<0xB1>(w0, w1, lane & 1);
+    quad_xchg<0xB1>(w2, w3, lane & 1);
+    uint32_t p0 = pack_bf16x2(__uint_as_float(w0), __uint_as_float(w1));
+    uint32_t p1 = pack_bf16x2(__uint_as_float(w2), __uint_as_float(w3));
+    quad_xchg<0x4E>(p0, p1, lane & 2);
+    moe_i32x2_t o;
+    o.x = (int)p0;
+    o.y = (int)p1;
+    buffer_store_i32x2(o, rs, voff, soff, 0);
+}
+__device__ __forceinline__ void store_rows4_f32(const float (&v)[4], i32x4_t rs, int voff,
+                                                int soff, int lane) {
+    uint32_t w0 = __float_as_uint(v[0]), w1 = __float_as_uint(v[1]);
+    uint32_t w2 = __float_as_uint(v[2]), w3 = __float_as_uint(v[3]);
+    quad_xchg<0xB1>(w0, w1, lane & 1);
+    quad_xchg<0xB1>(w2, w3, lane & 1);
+    quad_xchg<0x4E>(w0, w2, lane & 2);
+    quad_xchg<0x4E>(w1, w3, lane & 2);
+    f32x4_t o;
+    o.x = __uint_as_float(w0);
+    o.y = __uint_as_float(w1);
+    o.z = __uint_as_float(w2);
+    o.w = __uint_as_float(w3);
+    // The whole offset goes in the vector operand, soffset stays 0: with a
+    // register soffset, the compiler let the next VALU write the store's data
+    // registers at once, and the first dword of some lanes' stores then held
+    // the new value (measured wrong outputs).  With soffset 0 it pads the
+    // store with the wait state a 16-byte store needs.
+    buffer_store_f32x4(o, rs, voff + soff, 0, 0);
 }
 
 // LDS swizzles (16-byte chunk index XOR).  A rows are 128 bytes: XOR with

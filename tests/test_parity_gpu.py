@@ -19,7 +19,8 @@ from oracle import moe_oracle as M
 from oracle import near_tie_tokens
 from mixture_experts_layer_08_amd import ops
 from mixture_experts_layer_08_amd.layer import MoELayerGPU, x_to_device
-from mixture_experts_layer_08_amd.synth import CONFIGS, MoEConfig, drop_free, make_inputs
+from mixture_experts_layer_08_amd.synth import (CONFIGS, MoEConfig, bf16_bits_to_f32, drop_free,
+                                                f32_to_bf16_bits, make_inputs)
 
 from parity_util import assert_rel, assert_rows_close, log, to_dev, to_np
 
@@ -194,6 +195,19 @@ def test_stages_on_oracle_inputs(name):
         n = int(ref.disp.kept[e])
         np.testing.assert_array_equal(ygn[e, :n], yd[e, :n], err_msg=f"{name}: gathered y_disp[{e}]")
         np.testing.assert_array_equal(hgn[e, :n], hh[e, :n], err_msg=f"{name}: gathered h[{e}]")
+    if cfg.dtype == "bf16":
+        # without a workspace every tile finishes in the product kernel's own
+        # epilogue (with one, a partly filled last round is cut into K pieces
+        # that the tail reduction finishes, which is all these small shapes have)
+        yw, hw = ops.moe_expert_ffn(x_disp, kept, layer.w1, layer.w3, layer.w2, layer.b1,
+                                    layer.b2, act=cfg.act)
+        torch.cuda.synchronize()
+        ywn, hwn = to_np(yw), to_np(hw)
+        for e in range(cfg.E):
+            n = int(ref.disp.kept[e])
+            if n:
+                _check_h(cfg, hwn[e, :n], ref.h[e, :n], f"{name}: h[{e}], no workspace")
+                _check_y(cfg, ywn[e, :n], ref.y_disp[e, :n], f"{name}: y_disp[{e}], no workspace")
     # combine of the oracle's expert outputs (stored in fp32, as the library keeps them)
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     ydisp_store = ref.y_disp.astype(np.float32).astype(np.float64)
@@ -225,6 +239,50 @@ def test_stages_on_oracle_inputs(name):
         got2 = to_np(y2)
         assert np.all(np.abs(got2 - want2) <= 2.0 ** -8 * np.abs(want2) + 1e-30 +
                       1e-6 * np.sqrt(np.mean(want2 * want2, axis=1, keepdims=True)))
+
+
+# Expert row counts whose last row tile is thin (at most 64 of 256 rows):
+# the products schedule those tiles after all others.  Last row tiles of 8,
+# 64 (the bound), 1 and 44 rows, an expert with only a thin tile, one with no
+# rows, and last tiles of 65 and 128 rows that stay in place; then a shape
+# whose other tiles fill exactly one round of 256 workgroups, so that with a
+# workspace the 96 thin tiles are the round cut along K.
+THIN_LAST = {
+    "mixed-swiglu": (MoEConfig("t-mix", "bf16", T=64, H=512, I=512, E=8, k=2, cf=1.0, seed=51),
+                     640, [520, 64, 1, 0, 300, 576, 577, 640]),
+    "mixed-gelu": (MoEConfig("t-mix-ge", "bf16", T=64, H=512, I=512, E=8, k=2, cf=1.0,
+                             act="gelu", seed=52),
+                   640, [520, 64, 1, 0, 300, 576, 577, 640]),
+    "one-round-swiglu": (MoEConfig("t-round", "bf16", T=64, H=256, I=4096, E=8, k=2, cf=1.0,
+                                   seed=53),
+                         320, [273, 256, 256, 257, 256, 256, 289, 256]),
+}
+
+
+@pytest.mark.parametrize("ws_on", [True, False], ids=["split", "whole"])
+@pytest.mark.parametrize("name", list(THIN_LAST))
+def test_thin_last_row_tiles(name, ws_on):
+    cfg, C, kept_l = THIN_LAST[name]
+    log(f"[thin-last] {name} ({'split' if ws_on else 'whole'}): kept {kept_l}")
+    inp = make_inputs(cfg)
+    rng = np.random.default_rng(cfg.seed + 1)
+    xd_bits = f32_to_bf16_bits(rng.standard_normal((cfg.E, C, cfg.H), dtype=np.float32))
+    xd = bf16_bits_to_f32(xd_bits).astype(np.float64)
+    layer = MoELayerGPU(cfg, inp, DEV, fused_gather=False)
+    x_disp = torch.from_numpy(xd_bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+    kept = to_dev(np.array(kept_l, dtype=np.int32), torch.int32)
+    ws = (torch.empty(ops.moe_expert_ffn_ws_bytes(), dtype=torch.uint8, device=DEV)
+          if ws_on else None)
+    y, h = ops.moe_expert_ffn(x_disp, kept, layer.w1, layer.w3, layer.w2, layer.b1, layer.b2,
+                              act=cfg.act, ws=ws)
+    torch.cuda.synchronize()
+    yn, hn = to_np(y), to_np(h)
+    for e, n in enumerate(kept_l):
+        if n == 0:
+            continue
+        hr, yr = M.expert_forward(inp, cfg.act, e, xd[e, :n])
+        _check_h(cfg, hn[e, :n], hr, f"{name}: h[{e}]")
+        _check_y(cfg, yn[e, :n], yr, f"{name}: y_disp[{e}]")
 
 
 # ---------------------------------------------------------- edge cases ----
