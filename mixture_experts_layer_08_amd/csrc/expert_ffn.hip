@@ -98,7 +98,6 @@ struct GemmArgs {
     // split-K of the last, partly filled round of tiles (null part: off)
     float* part;            // per-piece fp32 partial tiles, kPartBytes each
     int smax;               // at most this many pieces per tile
-    int minsteps;           // each piece keeps at least this many k-steps (set at launch)
     uint16_t* save0;        // *_SAVE modes: [E, C, N_out] g (or z)
     uint16_t* save1;        // SwiGLU: [E, C, N_out] u
     // 8-bit weights: e4m3 codes [E, N, K] (in place of B0 / B1) and the
@@ -197,39 +196,33 @@ __device__ __forceinline__ int tail_splits(const GemmArgs& g, int total, int G, 
     int sp = G / remt;
     if (sp > g.smax) sp = g.smax;
     if (sp > kSMax) sp = kSMax;
-    if (sp > nk / g.minsteps) sp = nk / g.minsteps;  // the k pipeline's lookahead
+    if (sp > nk / 2) sp = nk / 2;  // each piece keeps at least two k-steps
     return sp < 1 ? 1 : sp;
 }
 
-// LDS holds NA slots of A k-steps, then NB slots of B k-steps; stream step
-// p of a workgroup (its tiles' k-steps one after another) uses A slot p % NA
-// and B slot p % NB.
-//   * default: two slots each; the loads of step p+2 are issued once every
-//     wave is done with step p, so one k-step of loads is in flight while
-//     one is read.
-//   * DEEP (K of at least three steps): a third B slot, and the B loads of
-//     step p+3 are issued with the A loads of step p+2: the weights, which
-//     the tiles of one L2 share less than the rows, get two k-steps of
-//     lead.  2 x 32 KB + 3 x 32 KB fills the 160 KB of LDS.
+// LDS holds NS slots of A k-steps, then NS slots of B k-steps; stream step
+// p of a workgroup (its tiles' k-steps one after another) uses slot p % NS.
+//   * default: two slots; the loads of step p+2 are issued once every wave
+//     is done with step p, so one k-step of loads is in flight while one is
+//     read.  (A third B slot that issues the weight loads one step earlier
+//     measured no faster: the loads are not waiting on latency alone.)
 //   * THIN: 64-row tiles (every expert has at most 64 rows, as in a decode
-//     step) with three slots each, two k-steps of loads in flight: a thin
-//     tile does little MFMA work per k-step, and with two slots each k-step
-//     would wait a whole load round trip.
-template <int MODE, int BN, bool F8 = false, bool THIN = false, bool DEEP = false>
+//     step) with three slots, two k-steps of loads in flight: a thin tile
+//     does little MFMA work per k-step, and with two slots each k-step would
+//     wait a whole load round trip.
+template <int MODE, int BN, bool F8 = false, bool THIN = false>
 struct Epi {
     static constexpr int MB = mode_base(MODE);
     static_assert(BN == 256 || (BN == 128 && MB != MODE_SWIGLU), "B tile is 256 or 128 columns");
-    static_assert(!(THIN && DEEP), "thin tiles keep their own pipeline");
     static constexpr int BM = THIN ? 64 : kBM;
     // last row tiles of at most this many rows go to the end of the schedule
     static constexpr int THIN_ROWS = THIN ? 0 : 64;
-    static constexpr int NA = THIN ? 3 : 2;
-    static constexpr int NB = (THIN || DEEP) ? 3 : 2;
+    static constexpr int NS = THIN ? 3 : 2;
     static constexpr int STAGE_A = BM * kBK * 2;            // 32 KB (8 KB thin)
     static constexpr int STAGE_B = kBK * BN * (F8 ? 1 : 2);  // 32 or 16 KB (8 or 16 KB for codes)
     static constexpr int BN_OUT = (MB == MODE_SWIGLU) ? BN / 2 : BN;
     static constexpr int OUT_BYTES = (MB == MODE_DOWN) ? 4 : 2;
-    static constexpr size_t LDS = (size_t)NA * STAGE_A + (size_t)NB * STAGE_B;
+    static constexpr size_t LDS = (size_t)NS * (STAGE_A + STAGE_B);
     static_assert(LDS <= 160 * 1024, "LDS of one compute unit");
 };
 
@@ -248,9 +241,9 @@ struct TileCtx {
 
 // GATHER: the A rows are read from the token rows x[slot_token[e, r]]
 // instead of a dispatched copy (rows with token -1 read as zero).
-template <int MODE, int BN, bool GATHER, bool F8, bool THIN, bool DEEP>
+template <int MODE, int BN, bool GATHER, bool F8, bool THIN>
 __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
-    using EP = Epi<MODE, BN, F8, THIN, DEEP>;
+    using EP = Epi<MODE, BN, F8, THIN>;
     static_assert(!F8 || MODE == mode_base(MODE), "8-bit weights: inference products only");
     constexpr int MB = mode_base(MODE);
     constexpr bool SAVE = MODE != MB;
@@ -365,7 +358,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
     // as pointers for the fragment reads
     const uint32_t lds_base = (uint32_t)(uintptr_t)(const lds_void_t*)smem;
     auto a_at = [&](int slot) { return smem + slot * EP::STAGE_A; };
-    auto b_at = [&](int slot) { return smem + EP::NA * EP::STAGE_A + slot * EP::STAGE_B; };
+    auto b_at = [&](int slot) { return smem + EP::NS * EP::STAGE_A + slot * EP::STAGE_B; };
     auto issue_a = [&](const TileCtx& c, int kt, int slot) {
         const uint32_t st = lds_base + slot * EP::STAGE_A;
 #pragma unroll
@@ -382,7 +375,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
         }
     };
     auto issue_b = [&](const TileCtx& c, int kt, int slot) {
-        const uint32_t st = lds_base + EP::NA * EP::STAGE_A + slot * EP::STAGE_B;
+        const uint32_t st = lds_base + EP::NS * EP::STAGE_A + slot * EP::STAGE_B;
 #pragma unroll
         for (int q = 0; q < QB; ++q) {
             if (F8)
@@ -458,17 +451,12 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
 
     TileCtx cur = tile_at(0);
     if (!cur.valid) return;
-    // The first steps of the stream, in the order the loop issues them (the
-    // partial waits below count on it): A and B of steps 0 and 1, and with
-    // DEEP the B loads of step 2.
+    // the first two steps of the stream, in the order the loop issues them
+    // (the partial wait at a tile's start counts on it)
     issue_a(cur, cur.kb, 0);
     issue_b(cur, cur.kb, 0);
-    if (DEEP) issue_b(cur, cur.kb + 1, 1);
     issue_a(cur, cur.kb + 1, 1);
-    if (DEEP)
-        issue_b(cur, cur.kb + 2, 2);
-    else
-        issue_b(cur, cur.kb + 1, 1);
+    issue_b(cur, cur.kb + 1, 1);
     int p0 = 0;  // stream index of the current tile's first k-step
     for (int round = 0;; ++round) {
         const TileCtx nxt = tile_at(round + 1);
@@ -476,16 +464,16 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
         auto stream_a = [&](int p) {
             const int r = p - p0;
             if (r < cur.nks)
-                issue_a(cur, cur.kb + r, p % EP::NA);
+                issue_a(cur, cur.kb + r, p % EP::NS);
             else if (nxt.valid)
-                issue_a(nxt, nxt.kb + r - cur.nks, p % EP::NA);
+                issue_a(nxt, nxt.kb + r - cur.nks, p % EP::NS);
         };
         auto stream_b = [&](int p) {
             const int r = p - p0;
             if (r < cur.nks)
-                issue_b(cur, cur.kb + r, p % EP::NB);
+                issue_b(cur, cur.kb + r, p % EP::NS);
             else if (nxt.valid)
-                issue_b(nxt, nxt.kb + r - cur.nks, p % EP::NB);
+                issue_b(nxt, nxt.kb + r - cur.nks, p % EP::NS);
         };
         f32x16_t acc[TM][TN];
 #pragma unroll
@@ -508,17 +496,14 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
         // Software pipeline over k-steps of 64 (two 32-wide halves), stream
         // step p = p0 + kt: the second half of step p is read while the first
         // half's MFMAs run; then the barrier (step p+1 has landed, nobody
-        // reads step p any more), the loads of step p+2 (DEEP: A of p+2, B of
-        // p+3) go into the slots step p freed, and the first half of step p+1
-        // is read while the second half's MFMAs of step p run.  The tile's
-        // last step has no mid-step barrier; after its MFMAs a barrier frees
-        // its slots for the next tile's loads, so the next tile starts with
-        // its first steps in flight.  Waits are partial where the newest loads
-        // may stay outstanding (loads complete in issue order; any newer
-        // stores only make a wait longer): at the tile's start step p0 must
-        // have landed, with the loads issued after it (DEEP: B of p0+1, A of
-        // p0+1, B of p0+2; else A and B of p0+1) still in flight; at a
-        // mid-step barrier, with DEEP, the B loads of step p+2.  A wave with
+        // reads step p any more), the loads of step p+2 go into the slot step
+        // p freed, and the first half of step p+1 is read while the second
+        // half's MFMAs of step p run.  The tile's last step has no mid-step
+        // barrier; after its MFMAs a barrier frees its slot for the next
+        // tile's loads, so the next tile starts with its first two steps in
+        // flight.  At a tile's start only step p0 must have landed: the loads
+        // of step p0+1, issued after it, may stay in flight (loads complete in
+        // issue order; any newer stores only make the wait longer).  A wave with
         // rows at or past kept[e] (the tail of an expert's last row tile) runs
         // the same loop with fragment reads and MFMAs for its live 32-row
         // blocks only (none when every row is past kept): it issues the same
@@ -528,10 +513,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
         auto kloop = [&](auto ni) {
             constexpr bool M = decltype(ni)::value > 0;
             bf16x8_t a0[2][TM], b0[2][TN], a1[2][TM], b1[2][TN];
-            if (DEEP)
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * QB + QA) : "memory");
-            else
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(QA + QB) : "memory");
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(QA + QB) : "memory");
             __syncthreads();
             if (GATHER) {
                 // The row tokens were loaded by compiler-visible loads; using
@@ -541,25 +523,22 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
 #pragma unroll
                 for (int q = 0; q < QA; ++q) asm volatile("" ::"v"(cur.tok[q]));
             }
-            if (M) load_frags(ni, p0 % EP::NA, p0 % EP::NB, 0, a0, b0);
+            if (M) load_frags(ni, p0 % EP::NS, p0 % EP::NS, 0, a0, b0);
             const int nks = cur.nks;
             int kt = 0;
             for (; kt + 1 < nks; ++kt) {
                 const int p = p0 + kt;
                 if (M) {
-                    load_frags(ni, p % EP::NA, p % EP::NB, 1, a1, b1);
+                    load_frags(ni, p % EP::NS, p % EP::NS, 1, a1, b1);
                     mma(ni, a0, b0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                if (DEEP && (kt + 2 < nks || nxt.valid))
-                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(QB) : "memory");
-                else
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
                 stream_a(p + 2);
-                stream_b(DEEP ? p + 3 : p + 2);
+                stream_b(p + 2);
                 if (M) {
-                    load_frags(ni, (p + 1) % EP::NA, (p + 1) % EP::NB, 0, a0, b0);
+                    load_frags(ni, (p + 1) % EP::NS, (p + 1) % EP::NS, 0, a0, b0);
                     mma(ni, a1, b1);
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -567,14 +546,14 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
             // the tile's last step
             const int p = p0 + kt;
             if (M) {
-                load_frags(ni, p % EP::NA, p % EP::NB, 1, a1, b1);
+                load_frags(ni, p % EP::NS, p % EP::NS, 1, a1, b1);
                 mma(ni, a0, b0);
                 mma(ni, a1, b1);
             }
             __builtin_amdgcn_sched_barrier(0);
             __syncthreads();  // every wave is done with step p
             stream_a(p + 2);
-            stream_b(DEEP ? p + 3 : p + 2);
+            stream_b(p + 2);
         };
         // THIN: three slots, one barrier per k-step.  Step p+2 is loaded
         // into the slots step p-1 used (free once every wave has passed this
@@ -884,12 +863,11 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
 }
 
 
-template <int MODE, int BN, bool GATHER, bool F8, bool THIN, bool DEEP>
-moe_status_t launch_gemm_k(const GemmArgs& args, hipStream_t st) {
-    using EP = Epi<MODE, BN, F8, THIN, DEEP>;
-    GemmArgs a = args;
-    a.minsteps = DEEP ? 3 : 2;  // the product and its tail reduction agree on the split
-    auto kern = grouped_gemm_kernel<MODE, BN, GATHER, F8, THIN, DEEP>;
+template <int MODE, int BN, bool GATHER = false, bool F8 = false, bool THIN = false>
+moe_status_t launch_gemm(const GemmArgs& args, hipStream_t st) {
+    using EP = Epi<MODE, BN, F8, THIN>;
+    const GemmArgs& a = args;
+    auto kern = grouped_gemm_kernel<MODE, BN, GATHER, F8, THIN>;
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)EP::LDS) != hipSuccess)
         return MOE_ERR_LAUNCH;
@@ -909,18 +887,6 @@ moe_status_t launch_gemm_k(const GemmArgs& args, hipStream_t st) {
         }
     }
     return MOE_OK;
-}
-
-// Full-size tiles take the deeper weight prefetch when K has at least three
-// k-steps (every split piece then keeps three).
-template <int MODE, int BN, bool GATHER = false, bool F8 = false, bool THIN = false>
-moe_status_t launch_gemm(const GemmArgs& a, hipStream_t st) {
-    if constexpr (THIN) {
-        return launch_gemm_k<MODE, BN, GATHER, F8, true, false>(a, st);
-    } else {
-        if (a.K / kBK >= 3) return launch_gemm_k<MODE, BN, GATHER, F8, false, true>(a, st);
-        return launch_gemm_k<MODE, BN, GATHER, F8, false, false>(a, st);
-    }
 }
 
 // A single-matrix product (GELU first product, down product) can run with
