@@ -12,7 +12,8 @@
 //
 // Design (gfx950): one persistent kernel per product.  The tile list is
 // rebuilt on the device from kept[e] (no host round trip): expert e has
-// ceil(kept[e] / 256) row tiles times N / BN_OUT column tiles.  Workgroup b
+// ceil(kept[e] / 256) row tiles times N / BN_OUT column tiles, and last row
+// tiles of at most 64 rows are scheduled after all other tiles.  Workgroup b
 // sits on XCD b % 8; in full rounds it takes tile r*G + (b % 8)*(G/8) + b/8,
 // so each XCD works through a contiguous run of tiles, ordered expert by
 // expert in groups that cover every row tile of an expert across a few
@@ -54,9 +55,10 @@
 //   SwiGLU:  a tile holds matching gate and up columns, so
 //            h = silu(g) * u needs no extra pass;
 //   GELU:    h = gelu_erf(acc + b1);   second product: y = acc (+ b2).
-// h is rounded to bf16, y stays fp32; both are stored straight from the
-// accumulators through a descriptor that ends at row kept[e], so the
-// hardware drops the padding rows' stores.
+// h is rounded to bf16, y stays fp32; a quad transpose gives each lane four
+// consecutive columns, stored with one 8- or 16-byte store through a
+// descriptor that ends at row kept[e], so the hardware drops the padding
+// rows' stores.
 #include "moe_common.h"
 #include "gemm_common.h"
 #include "internal.h"
