@@ -799,7 +799,7 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g, int G) {
             if (MB == MODE_DOWN)
                 static_cast<float*>(g.out)[o] = v;
             else
-                static_cast<uint16_t*>(g.out)[o] = bf16_rn(v);
+                static_cast<uint16_t*>(g.out)[o] = (uint16_t)f2bf(v);
         }
     }
 }

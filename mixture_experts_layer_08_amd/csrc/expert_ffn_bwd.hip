@@ -389,18 +389,22 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
             const int vel = (wm * WM_ROWS + lane % 32) * g.N + wn * WN_COLS + (lane / 32) * 4;
             if (EPI == EPI_F32) {
                 // plain layout: element q of lane l is row 8*(q/4) + 4*(l/32) +
-                // q%4, column l%32 of its 32 x 32 block
+                // q%4, column l%32 of its 32 x 32 block; a quad transpose over
+                // each four rows leaves lane l with row 8*(q/4) + 4*(l/32) +
+                // l%4, columns (l%32 & ~3) .. +3: one 16-byte store
                 const i32x4_t rsO = make_rsrc(static_cast<float*>(g.out) + obase, obytes * 4);
-                const int row_l = wm * WM_ROWS + (lane / 32) * 4;
+                const int row_t = wm * WM_ROWS + (lane / 32) * 4 + (lane & 3);
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
-                    const int voff = (row_l * g.N + wn * WN_COLS + j * 32 + lane % 32) * 4;
+                    const int voff = (row_t * g.N + wn * WN_COLS + j * 32 + ((lane % 32) & ~3)) * 4;
 #pragma unroll
                     for (int i = 0; i < TM; ++i)
 #pragma unroll
-                        for (int q = 0; q < 16; ++q)
-                            buffer_store_f32(acc[i][j][q], rsO, voff,
-                                             ((i * 32 + (q / 4) * 8 + (q % 4)) * g.N) * 4, 0);
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            const float v[4] = {acc[i][j][4 * q4], acc[i][j][4 * q4 + 1],
+                                                acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]};
+                            store_rows4_f32(v, rsO, voff, ((i * 32 + q4 * 8) * g.N) * 4, lane);
+                        }
                 }
             } else {
                 const i32x4_t rsO = make_rsrc(static_cast<uint16_t*>(g.out) + obase, obytes * 2);
@@ -434,7 +438,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
                                 if (EPI == EPI_DH_SWIGLU) {
                                     const uint32_t wu = (uint32_t)su[qq][c / 2];
                                     const float u = (c & 1) ? bf_hi(wu) : bf_lo(wu);
-                                    const float sg = 1.0f / (1.0f + __expf(-a));
+                                    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-a));
                                     const float dsilu = sg * (1.0f + a * (1.0f - sg));
                                     r0[c] = dh * u * dsilu;
                                     r1[c] = dh * a * sg;
@@ -536,7 +540,7 @@ __global__ __launch_bounds__(256) void bwd_tail_reduce_kernel(BwdArgs g, int G) 
                 if (EPI == EPI_DH_SWIGLU) {
                     const uint32_t xu = c < 2 ? wu.x : wu.y;
                     const float u = (c & 1) ? bf_hi(xu) : bf_lo(xu);
-                    const float sg = 1.0f / (1.0f + __expf(-a));
+                    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-a));
                     const float dsilu = sg * (1.0f + a * (1.0f - sg));
                     r0[c] = dh[c] * u * dsilu;
                     r1[c] = dh[c] * a * sg;

@@ -118,17 +118,6 @@ __device__ __forceinline__ float gelu_f(float z) {
     return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
 }
 
-// Round to nearest even bf16 (v_cvt_pk_bf16_f32), two values per word, lo
-// in the low half.
-typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    const bf16x2_v v = {(__bf16)lo, (__bf16)hi};
-    return __builtin_bit_cast(uint32_t, v);
-}
-__device__ __forceinline__ uint16_t bf16_rn(float f) {
-    return __builtin_bit_cast(uint16_t, (__bf16)f);
-}
-
 // Exchange inside lane pairs (CTRL 0xB1: lanes XOR 1) or pairs of pairs
 // (CTRL 0x4E: lanes XOR 2) by DPP quad permutes: the lower lane of a pair
 // keeps a and receives the partner's a into b; the upper lane keeps b and
@@ -153,8 +142,8 @@ __device__ __forceinline__ void store_rows4_bf16(const float (&v)[4], i32x4_t rs
     uint32_t w2 = __float_as_uint(v[2]), w3 = __float_as_uint(v[3]);
     quad_xchg<0xB1>(w0, w1, lane & 1);
     quad_xchg<0xB1>(w2, w3, lane & 1);
-    uint32_t p0 = pack_bf16x2(__uint_as_float(w0), __uint_as_float(w1));
-    uint32_t p1 = pack_bf16x2(__uint_as_float(w2), __uint_as_float(w3));
+    uint32_t p0 = pack_bf2(__uint_as_float(w0), __uint_as_float(w1));
+    uint32_t p1 = pack_bf2(__uint_as_float(w2), __uint_as_float(w3));
     quad_xchg<0x4E>(p0, p1, lane & 2);
     moe_i32x2_t o;
     o.x = (int)p0;

@@ -22,15 +22,16 @@ __device__ __forceinline__ float bf2f(uint32_t b16) {
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// fp32 -> bf16 bit pattern, round to nearest, ties to even; NaN stays NaN.
+// fp32 -> bf16 bit pattern, round to nearest, ties to even; NaN stays NaN
+// (v_cvt_pk_bf16_f32, two values per instruction in pack_bf2, lo in the
+// low half).
+typedef __bf16 bf16x2_pk_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x40u;
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-    return f2bf(lo) | (f2bf(hi) << 16);
+    const bf16x2_pk_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
