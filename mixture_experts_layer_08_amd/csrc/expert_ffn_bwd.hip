@@ -105,10 +105,6 @@ struct BTile {
 template <int SCHED, int EPI>
 __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs g) {
     constexpr bool KC = SCHED == SCHED_DGRAD;   // both operands k-contiguous
-    // dh epilogues run with the operands swapped (four consecutive columns
-    // per lane: vector side reads); fp32 outputs keep the plain layout, whose
-    // stores cover 128 contiguous bytes of a row per half-wave
-    constexpr bool SWAP = EPI != EPI_F32;
     constexpr int kStage = 2 * kStageA;         // A 32 KB + B 32 KB
     constexpr int WM_ROWS = kBM / kWMn, WN_COLS = kBNMax / kWN;
     constexpr int TM = WM_ROWS / 32, TN = WN_COLS / 32;
@@ -294,10 +290,8 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
-                        acc[i][j] = SWAP ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                               bfr[ss][j], af[ss][i], acc[i][j], 0, 0, 0)
-                                         : __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                               af[ss][i], bfr[ss][j], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ss][i], bfr[ss][j],
+                                                                            acc[i][j], 0, 0, 0);
         };
         // The forward's pipeline: one barrier per k-step, the second half of
         // step kt read while the first half's MFMAs run, step kt+2's loads
@@ -375,25 +369,21 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
             break;
         }
 
-        // epilogue.  The dh products run with the operands swapped (C^T =
-        // B^T A^T), so accumulator element q of lane l is output row l%32 and
-        // column 8*(q/4) + 4*(l/32) + q%4 of its 32 x 32 block: four
-        // consecutive columns per lane, read (g, u or z) and written (dg, du
-        // or dz) as one 8-byte access each.  fp32 outputs use the plain
-        // layout.  Descriptors end at the last valid row, so padding rows are
-        // neither read nor written.
+        // epilogue.  Element q of a 32 x 32 accumulator in lane l is row
+        // 8*(q/4) + 4*(l/32) + q%4, column l%32 of its block; a quad transpose
+        // over each four rows leaves lane l with row 8*(q/4) + 4*(l/32) + l%4,
+        // columns (l%32 & ~3) .. +3, so fp32 outputs go out as one 16-byte
+        // store and the dh epilogues read g, u (or z) and write dg, du (or dz)
+        // with one 8-byte access each: every access of a wave covers 8 rows of
+        // 64 or 128 contiguous bytes.  Descriptors end at the last valid row,
+        // so padding rows are neither read nor written.
         {
             const int R = KC ? (int)g.C : g.M;  // rows of the output per expert
             const size_t obase = ((size_t)cur.e * R + cur.m0) * g.N + cur.n0;
             const uint32_t obytes = (uint32_t)(((size_t)cur.rows * g.N - cur.n0));
-            const int vel = (wm * WM_ROWS + lane % 32) * g.N + wn * WN_COLS + (lane / 32) * 4;
+            const int row_t = wm * WM_ROWS + (lane / 32) * 4 + (lane & 3);
             if (EPI == EPI_F32) {
-                // plain layout: element q of lane l is row 8*(q/4) + 4*(l/32) +
-                // q%4, column l%32 of its 32 x 32 block; a quad transpose over
-                // each four rows leaves lane l with row 8*(q/4) + 4*(l/32) +
-                // l%4, columns (l%32 & ~3) .. +3: one 16-byte store
                 const i32x4_t rsO = make_rsrc(static_cast<float*>(g.out) + obase, obytes * 4);
-                const int row_t = wm * WM_ROWS + (lane / 32) * 4 + (lane & 3);
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const int voff = (row_t * g.N + wn * WN_COLS + j * 32 + ((lane % 32) & ~3)) * 4;
@@ -414,52 +404,61 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
                     rsO1 = make_rsrc(g.out1 + obase, obytes * 2);
                     rs1 = make_rsrc(g.side1 + obase, obytes * 2);
                 }
+                // side reads of the next 32 x 32 block are in flight while the
+                // current block's math and stores run
+                moe_i32x2_t sa[2][4], su[2][4];
+                auto side = [&](int blk, moe_i32x2_t (&a)[4], moe_i32x2_t (&u)[4]) {
+                    const int i = blk % TM, j = blk / TM;
+                    const int voff = (row_t * g.N + wn * WN_COLS + j * 32 + ((lane % 32) & ~3)) * 2;
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int so = ((i * 32 + q4 * 8) * g.N) * 2;
+                        a[q4] = buffer_load_i32x2(rs0, voff, so, 0);
+                        if (EPI == EPI_DH_SWIGLU) u[q4] = buffer_load_i32x2(rs1, voff, so, 0);
+                    }
+                };
+                side(0, sa[0], su[0]);
 #pragma unroll
-                    for (int j = 0; j < TN; ++j) {
-                        // all side reads of this 32 x 32 block first, then the math
-                        moe_i32x2_t sa[4], su[4];
+                for (int blk = 0; blk < TM * TN; ++blk) {
+                    const int i = blk % TM, j = blk / TM;
+                    if (blk + 1 < TM * TN) side(blk + 1, sa[(blk + 1) & 1], su[(blk + 1) & 1]);
+                    const int voff = (row_t * g.N + wn * WN_COLS + j * 32 + ((lane % 32) & ~3)) * 2;
 #pragma unroll
-                        for (int qq = 0; qq < 4; ++qq) {
-                            const int so = (i * 32 * g.N + j * 32 + qq * 8) * 2;
-                            sa[qq] = buffer_load_i32x2(rs0, vel * 2, so, 0);
-                            if (EPI == EPI_DH_SWIGLU) su[qq] = buffer_load_i32x2(rs1, vel * 2, so, 0);
-                        }
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int so = ((i * 32 + q4 * 8) * g.N) * 2;
+                        float dh[4] = {acc[i][j][4 * q4], acc[i][j][4 * q4 + 1],
+                                       acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]};
+                        quad_transpose_f32(dh, lane);
+                        float r0[4], r1[4];
 #pragma unroll
-                        for (int qq = 0; qq < 4; ++qq) {
-                            const int so = (i * 32 * g.N + j * 32 + qq * 8) * 2;
-                            float r0[4], r1[4];
-#pragma unroll
-                            for (int c = 0; c < 4; ++c) {
-                                const uint32_t wa = (uint32_t)sa[qq][c / 2];
-                                const float a = (c & 1) ? bf_hi(wa) : bf_lo(wa);
-                                const float dh = acc[i][j][qq * 4 + c];
-                                if (EPI == EPI_DH_SWIGLU) {
-                                    const uint32_t wu = (uint32_t)su[qq][c / 2];
-                                    const float u = (c & 1) ? bf_hi(wu) : bf_lo(wu);
-                                    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-a));
-                                    const float dsilu = sg * (1.0f + a * (1.0f - sg));
-                                    r0[c] = dh * u * dsilu;
-                                    r1[c] = dh * a * sg;
-                                } else {
-                                    const float cdf = 0.5f * (1.0f + erff(a * 0.70710678118654752f));
-                                    const float pdf = 0.39894228040143268f * __expf(-0.5f * a * a);
-                                    r0[c] = dh * (cdf + a * pdf);
-                                }
-                            }
-                            moe_i32x2_t o0;
-                            o0.x = (int)pack_bf2(r0[0], r0[1]);
-                            o0.y = (int)pack_bf2(r0[2], r0[3]);
-                            buffer_store_i32x2(o0, rsO, vel * 2, so, 0);
+                        for (int c = 0; c < 4; ++c) {
+                            const uint32_t wa = (uint32_t)sa[blk & 1][q4][c / 2];
+                            const float a = (c & 1) ? bf_hi(wa) : bf_lo(wa);
                             if (EPI == EPI_DH_SWIGLU) {
-                                moe_i32x2_t o1;
-                                o1.x = (int)pack_bf2(r1[0], r1[1]);
-                                o1.y = (int)pack_bf2(r1[2], r1[3]);
-                                buffer_store_i32x2(o1, rsO1, vel * 2, so, 0);
+                                const uint32_t wu = (uint32_t)su[blk & 1][q4][c / 2];
+                                const float u = (c & 1) ? bf_hi(wu) : bf_lo(wu);
+                                const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+                                const float dsilu = sg * (1.0f + a * (1.0f - sg));
+                                r0[c] = dh[c] * u * dsilu;
+                                r1[c] = dh[c] * a * sg;
+                            } else {
+                                const float cdf = 0.5f * (1.0f + erff(a * 0.70710678118654752f));
+                                const float pdf = 0.39894228040143268f * __expf(-0.5f * a * a);
+                                r0[c] = dh[c] * (cdf + a * pdf);
                             }
+                        }
+                        moe_i32x2_t o0;
+                        o0.x = (int)pack_bf2(r0[0], r0[1]);
+                        o0.y = (int)pack_bf2(r0[2], r0[3]);
+                        buffer_store_i32x2(o0, rsO, voff, so, 0);
+                        if (EPI == EPI_DH_SWIGLU) {
+                            moe_i32x2_t o1;
+                            o1.x = (int)pack_bf2(r1[0], r1[1]);
+                            o1.y = (int)pack_bf2(r1[2], r1[3]);
+                            buffer_store_i32x2(o1, rsO1, voff, so, 0);
                         }
                     }
+                }
             }
         }
         if (!nxt.valid) break;
@@ -472,7 +471,10 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
 // recomputes the schedule from kept[], sums each element's partials in piece
 // order (the result does not depend on which piece finished first) and runs
 // the product's epilogue.  A work item is one 16-byte group of one product
-// thread (four consecutive output columns of one row).
+// thread: rows row0 .. row0+3 of one output column.  The four threads of a
+// quad hold four consecutive columns (consecutive product threads), so the
+// dh epilogues transpose each quad as the product does and read and write
+// four consecutive columns of one row per thread.
 template <int EPI>
 __global__ __launch_bounds__(256) void bwd_tail_reduce_kernel(BwdArgs g, int G) {
     constexpr int WM_ROWS = kBM / kWMn, WN_COLS = kBNMax / kWN;
@@ -510,9 +512,9 @@ __global__ __launch_bounds__(256) void bwd_tail_reduce_kernel(BwdArgs g, int G) 
             const float4 v = part[base + pc * PSTRIDE];
             s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
         }
+        // the group holds rows row0 .. row0+3 of one column
+        const int row0 = m0 + wm * WM_ROWS + i * 32 + 8 * q4 + 4 * (vlane / 32);
         if (EPI == EPI_F32) {
-            // plain layout: the group holds rows row0 .. row0+3 of one column
-            const int row0 = m0 + wm * WM_ROWS + i * 32 + 8 * q4 + 4 * (vlane / 32);
             const int col = n0 + wn * WN_COLS + j * 32 + vlane % 32;
             const float v4[4] = {s.x, s.y, s.z, s.w};
 #pragma unroll
@@ -522,13 +524,15 @@ __global__ __launch_bounds__(256) void bwd_tail_reduce_kernel(BwdArgs g, int G) 
             }
             continue;
         }
-        // swapped layout: the group holds four consecutive columns of one row
-        const int row = m0 + wm * WM_ROWS + i * 32 + vlane % 32;
+        // quad transpose (every lane of the wave is here: the skip above is
+        // per wave): row row0 + vlane % 4, columns col4 .. col4 + 3
+        float dh[4] = {s.x, s.y, s.z, s.w};
+        quad_transpose_f32(dh, vlane);
+        const int row = row0 + (vlane & 3);
         if (row >= kept) continue;                         // not an output row
-        const int col = n0 + wn * WN_COLS + j * 32 + 8 * q4 + 4 * (vlane / 32);
-        const size_t o = ((size_t)e * g.C + row) * g.N + col;
+        const int col4 = n0 + wn * WN_COLS + j * 32 + ((vlane % 32) & ~3);
+        const size_t o = ((size_t)e * g.C + row) * g.N + col4;
         {
-            const float dh[4] = {s.x, s.y, s.z, s.w};
             const uint2 wa = *reinterpret_cast<const uint2*>(g.side0 + o);
             uint2 wu = make_uint2(0u, 0u);
             if (EPI == EPI_DH_SWIGLU) wu = *reinterpret_cast<const uint2*>(g.side1 + o);

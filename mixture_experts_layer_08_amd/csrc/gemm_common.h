@@ -150,19 +150,29 @@ __device__ __forceinline__ void store_rows4_bf16(const float (&v)[4], i32x4_t rs
     o.y = (int)p1;
     buffer_store_i32x2(o, rs, voff, soff, 0);
 }
-__device__ __forceinline__ void store_rows4_f32(const float (&v)[4], i32x4_t rs, int voff,
-                                                int soff, int lane) {
+// The transpose alone (fp32): v[0..3] = rows r .. r+3 of column c0 + (lane
+// & 3) in, row r + (lane & 3), columns c0 .. c0+3 out.
+__device__ __forceinline__ void quad_transpose_f32(float (&v)[4], int lane) {
     uint32_t w0 = __float_as_uint(v[0]), w1 = __float_as_uint(v[1]);
     uint32_t w2 = __float_as_uint(v[2]), w3 = __float_as_uint(v[3]);
     quad_xchg<0xB1>(w0, w1, lane & 1);
     quad_xchg<0xB1>(w2, w3, lane & 1);
     quad_xchg<0x4E>(w0, w2, lane & 2);
     quad_xchg<0x4E>(w1, w3, lane & 2);
+    v[0] = __uint_as_float(w0);
+    v[1] = __uint_as_float(w1);
+    v[2] = __uint_as_float(w2);
+    v[3] = __uint_as_float(w3);
+}
+__device__ __forceinline__ void store_rows4_f32(const float (&vin)[4], i32x4_t rs, int voff,
+                                                int soff, int lane) {
+    float v[4] = {vin[0], vin[1], vin[2], vin[3]};
+    quad_transpose_f32(v, lane);
     f32x4_t o;
-    o.x = __uint_as_float(w0);
-    o.y = __uint_as_float(w1);
-    o.z = __uint_as_float(w2);
-    o.w = __uint_as_float(w3);
+    o.x = v[0];
+    o.y = v[1];
+    o.z = v[2];
+    o.w = v[3];
     // The whole offset goes in the vector operand, soffset stays 0: with a
     // register soffset, the compiler let the next VALU write the store's data
     // registers at once, and the first dword of some lanes' stores then held
