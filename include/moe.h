@@ -395,7 +395,8 @@ moe_status_t moe_dispatch_bwd(void* stream, const float* dx_disp,
  *   dlogits [T, E] fp32 out   gradient of the router logits
  *   dx      [T, H] fp32 in/out dx += dlogits W_r^T (NULL: skipped)
  *   dw_r    [H, E] fp32 out;  db_r [E] fp32 out (NULL when there is no bias)
- *   ws      moe_route_bwd_ws_bytes(T, H, E) bytes */
+ *   ws      moe_route_bwd_ws_bytes(T, H, E) bytes
+ * H a multiple of 8; x, w_r, dx and ws 16-byte aligned (MOE_ERR_ALIGN). */
 moe_status_t moe_route_bwd(void* stream, moe_dtype_t dtype, moe_route_mode_t mode,
                            const void* x, const void* w_r, const float* probs,
                            const int32_t* topk_idx, const float* topk_w,

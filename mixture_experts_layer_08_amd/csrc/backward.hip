@@ -138,15 +138,32 @@ __global__ __launch_bounds__(256) void route_bwd_dx_kernel(const float* __restri
         for (int e0 = 0; e0 < E; e0 += 8) {
             const int ne = E - e0 < 8 ? E - e0 : 8;
             float wv[8][8];
+            if (ne == 8 && E % 8 == 0) {  // 8 experts of a W_r row: one or two 16-byte loads
 #pragma unroll
-            for (int c = 0; c < 8; ++c)
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int64_t o = (int64_t)(h0 + c) * E + e0 + u;
-                    wv[c][u] = u < ne ? (BF16 ? bf2f(static_cast<const uint16_t*>(w_r)[o])
-                                              : static_cast<const float*>(w_r)[o])
-                                      : 0.f;
+                for (int c = 0; c < 8; ++c) {
+                    const int64_t o = (int64_t)(h0 + c) * E + e0;
+                    if (BF16) {
+                        const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(w_r) + o);
+                        wv[c][0] = bf_lo(q.x); wv[c][1] = bf_hi(q.x); wv[c][2] = bf_lo(q.y); wv[c][3] = bf_hi(q.y);
+                        wv[c][4] = bf_lo(q.z); wv[c][5] = bf_hi(q.z); wv[c][6] = bf_lo(q.w); wv[c][7] = bf_hi(q.w);
+                    } else {
+                        const float4 q0 = *reinterpret_cast<const float4*>(static_cast<const float*>(w_r) + o);
+                        const float4 q1 = *reinterpret_cast<const float4*>(static_cast<const float*>(w_r) + o + 4);
+                        wv[c][0] = q0.x; wv[c][1] = q0.y; wv[c][2] = q0.z; wv[c][3] = q0.w;
+                        wv[c][4] = q1.x; wv[c][5] = q1.y; wv[c][6] = q1.z; wv[c][7] = q1.w;
+                    }
                 }
+            } else {
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int64_t o = (int64_t)(h0 + c) * E + e0 + u;
+                        wv[c][u] = u < ne ? (BF16 ? bf2f(static_cast<const uint16_t*>(w_r)[o])
+                                                  : static_cast<const float*>(w_r)[o])
+                                          : 0.f;
+                    }
+            }
 #pragma unroll
             for (int i = 0; i < kDxTok; ++i) {
 #pragma unroll
@@ -170,50 +187,101 @@ __global__ __launch_bounds__(256) void route_bwd_dx_kernel(const float* __restri
     }
 }
 
-// Partial sums over token chunks: part[b][h][e] = sum_{t in chunk b} x[t, h]
-// dl[t, e] (thread: one h, 8 experts), and pb[b][e] = sum_{t in chunk b}
-// dl[t, e] (first column block only).  Chunks are summed in order below.
+// Partial sums over token chunks: part[b][e][h] = sum_{t in chunk b} x[t, h]
+// dl[t, e], and pb[b][e] = sum_{t in chunk b} dl[t, e] (first column block
+// only).  One wave per block: lane l takes the 8 consecutive columns h0 =
+// blockIdx.y * 512 + 8 l (one 16-byte load of x per token for bf16) and 8
+// experts e0.., with dl of the chunk staged in LDS; tokens are summed in
+// order, and the chunks in chunk order below.  A lane stores its 8 columns
+// of one expert as two 16-byte stores (a wave: 2 KB contiguous).
+constexpr int kWpCols = 512;  // columns per block
 template <bool BF16>
-__global__ __launch_bounds__(256) void route_bwd_wpart_kernel(const void* __restrict__ x,
-                                                              const float* __restrict__ dl,
-                                                              int64_t T, int H, int E, int tb,
-                                                              float* __restrict__ part,
-                                                              float* __restrict__ pb) {
+__global__ __launch_bounds__(64) void route_bwd_wpart_kernel(const void* __restrict__ x,
+                                                             const float* __restrict__ dl,
+                                                             int64_t T, int H, int E, int tb,
+                                                             float* __restrict__ part,
+                                                             float* __restrict__ pb) {
     __shared__ float s_dl[64 * 8];
+    const int lane = threadIdx.x;
     const int b = blockIdx.x;
-    const int h = blockIdx.y * 256 + threadIdx.x;
+    const int h0 = blockIdx.y * kWpCols + lane * 8;
     const int e0 = blockIdx.z * 8;
     const int ne = E - e0 < 8 ? E - e0 : 8;
+    const bool live = h0 < H;  // H is a multiple of 8
     const int64_t t0 = (int64_t)b * tb;
     int64_t t1 = t0 + tb;
     if (t1 > T) t1 = T;
-    float acc[8], accb[8];
+    float acc[8][8], accb[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = accb[c] = 0.f;
+    for (int c = 0; c < 8; ++c) {
+        accb[c] = 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[c][u] = 0.f;
+    }
     for (int64_t tc = t0; tc < t1; tc += 64) {
         const int n = (int)(t1 - tc < 64 ? t1 - tc : 64);
         __syncthreads();
-        for (int q = threadIdx.x; q < n * 8; q += 256) {
+        for (int q = lane; q < n * 8; q += 64) {
             const int tt = q / 8, c = q % 8;
             s_dl[q] = c < ne ? dl[(tc + tt) * E + e0 + c] : 0.f;
         }
         __syncthreads();
-#pragma unroll 8
-        for (int tt = 0; tt < n; ++tt) {
-            const float xv = h < H ? (BF16 ? bf2f(static_cast<const uint16_t*>(x)[(tc + tt) * H + h])
-                                           : static_cast<const float*>(x)[(tc + tt) * H + h])
-                                   : 0.f;
+        // x of 16 tokens in flight at once, then their FMAs in token order
+        for (int g0 = 0; g0 < n; g0 += 16) {
+            uint4 xq[16];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                acc[c] = fmaf(xv, s_dl[tt * 8 + c], acc[c]);
-                accb[c] += s_dl[tt * 8 + c];
+            for (int v = 0; v < 16; ++v) {
+                xq[v] = make_uint4(0u, 0u, 0u, 0u);
+                if (live && g0 + v < n) {
+                    if (BF16) {
+                        xq[v] = *reinterpret_cast<const uint4*>(
+                            static_cast<const uint16_t*>(x) + (tc + g0 + v) * H + h0);
+                    }
+                }
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                if (g0 + v >= n) break;
+                const int tt = g0 + v;
+                float xv[8];
+                if (BF16) {
+                    const uint4 q = xq[v];
+                    xv[0] = bf_lo(q.x); xv[1] = bf_hi(q.x); xv[2] = bf_lo(q.y); xv[3] = bf_hi(q.y);
+                    xv[4] = bf_lo(q.z); xv[5] = bf_hi(q.z); xv[6] = bf_lo(q.w); xv[7] = bf_hi(q.w);
+                } else if (live) {
+                    const float* xr = static_cast<const float*>(x) + (tc + tt) * H + h0;
+                    const float4 q0 = *reinterpret_cast<const float4*>(xr);
+                    const float4 q1 = *reinterpret_cast<const float4*>(xr + 4);
+                    xv[0] = q0.x; xv[1] = q0.y; xv[2] = q0.z; xv[3] = q0.w;
+                    xv[4] = q1.x; xv[5] = q1.y; xv[6] = q1.z; xv[7] = q1.w;
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) xv[c] = 0.f;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float d = s_dl[tt * 8 + u];
+                    accb[u] += d;
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) acc[c][u] = fmaf(xv[c], d, acc[c][u]);
+                }
             }
         }
     }
-    if (h < H)
-        for (int c = 0; c < ne; ++c) part[((int64_t)b * H + h) * E + e0 + c] = acc[c];
-    if (blockIdx.y == 0 && threadIdx.x == 0)
-        for (int c = 0; c < ne; ++c) pb[(int64_t)b * E + e0 + c] = accb[c];
+    if (live) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (u < ne) {
+                float4* o = reinterpret_cast<float4*>(part + ((int64_t)b * E + e0 + u) * H + h0);
+                o[0] = make_float4(acc[0][u], acc[1][u], acc[2][u], acc[3][u]);
+                o[1] = make_float4(acc[4][u], acc[5][u], acc[6][u], acc[7][u]);
+            }
+    }
+    if (blockIdx.y == 0 && lane == 0) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (u < ne) pb[(int64_t)b * E + e0 + u] = accb[u];
+    }
 }
 
 __global__ __launch_bounds__(256) void route_bwd_wfinal_kernel(const float* __restrict__ part,
@@ -221,6 +289,7 @@ __global__ __launch_bounds__(256) void route_bwd_wfinal_kernel(const float* __re
                                                                int nb, int H, int E,
                                                                float* __restrict__ dw_r,
                                                                float* __restrict__ db_r) {
+    // thread i: expert i / H, column i % H (the partials are [nb][E][H])
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < (int64_t)H * E) {
         float s = 0.f;
@@ -233,7 +302,7 @@ __global__ __launch_bounds__(256) void route_bwd_wfinal_kernel(const float* __re
             for (int u = 0; u < 8; ++u) s += v[u];
         }
         for (; b < nb; ++b) s += part[(int64_t)b * H * E + i];
-        dw_r[i] = s;
+        dw_r[(i % H) * E + i / H] = s;
     }
     if (db_r && i < E) {
         float s = 0.f;
@@ -242,9 +311,10 @@ __global__ __launch_bounds__(256) void route_bwd_wfinal_kernel(const float* __re
     }
 }
 
+// tokens per partial-sum chunk: at most 128 chunks, at least 32 tokens each
 int route_chunk(int64_t T) {
     int64_t tb = (T + 127) / 128;
-    if (tb < 64) tb = 64;
+    if (tb < 32) tb = 32;
     return (int)tb;
 }
 
@@ -299,6 +369,8 @@ extern "C" moe_status_t moe_route_bwd(void* stream, moe_dtype_t dtype, moe_route
     if (!dw_r || !w_r) return MOE_ERR_NULL;
     if (T > 0 && (!x || !probs || !topk_idx || !topk_w || !dw || !f || !dlogits)) return MOE_ERR_NULL;
     if (dx && !moe_aligned16(dx)) return MOE_ERR_ALIGN;
+    if (T > 0 && (!moe_aligned16(x) || !moe_aligned16(w_r) || (ws && !moe_aligned16(ws))))
+        return MOE_ERR_ALIGN;
     if (T > 0 && (!ws || ws_bytes < moe_route_bwd_ws_bytes(T, H, E))) return MOE_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool bf = dtype == MOE_BF16;
@@ -337,12 +409,12 @@ extern "C" moe_status_t moe_route_bwd(void* stream, moe_dtype_t dtype, moe_route
     const int nb = (int)((T + tb - 1) / tb);
     float* part = static_cast<float*>(ws);
     float* pb = part + (size_t)nb * H * E;
-    dim3 gw((unsigned)nb, (unsigned)((H + 255) / 256), (unsigned)((E + 7) / 8));
+    dim3 gw((unsigned)nb, (unsigned)((H + kWpCols - 1) / kWpCols), (unsigned)((E + 7) / 8));
     if (bf)
-        hipLaunchKernelGGL(route_bwd_wpart_kernel<true>, gw, dim3(256), 0, st, x, dlogits, T, (int)H,
+        hipLaunchKernelGGL(route_bwd_wpart_kernel<true>, gw, dim3(64), 0, st, x, dlogits, T, (int)H,
                            E, tb, part, pb);
     else
-        hipLaunchKernelGGL(route_bwd_wpart_kernel<false>, gw, dim3(256), 0, st, x, dlogits, T,
+        hipLaunchKernelGGL(route_bwd_wpart_kernel<false>, gw, dim3(64), 0, st, x, dlogits, T,
                            (int)H, E, tb, part, pb);
     MOE_CHECK_LAUNCH();
     hipLaunchKernelGGL(route_bwd_wfinal_kernel, dim3((unsigned)((H * E + 255) / 256)), dim3(256), 0,

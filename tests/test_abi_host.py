@@ -240,6 +240,30 @@ def test_dispatch_aux_argument_errors(L):
     assert d(xd=MIS) == ALIGN
 
 
+def route_bwd(L, dtype=1, mode=0, x=P, w=P, probs=P, idx=P, tw=P, dw=P, f=P, T=64, H=256, E=8,
+              k=2, seq=0, dl=P, dx=P, dwr=P, dbr=None, ws=P, wsb=1 << 30):
+    return L.moe_route_bwd(None, dtype, mode, x, w, probs, idx, tw, dw, f, 0.01, 0.5, T, H, E, k,
+                           seq, dl, dx, dwr, dbr, ws, wsb)
+
+
+def test_route_bwd_argument_errors(L):
+    assert route_bwd(L, dtype=7) == DTYPE
+    assert route_bwd(L, mode=3) == DTYPE
+    assert route_bwd(L, T=-1) == SHAPE
+    assert route_bwd(L, k=9, E=8) == SHAPE
+    assert route_bwd(L, E=65, k=2) == UNSUP
+    assert route_bwd(L, mode=1, seq=-1) == SHAPE
+    assert route_bwd(L, H=12) == ALIGN
+    assert route_bwd(L, dwr=None) == NULL
+    assert route_bwd(L, probs=None) == NULL
+    assert route_bwd(L, dx=MIS) == ALIGN
+    assert route_bwd(L, x=MIS) == ALIGN          # 16-byte vector loads of x rows
+    assert route_bwd(L, w=MIS) == ALIGN          # and of W_r rows
+    assert route_bwd(L, ws=MIS) == ALIGN         # 16-byte partial-sum stores
+    assert route_bwd(L, ws=None) == WS
+    assert route_bwd(L, wsb=16) == WS
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))

@@ -125,11 +125,19 @@ def test_backward_matches_oracle(name, train):
         f"worst weight-grad err/rms {worst:.3e}")
 
 
-@pytest.mark.parametrize("name", ["swiglu-e5-k3-bias", "gumbel-e16"])
+# router-only cases: E a multiple of 8 (the 16-byte W_r row loads), bf16
+# and fp32 inputs, token counts that end in a partial chunk
+ROUTE_CASES = {
+    "route-bf16-e8": MoEConfig("r-e8", "bf16", T=1000, H=512, I=256, E=8, k=2, cf=1.25, seed=37),
+    "route-f32-e8": MoEConfig("r-f32", "f32", T=300, H=136, I=64, E=8, k=2, cf=1.25, seed=38),
+}
+
+
+@pytest.mark.parametrize("name", ["swiglu-e5-k3-bias", "gumbel-e16"] + list(ROUTE_CASES))
 def test_route_bwd_on_oracle_inputs(name):
     """The router backward fed the oracle's own routing and dw: fp32
     arithmetic against float64, so 1e-4 of the matrix RMS."""
-    cfg = CASES[name]
+    cfg = CASES.get(name) or ROUTE_CASES[name]
     inp = make_inputs(cfg)
     g = np.random.default_rng(cfg.seed + 7)
     dy64 = bf16_bits_to_f32(f32_to_bf16_bits(g.standard_normal((cfg.T, cfg.H),
