@@ -380,7 +380,7 @@ def main():
               ("_fp8, e4m3 weights" if args.weights == "fp8" else "") + ": " +
               ("gate/up product with SwiGLU epilogue" if cfg.act == "swiglu" else
                "first product with bias + GELU epilogue") +
-              ", then down product, with their tail reductions)")
+              ", then down product; split last rounds finished in-kernel)")
     if t_hbm > t_mfma:
         roofline = {"bound": "hbm", "kernel": kernel, "achieved": round(ffn_gbs, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ffn_gbs / PEAK_HBM_GBS, 4),

@@ -193,12 +193,15 @@ moe_status_t moe_dispatch_aux(void* stream, moe_dtype_t dtype, const void* x,
  *                               the combine rounds only once); rows >=
  *                               kept[e] untouched
  *   ws     NULL, or a workspace of ws_bytes >= moe_expert_ffn_ws_bytes()
- *          bytes (16-byte aligned; contents need not be initialised).  With
- *          it, the second product's last, partly filled round of tiles is
- *          cut along K and the pieces' fp32 partial tiles are summed in a
- *          fixed order (results stay bitwise reproducible); without it, or
- *          when it is too small, that round runs whole.  Two calls that run
- *          at the same time must not share one ws.
+ *          bytes, 16-byte aligned and zero-filled before its first use (its
+ *          tile counters must start at zero; every call leaves them zero
+ *          again, so a workspace is cleared once, when it is allocated).
+ *          With it, each product's last, partly filled round of tiles is
+ *          cut along K: every piece stores its fp32 partial tile and the
+ *          piece that completes a tile sums the pieces in piece order
+ *          (results stay bitwise reproducible); without it, or when it is
+ *          too small, that round runs whole.  Two calls that run at the
+ *          same time must not share one ws.
  * bf16 runs on the matrix cores with fp32 accumulation; h is rounded to bf16
  * (nearest-even) between the two products.  An expert with kept = 0 is a
  * valid no-op.  bf16 limits: H a multiple of 256, I a multiple of 128
@@ -281,7 +284,8 @@ moe_status_t moe_expert_ffn_gather_fp8(void* stream, moe_act_t act, const void* 
                                        void* ws, size_t ws_bytes);
 
 /* Bytes of the optional moe_expert_ffn workspace on the current device:
- * 4 KiB of counters plus one 256 KiB fp32 tile per compute unit. */
+ * one 256 KiB fp32 tile per compute unit, then one 4-byte tile counter per
+ * compute unit (rounded up to 256 bytes). */
 size_t moe_expert_ffn_ws_bytes(void);
 
 /* Weighted combine back to token order.  [P1] section 2.4 and [P2]
@@ -346,7 +350,9 @@ moe_status_t moe_combine_bwd(void* stream, moe_dtype_t dtype, const void* dy,
  *   dx_disp [E, C, H] fp32 out   rows < kept[e] written
  *   dw1 [E, H, I], dw3 [E, H, I] (SwiGLU), dw2 [E, I, H]   fp32 out
  *   db1 [E, I] (GELU, required), db2 [E, H] (GELU, may be NULL)  fp32 out
- *   ws      moe_expert_ffn_bwd_ws_bytes(E, C, I) bytes, 16-byte aligned
+ *   ws      moe_expert_ffn_bwd_ws_bytes(E, C, I) bytes, 16-byte aligned,
+ *           zero-filled before its first use (the tile counters at its end;
+ *           every call leaves them zero again)
  *   saved   0: recompute the first product; else ws holds its saved planes
  * bf16 only (MOE_ERR_UNSUPPORTED for fp32); H and I multiples of 256. An
  * expert with no rows gets zero weight gradients. */
@@ -359,14 +365,15 @@ moe_status_t moe_expert_ffn_bwd(void* stream, moe_dtype_t dtype, moe_act_t act,
                                 void* ws, size_t ws_bytes, int saved);
 
 /* Bytes of moe_expert_ffn_bwd's workspace on the current device: five bf16
- * [E, C, I] planes, then one 256 KiB fp32 tile per compute unit (the split
- * tail rounds of the two input-gradient products). */
+ * [E, C, I] planes, then moe_expert_ffn_ws_bytes() bytes (the partial tiles
+ * of the split tail rounds and the forward products' tile counters). */
 size_t moe_expert_ffn_bwd_ws_bytes(int E, int64_t C, int64_t I);
 
 /* Training forward of the expert FFNs: the result of moe_expert_ffn
  * (y_disp [E, C, H] fp32; same products, same bounds), with h and the first
  * product's pre-activations written into ws (moe_expert_ffn_bwd_ws_bytes
- * bytes) for a later moe_expert_ffn_bwd(..., saved = 1) on the same x_disp,
+ * bytes, zero-filled before its first use as for moe_expert_ffn_bwd) for a
+ * later moe_expert_ffn_bwd(..., saved = 1) on the same x_disp,
  * kept and weights, which then skips its recompute (P3 section 3.3 trades
  * that recompute against memory; here the memory is five bf16 [E, C, I]
  * planes).  bf16 only; H and I multiples of 256. */

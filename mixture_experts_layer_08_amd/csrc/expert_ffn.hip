@@ -20,7 +20,8 @@
 // column tiles, and the A rows and B panels a group shares stay in that
 // XCD's L2.  The last, partly filled round goes round-robin over the XCDs;
 // when it would leave at least half of the workgroups idle its tiles are cut
-// along K into pieces, and tail_reduce_kernel finishes them.
+// along K into pieces, one per workgroup, and the piece that completes a
+// tile's count of stored pieces sums them and finishes the tile.
 //
 // Per tile: 256 x 256 outputs of the B tile (for SwiGLU 128 gate + 128 up
 // columns), K in steps of 64, 8 waves in a 2 x 4 grid, each wave 128 rows x
@@ -99,6 +100,7 @@ struct GemmArgs {
     int N;                  // output columns
     // split-K of the last, partly filled round of tiles (null part: off)
     float* part;            // per-piece fp32 partial tiles, kPartBytes each
+    uint32_t* cnt;          // per split tile: pieces stored so far (zero between launches)
     int smax;               // at most this many pieces per tile
     uint16_t* save0;        // *_SAVE modes: [E, C, N_out] g (or z)
     uint16_t* save1;        // SwiGLU: [E, C, N_out] u
@@ -224,7 +226,8 @@ struct Epi {
     static constexpr int STAGE_B = kBK * BN * (F8 ? 1 : 2);  // 32 or 16 KB (8 or 16 KB for codes)
     static constexpr int BN_OUT = (MB == MODE_SWIGLU) ? BN / 2 : BN;
     static constexpr int OUT_BYTES = (MB == MODE_DOWN) ? 4 : 2;
-    static constexpr size_t LDS = (size_t)NS * (STAGE_A + STAGE_B);
+    static constexpr size_t SLOTS = (size_t)NS * (STAGE_A + STAGE_B);
+    static constexpr size_t LDS = SLOTS + 16;  // + a word that broadcasts a split tile's state
     static_assert(LDS <= 160 * 1024, "LDS of one compute unit");
 };
 
@@ -270,8 +273,9 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
     const int nk = g.K / kBK;
     // Whole tiles fill `full` rounds; the last round's `remt` tiles may be cut
     // along K into `splits` pieces, one per workgroup.  A piece stores its
-    // fp32 partial tile; tail_reduce_kernel, launched next, sums the pieces
-    // of each tile in piece order and runs the epilogue.
+    // fp32 partial tile and counts itself in the tile's counter; the piece
+    // that completes the count sums the pieces in piece order and runs the
+    // epilogue.
     const int full = total / G;
     const int remt = total - full * G;
     const int splits = __builtin_amdgcn_readfirstlane(tail_splits(g, total, G, nk));
@@ -453,6 +457,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
 
     TileCtx cur = tile_at(0);
     if (!cur.valid) return;
+    bool finish = false;  // this workgroup finishes its split tile after the loop
     // the first two steps of the stream, in the order the loop issues them
     // (the partial wait at a tile's start counts on it)
     issue_a(cur, cur.kb, 0);
@@ -615,13 +620,20 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
         }
 
         if (cur.pslot >= 0) {
-            // a piece of a split tail tile: store the fp32 partial, lane-major
-            // (16-byte group gi of thread tid at gi * kGThreads + tid); the
-            // tail reduction finishes the tile.  Pieces are the last round.
+            // A piece of a split tail tile (pieces are the last round): store
+            // the fp32 partial, lane-major (16-byte group gi of thread tid at
+            // gi * kGThreads + tid), skipping 32-row blocks wholly past
+            // kept[e], which nobody reads.  The pieces of a tile sit on
+            // different XCDs, each with its own L2, so partials are written
+            // and read at system scope (through to memory), and a piece counts
+            // itself in the tile's counter (a system-scope atomic) only once
+            // every wave's stores have completed.  The piece that brings the
+            // count to `splits` finishes the tile after the loop and sets the
+            // counter back to zero for the next launch; the others are done.
+            // (No L2-wide write-back or invalidate: those cost tens of
+            // microseconds when every piece does them.)
             const i32x4_t rsP = make_rsrc(g.part + (size_t)cur.pslot * (kPartBytes / 4),
                                           (uint32_t)kPartBytes);
-            // (32-row blocks wholly past kept[e] are skipped: the reduction
-            // never reads them)
             constexpr int NG = TM * TN * 4;
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
@@ -632,8 +644,21 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
                 v.y = acc[i][j][4 * q4 + 1];
                 v.z = acc[i][j][4 * q4 + 2];
                 v.w = acc[i][j][4 * q4 + 3];
-                buffer_store_f32x4(v, rsP, (gi * kGThreads + tid) * 16, 0, 0);
+                buffer_store_f32x4(v, rsP, (gi * kGThreads + tid) * 16, 0, kAuxSystem);
             }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            uint32_t* last = reinterpret_cast<uint32_t*>(smem + EP::SLOTS);
+            if (tid == 0) {
+                uint32_t* cnt = g.cnt + cur.pslot / splits;
+                const uint32_t before =
+                    __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                const bool fin = before == (uint32_t)(splits - 1);
+                if (fin) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                *last = fin ? 1u : 0u;
+            }
+            __syncthreads();
+            finish = *last != 0u;
             break;
         }
 
@@ -713,93 +738,89 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
         p0 += cur.nks;
         cur = tile_at(round + 1);  // recomputed: only what the prefetch needs stays live
     }
-}
+    if (SAVE || !finish) return;  // (the training variants never split)
 
-// ------------------------------------------------------- tail reduction ----
-// Finishes the split tail tiles of one grouped_gemm_kernel<MODE, BN> launch
-// of G workgroups: recomputes the same schedule from kept[], sums each
-// element's partials in piece order (the result does not depend on which
-// piece finished first) and runs the product's epilogue.  A work item is one
-// group of four accumulator values of one product thread, in the product's
-// register layout, so partial reads are 16-byte and coalesced.
-template <int MODE, int BN, bool THIN>
-__global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs g, int G) {
-    using EP = Epi<MODE, BN, false, THIN>;
-    constexpr int MB = mode_base(MODE);
-    constexpr int WM_ROWS = EP::BM / kWMn, WN_COLS = BN / kWN;
-    constexpr int TM = WM_ROWS / 32, TN = WN_COLS / 32;
-    constexpr int TNO = (MB == MODE_SWIGLU) ? TN / 2 : TN;
-    constexpr int PER_TILE = kGThreads * TM * TNO * 4;
-    const int NT = g.N / EP::BN_OUT;
-    const int lane = threadIdx.x % kWave;
-    const WaveSched ws = wave_sched(g, NT, EP::BM, EP::THIN_ROWS, lane);
-    const int total = ws.total;
-    const int splits = tail_splits(g, total, G, g.K / kBK);
-    if (splits <= 1) return;
-    const int full = total / G, remt = total - full * G;
-    const float4* part = reinterpret_cast<const float4*>(g.part);
-    constexpr size_t PSTRIDE = kPartBytes / 16;
-    for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < (int64_t)remt * PER_TILE;
-         w += (int64_t)gridDim.x * blockDim.x) {
-        const int t = (int)(w / PER_TILE);
-        int r = (int)(w - (int64_t)t * PER_TILE);
-        const int vt = r % kGThreads;  // the product thread that held these values
-        r /= kGThreads;
-        const int q4 = r % 4;
-        r /= 4;
-        const int jo = r % TNO, i = r / TNO;
-        int e, m_tile, n_tile;
-        map_tile_w(full * G + t, ws, g.E, NT, lane, e, m_tile, n_tile);  // t is wave-uniform
-        const int kept = __builtin_amdgcn_readlane(ws.kp, e);
-        const int vwave = vt / kWave, vlane = vt % kWave;
-        const int wm = vwave / kWN, wn = vwave % kWN;
-        const int m0 = m_tile * EP::BM, n0 = n_tile * EP::BN_OUT;
-        const int row0 = m0 + wm * WM_ROWS + i * 32 + q4 * 8 + (vlane / 32) * 4;
-        if (m0 + wm * WM_ROWS + i * 32 >= kept) continue;  // block past kept: no partials stored
-        const size_t base = (size_t)t * splits * PSTRIDE + vt;
-        const int gi0 = (i * TN + jo) * 4 + q4;                // gate / only operand
-        const int gi1 = (i * TN + jo + TN / 2) * 4 + q4;       // up (SwiGLU)
-        float4 s0 = part[base + (size_t)gi0 * kGThreads];
-        float4 s1 = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (MB == MODE_SWIGLU) s1 = part[base + (size_t)gi1 * kGThreads];
-        for (int pc = 1; pc < splits; ++pc) {
-            const float4 v0 = part[base + pc * PSTRIDE + (size_t)gi0 * kGThreads];
-            s0.x += v0.x; s0.y += v0.y; s0.z += v0.z; s0.w += v0.w;
-            if (MB == MODE_SWIGLU) {
-                const float4 v1 = part[base + pc * PSTRIDE + (size_t)gi1 * kGThreads];
-                s1.x += v1.x; s1.y += v1.y; s1.z += v1.z; s1.w += v1.w;
-            }
-        }
-        const int col = n0 + (MB == MODE_SWIGLU ? wn * (WN_COLS / 2) : wn * WN_COLS) + jo * 32 +
-                        vlane % 32;
-        float bv = 0.f;
-        if (MB != MODE_SWIGLU && g.bias) bv = bf2f(g.bias[(size_t)e * g.N + col]);
-        if (g.scale0) {  // 8-bit weights: the column scales
-            const float c0 = g.scale0[(size_t)e * g.N + col];
-            s0.x *= c0; s0.y *= c0; s0.z *= c0; s0.w *= c0;
-            if (MB == MODE_SWIGLU) {
-                const float c1 = g.scale1[(size_t)e * g.N + col];
-                s1.x *= c1; s1.y *= c1; s1.z *= c1; s1.w *= c1;
-            }
-        }
-        const float a0[4] = {s0.x, s0.y, s0.z, s0.w};
-        const float a1[4] = {s1.x, s1.y, s1.z, s1.w};
+    // The last piece of a split tile to arrive finishes it: each element's
+    // partials summed in piece order (the same sums whichever piece arrives
+    // last), then the epilogue's activation and stores.  Each thread reads
+    // the value groups it stored itself (16-byte, coalesced), one 32-row
+    // block at a time with every piece's loads in flight together (pieces
+    // past `splits` lie past the descriptor and read as zero; they are not
+    // added).  This runs after the tile loop, apart from its registers.
+    {
+        constexpr int TNO = (MB == MODE_SWIGLU) ? TN / 2 : TN;
+        constexpr int B = EP::OUT_BYTES;
+        const int piece = cur.pslot % splits;
+        const i32x4_t rsT = make_rsrc(g.part + (size_t)(cur.pslot - piece) * (kPartBytes / 4),
+                                      (uint32_t)(kPartBytes * splits));
+        const i32x4_t rsO = make_rsrc(
+            static_cast<unsigned char*>(g.out) + (((size_t)cur.e * g.C + cur.m0) * g.N + cur.n0) * B,
+            (uint32_t)(((size_t)(cur.kept - cur.m0) * g.N - cur.n0) * B));
+        const int row_t = wm * WM_ROWS + (lane / 32) * 4 + (lane & 3);
+        const uint16_t* biasb = g.bias ? g.bias + (size_t)cur.e * g.N + cur.n0 : nullptr;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int row = row0 + u;
-            if (row >= kept) break;
-            float v;
-            if (MB == MODE_SWIGLU)
-                v = silu_f(a0[u]) * a1[u];
-            else if (MB == MODE_GELU)
-                v = gelu_f(a0[u] + bv);
-            else
-                v = a0[u] + bv;
-            const size_t o = ((size_t)e * g.C + row) * g.N + col;
-            if (MB == MODE_DOWN)
-                static_cast<float*>(g.out)[o] = v;
-            else
-                static_cast<uint16_t*>(g.out)[o] = (uint16_t)f2bf(v);
+        for (int i = 0; i < TM; ++i) {
+            if (cur.m0 + wm * WM_ROWS + i * 32 >= cur.kept) break;  // no partials stored
+            f32x4_t sum[TN][4], part[kSMax - 1][TN][4];
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int off = (((i * TN + j) * 4 + q4) * kGThreads + tid) * 16;
+                    sum[j][q4] = buffer_load_f32x4(rsT, off, 0, kAuxSystem);
+#pragma unroll
+                    for (int pc = 1; pc < kSMax; ++pc)
+                        part[pc - 1][j][q4] =
+                            buffer_load_f32x4(rsT, pc * (int)kPartBytes + off, 0, kAuxSystem);
+                }
+#pragma unroll
+            for (int pc = 1; pc < kSMax; ++pc) {
+                if (pc >= splits) break;
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        sum[j][q4].x += part[pc - 1][j][q4].x;
+                        sum[j][q4].y += part[pc - 1][j][q4].y;
+                        sum[j][q4].z += part[pc - 1][j][q4].z;
+                        sum[j][q4].w += part[pc - 1][j][q4].w;
+                    }
+            }
+#pragma unroll
+            for (int j = 0; j < TNO; ++j) {
+                const int cbase = (MB == MODE_SWIGLU ? wn * (WN_COLS / 2) : wn * WN_COLS) + j * 32;
+                const int ocol = cbase + lane % 32;
+                const int voff = (row_t * g.N + cbase + ((lane % 32) & ~3)) * B;
+                float bv = 0.f;
+                if (MB != MODE_SWIGLU && biasb) bv = bf2f(biasb[ocol]);
+                float sc0 = 1.f, sc1 = 1.f;
+                if (F8) {  // 8-bit weights: the column scales
+                    sc0 = g.scale0[(size_t)cur.e * g.N + cur.n0 + ocol];
+                    if (MB == MODE_SWIGLU) sc1 = g.scale1[(size_t)cur.e * g.N + cur.n0 + ocol];
+                }
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int soff = ((i * 32 + q4 * 8) * g.N) * B;
+                    const f32x4_t a = sum[j][q4];
+                    const f32x4_t u = sum[(MB == MODE_SWIGLU) ? j + TN / 2 : j][q4];
+                    const float av[4] = {a.x, a.y, a.z, a.w};
+                    const float uv[4] = {u.x, u.y, u.z, u.w};
+                    float v[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (MB == MODE_SWIGLU)
+                            v[r] = F8 ? silu_f(av[r] * sc0) * (uv[r] * sc1) : silu_f(av[r]) * uv[r];
+                        else if (MB == MODE_GELU)
+                            v[r] = gelu_f((F8 ? av[r] * sc0 : av[r]) + bv);
+                        else
+                            v[r] = (F8 ? av[r] * sc0 : av[r]) + bv;
+                    }
+                    if (MB == MODE_DOWN)
+                        store_rows4_f32(v, rsO, voff, soff, lane);
+                    else
+                        store_rows4_bf16(v, rsO, voff, soff, lane);
+                }
+            }
         }
     }
 }
@@ -881,13 +902,6 @@ moe_status_t launch_gemm(const GemmArgs& args, hipStream_t st) {
     if (grid < 8) grid = 8;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kGThreads), EP::LDS, st, a);
     MOE_CHECK_LAUNCH();
-    if constexpr (MODE == mode_base(MODE)) {  // training variants never split
-        if (a.part) {  // finishes the split tail tiles, if the device schedule split any
-            hipLaunchKernelGGL((tail_reduce_kernel<MODE, BN, THIN>), dim3((unsigned)(4 * num_cus())),
-                               dim3(256), 0, st, a, (int)grid);
-            MOE_CHECK_LAUNCH();
-        }
-    }
     return MOE_OK;
 }
 
@@ -927,8 +941,14 @@ moe_status_t launch_first(moe_act_t act, const GemmArgs& a, hipStream_t st) {
 }  // namespace
 
 // Workspace of the split tail round: one fp32 partial tile per workgroup of
-// a full-device launch (the two products use it one after the other).
-static size_t ffn_ws_bytes() { return (size_t)num_cus() * kPartBytes; }
+// a full-device launch, then one counter per split tile (zero before the
+// first launch; every launch leaves them zero).  The two products use it one
+// after the other.
+static size_t ffn_cnt_bytes() { return ((size_t)num_cus() * 4 + 255) / 256 * 256; }
+static size_t ffn_ws_bytes() { return (size_t)num_cus() * kPartBytes + ffn_cnt_bytes(); }
+static uint32_t* ffn_cnt(void* ws) {
+    return reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(ws) + (size_t)num_cus() * kPartBytes);
+}
 
 extern "C" size_t moe_expert_ffn_ws_bytes(void) { return ffn_ws_bytes(); }
 
@@ -1014,6 +1034,7 @@ moe_status_t ffn_impl(void* stream, moe_dtype_t dtype, moe_act_t act, const void
     // with a workspace, each product may split its last, partly filled round
     const bool split = ws && ws_bytes >= ffn_ws_bytes();
     a1.part = split ? static_cast<float*>(ws) : nullptr;
+    a1.cnt = split ? ffn_cnt(ws) : nullptr;
     a1.smax = FFN1_SPLIT_MAX;
     const bool thin = C <= kThinRows;
     const int sel = (slot_token ? 4 : 0) + (f8 ? 2 : 0) + (thin ? 1 : 0);
@@ -1040,6 +1061,7 @@ moe_status_t ffn_impl(void* stream, moe_dtype_t dtype, moe_act_t act, const void
     a2.K = (int)I;
     a2.N = (int)H;
     a2.part = split ? static_cast<float*>(ws) : nullptr;
+    a2.cnt = split ? ffn_cnt(ws) : nullptr;
     a2.smax = FFN2_SPLIT_MAX;
     a2.Q0 = f8 ? static_cast<const uint8_t*>(w2) : nullptr;
     a2.Q1 = nullptr;
@@ -1076,6 +1098,7 @@ moe_status_t moe_ffn1_save(hipStream_t st, moe_act_t act, const void* x_disp, co
     a.K = (int)H;
     a.N = (int)I;
     a.part = nullptr;
+    a.cnt = nullptr;
     a.smax = 1;
     return act == MOE_ACT_SWIGLU ? launch_gemm<MODE_SWIGLU_SAVE, 256>(a, st)
                                  : launch_gemm<MODE_GELU_SAVE, 256>(a, st);
@@ -1101,6 +1124,7 @@ moe_status_t moe_ffn2(hipStream_t st, const void* h, const int32_t* kept, int E,
     a.K = (int)I;
     a.N = (int)H;
     a.part = (part && part_bytes >= ffn_ws_bytes()) ? static_cast<float*>(part) : nullptr;
+    a.cnt = a.part ? ffn_cnt(part) : nullptr;
     a.smax = FFN2_SPLIT_MAX;
     return launch_single<MODE_DOWN>(a, st);
 }

@@ -609,12 +609,14 @@ moe_status_t launch_bwd(const BwdArgs& a, int64_t max_tiles, hipStream_t st) {
 }
 
 // h, g, u, dg, du planes (GELU uses h, z, dz), then the split tails'
-// partial tiles: one per workgroup of a full-device launch
+// partial tiles (one per workgroup of a full-device launch) and the forward
+// down product's tile counters: the forward products' workspace
 size_t bwd_planes_bytes(int E, int64_t C, int64_t I) {
     return ((size_t)5 * E * C * I * 2 + 255) / 256 * 256;
 }
 size_t bwd_ws_bytes(int E, int64_t C, int64_t I) {
-    return bwd_planes_bytes(E, C, I) + (size_t)num_cus() * kBwdPartBytes;
+    static_assert(kBwdPartBytes == (size_t)kBM * kBNMax * 4, "the forward's partial tile");
+    return bwd_planes_bytes(E, C, I) + moe_expert_ffn_ws_bytes();
 }
 
 }  // namespace
@@ -790,6 +792,5 @@ extern "C" moe_status_t moe_expert_ffn_fwd_save(void* stream, moe_dtype_t dtype,
                                    sw ? wsb + 2 * plane : nullptr);
     if (s != MOE_OK) return s;
     void* part = static_cast<unsigned char*>(ws) + bwd_planes_bytes(E, C, I);
-    return moe_ffn2(st, h, kept, E, C, H, I, w2, b2, y_disp, part,
-                    (size_t)num_cus() * kBwdPartBytes);
+    return moe_ffn2(st, h, kept, E, C, H, I, w2, b2, y_disp, part, moe_expert_ffn_ws_bytes());
 }

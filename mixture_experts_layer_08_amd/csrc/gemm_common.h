@@ -34,6 +34,11 @@ __device__ void buffer_store_i32x2(moe_i32x2_t v, moe_i32x4_t rsrc, int voffset,
                                    int aux) __asm("llvm.amdgcn.raw.buffer.store.v2i32");
 __device__ moe_i32x2_t buffer_load_i32x2(moe_i32x4_t rsrc, int voffset, int soffset,
                                          int aux) __asm("llvm.amdgcn.raw.buffer.load.v2i32");
+__device__ moe::f32x4_t buffer_load_f32x4(moe_i32x4_t rsrc, int voffset, int soffset,
+                                         int aux) __asm("llvm.amdgcn.raw.buffer.load.v4f32");
+// cache policy of a buffer access (aux): system scope (sc0 sc1), which goes
+// past the per-XCD L2 caches to memory
+constexpr int kAuxSystem = 17;
 
 namespace {
 

@@ -14,7 +14,8 @@ moe_status_t moe_ffn1_save(hipStream_t st, moe_act_t act, const void* x_disp, co
                            const void* b1, void* h, void* save0, void* save1);
 
 // The second expert product, y_disp [E, C, H] fp32 = h W2 (+ b2), bf16 h and
-// W2; part / part_bytes: the split-tail workspace (null: no split).
+// W2; part / part_bytes: the split-tail workspace, laid out and cleared as
+// moe_expert_ffn's ws (null or too small: no split).
 moe_status_t moe_ffn2(hipStream_t st, const void* h, const int32_t* kept, int E, int64_t C,
                       int64_t H, int64_t I, const void* w2, const void* b2, void* y_disp,
                       void* part, size_t part_bytes);

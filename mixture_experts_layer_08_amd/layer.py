@@ -132,11 +132,13 @@ class MoELayerGPU:
         E, k, H, I = cfg.E, cfg.k, cfg.H, cfg.I
         i32, f32, td = torch.int32, torch.float32, self.tdtype
         e = lambda *s, dt=f32: torch.empty(s, dtype=dt, device=dev)  # noqa: E731
+        # the expert products' workspaces hold tile counters that start at zero
+        z = lambda n: torch.zeros(n, dtype=torch.uint8, device=dev)  # noqa: E731
         sh = {}
         if self.shared:
             sh = dict(sh_kept=torch.full((1,), T, dtype=i32, device=dev),
                       sh_h=e(1, T, cfg.shared_I, dt=td), sh_y=e(1, T, H),
-                      sh_ws=e(ops.moe_expert_ffn_ws_bytes(), dt=torch.uint8))
+                      sh_ws=z(ops.moe_expert_ffn_ws_bytes()))
         return Buffers(
             **sh,
             topk_idx=e(T, k, dt=i32), topk_w=e(T, k), probs=e(T, E), keys=e(T, E),
@@ -146,7 +148,7 @@ class MoELayerGPU:
             kept=e(E, dt=i32), dropped=e(1, dt=i32), h=e(E, C, I, dt=td),
             y_disp=e(E, C, H), y=e(T, H, dt=td),
             ws=e(max(1, ops.moe_workspace_bytes(T, E, k)), dt=torch.uint8),
-            ffn_ws=e(ops.moe_expert_ffn_ws_bytes(), dt=torch.uint8))
+            ffn_ws=z(ops.moe_expert_ffn_ws_bytes()))
 
     # the five steps, each one library call ---------------------------------
     def route(self, x: torch.Tensor, keys: bool = False):

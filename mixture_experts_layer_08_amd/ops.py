@@ -156,8 +156,9 @@ def moe_expert_ffn(x_disp: torch.Tensor, kept: torch.Tensor, w1: torch.Tensor,
                    b2: Optional[torch.Tensor] = None, *, act: str = "swiglu",
                    h_ws: Optional[torch.Tensor] = None, y_disp: Optional[torch.Tensor] = None,
                    ws: Optional[torch.Tensor] = None):
-    """ws: optional uint8 workspace (see moe_expert_ffn_ws_bytes); None runs
-    every round of tiles whole."""
+    """ws: optional uint8 workspace of moe_expert_ffn_ws_bytes() bytes,
+    zero-filled when allocated (its tile counters must start at zero; every
+    call leaves them zero); None runs every round of tiles whole."""
     E, C, H = x_disp.shape
     I = w1.shape[2]
     dev = x_disp.device
@@ -351,7 +352,7 @@ def moe_expert_ffn_bwd(x_disp: torch.Tensor, kept: torch.Tensor, w1: torch.Tenso
            "db1": torch.empty((E, I), dtype=f32, device=dev) if act == "gelu" else None,
            "db2": torch.empty((E, H), dtype=f32, device=dev) if act == "gelu" and has_b2 else None}
     if ws is None:
-        ws = torch.empty(max(16, int(lib().moe_expert_ffn_bwd_ws_bytes(E, C, I))),
+        ws = torch.zeros(max(16, int(lib().moe_expert_ffn_bwd_ws_bytes(E, C, I))),
                          dtype=torch.uint8, device=dev)
     st = lib().moe_expert_ffn_bwd(_stream(dev), _dtype_code(x_disp), ACTS[act], _ptr(x_disp),
                                   _ptr(kept), E, C, H, I, _ptr(w1), _ptr(w3), _ptr(w2), _ptr(b1),
@@ -365,7 +366,8 @@ def moe_expert_ffn_bwd(x_disp: torch.Tensor, kept: torch.Tensor, w1: torch.Tenso
 def moe_expert_ffn_bwd_ws(x_disp: torch.Tensor, I: int) -> torch.Tensor:
     """A workspace for moe_expert_ffn_fwd_save / moe_expert_ffn_bwd."""
     E, C, _ = x_disp.shape
-    return torch.empty(max(16, int(lib().moe_expert_ffn_bwd_ws_bytes(E, C, I))),
+    # zero-filled: the tile counters at its end must start at zero
+    return torch.zeros(max(16, int(lib().moe_expert_ffn_bwd_ws_bytes(E, C, I))),
                        dtype=torch.uint8, device=x_disp.device)
 
 

@@ -196,9 +196,9 @@ def test_stages_on_oracle_inputs(name):
         np.testing.assert_array_equal(ygn[e, :n], yd[e, :n], err_msg=f"{name}: gathered y_disp[{e}]")
         np.testing.assert_array_equal(hgn[e, :n], hh[e, :n], err_msg=f"{name}: gathered h[{e}]")
     if cfg.dtype == "bf16":
-        # without a workspace every tile finishes in the product kernel's own
-        # epilogue (with one, a partly filled last round is cut into K pieces
-        # that the tail reduction finishes, which is all these small shapes have)
+        # without a workspace every tile runs whole (with one, a partly filled
+        # last round is cut into K pieces and the last piece of each tile to
+        # arrive sums them, which is all these small shapes have)
         yw, hw = ops.moe_expert_ffn(x_disp, kept, layer.w1, layer.w3, layer.w2, layer.b1,
                                     layer.b2, act=cfg.act)
         torch.cuda.synchronize()
@@ -271,7 +271,7 @@ def test_thin_last_row_tiles(name, ws_on):
     layer = MoELayerGPU(cfg, inp, DEV, fused_gather=False)
     x_disp = torch.from_numpy(xd_bits.view(np.int16)).view(torch.bfloat16).to(DEV)
     kept = to_dev(np.array(kept_l, dtype=np.int32), torch.int32)
-    ws = (torch.empty(ops.moe_expert_ffn_ws_bytes(), dtype=torch.uint8, device=DEV)
+    ws = (torch.zeros(ops.moe_expert_ffn_ws_bytes(), dtype=torch.uint8, device=DEV)
           if ws_on else None)
     y, h = ops.moe_expert_ffn(x_disp, kept, layer.w1, layer.w3, layer.w2, layer.b1, layer.b2,
                               act=cfg.act, ws=ws)
@@ -283,6 +283,45 @@ def test_thin_last_row_tiles(name, ws_on):
         hr, yr = M.expert_forward(inp, cfg.act, e, xd[e, :n])
         _check_h(cfg, hn[e, :n], hr, f"{name}: h[{e}]")
         _check_y(cfg, yn[e, :n], yr, f"{name}: y_disp[{e}]")
+
+
+def test_split_tiles_leave_counters_zero():
+    """The pieces of a split tile count themselves in the workspace; the piece
+    that completes a tile resets its counter.  Calls with different kept[]
+    (other tiles split) on one workspace: a repeat of the first call gives the
+    same bits, and every counter ends at zero."""
+    cfg, C, kept_a = THIN_LAST["mixed-swiglu"]
+    kept_b = [640, 640, 0, 65, 1, 300, 128, 129]
+    log(f"[split counters] kept {kept_a}, then {kept_b}, then {kept_a} on one workspace")
+    inp = make_inputs(cfg)
+    rng = np.random.default_rng(cfg.seed + 1)
+    xd_bits = f32_to_bf16_bits(rng.standard_normal((cfg.E, C, cfg.H), dtype=np.float32))
+    xd = bf16_bits_to_f32(xd_bits).astype(np.float64)
+    layer = MoELayerGPU(cfg, inp, DEV, fused_gather=False)
+    x_disp = torch.from_numpy(xd_bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+    nbytes = ops.moe_expert_ffn_ws_bytes()
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    tile = 256 * 256 * 4
+    counters = ws[(nbytes // tile) * tile:]
+
+    def run(kept_l):
+        kept = to_dev(np.array(kept_l, dtype=np.int32), torch.int32)
+        y, h = ops.moe_expert_ffn(x_disp, kept, layer.w1, layer.w3, layer.w2, act=cfg.act, ws=ws)
+        torch.cuda.synchronize()
+        assert int(counters.count_nonzero()) == 0, "tile counters left non-zero"
+        return to_np(y).copy(), h.view(torch.int16).cpu().numpy().copy()
+
+    y1, h1 = run(kept_a)
+    y2, _ = run(kept_b)
+    y3, h3 = run(kept_a)
+    for e, n in enumerate(kept_a):
+        assert np.array_equal(y3[e, :n].view(np.uint32), y1[e, :n].view(np.uint32)), f"y[{e}]"
+        assert np.array_equal(h3[e, :n], h1[e, :n]), f"h[{e}]"
+    for e, n in enumerate(kept_b):
+        if n == 0:
+            continue
+        hr, yr = M.expert_forward(inp, cfg.act, e, xd[e, :n])
+        _check_y(cfg, y2[e, :n], yr, f"second call: y_disp[{e}]")
 
 
 # ---------------------------------------------------------- edge cases ----
