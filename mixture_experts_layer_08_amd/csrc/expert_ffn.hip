@@ -72,7 +72,7 @@
 #define FFN1_SPLIT_MAX 4  // most K pieces of a tail tile, first product
 #endif
 #ifndef FFN2_SPLIT_MAX
-#define FFN2_SPLIT_MAX 4  // and second product
+#define FFN2_SPLIT_MAX 8  // and second product
 #endif
 
 namespace {
@@ -113,7 +113,7 @@ struct GemmArgs {
 };
 
 constexpr size_t kPartBytes = (size_t)kBM * kBNMax * 4;  // one fp32 tile
-constexpr int kSMax = 4;  // most pieces per split tile
+constexpr int kSMax = 8;  // most pieces per split tile
 
 // ---------------------------------------------------------- tile schedule --
 // Expert e has ceil(kept[e] / BM) row tiles times NT column tiles.  A last
@@ -744,9 +744,10 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
     // partials summed in piece order (the same sums whichever piece arrives
     // last), then the epilogue's activation and stores.  Each thread reads
     // the value groups it stored itself (16-byte, coalesced), one 32-row
-    // block at a time with every piece's loads in flight together (pieces
-    // past `splits` lie past the descriptor and read as zero; they are not
-    // added).  This runs after the tile loop, apart from its registers.
+    // block at a time with the loads of two pieces in flight together
+    // (pieces past `splits` lie past the descriptor and read as zero; they
+    // are not added).  This runs after the tile loop, apart from its
+    // registers.
     {
         constexpr int TNO = (MB == MODE_SWIGLU) ? TN / 2 : TN;
         constexpr int B = EP::OUT_BYTES;
@@ -761,30 +762,39 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             if (cur.m0 + wm * WM_ROWS + i * 32 >= cur.kept) break;  // no partials stored
-            f32x4_t sum[TN][4], part[kSMax - 1][TN][4];
+            constexpr int PG = 2;  // pieces loaded together
+            f32x4_t sum[TN][4];
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int off = (((i * TN + j) * 4 + q4) * kGThreads + tid) * 16;
-                    sum[j][q4] = buffer_load_f32x4(rsT, off, 0, kAuxSystem);
-#pragma unroll
-                    for (int pc = 1; pc < kSMax; ++pc)
-                        part[pc - 1][j][q4] =
-                            buffer_load_f32x4(rsT, pc * (int)kPartBytes + off, 0, kAuxSystem);
-                }
-#pragma unroll
-            for (int pc = 1; pc < kSMax; ++pc) {
-                if (pc >= splits) break;
+            for (int pg = 0; pg < kSMax; pg += PG) {
+                if (pg >= splits) break;
+                f32x4_t part[PG][TN][4];
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) {
-                        sum[j][q4].x += part[pc - 1][j][q4].x;
-                        sum[j][q4].y += part[pc - 1][j][q4].y;
-                        sum[j][q4].z += part[pc - 1][j][q4].z;
-                        sum[j][q4].w += part[pc - 1][j][q4].w;
+                        const int off = (((i * TN + j) * 4 + q4) * kGThreads + tid) * 16;
+#pragma unroll
+                        for (int u = 0; u < PG; ++u)
+                            part[u][j][q4] = buffer_load_f32x4(
+                                rsT, (pg + u) * (int)kPartBytes + off, 0, kAuxSystem);
                     }
+#pragma unroll
+                for (int u = 0; u < PG; ++u) {
+                    if (pg + u >= splits) break;
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            if (pg + u == 0) {
+                                sum[j][q4] = part[u][j][q4];
+                                continue;
+                            }
+                            sum[j][q4].x += part[u][j][q4].x;
+                            sum[j][q4].y += part[u][j][q4].y;
+                            sum[j][q4].z += part[u][j][q4].z;
+                            sum[j][q4].w += part[u][j][q4].w;
+                        }
+                }
             }
 #pragma unroll
             for (int j = 0; j < TNO; ++j) {
