@@ -62,7 +62,7 @@ struct BwdArgs {
 };
 
 constexpr size_t kBwdPartBytes = (size_t)kBM * kBNMax * 4;  // one fp32 tile
-constexpr int kBwdSMax = 4;
+constexpr int kBwdSMax = 8;
 
 // DGRAD tiles fill total / G rounds of a G-workgroup launch; when the last
 // round would leave at least half of the workgroups idle, its tiles are cut
@@ -77,19 +77,44 @@ __device__ __forceinline__ int bwd_tail_splits(const BwdArgs& g, int total, int 
     return sp < 1 ? 1 : sp;
 }
 
-// The DGRAD schedule's per-expert row tiles and tile prefix (one thread).
-__device__ void bwd_prefix(const BwdArgs& g, bool KC, int NT, int* s_pref, int* s_mt) {
-    int cum = 0;
+// The schedule's per-expert row tiles and tile prefixes (one thread).  DGRAD
+// (row tiles over kept[e]) puts an expert's last row tile after every other
+// tile when it has at most 64 rows (thin: little MFMA work for a whole tile's
+// loads), as the forward products do: the main run (s_pref, s_mt row tiles
+// per expert), then the thin run (s_tpref, one row tile per expert that has
+// one), so the thin tiles fall in the last, split round.
+__device__ void bwd_prefix(const BwdArgs& g, bool KC, int NT, int* s_pref, int* s_mt,
+                           int* s_tpref) {
+    int cum = 0, tcum = 0;
     for (int e = 0; e < g.E; ++e) {
         int kp = g.kept[e];
         if (kp < 0) kp = 0;
         if (kp > g.C) kp = (int)g.C;
-        const int mt = KC ? (kp + kBM - 1) / kBM : g.M / kBM;
-        s_mt[e] = mt;
+        const int mt_all = KC ? (kp + kBM - 1) / kBM : g.M / kBM;
+        const int thin = (KC && mt_all > 0 && kp - (mt_all - 1) * kBM <= 64) ? 1 : 0;
+        s_mt[e] = mt_all - thin;
         s_pref[e] = cum;
-        cum += mt * NT;
+        s_tpref[e] = tcum;
+        cum += (mt_all - thin) * NT;
+        tcum += thin * NT;
     }
     s_pref[g.E] = cum;
+    s_tpref[g.E] = tcum;
+}
+
+// Tile `logical` of the schedule above -> expert, row tile and column tile.
+__device__ __forceinline__ void bwd_map_tile(int logical, const int* s_pref, const int* s_mt,
+                                             const int* s_tpref, int E, int NT, int& e,
+                                             int& m_tile, int& n_tile) {
+    if (logical < s_pref[E]) {
+        map_tile(logical, s_pref, s_mt, E, NT, e, m_tile, n_tile);
+        return;
+    }
+    const int t = logical - s_pref[E];
+    e = 0;
+    while (e + 1 < E && s_tpref[e + 1] <= t) ++e;
+    m_tile = s_mt[e];  // the thin tile follows the expert's main row tiles
+    n_tile = t - s_tpref[e];
 }
 
 struct BTile {
@@ -112,14 +137,15 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_pref[MOE_MAX_EXPERTS + 1];
     __shared__ int s_mt[MOE_MAX_EXPERTS];
+    __shared__ int s_tpref[MOE_MAX_EXPERTS + 1];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
     const int wm = wave / kWN, wn = wave % kWN;
     const int NT = g.N / kBNMax;
-    if (tid == 0) bwd_prefix(g, KC, NT, s_pref, s_mt);
+    if (tid == 0) bwd_prefix(g, KC, NT, s_pref, s_mt, s_tpref);
     __syncthreads();
-    const int total = __builtin_amdgcn_readfirstlane(s_pref[g.E]);
+    const int total = __builtin_amdgcn_readfirstlane(s_pref[g.E] + s_tpref[g.E]);
     const int G = gridDim.x;
     const int xcd = blockIdx.x % 8, slot8 = blockIdx.x / 8;
     const int full = total / G;
@@ -145,7 +171,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
         c.valid = logical < total;
         if (!c.valid) return c;
         int e, m_tile, n_tile;
-        map_tile(logical, s_pref, s_mt, g.E, NT, e, m_tile, n_tile);
+        bwd_map_tile(logical, s_pref, s_mt, s_tpref, g.E, NT, e, m_tile, n_tile);
         int kept = g.kept[e];
         if (kept < 0) kept = 0;
         if (kept > g.C) kept = (int)g.C;
@@ -252,14 +278,18 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
         const uint2 hi = __builtin_bit_cast(uint2, v[1]);
         return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
     };
-    auto load_frags = [&](int stage, int kk, bf16x8_t (&af)[2][TM], bf16x8_t (&bfr)[2][TN]) {
+    // (only the first NI 32-row blocks of the wave's A rows: the others lie
+    // past the valid rows)
+    auto load_frags = [&](auto ni, int stage, int kk, bf16x8_t (&af)[2][TM],
+                          bf16x8_t (&bfr)[2][TN]) {
+        constexpr int NI = decltype(ni)::value;
         const unsigned char* As = smem + stage * kStage;
         const unsigned char* Bs = As + kStageA;
 #pragma unroll
         for (int ss = 0; ss < 2; ++ss) {
             const int k16 = kk * 2 + ss;
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < NI; ++i)
                 af[ss][i] = KC ? frag_kc(As, wm * WM_ROWS + i * 32, k16)
                                : frag_mc(As, wm * WM_ROWS + i * 32, k16);
 #pragma unroll
@@ -283,11 +313,12 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-        auto mma = [&](const bf16x8_t (&af)[2][TM], const bf16x8_t (&bfr)[2][TN]) {
+        auto mma = [&](auto ni, const bf16x8_t (&af)[2][TM], const bf16x8_t (&bfr)[2][TN]) {
+            constexpr int NI = decltype(ni)::value;
 #pragma unroll
             for (int ss = 0; ss < 2; ++ss)
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
+                for (int i = 0; i < NI; ++i)
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ss][i], bfr[ss][j],
@@ -296,56 +327,64 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_bwd_kernel(BwdArgs 
         // The forward's pipeline: one barrier per k-step, the second half of
         // step kt read while the first half's MFMAs run, step kt+2's loads
         // issued into the stage step kt frees; the next tile's first two
-        // k-steps load during this tile's last two.  A wave whose rows are all
-        // past the valid rows runs the loop without reads or MFMAs.
-        auto kloop = [&](auto do_math) {
-            constexpr bool Mth = decltype(do_math)::value;
+        // k-steps load during this tile's last two.  A wave reads fragments
+        // and runs MFMAs for its 32-row blocks that hold valid rows only (none
+        // when all its rows are past them: thin last row tiles of an expert).
+        auto kloop = [&](auto ni) {
+            constexpr bool Mth = decltype(ni)::value > 0;
             bf16x8_t a0[2][TM], b0[2][TN], a1[2][TM], b1[2][TN];
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
-            if (Mth) load_frags(base, 0, a0, b0);
+            if (Mth) load_frags(ni, base, 0, a0, b0);
             const int nks = cur.nks;
             int kt = 0;
             for (; kt + 2 < nks; ++kt) {
                 const int s0 = (base + kt) & 1;
                 if (Mth) {
-                    load_frags(s0, 1, a1, b1);
-                    mma(a0, b0);
+                    load_frags(ni, s0, 1, a1, b1);
+                    mma(ni, a0, b0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
                 issue(cur, cur.kb + kt + 2, s0);
                 if (Mth) {
-                    load_frags(s0 ^ 1, 0, a0, b0);
-                    mma(a1, b1);
+                    load_frags(ni, s0 ^ 1, 0, a0, b0);
+                    mma(ni, a1, b1);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
             const int s0 = (base + kt) & 1;
             if (Mth) {
-                load_frags(s0, 1, a1, b1);
-                mma(a0, b0);
+                load_frags(ni, s0, 1, a1, b1);
+                mma(ni, a0, b0);
             }
             __builtin_amdgcn_sched_barrier(0);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             if (nxt.valid) issue(nxt, nxt.kb, s0);
             if (Mth) {
-                load_frags(s0 ^ 1, 0, a0, b0);
-                mma(a1, b1);
-                load_frags(s0 ^ 1, 1, a1, b1);
-                mma(a0, b0);
-                mma(a1, b1);
+                load_frags(ni, s0 ^ 1, 0, a0, b0);
+                mma(ni, a1, b1);
+                load_frags(ni, s0 ^ 1, 1, a1, b1);
+                mma(ni, a0, b0);
+                mma(ni, a1, b1);
             }
             __builtin_amdgcn_sched_barrier(0);
             __syncthreads();
             if (nxt.valid) issue(nxt, nxt.kb + 1, s0 ^ 1);
         };
-        if (wm * WM_ROWS < cur.rows)
-            kloop(std::true_type{});
-        else
-            kloop(std::false_type{});
+        {
+            const int wrows = cur.rows - wm * WM_ROWS;  // WGRAD: every row is valid
+            if (wrows > 64)
+                kloop(std::integral_constant<int, TM>{});
+            else if (wrows > 32)
+                kloop(std::integral_constant<int, (TM < 2 ? TM : 2)>{});
+            else if (wrows > 0)
+                kloop(std::integral_constant<int, 1>{});
+            else
+                kloop(std::integral_constant<int, 0>{});
+        }
 
         if (cur.pslot >= 0) {
             // a piece of a split tail tile: store the fp32 partial, lane-major
@@ -482,10 +521,11 @@ __global__ __launch_bounds__(256) void bwd_tail_reduce_kernel(BwdArgs g, int G) 
     constexpr int PER_TILE = kGThreads * TM * TN * 4;
     __shared__ int s_pref[MOE_MAX_EXPERTS + 1];
     __shared__ int s_mt[MOE_MAX_EXPERTS];
+    __shared__ int s_tpref[MOE_MAX_EXPERTS + 1];
     const int NT = g.N / kBNMax;
-    if (threadIdx.x == 0) bwd_prefix(g, true, NT, s_pref, s_mt);
+    if (threadIdx.x == 0) bwd_prefix(g, true, NT, s_pref, s_mt, s_tpref);
     __syncthreads();
-    const int total = s_pref[g.E];
+    const int total = s_pref[g.E] + s_tpref[g.E];
     const int splits = bwd_tail_splits(g, total, G, (g.A1 ? 2 : 1) * (g.K / kBK));
     if (splits <= 1) return;
     const int full = total / G, remt = total - full * G;
@@ -499,7 +539,7 @@ __global__ __launch_bounds__(256) void bwd_tail_reduce_kernel(BwdArgs g, int G) 
         const int gi = r / kGThreads;
         const int i = gi / (TN * 4), j = (gi / 4) % TN, q4 = gi % 4;
         int e, m_tile, n_tile;
-        map_tile(full * G + t, s_pref, s_mt, g.E, NT, e, m_tile, n_tile);
+        bwd_map_tile(full * G + t, s_pref, s_mt, s_tpref, g.E, NT, e, m_tile, n_tile);
         int kept = g.kept[e];
         if (kept > g.C) kept = (int)g.C;
         const int vwave = vt / kWave, vlane = vt % kWave;

@@ -47,6 +47,10 @@ CASES = {
                                   shared_I=512, seed=35),
     "gelu-e4-shared": MoEConfig("b-sh-ge", "bf16", T=400, H=256, I=256, E=4, k=2, cf=1.25,
                                 act="gelu", shared_I=256, seed=36),
+    # about 272 rows per expert: most experts have a thin last row tile (at most
+    # 64 rows), which the input-gradient products schedule last and split
+    "swiglu-e8-thin": MoEConfig("b-thin", "bf16", T=1090, H=256, I=256, E=8, k=2, cf=1.25,
+                                seed=37),
 }
 
 
