@@ -266,7 +266,8 @@ moe_status_t moe_dequantize_fp8(void* stream, const uint8_t* q, const float* sca
  * bf16 / bf16 / fp32 as for moe_expert_ffn.  The products run on the codes'
  * exact values in bf16 and each output column is multiplied by its scale
  * on the fp32 accumulator, so the result is the layer with the dequantised
- * weights.  Limits as for moe_expert_ffn; in addition H * I < 2^31. */
+ * weights.  Limits and the optional ws (zero-filled before its first use) as
+ * for moe_expert_ffn; in addition H * I < 2^31. */
 moe_status_t moe_expert_ffn_fp8(void* stream, moe_act_t act, const void* x_disp,
                                 const int32_t* kept, int E, int64_t C, int64_t H,
                                 int64_t I, const uint8_t* w1q, const uint8_t* w3q,
