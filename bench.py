@@ -270,8 +270,8 @@ def bench_shared(cfg, dev, args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs the layer on one GPU only; --gpus {args.gpus} is not "
-              "supported (see the design notes for how the layer would shard)", file=sys.stderr)
+        print(f"bench.py: the layer runs on one GPU only; --gpus {args.gpus} is not supported",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     from mixture_experts_layer_08_amd.layer import MoELayerGPU, x_to_device

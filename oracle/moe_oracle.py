@@ -14,8 +14,7 @@ Sources (cited by page and section; the pages are the authority):
   [P4] Long-context MoE training on one A100-80G, 2kiu.com/news/5130654
   [P5] pjlab-sys4nlp/llama-moe architecture essay, coreui.cn/article/2610641
 
-Readings taken where the pages are silent or disagree (each is repeated in
-the design notes):
+Readings taken where the pages are silent or disagree:
   * f_i = assignments to expert i / (T*k), counted from the router's top-k
     before any capacity drop ([P2] sections 2.3 and 3.1).
   * capacity C = ceil(T*k*cf/E), evaluated in float64 in that order.
