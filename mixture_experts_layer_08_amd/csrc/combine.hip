@@ -104,8 +104,8 @@ extern "C" moe_status_t moe_combine(void* stream, moe_dtype_t dtype, const void*
     if (k > MOE_MAX_TOPK || H > (1 << 22) || T * k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
     if (H % 8) return MOE_ERR_ALIGN;
     if (T == 0) return MOE_OK;
-    if (!slot || !topk_w || !y) return MOE_ERR_NULL;
-    if (y_disp && !moe_aligned16(y_disp)) return MOE_ERR_ALIGN;
+    if (!y_disp || !slot || !topk_w || !y) return MOE_ERR_NULL;
+    if (!moe_aligned16(y_disp)) return MOE_ERR_ALIGN;
     if (!moe_aligned16(y) || (y_shared && !moe_aligned16(y_shared))) return MOE_ERR_ALIGN;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int row_oct = (int)(H / 8);
@@ -132,8 +132,8 @@ extern "C" moe_status_t moe_dispatch_bwd(void* stream, const float* dx_disp, con
     if (k > MOE_MAX_TOPK || H > (1 << 22) || T * k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
     if (H % 8) return MOE_ERR_ALIGN;
     if (T == 0) return MOE_OK;
-    if (!slot || !dx) return MOE_ERR_NULL;
-    if ((dx_disp && !moe_aligned16(dx_disp)) || !moe_aligned16(dx) ||
+    if (!dx_disp || !slot || !dx) return MOE_ERR_NULL;
+    if (!moe_aligned16(dx_disp) || !moe_aligned16(dx) ||
         (dx_add && !moe_aligned16(dx_add)))
         return MOE_ERR_ALIGN;
     hipStream_t st = static_cast<hipStream_t>(stream);

@@ -1023,6 +1023,11 @@ moe_status_t ffn_impl(void* stream, moe_dtype_t dtype, moe_act_t act, const void
         if (q && !moe_aligned16(q)) return MOE_ERR_ALIGN;
     // code rows are addressed with 32-bit offsets from an expert's column
     if (f8 && (int64_t)H * I >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    // buffer descriptors hold 32-bit byte ranges and offsets: one expert's
+    // bf16 weight matrix (k-step offsets reach its end, a signed 32-bit
+    // soffset) and one expert's rows of x_disp, h and fp32 y_disp
+    if ((int64_t)H * I * 2 >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    if (C * (H > I ? H : I) * 4 >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
     GemmArgs a1;
     a1.A = static_cast<const uint16_t*>(A);
     a1.slot_token = slot_token;

@@ -152,6 +152,10 @@ def test_expert_ffn_argument_errors(L):
     assert f(w1=MIS) == ALIGN
     assert f(ws=MIS, wsb=1 << 30) == ALIGN
     assert f(C=0, xd=None, h=None, y=None) == OK
+    # 32-bit buffer ranges: one expert's weight matrix below 2^31 bytes, one
+    # expert's fp32 output rows below 2^32 bytes
+    assert f(H=32768, I=32768) == UNSUP
+    assert f(C=1 << 20, H=1024, I=1024) == UNSUP
 
 
 def test_expert_ffn_gather_argument_errors(L):
@@ -191,6 +195,8 @@ def test_combine_argument_errors(L):
     assert c(k=9) == UNSUP
     assert c(H=4) == ALIGN
     assert c(slot=None) == NULL
+    assert c(yd=None) == NULL                 # the expert rows are always read through slot
+    assert c(yd=MIS) == ALIGN
     assert c(y=MIS) == ALIGN
     assert c(ys=MIS) == ALIGN
     assert c(T=0, slot=None, y=None) == OK
@@ -242,6 +248,22 @@ def test_dispatch_aux_argument_errors(L):
     assert d(wsb=16) == WS
     assert d(ws=MIS) == ALIGN
     assert d(xd=MIS) == ALIGN
+
+
+def test_dispatch_bwd_argument_errors(L):
+    def d(**kw):
+        return L.moe_dispatch_bwd(None, kw.get("dxd", P), kw.get("slot", P), kw.get("T", 64),
+                                  kw.get("H", 256), kw.get("k", 2), kw.get("add", None),
+                                  kw.get("dx", P))
+    assert d(T=-1) == SHAPE
+    assert d(k=9) == UNSUP
+    assert d(H=4) == ALIGN
+    assert d(dxd=None) == NULL               # the copies' gradients are read through slot
+    assert d(slot=None) == NULL
+    assert d(dx=None) == NULL
+    assert d(dxd=MIS) == ALIGN
+    assert d(add=MIS) == ALIGN
+    assert d(T=0, dxd=None, slot=None, dx=None) == OK
 
 
 def route_bwd(L, dtype=1, mode=0, x=P, w=P, probs=P, idx=P, tw=P, dw=P, f=P, T=64, H=256, E=8,

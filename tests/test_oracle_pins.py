@@ -382,6 +382,30 @@ def test_bf16_rounding_is_nearest_even():
     np.testing.assert_array_equal(tb, f32_to_bf16_bits(r))
 
 
+def test_oracle_widen_decodes_every_bf16_pattern():
+    """The oracle's own bf16 -> float64 decode (every input passes through
+    it) against torch's bf16 -> float32 conversion, a separate
+    implementation, over all 65536 bit patterns: equal values (NaN patterns
+    stay NaN with the same sign), and fp32 inputs pass unchanged."""
+    torch = pytest.importorskip("torch")
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = M.widen(bits)
+    assert got.dtype == np.float64 and got.shape == bits.shape
+    want = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float32) \
+        .numpy().astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got[~nan], want[~nan])
+    np.testing.assert_array_equal(np.signbit(got), np.signbit(want))
+    # fixed points of the format: 1.0, -2.0, the largest finite value, the
+    # smallest subnormal, infinity
+    assert M.widen(np.array([0x3F80, 0xC000, 0x7F7F, 0x0001, 0x7F80], dtype=np.uint16)).tolist() \
+        == [1.0, -2.0, (2 - 2 ** -7) * 2.0 ** 127, 2.0 ** -133, math.inf]
+    f = np.array([1.5, -3.25e-7], dtype=np.float32)
+    np.testing.assert_array_equal(M.widen(f), f.astype(np.float64))
+    assert M.widen(None) is None
+
+
 # ----------------------------------------------------------------- P12 ----
 @pytest.mark.parametrize("act", ["swiglu", "gelu"])
 def test_p12_shared_expert(act):

@@ -353,7 +353,8 @@ def test_empty_and_degenerate_calls():
     x_disp, slot, slot_token, kept, dropped = ops.moe_dispatch(xx, layer.buf.topk_idx, 4, 0)
     torch.cuda.synchronize()
     assert np.all(to_np(slot) == -1) and int(to_np(dropped)[0]) == 80
-    y = ops.moe_combine(torch.zeros((0, 256), dtype=torch.float32, device=DEV), slot,
+    # (every slot is -1, so no expert row is read; one dummy row stands for y_disp)
+    y = ops.moe_combine(torch.zeros((1, 256), dtype=torch.float32, device=DEV), slot,
                         layer.buf.topk_w)
     torch.cuda.synchronize()
     assert np.all(to_np(y) == 0.0)
@@ -473,7 +474,7 @@ def test_deterministic_bitwise():
 # ---------------------------------------------------- full-size configs ----
 def test_full_config2_with_shared_expert():
     """The 4096-token layer plus a shared expert of intermediate size 4096
-    (run on its own stream, overlapping the routed path)."""
+    (enqueued first on the same stream as the routed path)."""
     cfg = CONFIGS[2].with_(shared_I=4096)
     log("[full] config 2 + shared expert (I_s 4096)")
     inp = make_inputs(cfg)
