@@ -1,29 +1,36 @@
 """Benchmark: one sparse-MoE FFN layer forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--config 5] [--also 2,3,4] [--gpus 1]
 
 A step is one whole layer forward (route, dispatch of the row maps with the
 aux statistics in the same pass, the grouped expert GEMM whose first product
 gathers its rows from x, combine) over one batch of synthetic input that is
 already resident in HBM.
-The default workload is the 2 x 2048-token layer (hidden 2048, SwiGLU
-intermediate 4096, 8 experts, top-2, capacity factor 1.25, bf16 with fp32
-accumulation); --config 6 is the drop-free 64-token decode step on the same
-layer.  Prints one JSON line.
 
-Timing:
+The headline workload is the largest one: the long-context layer (T = 32768
+tokens in one sequence, hidden 2048, SwiGLU intermediate 5632, 32 experts,
+top-2 Gumbel hard routing at temperature 1 + 1e-4 * 32768, capacity factor
+1.25, bf16 with fp32 accumulation).  The other workloads (--also, default the
+4096-token layer, the skewed 16384-token layer and the wide GELU layer) are
+measured the same way in the same process and reported as sub-records of the
+one JSON line ("workloads").  --config 6 is the drop-free 64-token decode step.
+
+Timing, per workload:
   * the timed region is exactly K whole-layer forwards, bracketed by device
-    synchronisation, with nothing else enqueued (it sets ms_per_step and
-    value);
-  * K more steps follow with HIP events on the launch stream between the
-    phases, so each phase's average duration is reported too (the expert
-    phase dominates and gives `roofline`, against the matrix-core peak or,
-    when its weights take longer to stream than its FLOP to compute, against
-    HBM);
-  * memory-bound phases are also timed in isolation after a 1 GiB write that
-    flushes the 256 MB Infinity Cache, so their bytes come from HBM;
+    synchronisation; HIP events recorded on the launch stream between the
+    phases inside that region give each phase's average duration, so
+    `value` (tokens per second of the region) and `roofline` (the expert
+    phase: both grouped-GEMM launches) come from the same steps;
+  * the same K steps without events follow (`ms_per_step_no_events`: what
+    the events cost);
+  * the GPU shader clock is sampled during the timed region where the
+    driver exposes it (sysfs pp_dpm_sclk);
+  * memory-bound phases are also timed alone after a 1 GiB write that
+    flushes the 256 MB Infinity Cache, so their bytes come from HBM; the
+    dispatch that copies rows into the per-expert buffer (the unfused path)
+    is timed the same way, as the HBM figure of dispatch;
   * the CPU oracle (float64, the reference implementation) is timed on the
-    host cores on one full layer forward of the same workload.
+    host cores on one or more full layer forwards of the same workload.
 
 Further measurements, each added to the same JSON line: --backward (a
 training step: forward keeping the dispatched rows, then the combine, expert,
@@ -56,8 +63,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=5,
+                    help="headline workload (default 5, the long-context 32768-token layer)")
+    ap.add_argument("--also", default="2,3,4",
+                    help="other workloads measured in the same run, comma-separated ids "
+                         "('' for none); each becomes a sub-record of the JSON line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle forwards are repeated until this much CPU time is timed")
     ap.add_argument("--iso-reps", type=int, default=10)
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward pass (combine, expert FFN, dispatch and router "
@@ -95,10 +108,14 @@ def algorithmic_work(cfg, kept: np.ndarray, dropped: int, weights: str = "bf16")
     # written; the row copy happens inside the first expert product's loads),
     # and it computes the aux statistics in the same pass (probs read once)
     dispatch_bytes = T * k * 4 + T * k * 4 + n_kept * 4 + T * E * 4
+    # the unfused dispatch also copies the kept rows: x read once, N_kept rows
+    # written, on top of the maps
+    copy_dispatch_bytes = T * H * esz + n_kept * H * esz + T * k * 4 + T * k * 4 + n_kept * 4
     # kept expert rows (fp32) read once, y written once, slot + weights read
     combine_bytes = n_kept * H * 4 + T * H * esz + T * k * 8
     return dict(n_kept=n_kept, ffn_flop=ffn_flop, ffn_bytes=ffn_bytes, route_bytes=route_bytes,
-                dispatch_bytes=dispatch_bytes, combine_bytes=combine_bytes, dropped=dropped)
+                dispatch_bytes=dispatch_bytes, copy_dispatch_bytes=copy_dispatch_bytes,
+                combine_bytes=combine_bytes, dropped=dropped)
 
 
 TRAFFIC_PROFILES = {
@@ -138,8 +155,10 @@ def gemm_source_digest() -> str:
     return hashlib.sha256(text.encode()).hexdigest()
 
 
-def cpu_baseline(cfg, inputs):
-    """The CPU oracle as it stands, timed on one full layer forward."""
+def cpu_baseline(cfg, inputs, seconds: float = 10.0):
+    """The CPU oracle as it stands, timed on whole layer forwards of the
+    workload (all T tokens each), repeated until `seconds` of CPU time have
+    been timed (at least one)."""
     from oracle import moe_oracle as M
     try:
         from threadpoolctl import threadpool_info
@@ -147,14 +166,14 @@ def cpu_baseline(cfg, inputs):
     except Exception:  # pragma: no cover
         blas = []
     threads = max([n for _, n in blas if n] or [1])
-    # repeat whole forwards until about 10 s of CPU work has been timed
     runs, dt = 0, 0.0
+    res = None
     while True:
         t0 = time.perf_counter()
         res = M.forward(inputs, cfg)
         dt += time.perf_counter() - t0
         runs += 1
-        if dt >= 10.0 or runs >= 50:
+        if dt >= seconds or runs >= 50:
             break
     cpu_model = ""
     try:
@@ -168,11 +187,64 @@ def cpu_baseline(cfg, inputs):
     return {
         "value": round(runs * cfg.T / dt, 3), "unit": "tokens/s", "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{runs} full layer forwards of the same workload ({cfg.T} tokens each), "
+        "sample": f"{runs} full layer forward(s) of the same workload ({cfg.T} tokens each), "
                   f"float64 numpy with BLAS products; {dt:.2f} s in total",
         "affinity_cores": len(os.sched_getaffinity(0)), "cpu": cpu_model, "blas": blas,
         "phase_s": {k: round(v, 4) for k, v in res.timings.items()},
     }
+
+
+class ClockSampler:
+    """Samples the GPU shader clock (the active level of sysfs pp_dpm_sclk)
+    from a host thread while the timed region runs; empty where the driver
+    does not expose it."""
+
+    def __init__(self, period_s: float = 0.002):
+        import glob
+        import threading
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thr = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        import re
+        for p in self.paths:
+            try:
+                for line in open(p):
+                    if line.rstrip().endswith("*"):
+                        m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                        if m:
+                            return int(m.group(1))
+            except OSError:
+                continue
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            time.sleep(self.period)
+
+    def __enter__(self):
+        if self.paths:
+            self._thr.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.paths:
+            self._thr.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        a = np.array(self.samples)
+        return {"samples": int(a.size), "mhz_median": float(np.median(a)),
+                "mhz_min": int(a.min()), "mhz_max": int(a.max()),
+                "source": "sysfs pp_dpm_sclk, active level"}
 
 
 def bench_backward(cfg, inputs, dev, args):
@@ -267,61 +339,66 @@ def bench_shared(cfg, dev, args):
             "shared_expert_TFLOP/s": round(sh_flop / (res["shared"] * 1e-3) / 1e12, 2)}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py: the layer runs on one GPU only; --gpus {args.gpus} is not supported",
-              file=sys.stderr)
-        sys.exit(2)
+def workload_name(cfg, weights):
+    return (f"{cfg.name}: one MoE FFN layer forward, T={cfg.T} ({cfg.batch}x{cfg.seq_len}), "
+            f"H={cfg.H}, I={cfg.I}, E={cfg.E}, top-{cfg.k}, cf={cfg.cf}, {cfg.act}, "
+            f"{cfg.route} router" + (", router bias +2 on expert 0" if cfg.router_bias0 else "")
+            + (", e4m3 expert weights with per-column scales" if weights == "fp8" else ""))
+
+
+def run_workload(cid, args, with_cpu: bool):
+    """Measure one workload; returns its record (the fields of the JSON line)."""
     import torch
     from mixture_experts_layer_08_amd.layer import MoELayerGPU, x_to_device
     from mixture_experts_layer_08_amd.synth import CONFIGS, make_inputs
 
-    cfg = CONFIGS[args.config]
-    print(f"[bench] generating inputs for {cfg.name}", file=sys.stderr, flush=True)
+    cfg = CONFIGS[cid]
+    print(f"[bench] {cfg.name}: generating inputs", file=sys.stderr, flush=True)
     inputs = make_inputs(cfg)
     dev = "cuda:0"
     layer = MoELayerGPU(cfg, inputs, dev, weights=args.weights)
     x = x_to_device(inputs, cfg, dev)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
-
     for _ in range(args.warmup):
         layer.forward(x)
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    print(f"[bench] {cfg.name}: warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
     K = args.steps
-    # the timed region: K whole-layer forwards, nothing else enqueued
+    # the timed region: K whole-layer forwards, with HIP events between the
+    # phases on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    torch.cuda.synchronize()
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        for s_ in range(K):
+            e = ev[s_]
+            e[0].record(stream)
+            layer.route(x)
+            e[1].record(stream)
+            layer.dispatch_aux(x)
+            e[2].record(stream)
+            layer.experts(x)
+            e[3].record(stream)
+            layer.combine()
+            e[4].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    names = ["route", "dispatch", "expert_ffn", "combine"]
+    ph = {n: float(np.mean([ev[s_][i].elapsed_time(ev[s_][i + 1]) for s_ in range(K)]))
+          for i, n in enumerate(names)}
+    dev_ms = float(np.mean([ev[s_][0].elapsed_time(ev[s_][4]) for s_ in range(K)]))
+    ms_per_step = wall * 1e3 / K
+    # the same K steps with nothing but the layer enqueued
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(K):
         layer.forward(x)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # the same K steps again with HIP events between the phases (on the launch
-    # stream) for the per-phase times; the events add a little time per step,
-    # so this loop does not set ms_per_step
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
-    torch.cuda.synchronize()
-    for s in range(K):
-        e = ev[s]
-        e[0].record(stream)
-        layer.route(x)
-        e[1].record(stream)
-        layer.dispatch_aux(x)
-        e[2].record(stream)
-        layer.experts(x)
-        e[3].record(stream)
-        layer.combine()
-        e[4].record(stream)
-    torch.cuda.synchronize()
-    names = ["route", "dispatch", "expert_ffn", "combine"]
-    ph = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)]))
-          for i, n in enumerate(names)}
-    dev_ms = float(np.mean([ev[s][0].elapsed_time(ev[s][4]) for s in range(K)]))
-    ms_per_step = wall * 1e3 / K
-    print(f"[bench] timed {K} steps: {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
+    ms_plain = (time.perf_counter() - t0) * 1e3 / K
+    print(f"[bench] {cfg.name}: timed {K} steps: {ms_per_step:.4f} ms/step "
+          f"({ms_plain:.4f} without events)", file=sys.stderr, flush=True)
 
     kept = layer.buf.kept.cpu().numpy()
     dropped = int(layer.buf.dropped.cpu()[0])
@@ -329,9 +406,8 @@ def main():
 
     # memory-bound phases in isolation, after flushing the Infinity Cache
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    iso = {}
-    for n, fn in (("route", lambda: layer.route(x)), ("dispatch", lambda: layer.dispatch_aux(x)),
-                  ("combine", layer.combine)):
+
+    def cold(fn):
         ts = []
         for _ in range(args.iso_reps):
             flush.fill_(1)
@@ -342,17 +418,24 @@ def main():
             b.record(stream)
             torch.cuda.synchronize()
             ts.append(a.elapsed_time(b))
-        iso[n] = float(np.median(ts))
-    del flush
+        return float(np.median(ts))
+
+    iso = {"route": cold(lambda: layer.route(x)), "dispatch": cold(lambda: layer.dispatch_aux(x)),
+           "combine": cold(layer.combine)}
+    # the unfused dispatch that copies the kept rows into x_disp [E, C, H]
+    copy_layer_buf = torch.empty((cfg.E, layer.C, cfg.H), dtype=layer.tdtype, device=dev)
+    from mixture_experts_layer_08_amd import ops
+    b = layer.buf
+
+    def copy_dispatch():
+        ops.moe_dispatch_aux(x, b.topk_idx, b.probs, cfg.E, layer.C, cfg.alpha, ws=b.ws,
+                             x_disp=copy_layer_buf, slot=b.slot, slot_token=b.slot_token,
+                             kept=b.kept, dropped=b.dropped, counts=b.counts, f=b.f, p=b.p,
+                             l_aux=b.l_aux, copy=True)
+    iso["dispatch_copy"] = cold(copy_dispatch)
+    del flush, copy_layer_buf
     layer.forward(x)        # leave buffers consistent
     torch.cuda.synchronize()
-    if args.copy_calibration:
-        src = torch.ones(1 << 28, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     gemm_ms = ph["expert_ffn"]
     achieved_tflops = work["ffn_flop"] / (gemm_ms * 1e-3) / 1e12
@@ -360,12 +443,18 @@ def main():
     for n, key in (("route", "route_bytes"), ("dispatch", "dispatch_bytes"),
                    ("combine", "combine_bytes")):
         gbs = work[key] / (ph[n] * 1e-3) / 1e9
+        g2 = work[key] / (iso[n] * 1e-3) / 1e9
         phases[n] = {"ms": round(ph[n], 5), "bytes": work[key], "GB/s": round(gbs, 1),
-                     "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
-        if n in iso:
-            g2 = work[key] / (iso[n] * 1e-3) / 1e9
-            phases[n].update({"ms_cold": round(iso[n], 5), "GB/s_cold": round(g2, 1),
-                              "hbm_frac_cold": round(g2 / PEAK_HBM_GBS, 4)})
+                     "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "ms_cold": round(iso[n], 5),
+                     "GB/s_cold": round(g2, 1), "hbm_frac_cold": round(g2 / PEAK_HBM_GBS, 4)}
+    phases["dispatch"]["note"] = ("index-only dispatch of the fused-gather layer (maps and aux "
+                                  "statistics, no row copy): a latency, not an HBM stream")
+    gcp = work["copy_dispatch_bytes"] / (iso["dispatch_copy"] * 1e-3) / 1e9
+    phases["dispatch_copy"] = {"ms_cold": round(iso["dispatch_copy"], 5),
+                               "bytes": work["copy_dispatch_bytes"], "GB/s_cold": round(gcp, 1),
+                               "hbm_frac_cold": round(gcp / PEAK_HBM_GBS, 4),
+                               "note": "dispatch with the row copy into [E, C, H] (x read once, "
+                                       "kept rows written), timed alone after a cache flush"}
     ffn_gbs = work["ffn_bytes"] / (gemm_ms * 1e-3) / 1e9
     phases["expert_ffn"] = {"ms": round(gemm_ms, 5), "flop": work["ffn_flop"],
                             "TFLOP/s": round(achieved_tflops, 2),
@@ -380,7 +469,7 @@ def main():
               ("_fp8, e4m3 weights" if args.weights == "fp8" else "") + ": " +
               ("gate/up product with SwiGLU epilogue" if cfg.act == "swiglu" else
                "first product with bias + GELU epilogue") +
-              ", then down product; split last rounds finished in-kernel)")
+              ", then down product; both launches, timed together inside the timed region)")
     if t_hbm > t_mfma:
         roofline = {"bound": "hbm", "kernel": kernel, "achieved": round(ffn_gbs, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ffn_gbs / PEAK_HBM_GBS, 4),
@@ -394,42 +483,78 @@ def main():
                      "traffic_unit": "HBM bytes per expert phase (rocprofv3 FETCH_SIZE x2.0 + "
                                      "WRITE_SIZE x1.0, copy-calibrated)",
                      "avg_ms": round(gemm_ms, 5)})
-
-    out = {
-        "metric": METRIC,
+    rec = {
         "value": round(cfg.T / (ms_per_step * 1e-3), 1),
         "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
+        "ms_per_step_no_events": round(ms_plain, 5),
         "dtype": cfg.dtype,
-        "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: one MoE FFN layer forward, T={cfg.T} "
-                               f"({cfg.batch}x{cfg.seq_len}), H={cfg.H}, I={cfg.I}, E={cfg.E}, "
-                               f"top-{cfg.k}, cf={cfg.cf}, {cfg.act}, {cfg.route} router" +
-                               (", e4m3 expert weights with per-column scales"
-                                if args.weights == "fp8" else ""),
+        "config": {"workload": workload_name(cfg, args.weights),
                    "expert_weights": args.weights,
                    "tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I, "experts": cfg.E,
                    "top_k": cfg.k, "capacity_factor": cfg.cf,
                    "capacity": layer.C, "kept_rows": work["n_kept"], "dropped": dropped,
-                   "path": "route, dispatch (row maps) with aux statistics, gather-fused expert products, "
-                           "combine"},
+                   "path": "route, dispatch (row maps) with aux statistics, gather-fused expert "
+                           "products, combine"},
         "roofline": roofline,
         "phases": phases,
         "device_ms_per_step": round(dev_ms, 5),
+        "gpu_clock": clk.summary(),
     }
     if args.backward:
-        out["backward"] = bench_backward(cfg, inputs, dev, args)
+        rec["backward"] = bench_backward(cfg, inputs, dev, args)
     if args.shared:
-        out["shared_expert"] = bench_shared(cfg, dev, args)
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(cfg, inputs)
+        rec["shared_expert"] = bench_shared(cfg, dev, args)
+    del layer, x
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if with_cpu:
+        print(f"[bench] {cfg.name}: timing the CPU oracle", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(cfg, inputs, args.cpu_seconds)
+    return rec
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this benchmark runs the layer on one GPU; --gpus {args.gpus} is not "
+              "supported (the layer has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    also = [int(c) for c in args.also.split(",") if c.strip()] if args.also else []
+    also = [c for c in also if c != args.config]
+    head = run_workload(args.config, args, not args.no_cpu_baseline)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    subs = {}
+    for c in also:
+        subs[str(c)] = run_workload(c, args, not args.no_cpu_baseline)
+    out = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic",
+    }
+    for key in ("config", "roofline", "cpu_baseline", "phases", "ms_per_step_no_events",
+                "device_ms_per_step", "gpu_clock", "backward", "shared_expert"):
+        if key in head:
+            out[key] = head[key]
+    if subs:
+        out["workloads"] = subs
     print(json.dumps(out), flush=True)
 
 

@@ -107,7 +107,7 @@ def test_fp8_layer_matches_dequantised_oracle(name, fused):
     ok = np.all(to_np(b.topk_idx) == ref.route.idx, axis=1)
     ok &= np.all(to_np(b.slot) == ref.disp.slot, axis=1)
     assert ok.mean() > 0.95
-    worst = assert_rows_close(to_np(y)[ok], ref.y[ok], 2e-2, f"{name}: y")
+    worst = assert_rows_close(to_np(y)[ok], ref.y[ok], 2e-2, f"{name}: y", stored_bf16=True)
     log(f"[fp8] {name}: dropped {int(to_np(b.dropped)[0])}, worst err/rms {worst:.3e}")
 
 
@@ -134,20 +134,17 @@ def test_fp8_decode_config_full_size():
     b = layer.buf
     assert int(to_np(b.dropped)[0]) == 0
     ok = np.all(to_np(b.topk_idx) == ref.route.idx, axis=1)
-    worst = assert_rows_close(to_np(y)[ok], ref.y[ok], 2e-2, "decode fp8: y")
+    worst = assert_rows_close(to_np(y)[ok], ref.y[ok], 2e-2, "decode fp8: y", stored_bf16=True)
     log(f"[fp8] decode: {int(ok.sum())}/64 rows, worst err/rms {worst:.3e}")
 
 
-def test_fp8_config2_sampled():
+def test_fp8_config2_full():
     cfg = CONFIGS[2]
-    log("[fp8] 4096-token layer full size (sampled rows)")
+    log("[fp8] 4096-token layer full size, every row")
     inp, ref_inp, layer, y = _layer_case(cfg, True)
     b = layer.buf
-    r = M.route(inp, cfg)
-    d = M.dispatch(r.idx, cfg.E, layer.C)
-    ok = np.all(to_np(b.topk_idx) == r.idx, axis=1) & np.all(to_np(b.slot) == d.slot, axis=1)
-    rng = np.random.default_rng(47)
-    sample = np.sort(rng.choice(np.where(ok)[0], size=64, replace=False))
-    ref = M.forward(ref_inp, cfg, sample=sample)
-    worst = assert_rows_close(to_np(y)[sample], ref.y, 2e-2, "config 2 fp8: y (sampled)")
-    log(f"[fp8] config 2: worst err/rms {worst:.3e}")
+    ref = M.forward(ref_inp, cfg)
+    ok = np.all(to_np(b.topk_idx) == ref.route.idx, axis=1) & \
+        np.all(to_np(b.slot) == ref.disp.slot, axis=1)
+    worst = assert_rows_close(to_np(y)[ok], ref.y[ok], 2e-2, "config 2 fp8: y", stored_bf16=True)
+    log(f"[fp8] config 2: {int(ok.sum())}/{cfg.T} rows, worst err/rms {worst:.3e}")
