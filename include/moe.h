@@ -176,6 +176,29 @@ moe_status_t moe_dispatch_aux(void* stream, moe_dtype_t dtype, const void* x,
                               int32_t* counts, float* f, float* p, float* l_aux,
                               void* ws, size_t ws_bytes);
 
+/* moe_dispatch_aux without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, outputs and results as
+ * moe_dispatch_aux (the same kernels run); its workspace is instead a static
+ * device array of MOE_NOALLOC_SCRATCH_BYTES bytes inside the library, one
+ * per GPU, held until the process ends.  It calls no allocating routine.
+ *   - MOE_ERR_UNSUPPORTED when moe_workspace_bytes(T, E, k) exceeds
+ *     MOE_NOALLOC_SCRATCH_BYTES (e.g. above T * k = 2^19 at E = 64 or
+ *     2^22 at E = 8).
+ *   - Every call on one GPU shares that GPU's array: two calls that may
+ *     run at the same time on one GPU (different streams, no ordering
+ *     between them) race and give wrong results.  Calls ordered on one
+ *     stream are safe; nothing in the array needs clearing between them.
+ *   - MOE_ERR_LAUNCH when the array's device address cannot be looked up. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)2 << 20)
+moe_status_t moe_dispatch_aux_noalloc(void* stream, moe_dtype_t dtype, const void* x,
+                                      const int32_t* topk_idx, const float* probs,
+                                      int64_t T, int64_t H, int E, int k, int64_t C,
+                                      float alpha, void* x_disp, int32_t* slot,
+                                      int32_t* slot_token, int32_t* kept,
+                                      int32_t* dropped, int32_t* counts, float* f,
+                                      float* p, float* l_aux);
+
 /* Expert FFNs as one grouped GEMM over the dispatched rows.
  * [P2] sections 2.2 and 3.1 (each expert is an FFN; GELU expert with two
  * biased Linears), [P5] section 2.1 (SwiGLU), [P2] section 4.4 / [P5] 6.3

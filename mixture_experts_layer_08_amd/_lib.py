@@ -29,7 +29,7 @@ EXPORTS = ("moe_capacity", "moe_status_string", "moe_workspace_bytes", "moe_rout
            "moe_expert_ffn_bwd_ws_bytes", "moe_dispatch_bwd", "moe_route_bwd",
            "moe_route_bwd_ws_bytes", "moe_quantize_fp8", "moe_dequantize_fp8",
            "moe_expert_ffn_fp8", "moe_expert_ffn_gather_fp8", "moe_expert_ffn_fwd_save",
-           "moe_dispatch_aux")
+           "moe_dispatch_aux", "moe_dispatch_aux_noalloc")
 
 _lock = threading.Lock()
 _lib = None
@@ -63,6 +63,9 @@ def _declare(L: ctypes.CDLL) -> None:
     L.moe_dispatch_aux.argtypes = [vp, i32, vp, vp, vp, i64, i64, i32, i32, i64, f32, vp, vp, vp,
                                    vp, vp, vp, vp, vp, vp, vp, c.c_size_t]
     L.moe_dispatch_aux.restype = i32
+    L.moe_dispatch_aux_noalloc.argtypes = [vp, i32, vp, vp, vp, i64, i64, i32, i32, i64, f32, vp,
+                                           vp, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_dispatch_aux_noalloc.restype = i32
     L.moe_expert_ffn.argtypes = [vp, i32, i32, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp, vp,
                                  vp, vp, vp, c.c_size_t]
     L.moe_expert_ffn.restype = i32

@@ -26,6 +26,8 @@
 // L_aux from those totals and partial sums (both in block order).
 #include "moe_common.h"
 
+#include <mutex>
+
 namespace {
 
 constexpr int kDChunk = 256;           // assignments per histogram / rank block
@@ -349,14 +351,16 @@ extern "C" moe_status_t moe_dispatch(void* stream, moe_dtype_t dtype, const void
     return MOE_OK;
 }
 
-// Dispatch and the load-balancing statistics in one pass over the routing.
-extern "C" moe_status_t moe_dispatch_aux(void* stream, moe_dtype_t dtype, const void* x,
-                                         const int32_t* topk_idx, const float* probs, int64_t T,
-                                         int64_t H, int E, int k, int64_t C, float alpha,
-                                         void* x_disp, int32_t* slot, int32_t* slot_token,
-                                         int32_t* kept, int32_t* dropped, int32_t* counts,
-                                         float* f, float* p, float* l_aux, void* ws,
-                                         size_t ws_bytes) {
+namespace {
+
+// Dispatch and the load-balancing statistics in one pass over the routing;
+// ws holds the per-block histograms, offsets and partial sums.
+moe_status_t dispatch_aux_impl(void* stream, moe_dtype_t dtype, const void* x,
+                               const int32_t* topk_idx, const float* probs, int64_t T, int64_t H,
+                               int E, int k, int64_t C, float alpha, void* x_disp, int32_t* slot,
+                               int32_t* slot_token, int32_t* kept, int32_t* dropped,
+                               int32_t* counts, float* f, float* p, float* l_aux, void* ws,
+                               size_t ws_bytes) {
     if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_DTYPE;
     if (T < 0 || H <= 0 || E < 1 || k < 1 || k > E || C < 0) return MOE_ERR_SHAPE;
     if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
@@ -401,4 +405,59 @@ extern "C" moe_status_t moe_dispatch_aux(void* stream, moe_dtype_t dtype, const 
         MOE_CHECK_LAUNCH();
     }
     return MOE_OK;
+}
+
+// The workspace of moe_dispatch_aux_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it only stands for the symbol); it
+// uses the device address that hipGetSymbolAddress returns for the current
+// device, looked up once per device.
+constexpr size_t kNoallocScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (nullptr if it cannot be had).
+void* noalloc_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" moe_status_t moe_dispatch_aux(void* stream, moe_dtype_t dtype, const void* x,
+                                         const int32_t* topk_idx, const float* probs, int64_t T,
+                                         int64_t H, int E, int k, int64_t C, float alpha,
+                                         void* x_disp, int32_t* slot, int32_t* slot_token,
+                                         int32_t* kept, int32_t* dropped, int32_t* counts,
+                                         float* f, float* p, float* l_aux, void* ws,
+                                         size_t ws_bytes) {
+    return dispatch_aux_impl(stream, dtype, x, topk_idx, probs, T, H, E, k, C, alpha, x_disp, slot,
+                             slot_token, kept, dropped, counts, f, p, l_aux, ws, ws_bytes);
+}
+
+extern "C" moe_status_t moe_dispatch_aux_noalloc(void* stream, moe_dtype_t dtype, const void* x,
+                                                 const int32_t* topk_idx, const float* probs,
+                                                 int64_t T, int64_t H, int E, int k, int64_t C,
+                                                 float alpha, void* x_disp, int32_t* slot,
+                                                 int32_t* slot_token, int32_t* kept,
+                                                 int32_t* dropped, int32_t* counts, float* f,
+                                                 float* p, float* l_aux) {
+    if (T >= 0 && E >= 1 && E <= MOE_MAX_EXPERTS && k >= 1 && k <= MOE_MAX_TOPK &&
+        T * k < ((int64_t)1 << 31) && moe_dispatch_aux_ws_bytes(T, E, k) > kNoallocScratchBytes)
+        return MOE_ERR_UNSUPPORTED;  // the static workspace is too small for this call
+    void* ws = noalloc_scratch();
+    if (!ws) return MOE_ERR_LAUNCH;
+    return dispatch_aux_impl(stream, dtype, x, topk_idx, probs, T, H, E, k, C, alpha, x_disp, slot,
+                             slot_token, kept, dropped, counts, f, p, l_aux, ws,
+                             kNoallocScratchBytes);
 }
