@@ -404,13 +404,16 @@ def run_workload(cid, args, with_cpu: bool):
     dropped = int(layer.buf.dropped.cpu()[0])
     work = algorithmic_work(cfg, kept, dropped, args.weights)
 
-    # memory-bound phases in isolation, after flushing the Infinity Cache
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    # memory-bound phases in isolation, after flushing the Infinity Cache by
+    # reading 1 GiB (a read leaves clean lines behind: a write-based flush
+    # would leave dirty lines whose write-back the timed phase would pay)
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    sink = torch.empty((), dtype=torch.int64, device=dev)
 
     def cold(fn):
         ts = []
         for _ in range(args.iso_reps):
-            flush.fill_(1)
+            torch.sum(flush, dim=0, out=sink)
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
@@ -433,7 +436,7 @@ def run_workload(cid, args, with_cpu: bool):
                              kept=b.kept, dropped=b.dropped, counts=b.counts, f=b.f, p=b.p,
                              l_aux=b.l_aux, copy=True)
     iso["dispatch_copy"] = cold(copy_dispatch)
-    del flush, copy_layer_buf
+    del flush, sink, copy_layer_buf
     layer.forward(x)        # leave buffers consistent
     torch.cuda.synchronize()
 

@@ -10,9 +10,10 @@
 // The stable sort is a counting sort with a deterministic order, so every
 // integer output is reproducible bit for bit:
 //  1. histogram: per block of 256 assignments, LDS integer counts;
-//  2. scan: one small block turns the per-block counts into per-block
-//     starting rows for every expert (exclusive scan in block order), and
-//     finishes kept[e] = min(count, C) and the dropped total;
+//  2. scan: one block turns the per-block counts into per-block starting
+//     rows for every expert (exclusive scan in block order; with the aux
+//     statistics, 1024 threads over stripes of blocks), and finishes
+//     kept[e] = min(count, C) and the dropped total;
 //  3. rank: each wave walks 64 assignments at a time in (t, j) order; a
 //     ballot per distinct expert in the chunk gives each lane its rank among
 //     same-expert lanes; slot and slot_token follow;
@@ -89,50 +90,78 @@ __global__ __launch_bounds__(kDThreads) void disp_hist_aux_kernel(
 
 // The scan of disp_scan_kernel plus the statistics: counts[e] = the
 // expert's assignments before the drop, f = counts/(T k), P = (sum of the
-// block partials)/T, L_aux = alpha E sum_e f P.
-__global__ __launch_bounds__(MOE_MAX_EXPERTS) void disp_scan_aux_kernel(
+// block partials)/T, L_aux = alpha E sum_e f P.  One workgroup of 1024
+// threads: thread (r, e) owns stripe r of consecutive histogram blocks for
+// expert e, sums the stripe (its loads all in flight together), the stripe
+// totals are scanned in stripe order, and each thread then writes its
+// blocks' starting rows.  P adds each stripe's partial sums in block order,
+// then the stripes in order (a fixed order: deterministic).
+constexpr int kScanThreads = 1024;
+constexpr int kScanUnroll = 8;
+
+__global__ __launch_bounds__(kScanThreads) void disp_scan_aux_kernel(
     const int32_t* __restrict__ hist, const double* __restrict__ psum, int nb, int E, int64_t C,
     int64_t T, int k, float alpha, int32_t* __restrict__ off, int32_t* __restrict__ kept,
     int32_t* __restrict__ dropped, int32_t* __restrict__ counts, float* __restrict__ f,
     float* __restrict__ p, float* __restrict__ l_aux) {
+    __shared__ int64_t s_cnt[kScanThreads];     // [stripe][expert] counts
+    __shared__ double s_ps[kScanThreads];       // [stripe][expert] probability sums
     __shared__ int64_t over[MOE_MAX_EXPERTS];
     __shared__ double fp[MOE_MAX_EXPERTS];
-    const int e = threadIdx.x;
-    if (e < E) {
-        int64_t run = 0;
-        double ps = 0.0;
-        int b = 0;
-        for (; b + 8 <= nb; b += 8) {  // eight independent loads in flight, used in block order
-            int h[8];
-            double q[8];
+    const int tid = threadIdx.x;
+    const int R = kScanThreads / E;             // stripes
+    const int S = (nb + R - 1) / R;             // blocks per stripe
+    const int r = tid / E, e = tid % E;
+    const bool active = r < R;
+    const int b0 = r * S, b1 = min(b0 + S, nb);
+    int64_t cnt = 0;
+    double ps = 0.0;
+    if (active) {
+        for (int b = b0; b < b1; b += kScanUnroll) {
+            int h[kScanUnroll];
+            double q[kScanUnroll];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                h[u] = hist[(size_t)(b + u) * E + e];
-                q[u] = psum[(size_t)(b + u) * E + e];
+            for (int u = 0; u < kScanUnroll; ++u) {
+                h[u] = b + u < b1 ? hist[(size_t)(b + u) * E + e] : 0;
+                q[u] = b + u < b1 ? psum[(size_t)(b + u) * E + e] : 0.0;
             }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                off[(size_t)(b + u) * E + e] = (int32_t)run;
-                run += h[u];
-                ps += q[u];
+            for (int u = 0; u < kScanUnroll; ++u) {
+                cnt += h[u];
+                if (b + u < b1) ps += q[u];
             }
         }
-        for (; b < nb; ++b) {
-            off[(size_t)b * E + e] = (int32_t)run;
-            run += hist[(size_t)b * E + e];
-            ps += psum[(size_t)b * E + e];
-        }
-        kept[e] = (int32_t)(run < C ? run : C);
-        over[e] = run > C ? run - C : 0;
-        const double fe = T > 0 ? (double)run / ((double)T * k) : 0.0;
-        const double pe = T > 0 ? ps / (double)T : 0.0;
-        counts[e] = (int32_t)run;
-        f[e] = (float)fe;
-        p[e] = (float)pe;
-        fp[e] = fe * pe;
+        s_cnt[tid] = cnt;
+        s_ps[tid] = ps;
     }
     __syncthreads();
-    if (e == 0) {
+    if (tid < E) {  // stripe bases in stripe order; totals
+        int64_t run = 0;
+        double pt = 0.0;
+        for (int rr = 0; rr < R; ++rr) {
+            const int64_t c = s_cnt[rr * E + tid];
+            s_cnt[rr * E + tid] = run;
+            run += c;
+            pt += s_ps[rr * E + tid];
+        }
+        kept[tid] = (int32_t)(run < C ? run : C);
+        over[tid] = run > C ? run - C : 0;
+        const double fe = T > 0 ? (double)run / ((double)T * k) : 0.0;
+        const double pe = T > 0 ? pt / (double)T : 0.0;
+        counts[tid] = (int32_t)run;
+        f[tid] = (float)fe;
+        p[tid] = (float)pe;
+        fp[tid] = fe * pe;
+    }
+    __syncthreads();
+    if (active) {  // each block's starting row, from the stripe's base
+        int64_t run = s_cnt[tid];
+        for (int b = b0; b < b1; ++b) {
+            off[(size_t)b * E + e] = (int32_t)run;
+            run += hist[(size_t)b * E + e];
+        }
+    }
+    if (tid == 0) {
         int64_t d = 0;
         double acc = 0.0;
         for (int i = 0; i < E; ++i) {
@@ -388,7 +417,7 @@ moe_status_t dispatch_aux_impl(void* stream, moe_dtype_t dtype, const void* x,
                            A, E, k, hist, psum);
         MOE_CHECK_LAUNCH();
     }
-    hipLaunchKernelGGL(disp_scan_aux_kernel, dim3(1), dim3(MOE_MAX_EXPERTS), 0, st, hist, psum, nb, E,
+    hipLaunchKernelGGL(disp_scan_aux_kernel, dim3(1), dim3(kScanThreads), 0, st, hist, psum, nb, E,
                        C, T, k, alpha, off, kept, dropped, counts, f, p, l_aux);
     MOE_CHECK_LAUNCH();
     if (nb > 0 || C > 0) {

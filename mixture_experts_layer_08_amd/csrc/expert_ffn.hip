@@ -260,6 +260,13 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
     // 1 KB B loads per wave per k-step (codes: 16 rows of 64 bytes each)
     constexpr int QB = F8 ? BN / 16 / kNW : (BN / 128) * 16 / kNW;
     static_assert(QA == 1 || (QA <= 4 && QA % 2 == 0), "A loads per wave");
+    // store instructions of one wave's whole-tile epilogue (one per four
+    // rows of a 32 x 32 accumulator and output column block, plus the saved
+    // planes), and the waits of the tile that follows it (see kloop)
+    constexpr int TNO_E = (MB == MODE_SWIGLU) ? TN / 2 : TN;
+    constexpr int NS_EPI = TNO_E * TM * 4 * (1 + (SAVE ? (MB == MODE_SWIGLU ? 2 : 1) : 0));
+    constexpr int kWaitFirst = (QA + QB + NS_EPI) < 63 ? (QA + QB + NS_EPI) : 63;
+    constexpr int kWaitMid = NS_EPI < 63 ? NS_EPI : 63;
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int tid = threadIdx.x;
@@ -309,13 +316,23 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
         c.m0 = __builtin_amdgcn_readfirstlane(m_tile * EP::BM);
         c.n0 = __builtin_amdgcn_readfirstlane(n_tile * EP::BN_OUT);
         if (GATHER) {
-            // A: token rows; a row past kept (or an empty slot) reads as zero
+            // A: token rows; a row past kept (or an empty slot) reads as zero.
+            // The tokens of the wave's rows come in by scalar buffer loads
+            // (eight rows each, wave-uniform): they are counted by lgkmcnt,
+            // so using them never waits for the vector memory queue, which
+            // at a tile's start holds the next k-steps' loads and the last
+            // tile's epilogue stores.
             c.rsA = make_rsrc(g.A, (uint32_t)((size_t)g.a_rows * g.K * 2));
+            const i32x4_t rsT = make_rsrc(g.slot_token + (size_t)c.e * g.C, (uint32_t)c.kept * 4);
 #pragma unroll
-            for (int q = 0; q < QA; ++q) {  // branch-free: clamp, load, then select
-                const int row = c.m0 + (wave * QA + q) * 8 + lane / 8;
-                const int t = g.slot_token[(size_t)c.e * g.C + (row < c.kept ? row : c.kept - 1)];
-                c.tok[q] = row < c.kept ? t : -1;
+            for (int q = 0; q < QA; ++q) {
+                const int r0 = c.m0 + (wave * QA + q) * 8;
+                const moe_i32x8_t sv = s_buffer_load_i32x8(rsT, r0 * 4, 0);
+                const int j = lane / 8;
+                int t = sv[0];
+#pragma unroll
+                for (int u = 1; u < 8; ++u) t = j == u ? sv[u] : t;
+                c.tok[q] = r0 + j < c.kept ? t : -1;
             }
         } else {
             // A: rows m0.. of expert e; rows at or past kept read as zero
@@ -467,6 +484,9 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
     int p0 = 0;  // stream index of the current tile's first k-step
     for (int round = 0;; ++round) {
         const TileCtx nxt = tile_at(round + 1);
+        // every round after the first follows a whole tile's epilogue (a
+        // split piece ends the loop)
+        const bool epi_prev = round > 0;
         // loads of stream step p: the current tile or, past its end, the next
         auto stream_a = [&](int p) {
             const int r = p - p0;
@@ -517,16 +537,30 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
         // loads and joins the same barriers (a barrier counts arrivals, so
         // the loop variants stay in step).  sched_barrier(0) keeps each MFMA
         // group on its side of a barrier.
+        // After a whole tile's epilogue, the vector memory queue of each wave
+        // holds, in issue order: the loads of this tile's first step, those of
+        // its second step (QA + QB), then the epilogue's NS_EPI stores (vmcnt
+        // counts loads and stores and retires them in issue order).  A wait
+        // for vmcnt <= N completes everything older than the newest N
+        // operations, so the first step waits with N = QA + QB + NS_EPI and
+        // its mid-step wait (for the second step's loads) with N = NS_EPI:
+        // the stores stay in flight under the first step's MFMAs instead of
+        // draining before the tile starts.  NS_EPI counts the epilogue's
+        // store instructions, all issued unconditionally, so the waits are
+        // exact or stricter; the counter field holds at most 63.
         auto kloop = [&](auto ni) {
             constexpr bool M = decltype(ni)::value > 0;
             bf16x8_t a0[2][TM], b0[2][TN], a1[2][TM], b1[2][TN];
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(QA + QB) : "memory");
+            if (epi_prev)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitFirst) : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(QA + QB) : "memory");
             __syncthreads();
             if (GATHER) {
-                // The row tokens were loaded by compiler-visible loads; using
-                // them here makes the compiler's own wait for them happen once,
-                // now, instead of before every load issue inside the loop (where
-                // it would also wait for the k-step loads in flight).
+                // The row tokens come from scalar loads; using them here makes
+                // the compiler's wait for those (lgkmcnt, which also counts
+                // LDS reads) happen once, now, instead of before a load issue
+                // inside the loop, where fragment reads are in flight.
 #pragma unroll
                 for (int q = 0; q < QA; ++q) asm volatile("" ::"v"(cur.tok[q]));
             }
@@ -540,7 +574,10 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
                     mma(ni, a0, b0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                if (kt == 0 && epi_prev)
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitMid) : "memory");
+                else
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
                 stream_a(p + 2);
                 stream_b(p + 2);

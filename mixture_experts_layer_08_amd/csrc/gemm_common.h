@@ -36,6 +36,13 @@ __device__ moe_i32x2_t buffer_load_i32x2(moe_i32x4_t rsrc, int voffset, int soff
                                          int aux) __asm("llvm.amdgcn.raw.buffer.load.v2i32");
 __device__ moe::f32x4_t buffer_load_f32x4(moe_i32x4_t rsrc, int voffset, int soffset,
                                          int aux) __asm("llvm.amdgcn.raw.buffer.load.v4f32");
+typedef int moe_i32x8_t __attribute__((ext_vector_type(8)));
+// Scalar buffer load of eight consecutive dwords (wave-uniform offset; dwords
+// past the descriptor's range read as zero).  It is counted by lgkmcnt, not
+// vmcnt, so waiting for it never waits for the vector loads and stores in
+// flight.
+__device__ moe_i32x8_t s_buffer_load_i32x8(moe_i32x4_t rsrc, int offset,
+                                           int aux) __asm("llvm.amdgcn.s.buffer.load.v8i32");
 // cache policy of a buffer access (aux): system scope (sc0 sc1), which goes
 // past the per-XCD L2 caches to memory
 constexpr int kAuxSystem = 17;

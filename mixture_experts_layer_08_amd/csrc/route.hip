@@ -8,34 +8,44 @@
 // [P4] long-context page (2kiu.com/news/5130654) sections 2 and 5.2: Gumbel
 //      noise on the logits, hard top-k, temperature 1 + 1e-4 * seq_len.
 //
-// bf16 design (gfx950): the router is HBM-bound (x is read once, W_r is tiny
-// and lives in L2), but at E = 32 it is 32 FLOP per byte of x, above what
-// fp32 vector FMA sustains at HBM speed, so the product runs on the matrix
-// cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  One workgroup of 8
-// waves copies W_r into LDS once, in its own [H, E] layout (16-byte loads),
-// and reads MFMA B operands from it with gfx950's transpose LDS reads; it
-// then walks 16-token tiles.  Each
-// wave owns 1/8 of the hidden dimension and streams its x slice straight
-// from HBM into A-fragment registers (16 rows x 64 contiguous bytes per
-// load); the next tile's loads are issued before the current tile's
-// reduction and epilogue so HBM stays busy.  The 8 partial logit tiles are
-// summed in LDS in a fixed order, then lane groups of width G = 2^ceil(log2 E)
-// hold one token each for the softmax and the k rounds of arg-max.
+// bf16 design (gfx950): the router is HBM-bound (x is read once; W_r is
+// small and stays in L2), but at E = 32 it is 32 FLOP per byte of x, above
+// what fp32 vector FMA sustains at HBM speed, so the product runs on the
+// matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  Each wave owns
+// whole 16-token tiles over the full hidden dimension, so no partial logits
+// cross waves and no barrier waits on a tile: the wave streams its 16 rows of
+// x straight from HBM into A-operand registers in chunks of 256 hidden
+// entries, with the next chunk's loads in flight while the current one is
+// multiplied.  The workgroup's waves walk the chunks together and share the
+// matching 256 rows of W_r, staged in LDS (double-buffered, the next chunk's
+// rows loaded during the current chunk) in its own [H, E] layout and read as
+// MFMA B operands with gfx950's transposing LDS reads; any H that is a
+// multiple of 256 works, however many chunks it takes.  Softmax, Gumbel
+// noise and the k rounds of arg-max run on the accumulators in the MFMA's
+// own layout: lane l holds experts 16 n + l % 16 of tokens 4 (l / 16) ..
+// +3, so a token's experts sit in one 16-lane group and every reduction is
+// a 16-lane shuffle (ties go to the lower expert index).
 #include "moe_common.h"
 
 #include <math.h>
+
+#include <type_traits>
 
 namespace {
 
 using namespace moe;
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kTok = 16;          // tokens per tile (MFMA M)
-constexpr int kRWaves = 8;        // waves per router workgroup
-constexpr int kRThreads = kRWaves * kWave;
-constexpr int kMaxKsPerWave = 16; // 16 k-steps of 32 = 512 hidden per wave
+constexpr int kRMaxWaves = 8;     // waves per router workgroup (one tile each at a time)
+constexpr int kRMaxThreads = kRMaxWaves * kWave;
+constexpr int kKC = 256;          // hidden entries per chunk
+constexpr int kKS = kKC / 32;     // MFMA k-steps per chunk
+constexpr int kWStageMax = 128 * 1024;  // bytes of LDS for W_r
 
 struct RouteParams {
     const void* x;
@@ -157,110 +167,289 @@ __device__ void route_epilogue(const float* lg, int ld, int64_t t0, const RouteP
     }
 }
 
+// Softmax, Gumbel keys, top-k and renormalised weights of one wave's
+// 16-token tile, on the accumulators in the MFMA layout: acc[n][i] of lane l
+// is the logit of token t0 + 4 (l / 16) + i and expert 16 n + l % 16.
+// Gumbel noise of the tile's (token, expert) pairs in the accumulator layout
+// (it depends only on the counter (t, e) and the seed, so it is computed while
+// the tile's x loads are in flight); zero in softmax mode.
 template <int NTN>
-__global__ __launch_bounds__(kRThreads) void route_bf16_kernel(RouteParams p, int ntiles, int gw) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    const int H = p.H;
-    const int nks = H / 32;                    // k-steps of 32
-    const int ks_per_wave = nks / kRWaves;     // <= kMaxKsPerWave
-    uint4* wlds = reinterpret_cast<uint4*>(smem);                          // [H][16*NTN] bf16
-    f32x4_t* red = reinterpret_cast<f32x4_t*>(smem + (size_t)nks * NTN * 1024);  // [8][NTN][64]
-    float* lg = reinterpret_cast<float*>(red + kRWaves * NTN * kWave);     // [16][16*NTN]
-    constexpr int ld = 16 * NTN;
-
-    const int tid = threadIdx.x;
-    const int wave = tid / kWave;
-    const int lane = tid % kWave;
-    const uint16_t* xb = static_cast<const uint16_t*>(p.x);
-    const uint16_t* wr = static_cast<const uint16_t*>(p.w_r);
-
-    const int ks0 = wave * ks_per_wave;
-    // A fragment of k-step ks for this lane: x[t0 + lane%16][ks*32 + (lane/16)*8 .. +8]
-    auto load_tile = [&](uint4 (&a)[kMaxKsPerWave], int tile) {
-        int64_t row = (int64_t)tile * kTok + (lane % 16);
-        if (row >= p.T) row = p.T - 1;  // clamp: rows past T are never written out
-        const uint4* src = reinterpret_cast<const uint4*>(xb + row * H + (lane / 16) * 8);
+__device__ __forceinline__ void tile_noise(float (&gn)[NTN][4], int64_t t0, const RouteParams& p,
+                                           int lane) {
+    const int c = lane % 16, g = lane / 16;
 #pragma unroll
-        for (int i = 0; i < kMaxKsPerWave; ++i)
-            if (i < ks_per_wave) a[i] = src[(size_t)(ks0 + i) * 4];
-    };
-
-    uint4 a_cur[kMaxKsPerWave], a_nxt[kMaxKsPerWave];
-    int tile = blockIdx.x;
-    if (tile < ntiles) load_tile(a_cur, tile);
-
-    // Stage W_r [H, E] in LDS as [H][16*NTN] (experts past E are zero),
-    // 16-byte vectors when E is a multiple of 8.
-    constexpr int EP = 16 * NTN;
-    if (p.E % 8 == 0) {
-        const int vpr = p.E / 8;  // vectors per W_r row
-        for (int v = tid; v < H * vpr; v += kRThreads) {
-            const int h = v / vpr, c = v % vpr;
-            wlds[h * EP / 8 + c] = reinterpret_cast<const uint4*>(wr)[(size_t)h * vpr + c];
+    for (int n = 0; n < NTN; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t t = t0 + 4 * g + i;
+            const int e = 16 * n + c;
+            gn[n][i] = (p.mode == 1 && e < p.E && t < p.T)
+                           ? gumbel_from_word(philox_word0((uint32_t)t, (uint32_t)e, p.key0, p.key1))
+                           : 0.f;
         }
-        const int padv = (EP - p.E) / 8;
-        for (int v = tid; v < H * padv; v += kRThreads) {
-            const int h = v / padv, c = v % padv;
-            wlds[h * EP / 8 + vpr + c] = make_uint4(0, 0, 0, 0);
+}
+
+template <int NTN>
+__device__ __forceinline__ void route_tile_epilogue(const f32x4_t (&acc)[NTN],
+                                                    const float (&gn)[NTN][4],
+                                                    const float (&bias)[NTN], int64_t t0,
+                                                    const RouteParams& p, int lane) {
+    const int E = p.E, k = p.k;
+    const int c = lane % 16, g = lane / 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t t = t0 + 4 * g + i;
+        const bool tok_ok = t < p.T;
+        float key[NTN], z[NTN], prob[NTN];
+        bool ok[NTN];
+        float m = -INFINITY;
+#pragma unroll
+        for (int n = 0; n < NTN; ++n) {
+            const int e = 16 * n + c;
+            ok[n] = e < E;
+            const float l = acc[n][i] + bias[n];
+            key[n] = l;
+            z[n] = l;
+            if (p.mode == 1) {
+                key[n] = l + gn[n][i];
+                z[n] = key[n] * p.inv_tau;
+            }
+            if (!ok[n]) key[n] = z[n] = -INFINITY;
+            m = fmaxf(m, z[n]);
         }
-    } else {
-        uint16_t* w16 = reinterpret_cast<uint16_t*>(wlds);
-        for (int v = tid; v < H * EP; v += kRThreads) {
-            const int h = v / EP, e = v % EP;
-            w16[v] = e < p.E ? wr[(size_t)h * p.E + e] : (uint16_t)0;
+        m = group_max(m, 16);
+        float sum = 0.f;
+#pragma unroll
+        for (int n = 0; n < NTN; ++n) {
+            prob[n] = ok[n] ? expf(z[n] - m) : 0.f;
+            sum += prob[n];
+        }
+        sum = group_sum(sum, 16);
+#pragma unroll
+        for (int n = 0; n < NTN; ++n) {
+            prob[n] = ok[n] ? prob[n] / sum : 0.f;
+            if (ok[n] && tok_ok) {
+                p.probs[t * E + 16 * n + c] = prob[n];
+                if (p.keys) p.keys[t * E + 16 * n + c] = key[n];
+            }
+        }
+        // k rounds of arg-max over (key desc, index asc) across the 16 lanes
+        bool taken[NTN];
+#pragma unroll
+        for (int n = 0; n < NTN; ++n) taken[n] = !ok[n];
+        float wsum = 0.f, my_p = 0.f;
+        int my_sel = -1;
+        for (int j = 0; j < k; ++j) {
+            float bv = -INFINITY, bp = 0.f;
+            int bi = 0x7FFFFFFF;
+#pragma unroll
+            for (int n = 0; n < NTN; ++n) {  // this lane's best (lower n: lower index)
+                if (!taken[n] && (key[n] > bv || bi == 0x7FFFFFFF)) {
+                    bv = key[n];
+                    bi = 16 * n + c;
+                    bp = prob[n];
+                }
+            }
+#pragma unroll
+            for (int o = 8; o > 0; o >>= 1) {
+                const float ov = __shfl_xor(bv, o, 16);
+                const int oi = __shfl_xor(bi, o, 16);
+                const float op = __shfl_xor(bp, o, 16);
+                if (ov > bv || (ov == bv && oi < bi)) {
+                    bv = ov;
+                    bi = oi;
+                    bp = op;
+                }
+            }
+#pragma unroll
+            for (int n = 0; n < NTN; ++n)
+                if (16 * n + c == bi) taken[n] = true;
+            wsum += bp;
+            if (c == j) {
+                my_sel = bi;
+                my_p = bp;
+            }
+        }
+        if (tok_ok && c < k) {
+            p.topk_idx[t * k + c] = my_sel;
+            p.topk_w[t * k + c] = my_p / wsum;
         }
     }
-    __syncthreads();
+}
 
-    for (; tile < ntiles; tile += gridDim.x) {
-        f32x4_t acc[NTN];
+// buffer_load_dwordx4 ... lds: each lane's 16 bytes go to LDS at M0 + 16 * lane
+// (asm, so the compiler neither tracks nor waits for it: the kernel waits
+// with an explicit vmcnt(0) and a barrier before any wave reads the stage).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; nothing else here uses it
+__device__ __forceinline__ void w_dma16(i32x4_t rsrc, uint32_t lds_addr, int voffset) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+    rsrc.x = __builtin_amdgcn_readfirstlane(rsrc.x);
+    rsrc.y = __builtin_amdgcn_readfirstlane(rsrc.y);
+    rsrc.z = __builtin_amdgcn_readfirstlane(rsrc.z);
+    rsrc.w = __builtin_amdgcn_readfirstlane(rsrc.w);
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(m0), "v"(voffset), "s"(rsrc)
+        : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// W_r rows r0 .. r0 + rows into the LDS stage [rows][EP] bf16 (experts E ..
+// EP-1 zero).  E a multiple of 8: direct-to-LDS loads of 16-byte pieces, a
+// piece past the expert columns given an offset past the descriptor's range
+// (it reads as zero); otherwise element by element through registers.
+template <int NTN>
+__device__ void stage_w(const RouteParams& p, unsigned char* smem, int r0, int rows) {
+    constexpr int EP = 16 * NTN;
+    const int tid = threadIdx.x, nthr = blockDim.x, E = p.E;
+    const uint16_t* wr = static_cast<const uint16_t*>(p.w_r);
+    if (E % 8 == 0) {
+        const uint64_t a = reinterpret_cast<uint64_t>(wr);
+        i32x4_t rs;
+        rs.x = (int)(uint32_t)a;
+        rs.y = (int)(uint32_t)(a >> 32) & 0xFFFF;
+        rs.z = (int)(uint32_t)((size_t)p.H * E * 2);   // H * E * 2 < 2^27 (checked on the host)
+        rs.w = 0x00020000;
+        const uint32_t base = (uint32_t)(uintptr_t)(const lds_void_t*)smem;
+        const int nbytes = rows * EP * 2;               // a multiple of 1 KB
+        for (int o = (tid / kWave) * 1024; o < nbytes; o += (nthr / kWave) * 1024) {
+            const int lo = o + (tid % kWave) * 16;        // this lane's LDS byte
+            const int row = lo / (EP * 2), c16 = (lo % (EP * 2)) / 16;
+            const int voff = c16 * 8 < E ? ((r0 + row) * E + c16 * 8) * 2 : 0x7FFFFFF0;
+            w_dma16(rs, base + o, voff);
+        }
+    } else {
+        uint16_t* w16 = reinterpret_cast<uint16_t*>(smem);
+        for (int q = tid; q < rows * EP; q += nthr) {
+            const int h = q / EP, e = q % EP;
+            w16[q] = e < E ? wr[(size_t)(r0 + h) * E + e] : (uint16_t)0;
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Each wave owns whole 16-token tiles (tile t of a wave in round r is
+// (block * waves + wave) + r * grid * waves); every wave of a block runs the
+// same number of rounds.  W_r sits in LDS in stages of `hs` rows: when one
+// stage holds all of W_r it is loaded once and the waves never meet again;
+// otherwise the waves restage at each stage boundary of every tile.
+// The chunk stream runs in groups of three (three register buffers, the
+// loads of the chunk three ahead issued as each one is used) with uniform
+// control flow: every step issues its load (past the end, of the last
+// chunk again, which the caches hold), and the stream is padded to a
+// multiple of three with steps whose results are not used, so the
+// compiler's waits count all three buffers in flight.
+template <int NTN>
+__global__ __launch_bounds__(kRMaxThreads, 1) void route_bf16_kernel(RouteParams p, int ntiles,
+                                                                    int hs) {
+    extern __shared__ __align__(16) unsigned char smem[];   // W_r stage [hs][16 NTN] bf16
+    constexpr int EP = 16 * NTN;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int nw = blockDim.x / kWave;
+    const int H = p.H;
+    const int nch = H / kKC;                    // chunks per tile
+    const int chs = hs / kKC;                   // chunks per W_r stage
+    const bool restage = chs < nch;
+    const int per_round = gridDim.x * nw;
+    const int nrounds = (ntiles + per_round - 1) / per_round;
+    const int nsteps = nrounds * nch;           // < 2^31 (checked on the host)
+    const int npad = (nsteps + 2) / 3 * 3;
+    const uint16_t* xb = static_cast<const uint16_t*>(p.x);
+    const int tile0 = blockIdx.x * nw + wave;
+    if (nsteps == 0) return;
+
+    // A operand of k-step s of chunk ch of round r's tile:
+    // x[row][ch*256 + s*32 + (lane/16)*8 .. +8]
+    auto load_x = [&](uint4 (&a)[kKS], int gstep) {
+        if (gstep > nsteps - 1) gstep = nsteps - 1;
+        const int r = gstep / nch, ch = gstep - r * nch;
+        int64_t row = (int64_t)(tile0 + r * per_round) * kTok + (lane % 16);
+        if (row >= p.T) row = p.T - 1;  // clamp: rows past T are never written out
+        const uint4* src = reinterpret_cast<const uint4*>(xb + row * H + ch * kKC + (lane / 16) * 8);
+#pragma unroll
+        for (int s2 = 0; s2 < kKS; ++s2) a[s2] = src[s2 * 4];
+    };
+
+    float bias[NTN];
+#pragma unroll
+    for (int n = 0; n < NTN; ++n) {
+        const int e = 16 * n + lane % 16;
+        bias[n] = (p.b_r && e < p.E) ? p.b_r[e] : 0.f;
+    }
+    uint4 a0[kKS], a1[kKS], a2[kKS];
+    load_x(a0, 0);
+    load_x(a1, 1);
+    load_x(a2, 2);
+    stage_w<NTN>(p, smem, 0, restage ? hs : H);
+    __syncthreads();
+    // blocked sums: each chunk's 256 products are summed in a fresh
+    // accumulator and added to the running total, which keeps fp32 rounding
+    // of long hidden sizes near that of a 256-term sum
+    f32x4_t acc[NTN], tot[NTN];
+    float gn[NTN][4];
+#pragma unroll
+    for (int n = 0; n < NTN; ++n) tot[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    tile_noise<NTN>(gn, (int64_t)tile0 * kTok, p, lane);
+
+    int ch = 0, rnd = 0;   // chunk and round of the current step (wave-uniform)
+    // (the marker makes the three inlined steps different code, so the
+    // compiler keeps three register buffers instead of merging the steps
+    // into one body that copies buffers, which would wait for their loads)
+    auto step = [&](auto buf, uint4 (&a)[kKS], int gstep) {
+        asm volatile("; x buffer %0" ::"n"(decltype(buf)::value));
+        if (restage && ch % chs == 0 && gstep > 0 && gstep < nsteps) {  // uniform
+            __syncthreads();
+            const int r0 = ch * kKC;
+            stage_w<NTN>(p, smem, r0, min(hs, H - r0));
+            __syncthreads();
+        }
+        const unsigned char* wb = smem + (size_t)(ch % chs) * kKC * EP * 2;
 #pragma unroll
         for (int n = 0; n < NTN; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < kMaxKsPerWave; ++i) {
-            if (i < ks_per_wave) {
-                const bf16x8_t a = as_bf16x8(a_cur[i]);
+        for (int s2 = 0; s2 < kKS; ++s2) {
+            const bf16x8_t av = as_bf16x8(a[s2]);
 #pragma unroll
-                for (int n = 0; n < NTN; ++n) {
-                    // transpose reads: lane L of each 16-lane group points at
-                    // row k0 + L/4, experts 4*(L%4).., and receives expert L of
-                    // rows k0..k0+3 (two reads give the 8 k of the B operand)
-                    const unsigned char* wb = reinterpret_cast<const unsigned char*>(wlds);
-                    i16x4_t v[2];
+            for (int n = 0; n < NTN; ++n) {
+                // transpose reads: lane L of each 16-lane group points at
+                // row k0 + L/4, experts 4*(L%4).., and receives expert L of
+                // rows k0..k0+3 (two reads give the 8 k of the B operand)
+                i16x4_t v[2];
 #pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const int kr = (ks0 + i) * 32 + (lane / 16) * 8 + hh * 4 + (lane % 16) / 4;
-                        v[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(
-                            wb + (kr * EP + n * 16 + 4 * (lane % 4)) * 2));
-                    }
-                    const uint2 lo = __builtin_bit_cast(uint2, v[0]);
-                    const uint2 hi = __builtin_bit_cast(uint2, v[1]);
-                    const bf16x8_t b = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-                    acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[n], 0, 0, 0);
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int kr = s2 * 32 + (lane / 16) * 8 + hh * 4 + (lane % 16) / 4;
+                    v[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4_t*)(wb + (kr * EP + n * 16 + 4 * (lane % 4)) * 2));
                 }
+                const uint2 lo = __builtin_bit_cast(uint2, v[0]);
+                const uint2 hi = __builtin_bit_cast(uint2, v[1]);
+                const bf16x8_t bv = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+                acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[n], 0, 0, 0);
             }
         }
-        const int next = tile + gridDim.x;
-        if (next < ntiles) load_tile(a_nxt, next);
 #pragma unroll
-        for (int n = 0; n < NTN; ++n) red[(wave * NTN + n) * kWave + lane] = acc[n];
-        __syncthreads();
-        // fixed-order sum of the 8 partial tiles -> lg[token][expert]
-        for (int q = tid; q < kTok * ld; q += kRThreads) {
-            const int tt = q / ld, e = q % ld;
-            const int n = e / 16;
-            const int l = (tt / 4) * 16 + (e % 16);
-            const int r = tt % 4;
-            float s = 0.f;
+        for (int n = 0; n < NTN; ++n) tot[n] += acc[n];
+        load_x(a, gstep + 3);
+        if (ch == nch - 1 && gstep < nsteps) {
+            const int tile = tile0 + rnd * per_round;
+            if (tile < ntiles) route_tile_epilogue<NTN>(tot, gn, bias, (int64_t)tile * kTok, p, lane);
 #pragma unroll
-            for (int w = 0; w < kRWaves; ++w) s += red[(w * NTN + n) * kWave + l][r];
-            lg[tt * ld + e] = s;
+            for (int n = 0; n < NTN; ++n) tot[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            // the next tile's noise, while its first chunks' loads are in flight
+            tile_noise<NTN>(gn, (int64_t)(tile + per_round) * kTok, p, lane);
         }
-        __syncthreads();
-        route_epilogue(lg, ld, (int64_t)tile * kTok, p, gw);
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < kMaxKsPerWave; ++i) a_cur[i] = a_nxt[i];
+        if (++ch == nch) {
+            ch = 0;
+            ++rnd;
+        }
+    };
+    for (int gs = 0; gs < npad; gs += 3) {
+        step(std::integral_constant<int, 0>{}, a0, gs);
+        step(std::integral_constant<int, 1>{}, a1, gs + 1);
+        step(std::integral_constant<int, 2>{}, a2, gs + 2);
     }
 }
 
@@ -304,19 +493,25 @@ int num_cus() {
 
 template <int NTN>
 moe_status_t launch_bf16(const RouteParams& p, hipStream_t st) {
-    const int nks = p.H / 32;
-    const size_t lds = (size_t)nks * NTN * 1024 + (size_t)kRWaves * NTN * kWave * 16 +
-                       (size_t)kTok * 16 * NTN * 4;
-    if (lds > 160 * 1024) return MOE_ERR_UNSUPPORTED;
+    constexpr int EP = 16 * NTN;
+    // W_r rows per LDS stage: all of them when they fit, else a multiple of 256
+    int hs = p.H;
+    if ((size_t)hs * EP * 2 > (size_t)kWStageMax) hs = kWStageMax / (EP * 2) / kKC * kKC;
+    const size_t lds = (size_t)hs * EP * 2;
     if (hipFuncSetAttribute((const void*)route_bf16_kernel<NTN>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
         return MOE_ERR_LAUNCH;
     const int ntiles = (int)((p.T + kTok - 1) / kTok);
-    const int per_cu = lds <= 72 * 1024 ? 2 : 1;
-    int grid = num_cus() * per_cu;
-    if (grid > ntiles) grid = ntiles;
-    hipLaunchKernelGGL(route_bf16_kernel<NTN>, dim3(grid), dim3(kRThreads), lds, st, p, ntiles,
-                       group_width(p.E));
+    // one workgroup per compute unit, with as many waves (one tile each) as
+    // the tiles fill: small token counts spread over every compute unit
+    const int cus = num_cus();
+    int waves = (ntiles + cus - 1) / cus;
+    if (waves > kRMaxWaves) waves = kRMaxWaves;
+    if (waves < 1) waves = 1;
+    int grid = (ntiles + waves - 1) / waves;
+    if (grid > cus) grid = cus;
+    hipLaunchKernelGGL(route_bf16_kernel<NTN>, dim3(grid), dim3(waves * kWave), lds, st, p, ntiles,
+                       hs);
     MOE_CHECK_LAUNCH();
     return MOE_OK;
 }
@@ -362,8 +557,9 @@ extern "C" moe_status_t moe_route(void* stream, moe_dtype_t dtype, const void* x
         MOE_CHECK_LAUNCH();
         return MOE_OK;
     }
-    if (H % 256) return MOE_ERR_ALIGN;
-    if (H / 32 / kRWaves > kMaxKsPerWave) return MOE_ERR_UNSUPPORTED;
+    if (H % kKC) return MOE_ERR_ALIGN;
+    if (H * E * 2 >= ((int64_t)1 << 27)) return MOE_ERR_UNSUPPORTED;  // 32-bit LDS-load offsets
+    if (((T + kTok - 1) / kTok + 1) * (H / kKC) >= ((int64_t)1 << 30)) return MOE_ERR_UNSUPPORTED;
     if (!moe_aligned16(x) || !moe_aligned16(w_r)) return MOE_ERR_ALIGN;
     const int ntn = (E + 15) / 16;
     switch (ntn) {

@@ -91,7 +91,7 @@ def test_route_argument_errors(L):
     assert route(L, H=200) == ALIGN
     assert route(L, x=MIS) == ALIGN
     assert route(L, dtype=0, H=6) == ALIGN
-    assert route(L, H=256 * 32) == UNSUP           # more than 16 k-steps per wave
+    assert route(L, H=(1 << 20) + 256) == UNSUP     # hidden sizes up to 2^20 (any multiple of 256)
     assert route(L, T=0, x=None, w=None, outs=(None, None, None)) == OK
 
 

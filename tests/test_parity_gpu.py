@@ -155,6 +155,47 @@ def test_layer_end_to_end_small(name, fused):
         assert np.all(to_np(y)[all_drop] == 0.0)
 
 
+# ------------------------------------------------------------- router ----
+ROUTE_ONLY = {
+    # hidden sizes past the old 4096 limit, an odd number of 256-wide chunks,
+    # expert counts that are not a multiple of 8 (scalar W_r loads) and the
+    # largest (64, four 16-expert column blocks); token counts that end in a
+    # partial tile and in a partial set of tiles
+    "h8192-gumbel-e32": MoEConfig("r8k", "bf16", T=1000, H=8192, I=128, E=32, k=2, cf=1.25,
+                                  route="gumbel", seq=1000, seed=61),
+    "h4352-e5-k3-bias": MoEConfig("r4k", "bf16", T=777, H=4352, I=128, E=5, k=3, cf=1.0,
+                                  router_bias0=1.0, seed=62),
+    "h1280-e64-k8": MoEConfig("r64", "bf16", T=333, H=1280, I=128, E=64, k=8, cf=1.0, seed=63),
+    "h256-e1": MoEConfig("r1", "bf16", T=17, H=256, I=128, E=1, k=1, cf=1.0, seed=64),
+    "h768-e12-k2": MoEConfig("r12", "bf16", T=4099, H=768, I=128, E=12, k=2, cf=1.0, seed=65),
+}
+
+
+@pytest.mark.parametrize("name", list(ROUTE_ONLY))
+def test_route_shapes(name):
+    """The router alone against the oracle's on shapes the layer tests do not
+    reach: probabilities and weights to 1e-5, top-k sets bit-exact outside
+    near ties, keys (logits or Gumbel keys) to 1e-5 of their largest size."""
+    cfg = ROUTE_ONLY[name]
+    log(f"[route] {name}: T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} {cfg.route}")
+    rng = np.random.default_rng(cfg.seed)
+    x = f32_to_bf16_bits(rng.standard_normal((cfg.T, cfg.H), dtype=np.float32))
+    w_r = f32_to_bf16_bits(rng.standard_normal((cfg.H, cfg.E), dtype=np.float32) * np.float32(0.02))
+    b_r = None
+    if cfg.router_bias0:
+        b_r = np.zeros(cfg.E, dtype=np.float32)
+        b_r[0] = cfg.router_bias0
+    inp = {"x": x, "w_r": w_r, "b_r": b_r}
+    r = M.route(inp, cfg)
+    xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(DEV)
+    wd = torch.from_numpy(w_r.view(np.int16)).view(torch.bfloat16).to(DEV)
+    bd = None if b_r is None else torch.from_numpy(b_r).to(DEV)
+    idx, w, probs, keys = ops.moe_route(xd, wd, bd, cfg.k, mode=cfg.route, seed=cfg.seed,
+                                        seq_len=cfg.seq_len, want_keys=True)
+    torch.cuda.synchronize()
+    _route_compare(cfg, to_np(idx), to_np(w), to_np(probs), to_np(keys), r, name)
+
+
 # ------------------------------------------------------------ stage-wise ----
 @pytest.mark.parametrize("name", list(SMALL))
 def test_stages_on_oracle_inputs(name):
