@@ -407,8 +407,8 @@ def run_workload(cid, args, with_cpu: bool):
     # memory-bound phases in isolation, after flushing the Infinity Cache by
     # reading 1 GiB (a read leaves clean lines behind: a write-based flush
     # would leave dirty lines whose write-back the timed phase would pay)
-    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
-    sink = torch.empty((), dtype=torch.int64, device=dev)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # fp32 sum: no conversion pass
+    sink = torch.empty((), dtype=torch.float32, device=dev)
 
     def cold(fn):
         ts = []
