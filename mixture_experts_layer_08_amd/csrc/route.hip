@@ -11,7 +11,11 @@
 // bf16 design (gfx950): the router is HBM-bound (x is read once; W_r is
 // small and stays in L2), but at E = 32 it is 32 FLOP per byte of x, above
 // what fp32 vector FMA sustains at HBM speed, so the product runs on the
-// matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  Each wave owns
+// matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  Two kernels
+// share the epilogue's rules: with fewer 16-token tiles than 8 per compute
+// unit, a k-split kernel puts 8 waves on each tile (each 1/8 of the hidden
+// dimension) so that every compute unit streams; with more, the streaming
+// kernel below gives each wave whole tiles.  In the streaming kernel each wave owns
 // whole 16-token tiles over the full hidden dimension, so no partial logits
 // cross waves and no barrier waits on a tile: the wave streams its 16 rows of
 // x straight from HBM into A-operand registers in chunks of 256 hidden
@@ -46,6 +50,10 @@ constexpr int kRMaxThreads = kRMaxWaves * kWave;
 constexpr int kKC = 256;          // hidden entries per chunk
 constexpr int kKS = kKC / 32;     // MFMA k-steps per chunk
 constexpr int kWStageMax = 128 * 1024;  // bytes of LDS for W_r
+// the k-split kernel (fewer tiles): 8 waves share each 16-token tile
+constexpr int kKWaves = 8;
+constexpr int kKThreads = kKWaves * kWave;
+constexpr int kMaxKsPerWave = 16;       // k-steps of 32 per wave: H <= 4096
 
 struct RouteParams {
     const void* x;
@@ -331,16 +339,16 @@ __device__ void stage_w(const RouteParams& p, unsigned char* smem, int r0, int r
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// Each wave owns whole 16-token tiles (tile t of a wave in round r is
-// (block * waves + wave) + r * grid * waves); every wave of a block runs the
-// same number of rounds.  W_r sits in LDS in stages of `hs` rows: when one
-// stage holds all of W_r it is loaded once and the waves never meet again;
-// otherwise the waves restage at each stage boundary of every tile.
-// The chunk stream runs in groups of three (three register buffers, the
-// loads of the chunk three ahead issued as each one is used) with uniform
-// control flow: every step issues its load (past the end, of the last
-// chunk again, which the caches hold), and the stream is padded to a
-// multiple of three with steps whose results are not used, so the
+// The streaming kernel, for many tiles: each wave owns whole 16-token tiles
+// (tile t of a wave in round r is (block * waves + wave) + r * grid * waves;
+// every wave of a block runs the same number of rounds).  W_r sits in LDS in
+// stages of `hs` rows: when one stage holds all of W_r it is loaded once and
+// the waves never meet again; otherwise the waves restage at each stage
+// boundary of every tile.  The chunk stream runs in groups of three (three
+// register buffers, the loads of the chunk three ahead issued as each one is
+// used) with uniform control flow: every step issues its load (past the end,
+// of the last chunk again, which the caches hold), and the stream is padded
+// to a multiple of three with steps whose results are not used, so the
 // compiler's waits count all three buffers in flight.
 template <int NTN>
 __global__ __launch_bounds__(kRMaxThreads, 1) void route_bf16_kernel(RouteParams p, int ntiles,
@@ -453,6 +461,122 @@ __global__ __launch_bounds__(kRMaxThreads, 1) void route_bf16_kernel(RouteParams
     }
 }
 
+// The k-split kernel, for token counts that leave compute units idle with
+// one wave per tile: a workgroup of 8 waves copies W_r into LDS once, in its
+// own [H, E] layout (16-byte loads), then walks 16-token tiles; each wave owns
+// 1/8 of the hidden dimension and streams its x slice straight from HBM into
+// A-operand registers (16 rows x 64 contiguous bytes per load), the next
+// tile's loads issued before the current tile's reduction and epilogue; the
+// 8 partial logit tiles are summed in LDS in a fixed order, then lane groups
+// of width G = 2^ceil(log2 E) hold one token each for the softmax and the k
+// rounds of arg-max.
+template <int NTN>
+__global__ __launch_bounds__(kKThreads) void route_ksplit_kernel(RouteParams p, int ntiles, int gw) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int H = p.H;
+    const int nks = H / 32;                    // k-steps of 32
+    const int ks_per_wave = nks / kKWaves;     // <= kMaxKsPerWave
+    uint4* wlds = reinterpret_cast<uint4*>(smem);                          // [H][16*NTN] bf16
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(smem + (size_t)nks * NTN * 1024);  // [8][NTN][64]
+    float* lg = reinterpret_cast<float*>(red + kKWaves * NTN * kWave);     // [16][16*NTN]
+    constexpr int ld = 16 * NTN;
+
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    const uint16_t* xb = static_cast<const uint16_t*>(p.x);
+    const uint16_t* wr = static_cast<const uint16_t*>(p.w_r);
+
+    const int ks0 = wave * ks_per_wave;
+    // A fragment of k-step ks for this lane: x[t0 + lane%16][ks*32 + (lane/16)*8 .. +8]
+    auto load_tile = [&](uint4 (&a)[kMaxKsPerWave], int tile) {
+        int64_t row = (int64_t)tile * kTok + (lane % 16);
+        if (row >= p.T) row = p.T - 1;  // clamp: rows past T are never written out
+        const uint4* src = reinterpret_cast<const uint4*>(xb + row * H + (lane / 16) * 8);
+#pragma unroll
+        for (int i = 0; i < kMaxKsPerWave; ++i)
+            if (i < ks_per_wave) a[i] = src[(size_t)(ks0 + i) * 4];
+    };
+
+    uint4 a_cur[kMaxKsPerWave], a_nxt[kMaxKsPerWave];
+    int tile = blockIdx.x;
+    if (tile < ntiles) load_tile(a_cur, tile);
+
+    // Stage W_r [H, E] in LDS as [H][16*NTN] (experts past E are zero),
+    // 16-byte vectors when E is a multiple of 8.
+    constexpr int EP = 16 * NTN;
+    if (p.E % 8 == 0) {
+        const int vpr = p.E / 8;  // vectors per W_r row
+        for (int v = tid; v < H * vpr; v += kKThreads) {
+            const int h = v / vpr, c = v % vpr;
+            wlds[h * EP / 8 + c] = reinterpret_cast<const uint4*>(wr)[(size_t)h * vpr + c];
+        }
+        const int padv = (EP - p.E) / 8;
+        for (int v = tid; v < H * padv; v += kKThreads) {
+            const int h = v / padv, c = v % padv;
+            wlds[h * EP / 8 + vpr + c] = make_uint4(0, 0, 0, 0);
+        }
+    } else {
+        uint16_t* w16 = reinterpret_cast<uint16_t*>(wlds);
+        for (int v = tid; v < H * EP; v += kKThreads) {
+            const int h = v / EP, e = v % EP;
+            w16[v] = e < p.E ? wr[(size_t)h * p.E + e] : (uint16_t)0;
+        }
+    }
+    __syncthreads();
+
+    for (; tile < ntiles; tile += gridDim.x) {
+        f32x4_t acc[NTN];
+#pragma unroll
+        for (int n = 0; n < NTN; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < kMaxKsPerWave; ++i) {
+            if (i < ks_per_wave) {
+                const bf16x8_t a = as_bf16x8(a_cur[i]);
+#pragma unroll
+                for (int n = 0; n < NTN; ++n) {
+                    // transpose reads: lane L of each 16-lane group points at
+                    // row k0 + L/4, experts 4*(L%4).., and receives expert L of
+                    // rows k0..k0+3 (two reads give the 8 k of the B operand)
+                    const unsigned char* wb = reinterpret_cast<const unsigned char*>(wlds);
+                    i16x4_t v[2];
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int kr = (ks0 + i) * 32 + (lane / 16) * 8 + hh * 4 + (lane % 16) / 4;
+                        v[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(
+                            wb + (kr * EP + n * 16 + 4 * (lane % 4)) * 2));
+                    }
+                    const uint2 lo = __builtin_bit_cast(uint2, v[0]);
+                    const uint2 hi = __builtin_bit_cast(uint2, v[1]);
+                    const bf16x8_t b = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+                    acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[n], 0, 0, 0);
+                }
+            }
+        }
+        const int next = tile + gridDim.x;
+        if (next < ntiles) load_tile(a_nxt, next);
+#pragma unroll
+        for (int n = 0; n < NTN; ++n) red[(wave * NTN + n) * kWave + lane] = acc[n];
+        __syncthreads();
+        // fixed-order sum of the 8 partial tiles -> lg[token][expert]
+        for (int q = tid; q < kTok * ld; q += kKThreads) {
+            const int tt = q / ld, e = q % ld;
+            const int n = e / 16;
+            const int l = (tt / 4) * 16 + (e % 16);
+            const int r = tt % 4;
+            float s = 0.f;
+#pragma unroll
+            for (int w = 0; w < kKWaves; ++w) s += red[(w * NTN + n) * kWave + l][r];
+            lg[tt * ld + e] = s;
+        }
+        __syncthreads();
+        route_epilogue(lg, ld, (int64_t)tile * kTok, p, gw);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kMaxKsPerWave; ++i) a_cur[i] = a_nxt[i];
+    }
+}
+
 // fp32 router: plain fp32 dot products (small workloads).
 __global__ __launch_bounds__(256) void route_f32_kernel(RouteParams p, int ntiles, int gw) {
     __shared__ float lg[kTok * MOE_MAX_EXPERTS];
@@ -492,24 +616,48 @@ int num_cus() {
 }
 
 template <int NTN>
+moe_status_t launch_ksplit(const RouteParams& p, hipStream_t st) {
+    const int nks = p.H / 32;
+    const size_t lds = (size_t)nks * NTN * 1024 + (size_t)kKWaves * NTN * kWave * 16 +
+                       (size_t)kTok * 16 * NTN * 4;
+    if (lds > 160 * 1024) return MOE_ERR_UNSUPPORTED;
+    if (hipFuncSetAttribute((const void*)route_ksplit_kernel<NTN>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return MOE_ERR_LAUNCH;
+    const int ntiles = (int)((p.T + kTok - 1) / kTok);
+    const int per_cu = lds <= 72 * 1024 ? 2 : 1;
+    int grid = num_cus() * per_cu;
+    if (grid > ntiles) grid = ntiles;
+    hipLaunchKernelGGL(route_ksplit_kernel<NTN>, dim3(grid), dim3(kKThreads), lds, st, p, ntiles,
+                       group_width(p.E));
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
+}
+
+template <int NTN>
 moe_status_t launch_bf16(const RouteParams& p, hipStream_t st) {
     constexpr int EP = 16 * NTN;
     // W_r rows per LDS stage: all of them when they fit, else a multiple of 256
     int hs = p.H;
     if ((size_t)hs * EP * 2 > (size_t)kWStageMax) hs = kWStageMax / (EP * 2) / kKC * kKC;
-    const size_t lds = (size_t)hs * EP * 2;
-    if (hipFuncSetAttribute((const void*)route_bf16_kernel<NTN>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-        return MOE_ERR_LAUNCH;
     const int ntiles = (int)((p.T + kTok - 1) / kTok);
-    // one workgroup per compute unit, with as many waves (one tile each) as
-    // the tiles fill: small token counts spread over every compute unit
     const int cus = num_cus();
+    // fewer tiles than 8 per compute unit: the k-split kernel, which puts 8
+    // waves on each tile, when W_r fits its LDS image (H <= 4096)
+    if ((int64_t)ntiles < (int64_t)cus * kRMaxWaves && p.H / 32 / kKWaves <= kMaxKsPerWave) {
+        const moe_status_t s = launch_ksplit<NTN>(p, st);
+        if (s != MOE_ERR_UNSUPPORTED) return s;
+    }
+    // one workgroup per compute unit, up to 8 waves of one tile each
     int waves = (ntiles + cus - 1) / cus;
     if (waves > kRMaxWaves) waves = kRMaxWaves;
     if (waves < 1) waves = 1;
     int grid = (ntiles + waves - 1) / waves;
     if (grid > cus) grid = cus;
+    const size_t lds = (size_t)hs * EP * 2;
+    if (hipFuncSetAttribute((const void*)route_bf16_kernel<NTN>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return MOE_ERR_LAUNCH;
     hipLaunchKernelGGL(route_bf16_kernel<NTN>, dim3(grid), dim3(waves * kWave), lds, st, p, ntiles,
                        hs);
     MOE_CHECK_LAUNCH();
