@@ -120,9 +120,14 @@ def algorithmic_work(cfg, kept: np.ndarray, dropped: int, weights: str = "bf16")
 
 TRAFFIC_PROFILES = {
     "layer-bf16": os.path.join(ROOT, "profiles", "grouped_gemm_layer_bf16_4096tok_traffic.md"),
+    "skewed-bf16": os.path.join(ROOT, "profiles", "grouped_gemm_skewed_bf16_16384tok_traffic.md"),
+    "wide-gelu-bf16": os.path.join(ROOT, "profiles", "grouped_gemm_wide_gelu_bf16_8192tok_traffic.md"),
+    "long-gumbel-bf16": os.path.join(ROOT, "profiles",
+                                     "grouped_gemm_long_gumbel_bf16_32768tok_traffic.md"),
     "decode-bf16": os.path.join(ROOT, "profiles", "grouped_gemm_decode_bf16_64tok_traffic.md"),
 }
-GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_08_amd", "csrc", "expert_ffn.hip")
+GEMM_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_08_amd", "csrc", f)
+                for f in ("expert_ffn.hip", "gemm_common.h")]
 
 
 def measured_traffic(cfg):
@@ -144,11 +149,11 @@ def measured_traffic(cfg):
 
 
 def gemm_source_digest() -> str:
-    """sha256 of the GEMM source with comments and blank space removed, so
+    """sha256 of the GEMM sources with comments and blank space removed, so
     that only a change to the code itself invalidates recorded counters."""
     import hashlib
     import re
-    text = open(GEMM_SOURCE).read()
+    text = "\n".join(open(p).read() for p in GEMM_SOURCES)
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     text = " ".join(text.split())

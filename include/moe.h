@@ -86,9 +86,13 @@ int64_t moe_capacity(int64_t T, int k, int E, double cf);
 /* Static, NUL-terminated text for a status code (never NULL). */
 const char* moe_status_string(int status);
 
-/* Bytes of workspace moe_aux_stats and moe_dispatch need for T tokens,
- * E experts and top-k (the larger of the two).  0 if arguments are out of
- * range. */
+/* Bytes of workspace moe_aux_stats, moe_dispatch and moe_dispatch_aux need
+ * for T tokens, E experts and top-k: a 256-byte header of two arrival
+ * counters, then 16 bytes per (block, expert) for at most 64 blocks of
+ * 512 assignments or more (at most 65792 bytes).  0 if arguments are out
+ * of range.  The workspace must be zero-filled before its first use; every
+ * call of those three leaves its counters and flag words zero again, whatever
+ * the shape, so one workspace is cleared once and may be shared by them. */
 size_t moe_workspace_bytes(int64_t T, int E, int k);
 
 /* Router.  [P2] section 2.1 (score = x . W_r, softmax, keep the top-k);
@@ -125,7 +129,10 @@ moe_status_t moe_route(void* stream, moe_dtype_t dtype, const void* x,
  *   f        [E] fp32  out   counts / (T * k)
  *   p        [E] fp32  out   mean over tokens of probs[:, e]
  *   l_aux    [1] fp32  out   alpha * E * sum_e f[e] * p[e]
- *   ws       workspace of at least moe_workspace_bytes(T, E, k) bytes
+ *   ws       workspace of at least moe_workspace_bytes(T, E, k) bytes,
+ *            zero-filled before its first use, 16-byte aligned (may be
+ *            NULL when T = 0; unused when T * E <= 65536, where one
+ *            workgroup does the whole reduction)
  * Reductions run in a fixed order (fp64 partial sums): deterministic.
  * With T = 0 every output is zero. */
 moe_status_t moe_aux_stats(void* stream, const int32_t* topk_idx,
@@ -151,7 +158,13 @@ moe_status_t moe_aux_stats(void* stream, const int32_t* topk_idx,
  *   slot_token [E, C]    int32  out    token in that row, or -1
  *   kept       [E]       int32  out    min(assignments to e, C)
  *   dropped    [1]       int32  out    number of dropped assignments
- *   ws         workspace of at least moe_workspace_bytes(T, E, k) bytes
+ *   ws         workspace of at least moe_workspace_bytes(T, E, k) bytes,
+ *              zero-filled before its first use, 16-byte aligned (may be
+ *              NULL when T = 0)
+ * One launch computes the maps (plus one for the row copy): blocks of 512 or
+ * more assignments publish their per-expert counts in ws and each adds up
+ * those of the blocks before it; the last block to finish writes kept and
+ * dropped and clears what it used.
  * Expert ids outside [0, E) are a caller error (not checked on device). */
 moe_status_t moe_dispatch(void* stream, moe_dtype_t dtype, const void* x,
                           const int32_t* topk_idx, int64_t T, int64_t H, int E,
@@ -161,12 +174,12 @@ moe_status_t moe_dispatch(void* stream, moe_dtype_t dtype, const void* x,
 
 /* Dispatch and aux statistics in one pass: the outputs of moe_dispatch and of
  * moe_aux_stats (same arguments, same meanings: probs [T, E] fp32 and alpha
- * as for moe_aux_stats; counts, f, p, l_aux out) from the same launches —
- * the histogram blocks also sum their tokens' probabilities and the scan
- * block finishes the statistics, both in a fixed order (fp64 partial sums).
+ * as for moe_aux_stats; counts, f, p, l_aux out) from the same launch —
+ * each block also sums its tokens' probabilities and the last block to
+ * finish adds those sums in block order (fp64) and finishes the statistics.
  * [P2] sections 2.3 and 2.4, [P1] sections 2.4 and 3.2.
  *   ws  workspace of at least moe_workspace_bytes(T, E, k) bytes, 16-byte
- *       aligned
+ *       aligned, zero-filled before its first use
  * In addition T * E must be below 2^31. */
 moe_status_t moe_dispatch_aux(void* stream, moe_dtype_t dtype, const void* x,
                               const int32_t* topk_idx, const float* probs,
@@ -182,15 +195,15 @@ moe_status_t moe_dispatch_aux(void* stream, moe_dtype_t dtype, const void* x,
  * moe_dispatch_aux (the same kernels run); its workspace is instead a static
  * device array of MOE_NOALLOC_SCRATCH_BYTES bytes inside the library, one
  * per GPU, held until the process ends.  It calls no allocating routine.
- *   - MOE_ERR_UNSUPPORTED when moe_workspace_bytes(T, E, k) exceeds
- *     MOE_NOALLOC_SCRATCH_BYTES (e.g. above T * k = 2^19 at E = 64 or
- *     2^22 at E = 8).
+ *   - The largest workspace any accepted shape needs is 256 + 64 * 64 * 16
+ *     = 65792 bytes (E = 64), so every call the other checks accept fits;
+ *     MOE_ERR_UNSUPPORTED would report one that did not.
  *   - Every call on one GPU shares that GPU's array: two calls that may
  *     run at the same time on one GPU (different streams, no ordering
  *     between them) race and give wrong results.  Calls ordered on one
- *     stream are safe; nothing in the array needs clearing between them.
+ *     stream are safe: each leaves the array's counters and flags zero.
  *   - MOE_ERR_LAUNCH when the array's device address cannot be looked up. */
-#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)2 << 20)
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 10)
 moe_status_t moe_dispatch_aux_noalloc(void* stream, moe_dtype_t dtype, const void* x,
                                       const int32_t* topk_idx, const float* probs,
                                       int64_t T, int64_t H, int E, int k, int64_t C,

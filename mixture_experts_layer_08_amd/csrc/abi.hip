@@ -3,9 +3,7 @@
 
 #include "moe_common.h"
 
-size_t moe_aux_ws_bytes(int64_t T, int E);
 size_t moe_dispatch_ws_bytes(int64_t T, int E, int k);
-size_t moe_dispatch_aux_ws_bytes(int64_t T, int E, int k);
 
 // C = ceil(T * k * cf / E) in double, in that order.  [P2] MoE basics page
 // (dpshk.com/news/6005940) section 2.4 gives ceil(tokens / experts * cf);
@@ -33,9 +31,5 @@ extern "C" const char* moe_status_string(int status) {
 
 extern "C" size_t moe_workspace_bytes(int64_t T, int E, int k) {
     if (T < 0 || E < 1 || k < 1 || E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK) return 0;
-    const size_t a = moe_aux_ws_bytes(T, E);
-    const size_t d = moe_dispatch_ws_bytes(T, E, k);
-    const size_t da = moe_dispatch_aux_ws_bytes(T, E, k);
-    const size_t m = a > d ? a : d;
-    return m > da ? m : da;
+    return moe_dispatch_ws_bytes(T, E, k);
 }

@@ -132,7 +132,8 @@ class MoELayerGPU:
         E, k, H, I = cfg.E, cfg.k, cfg.H, cfg.I
         i32, f32, td = torch.int32, torch.float32, self.tdtype
         e = lambda *s, dt=f32: torch.empty(s, dtype=dt, device=dev)  # noqa: E731
-        # the expert products' workspaces hold tile counters that start at zero
+        # the dispatch workspace and the expert products' workspaces hold
+        # counters and flags that start at zero (every call leaves them zero)
         z = lambda n: torch.zeros(n, dtype=torch.uint8, device=dev)  # noqa: E731
         sh = {}
         if self.shared:
@@ -147,7 +148,7 @@ class MoELayerGPU:
             slot_token=e(E, C, dt=i32),
             kept=e(E, dt=i32), dropped=e(1, dt=i32), h=e(E, C, I, dt=td),
             y_disp=e(E, C, H), y=e(T, H, dt=td),
-            ws=e(max(1, ops.moe_workspace_bytes(T, E, k)), dt=torch.uint8),
+            ws=z(max(16, ops.moe_workspace_bytes(T, E, k))),
             ffn_ws=z(ops.moe_expert_ffn_ws_bytes()))
 
     # the five steps, each one library call ---------------------------------

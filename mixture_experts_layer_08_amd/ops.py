@@ -90,7 +90,7 @@ def moe_aux_stats(topk_idx: torch.Tensor, probs: torch.Tensor, E: int, alpha: fl
     p = _want(p, (E,), torch.float32, dev)
     l_aux = _want(l_aux, (1,), torch.float32, dev)
     if ws is None:
-        ws = torch.empty(max(1, moe_workspace_bytes(T, E, k)), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(max(16, moe_workspace_bytes(T, E, k)), dtype=torch.uint8, device=dev)
     st = lib().moe_aux_stats(_stream(dev), _ptr(topk_idx), _ptr(probs), T, E, k, float(alpha),
                              _ptr(counts), _ptr(f), _ptr(p), _ptr(l_aux), _ptr(ws), ws.numel())
     check("moe_aux_stats", st)
@@ -111,7 +111,7 @@ def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, C: int, *,
     kept = _want(kept, (E,), torch.int32, dev)
     dropped = _want(dropped, (1,), torch.int32, dev)
     if ws is None:
-        ws = torch.empty(max(1, moe_workspace_bytes(T, E, k)), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(max(16, moe_workspace_bytes(T, E, k)), dtype=torch.uint8, device=dev)
     st = lib().moe_dispatch(_stream(dev), _dtype_code(x), _ptr(x), _ptr(topk_idx), T, H, E, k, C,
                             _ptr(x_disp), _ptr(slot), _ptr(slot_token), _ptr(kept),
                             _ptr(dropped), _ptr(ws), ws.numel())
@@ -138,7 +138,7 @@ def moe_dispatch_aux(x: torch.Tensor, topk_idx: torch.Tensor, probs: torch.Tenso
     p = _want(p, (E,), torch.float32, dev)
     l_aux = _want(l_aux, (1,), torch.float32, dev)
     if ws is None:
-        ws = torch.empty(max(16, moe_workspace_bytes(T, E, k)), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(max(16, moe_workspace_bytes(T, E, k)), dtype=torch.uint8, device=dev)
     st = lib().moe_dispatch_aux(_stream(dev), _dtype_code(x), _ptr(x), _ptr(topk_idx), _ptr(probs),
                                 T, H, E, k, C, float(alpha), _ptr(x_disp), _ptr(slot),
                                 _ptr(slot_token), _ptr(kept), _ptr(dropped), _ptr(counts), _ptr(f),

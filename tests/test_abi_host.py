@@ -58,6 +58,19 @@ def test_status_strings(L):
     assert L.moe_status_string(0) == b"ok"
 
 
+def test_noalloc_scratch_covers_every_accepted_shape(L):
+    """The dispatch workspace is bounded (at most 64 blocks of 16-byte cells
+    per expert), so the no-allocation entry point's static array of
+    MOE_NOALLOC_SCRATCH_BYTES = 128 KiB holds it for every shape the other
+    checks accept."""
+    biggest = 256 + 64 * 64 * 16
+    for T, E, k in [((1 << 31) // 8 - 1, 64, 8), ((1 << 31) // 2 - 1, 64, 2), (1 << 20, 64, 2),
+                    (65536 * 2, 64, 1), (1, 1, 1)]:
+        need = L.moe_workspace_bytes(T, E, k)
+        assert 256 < need <= biggest <= (128 << 10), (T, E, k, need)
+    assert L.moe_workspace_bytes(1 << 20, 64, 2) == biggest
+
+
 def test_workspace_bytes(L):
     assert L.moe_workspace_bytes(32768, 32, 2) > 0
     assert L.moe_workspace_bytes(0, 8, 2) > 0

@@ -462,6 +462,80 @@ def test_dispatch_and_aux_both_sizes(T, E, k, cf):
     np.testing.assert_array_equal(to_np(xf).reshape(E * C, H)[rows], to_np(x)[st[rows]])
 
 
+def _skewed_routing(T, E, k, seed):
+    rng = np.random.default_rng(seed)
+    keys = rng.standard_normal((T, E)) + np.linspace(2.0, 0.0, E)   # some experts overflow
+    idx = np.argsort(-keys, axis=1, kind="stable")[:, :k].astype(np.int32)
+    probs = np.exp(keys - keys.max(axis=1, keepdims=True))
+    return idx, (probs / probs.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+# 8192 assignments: 16 blocks of one 512-assignment pass; 16386: 33 blocks;
+# 32770: 33 blocks of 512 x 2 (ranks in registers); 131072: 64 blocks of 4
+# passes; 131074: 52 blocks of 5; then 10 and 13 passes at 16 and 64 experts
+# (ranks recomputed after the block's first rows are known).  Up to 4096
+# assignments one workgroup does it all (the small and decode cases).
+@pytest.mark.parametrize("T,E,k,cf", [(4096, 8, 2, 1.25), (8192, 8, 2, 1.25),
+                                       (8193, 8, 2, 1.25), (16385, 8, 2, 1.25),
+                                       (65536, 8, 2, 1.25), (65537, 8, 2, 1.25),
+                                       (150000, 16, 2, 1.0), (100000, 64, 4, 1.0)])
+def test_dispatch_many_blocks_and_passes(T, E, k, cf):
+    """The dispatch on both sides of the one-workgroup limit and with several
+    512-assignment passes per block, in registers and recomputed: maps
+    bit-exact against the oracle's walk, statistics within 1e-5."""
+    log(f"[passes] T={T} E={E} k={k} cf={cf}")
+    idx, probs = _skewed_routing(T, E, k, T + E)
+    C = M.capacity(T, k, E, cf)
+    x = torch.zeros((T, 64), dtype=torch.bfloat16, device=DEV)
+    idx_d, probs_d = to_dev(idx, torch.int32), to_dev(probs, torch.float32)
+    _, slf, stf, kf, df, cnt, ff, pf, lf = ops.moe_dispatch_aux(x, idx_d, probs_d, E, C, 0.01,
+                                                                copy=False)
+    torch.cuda.synchronize()
+    d = M.dispatch(idx.astype(np.int64), E, C)
+    _dispatch_compare((to_np(slf), to_np(stf), to_np(kf), to_np(df)), d, f"passes T={T}")
+    a = M.aux_stats(idx.astype(np.int64), probs.astype(np.float64), E, 0.01)
+    np.testing.assert_array_equal(to_np(cnt), a.counts)
+    assert_rel(to_np(ff), a.f, 1e-5, "f")
+    assert_rel(to_np(pf), a.P, 1e-5, "p")
+    assert_rel(to_np(lf), [a.l_aux], 1e-5, "L_aux")
+    assert int(to_np(df)[0]) > 0, "the case should drop some assignments"
+
+
+def test_dispatch_workspace_shared_across_shapes():
+    """One zero-filled workspace, sized for the largest call, shared by
+    moe_aux_stats, moe_dispatch and moe_dispatch_aux at different shapes in
+    turn: every output bitwise equal to the same call on a fresh workspace,
+    and after every call the counters and count words (the header and
+    offsets 0 mod 16 past it) are zero again."""
+    shapes = [(40000, 16, 2), (3000, 8, 2), (20000, 64, 3), (9000, 16, 2), (40000, 16, 2)]
+    ws = torch.zeros(max(ops.moe_workspace_bytes(T, E, k) for T, E, k in shapes),
+                     dtype=torch.uint8, device=DEV)
+    for n, (T, E, k) in enumerate(shapes):
+        log(f"[shared ws] call {n}: T={T} E={E} k={k}")
+        idx, probs = _skewed_routing(T, E, k, 7 * n + 1)
+        idx_d, probs_d = to_dev(idx, torch.int32), to_dev(probs, torch.float32)
+        C = M.capacity(T, k, E, 1.0)
+        x = torch.zeros((T, 64), dtype=torch.bfloat16, device=DEV)
+        for kind in ("aux", "dispatch", "dispatch_aux"):
+            if kind == "aux":
+                got = ops.moe_aux_stats(idx_d, probs_d, E, 0.01, ws=ws)
+                want = ops.moe_aux_stats(idx_d, probs_d, E, 0.01)
+            elif kind == "dispatch":
+                got = ops.moe_dispatch(x, idx_d, E, C, ws=ws, copy=False)[1:]
+                want = ops.moe_dispatch(x, idx_d, E, C, copy=False)[1:]
+            else:
+                got = ops.moe_dispatch_aux(x, idx_d, probs_d, E, C, 0.01, ws=ws, copy=False)[1:]
+                want = ops.moe_dispatch_aux(x, idx_d, probs_d, E, C, 0.01, copy=False)[1:]
+            torch.cuda.synchronize()
+            for g, w in zip(got, want):
+                assert torch.equal(g, w), f"call {n} {kind}: outputs differ"
+            words = ws[:256].cpu().numpy()
+            assert not words.any(), f"call {n} {kind}: counters not cleared"
+            cells = ws[256:].cpu().numpy()
+            cells = cells[:cells.size // 16 * 16].reshape(-1, 16)[:, :8]
+            assert not cells.any(), f"call {n} {kind}: count words not cleared"
+
+
 @pytest.mark.parametrize("T", [1, 16, 64, 256])
 def test_decode_drop_free(T):
     """Drop-free decode steps (C = T): nothing dropped, every token's output
