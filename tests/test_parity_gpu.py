@@ -501,6 +501,30 @@ def test_dispatch_many_blocks_and_passes(T, E, k, cf):
     assert int(to_np(df)[0]) > 0, "the case should drop some assignments"
 
 
+# the multi-block dispatch (more than 4096 assignments) at its degenerate
+# cases: no capacity, one row per expert, one expert, every expert chosen
+@pytest.mark.parametrize("T,E,k,C", [(5000, 8, 2, 0), (5000, 8, 2, 1), (9000, 1, 1, 9000),
+                                     (700, 8, 8, 700), (3000, 64, 2, 37)])
+def test_dispatch_degenerate_many_blocks(T, E, k, C):
+    """Maps, kept, dropped and statistics bit-exact / within 1e-5 against the
+    oracle's walk in the one-launch dispatch's multi-block form."""
+    log(f"[degenerate] T={T} E={E} k={k} C={C}")
+    idx, probs = _skewed_routing(T, E, k, 3 * T + E)
+    x = torch.zeros((T, 64), dtype=torch.bfloat16, device=DEV)
+    idx_d, probs_d = to_dev(idx, torch.int32), to_dev(probs, torch.float32)
+    _, slf, stf, kf, df, cnt, ff, pf, lf = ops.moe_dispatch_aux(x, idx_d, probs_d, E, C, 0.01,
+                                                                copy=False)
+    _, sl2, st2, k2, d2 = ops.moe_dispatch(x, idx_d, E, C, copy=False)
+    torch.cuda.synchronize()
+    d = M.dispatch(idx.astype(np.int64), E, C)
+    _dispatch_compare((to_np(slf), to_np(stf), to_np(kf), to_np(df)), d, f"aux T={T} C={C}")
+    _dispatch_compare((to_np(sl2), to_np(st2), to_np(k2), to_np(d2)), d, f"maps T={T} C={C}")
+    a = M.aux_stats(idx.astype(np.int64), probs.astype(np.float64), E, 0.01)
+    np.testing.assert_array_equal(to_np(cnt), a.counts)
+    assert_rel(to_np(pf), a.P, 1e-5, "p")
+    assert_rel(to_np(lf), [a.l_aux], 1e-5, "L_aux")
+
+
 def test_dispatch_workspace_shared_across_shapes():
     """One zero-filled workspace, sized for the largest call, shared by
     moe_aux_stats, moe_dispatch and moe_dispatch_aux at different shapes in
