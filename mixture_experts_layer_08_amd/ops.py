@@ -83,6 +83,7 @@ def moe_route(x: torch.Tensor, w_r: torch.Tensor, b_r: Optional[torch.Tensor], k
 
 def moe_aux_stats(topk_idx: torch.Tensor, probs: torch.Tensor, E: int, alpha: float, *,
                   ws: Optional[torch.Tensor] = None, counts=None, f=None, p=None, l_aux=None):
+    """(counts, f, p, l_aux).  ws as for moe_dispatch (shared with it)."""
     T, k = topk_idx.shape
     dev = probs.device
     counts = _want(counts, (E,), torch.int32, dev)
@@ -101,7 +102,9 @@ def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, C: int, *,
                  ws: Optional[torch.Tensor] = None, x_disp=None, slot=None, slot_token=None,
                  kept=None, dropped=None, copy: bool = True):
     """copy=False: indices only (slot, slot_token, kept, dropped); x_disp is
-    then returned as None (for moe_expert_ffn_gather)."""
+    then returned as None (for moe_expert_ffn_gather).  A ws passed in must
+    have been zero-filled before its first use (each call leaves it zero);
+    without one a zero-filled workspace is allocated."""
     T, H = x.shape
     k = topk_idx.shape[1]
     dev = x.device
@@ -124,7 +127,7 @@ def moe_dispatch_aux(x: torch.Tensor, topk_idx: torch.Tensor, probs: torch.Tenso
                      slot_token=None, kept=None, dropped=None, counts=None, f=None, p=None,
                      l_aux=None, copy: bool = True):
     """moe_dispatch and moe_aux_stats in one pass: (x_disp, slot, slot_token,
-    kept, dropped, counts, f, p, l_aux)."""
+    kept, dropped, counts, f, p, l_aux).  ws as for moe_dispatch."""
     T, H = x.shape
     k = topk_idx.shape[1]
     dev = x.device
