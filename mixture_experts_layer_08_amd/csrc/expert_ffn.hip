@@ -773,7 +773,13 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
         }
         if (!nxt.valid) break;
         p0 += cur.nks;
-        cur = tile_at(round + 1);  // recomputed: only what the prefetch needs stays live
+        // the next tile was computed at the top of this round (the prefetch
+        // used it); the 8-bit gathered variant recomputes it, which keeps
+        // fewer registers live across its loop
+        if constexpr (GATHER && F8)
+            cur = tile_at(round + 1);
+        else
+            cur = nxt;
     }
     if (SAVE || !finish) return;  // (the training variants never split)
 
