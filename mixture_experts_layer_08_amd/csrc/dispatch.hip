@@ -92,8 +92,9 @@ __device__ __forceinline__ unsigned long long ld_word(const unsigned long long* 
 __device__ __forceinline__ void st_word(unsigned long long* q, unsigned long long v) {
     __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// A published count word (spins until its flag is set; gives up, as zero,
-// after kSpinLimit tries).
+// A published count word's count (spins until its flag is set; gives up
+// after kSpinLimit tries, which only a workspace that was not zero reaches,
+// and then returns whatever the word holds).
 __device__ __forceinline__ int published_count(const unsigned long long* q) {
     unsigned long long w = ld_word(q);
     for (int i = 0; !(w & kPublished) && i < kSpinLimit; ++i) {
