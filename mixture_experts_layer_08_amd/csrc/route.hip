@@ -485,7 +485,6 @@ __global__ __launch_bounds__(kKThreads) void route_ksplit_kernel(RouteParams p, 
     const int wave = tid / kWave;
     const int lane = tid % kWave;
     const uint16_t* xb = static_cast<const uint16_t*>(p.x);
-    const uint16_t* wr = static_cast<const uint16_t*>(p.w_r);
 
     const int ks0 = wave * ks_per_wave;
     // A fragment of k-step ks for this lane: x[t0 + lane%16][ks*32 + (lane/16)*8 .. +8]
@@ -502,27 +501,11 @@ __global__ __launch_bounds__(kKThreads) void route_ksplit_kernel(RouteParams p, 
     int tile = blockIdx.x;
     if (tile < ntiles) load_tile(a_cur, tile);
 
-    // Stage W_r [H, E] in LDS as [H][16*NTN] (experts past E are zero),
-    // 16-byte vectors when E is a multiple of 8.
+    // Stage W_r [H, E] in LDS as [H][16*NTN] (experts past E are zero); with
+    // E a multiple of 8 by direct-to-LDS loads, all in flight together with
+    // the x loads above.
     constexpr int EP = 16 * NTN;
-    if (p.E % 8 == 0) {
-        const int vpr = p.E / 8;  // vectors per W_r row
-        for (int v = tid; v < H * vpr; v += kKThreads) {
-            const int h = v / vpr, c = v % vpr;
-            wlds[h * EP / 8 + c] = reinterpret_cast<const uint4*>(wr)[(size_t)h * vpr + c];
-        }
-        const int padv = (EP - p.E) / 8;
-        for (int v = tid; v < H * padv; v += kKThreads) {
-            const int h = v / padv, c = v % padv;
-            wlds[h * EP / 8 + vpr + c] = make_uint4(0, 0, 0, 0);
-        }
-    } else {
-        uint16_t* w16 = reinterpret_cast<uint16_t*>(wlds);
-        for (int v = tid; v < H * EP; v += kKThreads) {
-            const int h = v / EP, e = v % EP;
-            w16[v] = e < p.E ? wr[(size_t)h * p.E + e] : (uint16_t)0;
-        }
-    }
+    stage_w<NTN>(p, smem, 0, H);
     __syncthreads();
 
     for (; tile < ntiles; tile += gridDim.x) {
