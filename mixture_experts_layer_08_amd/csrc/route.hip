@@ -11,24 +11,24 @@
 // bf16 design (gfx950): the router is HBM-bound (x is read once; W_r is
 // small and stays in L2), but at E = 32 it is 32 FLOP per byte of x, above
 // what fp32 vector FMA sustains at HBM speed, so the product runs on the
-// matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  Two kernels
-// share the epilogue's rules: with fewer 16-token tiles than 8 per compute
-// unit, a k-split kernel puts 8 waves on each tile (each 1/8 of the hidden
-// dimension) so that every compute unit streams; with more, the streaming
-// kernel below gives each wave whole tiles.  In the streaming kernel each wave owns
-// whole 16-token tiles over the full hidden dimension, so no partial logits
-// cross waves and no barrier waits on a tile: the wave streams its 16 rows of
-// x straight from HBM into A-operand registers in chunks of 256 hidden
-// entries, with the next chunk's loads in flight while the current one is
-// multiplied.  The workgroup's waves walk the chunks together and share the
-// matching 256 rows of W_r, staged in LDS (double-buffered, the next chunk's
-// rows loaded during the current chunk) in its own [H, E] layout and read as
-// MFMA B operands with gfx950's transposing LDS reads; any H that is a
-// multiple of 256 works, however many chunks it takes.  Softmax, Gumbel
-// noise and the k rounds of arg-max run on the accumulators in the MFMA's
-// own layout: lane l holds experts 16 n + l % 16 of tokens 4 (l / 16) ..
-// +3, so a token's experts sit in one 16-lane group and every reduction is
-// a 16-lane shuffle (ties go to the lower expert index).
+// matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  Three kernels
+// share the epilogue's rules:
+//   * fewer 16-token tiles than 8 per compute unit: a k-split kernel puts 8
+//     waves on each tile (each 1/8 of the hidden dimension) so that every
+//     compute unit streams;
+//   * more: each wave owns whole 16-token tiles over the full hidden
+//     dimension, so no partial logits cross waves.  The staged kernel (full
+//     workgroups, E a multiple of 8, at most 32 experts) passes x and W_r
+//     through LDS together in chunks, every load a direct-to-LDS load of
+//     whole row segments; the streaming kernel (every other shape) streams
+//     x straight into A-operand registers with W_r staged in LDS.
+// W_r sits in LDS in its own [H, E] layout and is read as MFMA B operands
+// with gfx950's transposing LDS reads; any H that is a multiple of 256
+// works.  Softmax, Gumbel noise and the k rounds of arg-max run on the
+// accumulators in the MFMA's own layout: lane l holds experts 16 n + l % 16
+// of tokens 4 (l / 16) .. +3, so a token's experts sit in one 16-lane row
+// and every reduction is a DPP exchange inside the row (ties go to the lower
+// expert index).
 #include "moe_common.h"
 
 #include <math.h>
@@ -197,6 +197,45 @@ __device__ __forceinline__ void tile_noise(float (&gn)[NTN][4], int64_t t0, cons
         }
 }
 
+// Exchanges inside 16-lane rows by DPP: lanes xor 1 and xor 2 (quad
+// permutes), lane i <-> 7 - i inside each half row (half mirror) and
+// i <-> 15 - i inside the row (mirror).  After the four, each in turn
+// combined with the lane's own partial result, every lane of a row holds the
+// row's max, sum or arg-max, computed without LDS traffic.  Every lane of
+// the wave must be active.
+template <int CTRL>
+__device__ __forceinline__ int dpp16(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp16f(float v) {
+    return __builtin_bit_cast(float, dpp16<CTRL>(__builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp16f<0xB1>(v));
+    v = fmaxf(v, dpp16f<0x4E>(v));
+    v = fmaxf(v, dpp16f<0x141>(v));
+    return fmaxf(v, dpp16f<0x140>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp16f<0xB1>(v);
+    v += dpp16f<0x4E>(v);
+    v += dpp16f<0x141>(v);
+    return v + dpp16f<0x140>(v);
+}
+// the best of (value desc, index asc) with its carried probability
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& bv, int& bi, float& bp) {
+    const float ov = dpp16f<CTRL>(bv);
+    const int oi = dpp16<CTRL>(bi);
+    const float op = dpp16f<CTRL>(bp);
+    if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+        bp = op;
+    }
+}
+
 template <int NTN>
 __device__ __forceinline__ void route_tile_epilogue(const f32x4_t (&acc)[NTN],
                                                     const float (&gn)[NTN][4],
@@ -225,17 +264,18 @@ __device__ __forceinline__ void route_tile_epilogue(const f32x4_t (&acc)[NTN],
             if (!ok[n]) key[n] = z[n] = -INFINITY;
             m = fmaxf(m, z[n]);
         }
-        m = group_max(m, 16);
+        m = row16_max(m);
         float sum = 0.f;
 #pragma unroll
         for (int n = 0; n < NTN; ++n) {
-            prob[n] = ok[n] ? expf(z[n] - m) : 0.f;
+            prob[n] = ok[n] ? __expf(z[n] - m) : 0.f;
             sum += prob[n];
         }
-        sum = group_sum(sum, 16);
+        sum = row16_sum(sum);
+        const float rs = __builtin_amdgcn_rcpf(sum);
 #pragma unroll
         for (int n = 0; n < NTN; ++n) {
-            prob[n] = ok[n] ? prob[n] / sum : 0.f;
+            prob[n] = ok[n] ? prob[n] * rs : 0.f;
             if (ok[n] && tok_ok) {
                 p.probs[t * E + 16 * n + c] = prob[n];
                 if (p.keys) p.keys[t * E + 16 * n + c] = key[n];
@@ -258,17 +298,10 @@ __device__ __forceinline__ void route_tile_epilogue(const f32x4_t (&acc)[NTN],
                     bp = prob[n];
                 }
             }
-#pragma unroll
-            for (int o = 8; o > 0; o >>= 1) {
-                const float ov = __shfl_xor(bv, o, 16);
-                const int oi = __shfl_xor(bi, o, 16);
-                const float op = __shfl_xor(bp, o, 16);
-                if (ov > bv || (ov == bv && oi < bi)) {
-                    bv = ov;
-                    bi = oi;
-                    bp = op;
-                }
-            }
+            argmax_step<0xB1>(bv, bi, bp);
+            argmax_step<0x4E>(bv, bi, bp);
+            argmax_step<0x141>(bv, bi, bp);
+            argmax_step<0x140>(bv, bi, bp);
 #pragma unroll
             for (int n = 0; n < NTN; ++n)
                 if (16 * n + c == bi) taken[n] = true;
@@ -461,6 +494,207 @@ __global__ __launch_bounds__(kRMaxThreads, 1) void route_bf16_kernel(RouteParams
     }
 }
 
+// buffer_load_dword ... lds: each lane's 4 bytes go to LDS at M0 + 4 * lane.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; nothing else here uses it
+__device__ __forceinline__ void w_dma4(i32x4_t rsrc, uint32_t lds_addr, int voffset) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+    rsrc.x = __builtin_amdgcn_readfirstlane(rsrc.x);
+    rsrc.y = __builtin_amdgcn_readfirstlane(rsrc.y);
+    rsrc.z = __builtin_amdgcn_readfirstlane(rsrc.z);
+    rsrc.w = __builtin_amdgcn_readfirstlane(rsrc.w);
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dword %1, %2, 0 offen lds"
+        :
+        : "s"(m0), "v"(voffset), "s"(rsrc)
+        : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ i32x4_t route_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4_t rs;
+    rs.x = (int)(uint32_t)a;
+    rs.y = (int)(uint32_t)(a >> 32) & 0xFFFF;
+    rs.z = (int)bytes;
+    rs.w = 0x00020000;
+    return rs;
+}
+
+// The staged kernel, for many tiles with full workgroups (8 waves, each
+// owning whole 16-token tiles as in the streaming kernel above): x and
+// W_r both pass through LDS in chunks of kSC hidden entries, so every global
+// load is a direct-to-LDS load of whole 256-byte row segments (16 rows x 256
+// bytes per wave and chunk, four loads) and W_r needs no up-front copy (a
+// chunk's kSC rows of it, 256 * EP bytes, come with the chunk).  kSStages
+// stages rotate through LDS: while chunk c is multiplied, the loads of chunks
+// c+1 .. c+kSStages-1 are in flight; one barrier per chunk (every wave's loads
+// of chunk c have landed, and nobody reads chunk c-1's stage any more, which
+// then takes chunk c+kSStages-1).  x rows sit in LDS 256 bytes apart with the
+// 16-byte piece q of row r at slot q ^ (r % 16), so the A-fragment reads
+// (16 rows, one piece each) hit distinct banks.  Products are summed per
+// 256 hidden entries in a fresh accumulator, then added to the running
+// total, as in the streaming kernel (the blocks in the workgroup's chunk
+// order, below).  A tile's Gumbel noise is computed one value per chunk
+// step, while the loads are in flight.  Measured at 32768 tokens, 32
+// experts, H = 2048: 37 us after an Infinity Cache flush, against 47 us for
+// the streaming kernel (whose per-wave register loads read 16 rows x 64
+// bytes each); the softmax / top-k epilogue of the single round of tiles is
+// about 5 us of it.
+constexpr int kSC = 128;      // hidden entries per chunk
+constexpr int kSStages = 4;
+constexpr int kSWaves = 8;
+template <int NTN>
+struct StagedGeom {
+    static constexpr int EP = 16 * NTN;
+    static constexpr int X_BYTES = kSWaves * kTok * kSC * 2;  // 32 KB
+    static constexpr int W_BYTES = kSC * EP * 2;              // 4 KB per 16 experts
+    static constexpr int STAGE = X_BYTES + W_BYTES;
+    static constexpr int W_LOADS = W_BYTES / 256 / kSWaves;   // dword loads per wave
+    static constexpr int LOADS = 4 + W_LOADS;                  // per wave and chunk
+    static constexpr size_t LDS = (size_t)kSStages * STAGE;
+};
+
+template <int NTN>
+__global__ __launch_bounds__(kSWaves * kWave, 1) void route_staged_kernel(RouteParams p, int ntiles) {
+    using SG = StagedGeom<NTN>;
+    constexpr int EP = SG::EP;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int H = p.H, E = p.E;
+    const int nch = H / kSC;
+    const int per_round = gridDim.x * kSWaves;
+    const int nrounds = (ntiles + per_round - 1) / per_round;
+    const int nsteps = nrounds * nch;
+    const int tile0 = blockIdx.x * kSWaves + wave;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_void_t*)smem;
+    const i32x4_t rsX = route_rsrc(p.x, (uint32_t)((size_t)p.T * H * 2));
+    const i32x4_t rsW = route_rsrc(p.w_r, (uint32_t)((size_t)H * E * 2));
+
+    // Workgroup b walks the chunks of its tiles starting at chunk rot and
+    // wrapping around: the workgroups of odd XCDs (b % 8) start half a row
+    // later, so that at any moment the XCDs read two different halves of
+    // their x rows instead of all the same 256 bytes of every row (measured
+    // at H = 2048: 47 -> 39 us cold for 32768 tokens; offsets of 1 KB by
+    // XCD about the same, offsets varying inside an XCD slower).  rot is
+    // even: the 256-entry blocks stay whole.
+    const int rot = (blockIdx.x & 1u) ? ((nch / 2) & ~1) : 0;
+    // loads of step gs (past the end: the last step again, into a stage
+    // nobody reads, so every step issues the same loads)
+    auto issue = [&](int gs) {
+        if (gs > nsteps - 1) gs = nsteps - 1;
+        const int r = gs / nch;
+        int ch = gs - r * nch + rot;
+        if (ch >= nch) ch -= nch;
+        const uint32_t st = lds0 + (uint32_t)((gs % kSStages) * SG::STAGE);
+        // x: load j covers rows 4j .. 4j+3 of the wave's 16; lane -> row
+        // 4j + lane / 16, LDS slot lane % 16 holding piece slot ^ row
+        const int64_t trow0 = (int64_t)(tile0 + r * per_round) * kTok;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int rr = 4 * j + lane / 16;
+            int64_t t = trow0 + rr;
+            if (t >= p.T) t = p.T - 1;  // clamp: rows past T are never written out
+            const int piece = (lane % 16) ^ rr;
+            const int voff = (int)((t * H + (int64_t)ch * kSC) * 2) + piece * 16;
+            w_dma16(rsX, st + wave * (kTok * kSC * 2) + j * 1024, voff);
+        }
+        // W_r rows ch*kSC .. +kSC as [kSC][EP], 256 bytes per load; experts
+        // past E read as zero (offset past the descriptor's range)
+#pragma unroll
+        for (int u = 0; u < SG::W_LOADS; ++u) {
+            const int i = wave * SG::W_LOADS + u;
+            const int b = i * 256 + lane * 4;          // byte in the stage's W image
+            const int kr = b / (EP * 2), e = (b % (EP * 2)) / 2;
+            const int voff = e < E ? ((ch * kSC + kr) * E + e) * 2 : 0x7FFFFFF0;
+            w_dma4(rsW, st + SG::X_BYTES + i * 256, voff);
+        }
+    };
+
+    float bias[NTN];
+#pragma unroll
+    for (int n = 0; n < NTN; ++n) {
+        const int e = 16 * n + lane % 16;
+        bias[n] = (p.b_r && e < E) ? p.b_r[e] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < kSStages - 1; ++q) issue(q);
+    f32x4_t acc[NTN], tot[NTN];
+    float gn[NTN][4];
+#pragma unroll
+    for (int n = 0; n < NTN; ++n) {
+        tot[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int n = 0; n < NTN; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gn[n][i] = 0.f;
+    const int arow = lane % 16, agrp = lane / 16;
+    for (int gs = 0; gs < nsteps; ++gs) {
+        const int r = gs / nch, ch = gs - r * nch;
+        const int tile = tile0 + r * per_round;
+        // this step's loads have landed once at most the newer steps' loads
+        // (and any stores issued after them) are outstanding: loads and
+        // stores retire in issue order
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kSStages - 2) * SG::LOADS) : "memory");
+        __syncthreads();
+        issue(gs + kSStages - 1);
+        // Gumbel noise of this tile's value q = 4 n + i at step q (the rest
+        // at the tile's last step when it has fewer steps than values)
+        if (p.mode == 1) {
+#pragma unroll
+            for (int q = 0; q < 4 * NTN; ++q)
+                if (q == ch || (ch == nch - 1 && q > ch)) {
+                    const int64_t t = (int64_t)tile * kTok + 4 * agrp + q % 4;
+                    const int e = 16 * (q / 4) + lane % 16;
+                    gn[q / 4][q % 4] =
+                        (e < E && t < p.T)
+                            ? gumbel_from_word(philox_word0((uint32_t)t, (uint32_t)e, p.key0, p.key1))
+                            : 0.f;
+                }
+        }
+        const unsigned char* xs = smem + (gs % kSStages) * SG::STAGE + wave * (kTok * kSC * 2);
+        const unsigned char* wb = smem + (gs % kSStages) * SG::STAGE + SG::X_BYTES;
+#pragma unroll
+        for (int s2 = 0; s2 < kSC / 32; ++s2) {
+            const int slot = (4 * s2 + agrp) ^ arow;
+            const bf16x8_t av = as_bf16x8(*reinterpret_cast<const uint4*>(xs + arow * (kSC * 2) + slot * 16));
+#pragma unroll
+            for (int n = 0; n < NTN; ++n) {
+                i16x4_t v[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int kr = s2 * 32 + agrp * 8 + hh * 4 + (lane % 16) / 4;
+                    v[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4_t*)(wb + (kr * EP + n * 16 + 4 * (lane % 4)) * 2));
+                }
+                const uint2 lo = __builtin_bit_cast(uint2, v[0]);
+                const uint2 hi = __builtin_bit_cast(uint2, v[1]);
+                const bf16x8_t bv = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+                acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[n], 0, 0, 0);
+            }
+        }
+        // blocks of 256 hidden entries (two chunks; a last odd chunk alone)
+        if ((ch & 1) || ch == nch - 1) {
+#pragma unroll
+            for (int n = 0; n < NTN; ++n) {
+                tot[n] += acc[n];
+                acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        if (ch == nch - 1) {
+            if (tile < ntiles) route_tile_epilogue<NTN>(tot, gn, bias, (int64_t)tile * kTok, p, lane);
+#pragma unroll
+            for (int n = 0; n < NTN; ++n) tot[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    // the padding steps' loads still write LDS: let them land before the
+    // workgroup's LDS is released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // The k-split kernel, for token counts that leave compute units idle with
 // one wave per tile: a workgroup of 8 waves copies W_r into LDS once, in its
 // own [H, E] layout (16-byte loads), then walks 16-token tiles; each wave owns
@@ -486,7 +720,11 @@ __global__ __launch_bounds__(kKThreads) void route_ksplit_kernel(RouteParams p, 
     const int lane = tid % kWave;
     const uint16_t* xb = static_cast<const uint16_t*>(p.x);
 
-    const int ks0 = wave * ks_per_wave;
+    // wave w takes hidden slice (w + 4 (b & 1)) % 8: the workgroups of odd
+    // XCDs start half a row later (see the staged kernel); partials are
+    // summed by slice, so the sums do not depend on the assignment
+    const int slice = (wave + ((blockIdx.x & 1u) ? kKWaves / 2 : 0)) % kKWaves;
+    const int ks0 = slice * ks_per_wave;
     // A fragment of k-step ks for this lane: x[t0 + lane%16][ks*32 + (lane/16)*8 .. +8]
     auto load_tile = [&](uint4 (&a)[kMaxKsPerWave], int tile) {
         int64_t row = (int64_t)tile * kTok + (lane % 16);
@@ -539,7 +777,7 @@ __global__ __launch_bounds__(kKThreads) void route_ksplit_kernel(RouteParams p, 
         const int next = tile + gridDim.x;
         if (next < ntiles) load_tile(a_nxt, next);
 #pragma unroll
-        for (int n = 0; n < NTN; ++n) red[(wave * NTN + n) * kWave + lane] = acc[n];
+        for (int n = 0; n < NTN; ++n) red[(slice * NTN + n) * kWave + lane] = acc[n];
         __syncthreads();
         // fixed-order sum of the 8 partial tiles -> lg[token][expert]
         for (int q = tid; q < kTok * ld; q += kKThreads) {
@@ -598,6 +836,15 @@ int num_cus() {
     return n;
 }
 
+// LDS one workgroup may hold on the current device (0 if unknown)
+size_t max_lds() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || n <= 0)
+        return 0;
+    return (size_t)n;
+}
+
 template <int NTN>
 moe_status_t launch_ksplit(const RouteParams& p, hipStream_t st) {
     const int nks = p.H / 32;
@@ -637,6 +884,19 @@ moe_status_t launch_bf16(const RouteParams& p, hipStream_t st) {
     if (waves < 1) waves = 1;
     int grid = (ntiles + waves - 1) / waves;
     if (grid > cus) grid = cus;
+    // full workgroups: x and W_r staged through LDS together (x addressed
+    // with 32-bit byte offsets, W_r by 4-byte loads of expert pairs)
+    if (waves == kSWaves && p.E % 8 == 0 && (int64_t)p.T * p.H * 2 < ((int64_t)1 << 31) &&
+        StagedGeom<NTN>::LDS <= max_lds()) {
+        using SG = StagedGeom<NTN>;
+        if (hipFuncSetAttribute((const void*)route_staged_kernel<NTN>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)SG::LDS) != hipSuccess)
+            return MOE_ERR_LAUNCH;
+        hipLaunchKernelGGL(route_staged_kernel<NTN>, dim3(grid), dim3(kSWaves * kWave), SG::LDS, st,
+                           p, ntiles);
+        MOE_CHECK_LAUNCH();
+        return MOE_OK;
+    }
     const size_t lds = (size_t)hs * EP * 2;
     if (hipFuncSetAttribute((const void*)route_bf16_kernel<NTN>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)

@@ -168,6 +168,25 @@ ROUTE_ONLY = {
     "h1280-e64-k8": MoEConfig("r64", "bf16", T=333, H=1280, I=128, E=64, k=8, cf=1.0, seed=63),
     "h256-e1": MoEConfig("r1", "bf16", T=17, H=256, I=128, E=1, k=1, cf=1.0, seed=64),
     "h768-e12-k2": MoEConfig("r12", "bf16", T=4099, H=768, I=128, E=12, k=2, cf=1.0, seed=65),
+    # at least 8 tiles of 16 tokens per compute unit (on 256 compute units):
+    # the kernels that give each wave whole tiles, x and W_r staged through
+    # LDS (16 and 24 experts; a second, partial round of tiles ending in a
+    # partial tile; H = 4096 with a router bias; H = 768, whose half-row
+    # start is an odd chunk pair; H = 256, two chunks for eight noise values
+    # per lane), and W_r alone in LDS (40 experts, past the staged kernel's
+    # LDS; 12 experts, not a multiple of 8)
+    "t40007-e16-gumbel": MoEConfig("s16", "bf16", T=40007, H=2048, I=128, E=16, k=2, cf=1.0,
+                                   route="gumbel", seq=40007, seed=66),
+    "t33000-h4096-e32-bias": MoEConfig("s32", "bf16", T=33000, H=4096, I=128, E=32, k=2, cf=1.0,
+                                       router_bias0=1.5, seed=67),
+    "t32768-e24-k3": MoEConfig("s24", "bf16", T=32768, H=2048, I=128, E=24, k=3, cf=1.0, seed=68),
+    "t32768-h768-e8-gumbel": MoEConfig("s8", "bf16", T=32768, H=768, I=128, E=8, k=2, cf=1.0,
+                                       route="gumbel", seq=32768, seed=71),
+    "t32768-h256-e32-gumbel": MoEConfig("s32n", "bf16", T=32768, H=256, I=128, E=32, k=4,
+                                        cf=1.0, route="gumbel", seq=32768, seed=72),
+    "t32800-e40-gumbel": MoEConfig("s40", "bf16", T=32800, H=1024, I=128, E=40, k=2, cf=1.0,
+                                   route="gumbel", seq=32800, seed=69),
+    "t32790-e12": MoEConfig("s12", "bf16", T=32790, H=1024, I=128, E=12, k=2, cf=1.0, seed=70),
 }
 
 
