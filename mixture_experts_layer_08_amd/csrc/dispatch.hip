@@ -19,9 +19,10 @@
 //  1. each wave walks its 64 m assignments 64 at a time; a ballot per
 //     distinct expert gives each lane its rank among earlier same-expert
 //     lanes and the wave's running count per expert;
-//  2. the block publishes its count per expert as one 64-bit word (a flag
-//     bit above the count, so the word is read whole or not at all) and
-//     adds up the words of every earlier block, waiting on any not yet
+//  2. the block publishes its count per expert (and, for the statistics,
+//     its fp64 sum of the router probabilities) as two 64-bit words, each
+//     with a flag bit, so a word is read whole or not at all, and adds up
+//     the count words of every earlier block, waiting on any not yet
 //     published: its first row per expert.  Blocks publish before they
 //     read, and wait only on earlier tickets, so every wait ends; there is
 //     no chain of inclusive prefixes, so no block waits for more than one
@@ -31,11 +32,13 @@
 //  4. the last block to arrive (a second counter) totals the counts (and,
 //     for the statistics, the blocks' fp64 probability sums in block order:
 //     deterministic), writes kept, dropped, counts, f, P, L_aux, marks the
-//     rows past kept[e] empty, and clears the counters and count words.
-// So the workspace must be zero before its first use and every call leaves
-// it zero again (the fp64 sums are written before they are read and sit at
-// offsets no count word of any shape uses).  The row copy (x_disp) is a
-// separate token-major launch with many blocks: bandwidth-bound.
+//     rows past kept[e] empty, and clears the counters and the words.
+// Every value that crosses blocks travels in a flagged word that its reader
+// waits on, so the arrival counter needs no release / acquire ordering (with
+// it, and the sums as plain stores: 0.4-1.4 us more per call at 8192-65536
+// assignments).  The workspace must be zero before its first use and every
+// call leaves it zero again.  The row copy (x_disp) is a separate
+// token-major launch with many blocks: bandwidth-bound.
 #include "moe_common.h"
 
 #include <mutex>
@@ -46,17 +49,20 @@ constexpr int kOThreads = 512;               // 8 waves per block
 constexpr int kOWaves = kOThreads / 64;
 constexpr int kOMaxBlocks = 64;
 constexpr int kORegPasses = 8;
-constexpr unsigned long long kPublished = 1ull << 32;
+constexpr unsigned long long kPublished = 1ull << 63;  // flag of a published word
 constexpr int kSpinLimit = 1 << 20;          // ~1 s: only a workspace that was not zero gets there
 constexpr int kCopyTok = 8;                  // tokens per copy block
 constexpr size_t kHeaderBytes = 256;         // two arrival counters
 
-// One per (block, expert): the block's published count and its fp64 sum of
-// the router probabilities of its tokens for that expert.
+// One per (block, expert), both words flagged when published: word = the
+// block's row count for the expert (bits 32..62) and the low half of its
+// fp64 sum of the router probabilities of its tokens for that expert (bits
+// 0..31); hi = the high half of that sum (bits 0..31).
 struct DispCell {
     unsigned long long word;
-    double psum;
+    unsigned long long hi;
 };
+__device__ __forceinline__ int word_count(unsigned long long w) { return (int)((w >> 32) & 0x7fffffffu); }
 
 struct DispGeom {
     int nb;  // blocks
@@ -92,16 +98,16 @@ __device__ __forceinline__ unsigned long long ld_word(const unsigned long long* 
 __device__ __forceinline__ void st_word(unsigned long long* q, unsigned long long v) {
     __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// A published count word's count (spins until its flag is set; gives up
-// after kSpinLimit tries, which only a workspace that was not zero reaches,
-// and then returns whatever the word holds).
-__device__ __forceinline__ int published_count(const unsigned long long* q) {
+// A published word (spins until its flag is set; gives up after kSpinLimit
+// tries, which only a workspace that was not zero reaches, and then returns
+// whatever the word holds).
+__device__ __forceinline__ unsigned long long published_word(const unsigned long long* q) {
     unsigned long long w = ld_word(q);
     for (int i = 0; !(w & kPublished) && i < kSpinLimit; ++i) {
         __builtin_amdgcn_s_sleep(1);
         w = ld_word(q);
     }
-    return (int)(w & 0x7fffffffu);
+    return w;
 }
 
 // Sum over tokens t = t0, t0 + step, ... < t1 of probs[t, e] in token order
@@ -204,8 +210,7 @@ __device__ __forceinline__ void add_published(const DispCell* cell, int n, int E
         for (int u = 0; u < kLoadBatch; ++u) {
             const int q = q0 + u * kOThreads;
             if (q < n) {
-                const int c = (w[u] & kPublished) ? (int)(w[u] & 0x7fffffffu)
-                                                  : published_count(&cell[q].word);
+                const int c = word_count((w[u] & kPublished) ? w[u] : published_word(&cell[q].word));
                 atomicAdd(&cnt[q % E], c);
             }
         }
@@ -292,7 +297,13 @@ __global__ __launch_bounds__(kOThreads) void disp_onepass_kernel(OnePassArgs a) 
                 tot[w][tid] = acc;
                 acc += c;
             }
-            st_word(&a.cell[(size_t)b * E + tid].word, kPublished | (unsigned)acc);
+            // with the statistics, the block's probability sum goes with its
+            // count (block_prob_sums' thread tid wrote bsum[tid])
+            const unsigned long long ps =
+                MODE != kMaps ? (unsigned long long)__double_as_longlong(bsum[tid]) : 0ull;
+            st_word(&a.cell[(size_t)b * E + tid].word,
+                    kPublished | ((unsigned long long)acc << 32) | (ps & 0xffffffffull));
+            if (MODE != kMaps) st_word(&a.cell[(size_t)b * E + tid].hi, kPublished | (ps >> 32));
         }
         // 2. rows taken by earlier blocks: every earlier block's word
         if (MODE != kStats) add_published(a.cell, b * E, E, first);
@@ -326,14 +337,11 @@ __global__ __launch_bounds__(kOThreads) void disp_onepass_kernel(OnePassArgs a) 
                 }
             }
         }
-        // 4. arrival; the sums are published by the thread that counts the
-        // arrival, before it (release), and read by the last block after it
-        // (acquire)
+        // 4. arrival (relaxed: the last block waits on the flags of the
+        // words it reads)
         if (tid == 0) {
-            if (MODE != kMaps)
-                for (int e = 0; e < E; ++e) a.cell[(size_t)b * E + e].psum = bsum[e];
             const unsigned old =
-                __hip_atomic_fetch_add(&a.hdr[1], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(&a.hdr[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             s_last = old == (unsigned)a.nb - 1;
         }
         __syncthreads();
@@ -355,15 +363,22 @@ __global__ __launch_bounds__(kOThreads) void disp_onepass_kernel(OnePassArgs a) 
         double s = 0.0;
         if (r < rows)
             for (int j0 = r * S; j0 < j1; j0 += kLoadBatch) {
-                double v[kLoadBatch];
+                unsigned long long lo[kLoadBatch], hi[kLoadBatch];
+#pragma unroll
+                for (int u = 0; u < kLoadBatch; ++u) {
+                    const DispCell* c = &a.cell[(size_t)(j0 + u) * E + e];
+                    lo[u] = j0 + u < j1 ? ld_word(&c->word) : kPublished;
+                    hi[u] = j0 + u < j1 ? ld_word(&c->hi) : kPublished;
+                }
 #pragma unroll
                 for (int u = 0; u < kLoadBatch; ++u)
-                    v[u] = j0 + u < j1 ? __hip_atomic_load(&a.cell[(size_t)(j0 + u) * E + e].psum,
-                                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                       : 0.0;
-#pragma unroll
-                for (int u = 0; u < kLoadBatch; ++u)
-                    if (j0 + u < j1) s += v[u];
+                    if (j0 + u < j1) {
+                        const DispCell* c = &a.cell[(size_t)(j0 + u) * E + e];
+                        if (!(lo[u] & kPublished)) lo[u] = published_word(&c->word);
+                        if (!(hi[u] & kPublished)) hi[u] = published_word(&c->hi);
+                        s += __longlong_as_double((long long)(((hi[u] & 0xffffffffull) << 32) |
+                                                              (lo[u] & 0xffffffffull)));
+                    }
             }
         colsum[tid] = s;
     }
@@ -402,7 +417,10 @@ __global__ __launch_bounds__(kOThreads) void disp_onepass_kernel(OnePassArgs a) 
         for (int e = 0; e < E; ++e)
             for (int64_t q = keptL[e] + tid; q < a.C; q += kOThreads) a.slot_token[e * a.C + q] = -1;
     if (nb > 0) {
-        for (int q = tid; q < nb * E; q += kOThreads) st_word(&a.cell[q].word, 0ull);
+        for (int q = tid; q < nb * E; q += kOThreads) {
+            st_word(&a.cell[q].word, 0ull);
+            st_word(&a.cell[q].hi, 0ull);
+        }
         if (tid == 0) {
             __hip_atomic_store(&a.hdr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&a.hdr[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
