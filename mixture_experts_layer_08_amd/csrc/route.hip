@@ -109,94 +109,6 @@ __device__ __forceinline__ float gumbel_from_word(uint32_t w) {
     return -logf(nl);
 }
 
-// Softmax / top-k / renormalisation on a tile of logits in LDS.
-// lg: [kTok][ld] fp32 logits (bias not yet added).  Every thread of the
-// block must call this (groups exchange values with lane shuffles).
-__device__ void route_epilogue(const float* lg, int ld, int64_t t0, const RouteParams& p,
-                               int gw) {
-    const int tid = threadIdx.x;
-    const int per_pass = blockDim.x / gw;
-    const int E = p.E, k = p.k;
-    for (int pass = 0; pass * per_pass < kTok; ++pass) {
-        const int tt = pass * per_pass + tid / gw;
-        const int e = tid % gw;
-        const int64_t t = t0 + tt;
-        const bool tok_ok = (tt < kTok) && (t < p.T);
-        const bool valid = tok_ok && (e < E);
-        float l = -INFINITY;
-        if (valid) {
-            l = lg[tt * ld + e];
-            if (p.b_r) l += p.b_r[e];
-        }
-        float key = l;
-        float z = l;  // softmax argument
-        if (p.mode == 1 && valid) {
-            key = l + gumbel_from_word(philox_word0((uint32_t)t, (uint32_t)e, p.key0, p.key1));
-            z = key * p.inv_tau;
-        }
-        // probabilities
-        const float m = group_max(z, gw);
-        const float ex = valid ? expf(z - m) : 0.f;
-        const float s = group_sum(ex, gw);
-        const float prob = valid ? ex / s : 0.f;
-        if (valid) {
-            p.probs[t * E + e] = prob;
-            if (p.keys) p.keys[t * E + e] = key;
-        }
-        // k rounds of arg-max over (key desc, index asc)
-        bool taken = !valid;
-        float wsum = 0.f;
-        int my_sel = -1;
-        float my_prob = 0.f;
-        for (int j = 0; j < k; ++j) {
-            float bv = taken ? -INFINITY : key;
-            int bi = taken ? 0x7FFFFFFF : e;
-            for (int o = gw >> 1; o > 0; o >>= 1) {
-                const float ov = __shfl_xor(bv, o, gw);
-                const int oi = __shfl_xor(bi, o, gw);
-                if (ov > bv || (ov == bv && oi < bi)) {
-                    bv = ov;
-                    bi = oi;
-                }
-            }
-            const int base = (threadIdx.x % kWave) / gw * gw;
-            const float pw = __shfl(prob, base + (bi < gw ? bi : 0), kWave);
-            if (e == bi) taken = true;
-            wsum += pw;
-            if (e == j) {
-                my_sel = bi;
-                my_prob = pw;
-            }
-        }
-        if (tok_ok && e < k) {
-            p.topk_idx[t * k + e] = my_sel;
-            p.topk_w[t * k + e] = my_prob / wsum;
-        }
-    }
-}
-
-// Softmax, Gumbel keys, top-k and renormalised weights of one wave's
-// 16-token tile, on the accumulators in the MFMA layout: acc[n][i] of lane l
-// is the logit of token t0 + 4 (l / 16) + i and expert 16 n + l % 16.
-// Gumbel noise of the tile's (token, expert) pairs in the accumulator layout
-// (it depends only on the counter (t, e) and the seed, so it is computed while
-// the tile's x loads are in flight); zero in softmax mode.
-template <int NTN>
-__device__ __forceinline__ void tile_noise(float (&gn)[NTN][4], int64_t t0, const RouteParams& p,
-                                           int lane) {
-    const int c = lane % 16, g = lane / 16;
-#pragma unroll
-    for (int n = 0; n < NTN; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t t = t0 + 4 * g + i;
-            const int e = 16 * n + c;
-            gn[n][i] = (p.mode == 1 && e < p.E && t < p.T)
-                           ? gumbel_from_word(philox_word0((uint32_t)t, (uint32_t)e, p.key0, p.key1))
-                           : 0.f;
-        }
-}
-
 // Exchanges inside 16-lane rows by DPP: lanes xor 1 and xor 2 (quad
 // permutes), lane i <-> 7 - i inside each half row (half mirror) and
 // i <-> 15 - i inside the row (mirror).  After the four, each in turn
@@ -234,6 +146,120 @@ __device__ __forceinline__ void argmax_step(float& bv, int& bi, float& bp) {
         bi = oi;
         bp = op;
     }
+}
+
+// Reductions over aligned groups of gw lanes (gw a power of two, uniform):
+// the DPP exchanges above inside 16-lane rows, lane shuffles past 16.
+__device__ __forceinline__ float group_max_dpp(float v, int gw) {
+    if (gw > 1) v = fmaxf(v, dpp16f<0xB1>(v));
+    if (gw > 2) v = fmaxf(v, dpp16f<0x4E>(v));
+    if (gw > 4) v = fmaxf(v, dpp16f<0x141>(v));
+    if (gw > 8) v = fmaxf(v, dpp16f<0x140>(v));
+    for (int o = 16; o < gw; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, gw));
+    return v;
+}
+__device__ __forceinline__ float group_sum_dpp(float v, int gw) {
+    if (gw > 1) v += dpp16f<0xB1>(v);
+    if (gw > 2) v += dpp16f<0x4E>(v);
+    if (gw > 4) v += dpp16f<0x141>(v);
+    if (gw > 8) v += dpp16f<0x140>(v);
+    for (int o = 16; o < gw; o <<= 1) v += __shfl_xor(v, o, gw);
+    return v;
+}
+// the best (value desc, index asc) over the group, in every lane of it
+__device__ __forceinline__ void group_argmax_dpp(float& bv, int& bi, int gw) {
+    auto take = [&](float ov, int oi) {
+        if (ov > bv || (ov == bv && oi < bi)) {
+            bv = ov;
+            bi = oi;
+        }
+    };
+    if (gw > 1) take(dpp16f<0xB1>(bv), dpp16<0xB1>(bi));
+    if (gw > 2) take(dpp16f<0x4E>(bv), dpp16<0x4E>(bi));
+    if (gw > 4) take(dpp16f<0x141>(bv), dpp16<0x141>(bi));
+    if (gw > 8) take(dpp16f<0x140>(bv), dpp16<0x140>(bi));
+    for (int o = 16; o < gw; o <<= 1) take(__shfl_xor(bv, o, gw), __shfl_xor(bi, o, gw));
+}
+
+// Softmax / top-k / renormalisation on a tile of logits in LDS.
+// lg: [kTok][ld] fp32 logits (bias not yet added).  Every thread of the
+// block must call this (groups exchange values by DPP and lane shuffles).
+__device__ void route_epilogue(const float* lg, int ld, int64_t t0, const RouteParams& p,
+                               int gw) {
+    const int tid = threadIdx.x;
+    const int per_pass = blockDim.x / gw;
+    const int E = p.E, k = p.k;
+    for (int pass = 0; pass * per_pass < kTok; ++pass) {
+        const int tt = pass * per_pass + tid / gw;
+        const int e = tid % gw;
+        const int64_t t = t0 + tt;
+        const bool tok_ok = (tt < kTok) && (t < p.T);
+        const bool valid = tok_ok && (e < E);
+        float l = -INFINITY;
+        if (valid) {
+            l = lg[tt * ld + e];
+            if (p.b_r) l += p.b_r[e];
+        }
+        float key = l;
+        float z = l;  // softmax argument
+        if (p.mode == 1 && valid) {
+            key = l + gumbel_from_word(philox_word0((uint32_t)t, (uint32_t)e, p.key0, p.key1));
+            z = key * p.inv_tau;
+        }
+        // probabilities
+        const float m = group_max_dpp(z, gw);
+        const float ex = valid ? __expf(z - m) : 0.f;
+        const float s = group_sum_dpp(ex, gw);
+        const float prob = valid ? ex * __builtin_amdgcn_rcpf(s) : 0.f;
+        if (valid) {
+            p.probs[t * E + e] = prob;
+            if (p.keys) p.keys[t * E + e] = key;
+        }
+        // k rounds of arg-max over (key desc, index asc)
+        bool taken = !valid;
+        float wsum = 0.f;
+        int my_sel = -1;
+        float my_prob = 0.f;
+        for (int j = 0; j < k; ++j) {
+            float bv = taken ? -INFINITY : key;
+            int bi = taken ? 0x7FFFFFFF : e;
+            group_argmax_dpp(bv, bi, gw);
+            const int base = (threadIdx.x % kWave) / gw * gw;
+            const float pw = __shfl(prob, base + (bi < gw ? bi : 0), kWave);
+            if (e == bi) taken = true;
+            wsum += pw;
+            if (e == j) {
+                my_sel = bi;
+                my_prob = pw;
+            }
+        }
+        if (tok_ok && e < k) {
+            p.topk_idx[t * k + e] = my_sel;
+            p.topk_w[t * k + e] = my_prob / wsum;
+        }
+    }
+}
+
+// Softmax, Gumbel keys, top-k and renormalised weights of one wave's
+// 16-token tile, on the accumulators in the MFMA layout: acc[n][i] of lane l
+// is the logit of token t0 + 4 (l / 16) + i and expert 16 n + l % 16.
+// Gumbel noise of the tile's (token, expert) pairs in the accumulator layout
+// (it depends only on the counter (t, e) and the seed, so it is computed while
+// the tile's x loads are in flight); zero in softmax mode.
+template <int NTN>
+__device__ __forceinline__ void tile_noise(float (&gn)[NTN][4], int64_t t0, const RouteParams& p,
+                                           int lane) {
+    const int c = lane % 16, g = lane / 16;
+#pragma unroll
+    for (int n = 0; n < NTN; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t t = t0 + 4 * g + i;
+            const int e = 16 * n + c;
+            gn[n][i] = (p.mode == 1 && e < p.E && t < p.T)
+                           ? gumbel_from_word(philox_word0((uint32_t)t, (uint32_t)e, p.key0, p.key1))
+                           : 0.f;
+        }
 }
 
 template <int NTN>
