@@ -270,6 +270,39 @@ moe_status_t moe_expert_ffn_gather(void* stream, moe_dtype_t dtype, moe_act_t ac
                                    const void* b2, void* h_ws, void* y_disp,
                                    void* ws, size_t ws_bytes);
 
+/* moe_expert_ffn_gather with moe_combine fused into the down product:
+ * [P3] section 2.1 reads each expert's rows by routing index inside the
+ * expert kernel, and the weighted sum of [P1] section 2.4 / [P2] section 3.1
+ * is done by the down product's tiles instead of a separate pass.  The
+ * tile holding the last of a token's kept copies to finish (a token's only
+ * copy, at once) computes the token's output columns exactly as
+ * moe_combine does (the addend row or zero, then fused multiply-adds of
+ * w[t, j] * y_disp row for j = 0 .. k-1 in order, a dropped copy adding
+ * w * 0, one bf16 rounding), so y is bitwise moe_combine's whichever copy
+ * finishes last; tokens with no kept copy get their row from a small pass.
+ *
+ *   slot, topk_w [T, k]      moe_dispatch's slot and moe_route's weights
+ *   y_shared     [T, H] fp32 optional addend row (shared expert) or NULL
+ *   y_disp       [E, C, H] fp32  workspace (holds the expert rows after
+ *                                the call, as moe_expert_ffn_gather's)
+ *   ws           >= moe_expert_ffn_combine_ws_bytes(T, H) bytes, 16-byte
+ *                aligned, zero-filled before its first use; every call
+ *                leaves it zero again (per-token counters and the split
+ *                tail's workspace).  Required (MOE_ERR_WORKSPACE).  Two
+ *                calls that run at the same time must not share one ws.
+ *   y            [T, H] bf16 out
+ * bf16 activations and weights only; other arguments and limits as for
+ * moe_expert_ffn_gather, and E * C * H * 4 below 2^32. */
+size_t moe_expert_ffn_combine_ws_bytes(int64_t T, int64_t H);
+moe_status_t moe_expert_ffn_gather_combine(void* stream, moe_act_t act, const void* x,
+                                           const int32_t* slot_token, const int32_t* slot,
+                                           const float* topk_w, int64_t T, int k,
+                                           const int32_t* kept, int E, int64_t C, int64_t H,
+                                           int64_t I, const void* w1, const void* w3,
+                                           const void* w2, const void* b1, const void* b2,
+                                           const float* y_shared, void* h_ws, void* y_disp,
+                                           void* ws, size_t ws_bytes, void* y);
+
 /* ------------------------------------------------------ 8-bit weights ----
  * [P4] section 3 keeps the expert weights in 8 bits and restores them with
  * a scale computed per expert and per dimension; [P1] section 5.2 and [P5]

@@ -29,7 +29,8 @@ EXPORTS = ("moe_capacity", "moe_status_string", "moe_workspace_bytes", "moe_rout
            "moe_expert_ffn_bwd_ws_bytes", "moe_dispatch_bwd", "moe_route_bwd",
            "moe_route_bwd_ws_bytes", "moe_quantize_fp8", "moe_dequantize_fp8",
            "moe_expert_ffn_fp8", "moe_expert_ffn_gather_fp8", "moe_expert_ffn_fwd_save",
-           "moe_dispatch_aux", "moe_dispatch_aux_noalloc")
+           "moe_dispatch_aux", "moe_dispatch_aux_noalloc", "moe_expert_ffn_gather_combine",
+           "moe_expert_ffn_combine_ws_bytes")
 
 _lock = threading.Lock()
 _lib = None
@@ -103,6 +104,12 @@ def _declare(L: ctypes.CDLL) -> None:
     L.moe_expert_ffn_gather_fp8.argtypes = [vp, i32, vp, vp, i64, vp, i32, i64, i64, i64, vp, vp,
                                             vp, vp, vp, vp, vp, vp, vp, vp, vp, c.c_size_t]
     L.moe_expert_ffn_gather_fp8.restype = i32
+    L.moe_expert_ffn_gather_combine.argtypes = [vp, i32, vp, vp, vp, vp, i64, i32, vp, i32, i64,
+                                                i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                c.c_size_t, vp]
+    L.moe_expert_ffn_gather_combine.restype = i32
+    L.moe_expert_ffn_combine_ws_bytes.argtypes = [i64, i64]
+    L.moe_expert_ffn_combine_ws_bytes.restype = c.c_size_t
 
 
 def lib() -> ctypes.CDLL:

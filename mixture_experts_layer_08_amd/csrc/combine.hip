@@ -15,6 +15,7 @@
 // slot[], accumulates in fp32 and writes the row once (bf16 output is
 // rounded once, to nearest-even).
 #include "moe_common.h"
+#include "internal.h"
 
 namespace {
 
@@ -94,7 +95,61 @@ __global__ __launch_bounds__(kCThreads) void combine_kernel(const float4* __rest
     }
 }
 
+// Tokens none of whose copies was kept: their output row is the sum above
+// over no expert rows (the addend row, or zero, with w_j * 0 added for each
+// j), rounded once to bf16.  The down product with the combine fused writes
+// every other token's row.  One thread per token finds the tokens; each
+// wave then writes its tokens' rows with all its lanes.
+__global__ __launch_bounds__(256) void combine_empty_kernel(const int32_t* __restrict__ slot,
+                                                            const float* __restrict__ w,
+                                                            const float4* __restrict__ yadd,
+                                                            int64_t T, int k, int row_oct,
+                                                            uint4* __restrict__ y) {
+    const int lane = threadIdx.x % kWave;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    bool empty = t < T;
+    for (int j = 0; empty && j < k; ++j)
+        if (slot[t * k + j] >= 0) empty = false;
+    uint64_t m = __ballot(empty);
+    const int64_t tw = t - lane;  // the wave's first token
+    while (m) {
+        const int64_t tt = tw + __builtin_ctzll(m);
+        m &= m - 1;
+        for (int v = lane; v < row_oct; v += kWave) {
+            float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
+            if (yadd) {
+                a0 = yadd[(tt * row_oct + v) * 2];
+                a1 = yadd[(tt * row_oct + v) * 2 + 1];
+            }
+            for (int j = 0; j < k; ++j) {
+                const float wj = w[tt * k + j];
+                a0.x = fmaf(wj, 0.f, a0.x);
+                a0.y = fmaf(wj, 0.f, a0.y);
+                a0.z = fmaf(wj, 0.f, a0.z);
+                a0.w = fmaf(wj, 0.f, a0.w);
+                a1.x = fmaf(wj, 0.f, a1.x);
+                a1.y = fmaf(wj, 0.f, a1.y);
+                a1.z = fmaf(wj, 0.f, a1.z);
+                a1.w = fmaf(wj, 0.f, a1.w);
+            }
+            y[tt * row_oct + v] = make_uint4(pack_bf2(a0.x, a0.y), pack_bf2(a0.z, a0.w),
+                                             pack_bf2(a1.x, a1.y), pack_bf2(a1.z, a1.w));
+        }
+    }
+}
+
 }  // namespace
+
+moe_status_t moe_combine_empty(hipStream_t st, const int32_t* slot, const float* topk_w, int64_t T,
+                               int64_t H, int k, const float* y_shared, void* y) {
+    if (T == 0) return MOE_OK;
+    const int64_t grid = (T + 255) / 256;
+    hipLaunchKernelGGL(combine_empty_kernel, dim3((unsigned)grid), dim3(256), 0, st, slot, topk_w,
+                       reinterpret_cast<const float4*>(y_shared), T, k, (int)(H / 8),
+                       static_cast<uint4*>(y));
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
+}
 
 extern "C" moe_status_t moe_combine(void* stream, moe_dtype_t dtype, const void* y_disp,
                                     const int32_t* slot, const float* topk_w, int64_t T, int64_t H,

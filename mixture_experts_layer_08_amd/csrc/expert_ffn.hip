@@ -83,7 +83,17 @@ using namespace moe;
 // stores the pre-activations the backward needs (SwiGLU: g = X W_gate and
 // u = X W_up; GELU: z = X W1 + b1), rounded to bf16.
 enum { MODE_SWIGLU_SAVE = 3, MODE_GELU_SAVE = 4 };
-constexpr int mode_base(int m) { return m == MODE_SWIGLU_SAVE ? MODE_SWIGLU : m == MODE_GELU_SAVE ? MODE_GELU : m; }
+// The down product with the combine fused into its epilogue (inference):
+// each tile's rows are stored as in MODE_DOWN, then the last of a token's
+// kept copies to arrive writes the token's output row (see fused_finish).
+enum { MODE_DOWN_FUSED = 5 };
+constexpr int mode_base(int m) {
+    return m == MODE_SWIGLU_SAVE ? MODE_SWIGLU
+         : m == MODE_GELU_SAVE   ? MODE_GELU
+         : m == MODE_DOWN_FUSED  ? MODE_DOWN
+                                 : m;
+}
+constexpr bool mode_saves(int m) { return m == MODE_SWIGLU_SAVE || m == MODE_GELU_SAVE; }
 
 struct GemmArgs {
     const uint16_t* A;      // [E, C, K], or with slot_token the token rows [a_rows, K]
@@ -110,6 +120,15 @@ struct GemmArgs {
     const uint8_t* Q1;
     const float* scale0;
     const float* scale1;
+    // MODE_DOWN_FUSED: the combine's inputs and output
+    const int32_t* row_token;  // [E, C] token of each row (moe_dispatch's slot_token)
+    const int32_t* slot;       // [T, k] row of each copy (e * C + r), or -1 (dropped)
+    const float* topk_w;       // [T, k] combine weights
+    const float* yadd;         // [T, N] fp32 addend row (shared expert) or null
+    uint16_t* y;               // [T, N] bf16 output
+    uint32_t* tcnt;            // [T, N / 128] copies stored so far per token and column
+                               // tile (zero between launches)
+    int k;
 };
 
 constexpr size_t kPartBytes = (size_t)kBM * kBNMax * 4;  // one fp32 tile
@@ -227,7 +246,12 @@ struct Epi {
     static constexpr int BN_OUT = (MB == MODE_SWIGLU) ? BN / 2 : BN;
     static constexpr int OUT_BYTES = (MB == MODE_DOWN) ? 4 : 2;
     static constexpr size_t SLOTS = (size_t)NS * (STAGE_A + STAGE_B);
-    static constexpr size_t LDS = SLOTS + 16;  // + a word that broadcasts a split tile's state
+    // MODE_DOWN_FUSED: after the split-state word, a count and the tile's
+    // finishing rows (token, then the token's k rows and weights)
+    static constexpr size_t FUSE_LDS =
+        MODE == MODE_DOWN_FUSED ? 16 + (size_t)BM * 4 * (1 + 2 * MOE_MAX_TOPK) : 0;
+    // + a word that broadcasts a split tile's state
+    static constexpr size_t LDS = SLOTS + 16 + FUSE_LDS;
     static_assert(LDS <= 160 * 1024, "LDS of one compute unit");
 };
 
@@ -249,9 +273,14 @@ struct TileCtx {
 template <int MODE, int BN, bool GATHER, bool F8, bool THIN>
 __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     using EP = Epi<MODE, BN, F8, THIN>;
-    static_assert(!F8 || MODE == mode_base(MODE), "8-bit weights: inference products only");
+    static_assert(!F8 || !mode_saves(MODE), "8-bit weights: inference products only");
     constexpr int MB = mode_base(MODE);
-    constexpr bool SAVE = MODE != MB;
+    constexpr bool SAVE = mode_saves(MODE);
+    constexpr bool FUSE = MODE == MODE_DOWN_FUSED;
+    // y_disp rows of the fused down product are read by other workgroups
+    // (a token's copies sit in different experts' tiles, on any XCD), so they
+    // are written through to memory
+    constexpr int AUX_OUT = FUSE ? kAuxSystem : 0;
     constexpr int WM_ROWS = EP::BM / kWMn;    // rows per wave
     constexpr int WN_COLS = BN / kWN;         // B columns per wave
     constexpr int TM = WM_ROWS / 32, TN = WN_COLS / 32;  // 32 x 32 MFMA tiles per wave
@@ -468,6 +497,133 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
                 const uint2 lo = __builtin_bit_cast(uint2, v[0]);
                 const uint2 hi = __builtin_bit_cast(uint2, v[1]);
                 bfr[ss][j] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+            }
+        }
+    };
+
+    // MODE_DOWN_FUSED, after a tile's rows are stored (y_disp, written
+    // through to memory): the combine of [P1] section 2.4 / [P2] section 3.1
+    // for the tokens this tile completes.  Each token has n kept copies in n
+    // different experts' tiles, and a counter per token and column tile
+    // counts the copies stored so far; the tile that brings it to n (or a
+    // token's only copy) writes that token's output columns: the addend row
+    // (or zero), then w_j * y_j added for j = 0 .. k-1 in order by fused
+    // multiply-add (a dropped copy adds w_j * 0), rounded once to bf16 --
+    // the same operations as moe_combine, so the output is bitwise the same
+    // whichever copy arrives last.
+    //   1. every wave waits until its stores have completed, then a barrier:
+    //      the tile's rows are in memory before any count includes them;
+    //   2. one thread per tile row reads its token, the token's k rows and
+    //      weights, and counts the copy with a system-scope atomic (the
+    //      counter is set back to zero by the copy that completes it); the
+    //      completed tokens are listed in LDS;
+    //   3. the workgroup reads the listed tokens' rows (system scope: other
+    //      XCDs wrote them), eight columns per thread, and writes y.
+    // The wait in step 1 also drains the next tile's first loads, so the
+    // next tile's partial waits hold trivially.
+    auto fused_finish = [&](const TileCtx& c) {
+        if constexpr (FUSE) {
+            constexpr int BNO = EP::BN_OUT;
+            constexpr int TPR = BNO / 8;            // threads per row
+            constexpr int RPP = kGThreads / TPR;    // rows per pass
+            constexpr int U = 2;                    // passes with loads in flight together
+            constexpr int KM = MOE_MAX_TOPK;
+            int* s_cnt = reinterpret_cast<int*>(smem + EP::SLOTS + 16);
+            int* s_tok = s_cnt + 4;
+            int* s_slot = s_tok + EP::BM;
+            float* s_w = reinterpret_cast<float*>(s_slot + EP::BM * KM);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (tid == 0) *s_cnt = 0;
+            __syncthreads();
+            const int k = g.k;
+            if (tid < EP::BM && c.m0 + tid < c.kept) {
+                const int t = g.row_token[(size_t)c.e * g.C + c.m0 + tid];
+                int sl[KM];
+                float wv[KM];
+                int n = 0;
+#pragma unroll
+                for (int j = 0; j < KM; ++j) {
+                    if (j < k) {
+                        sl[j] = g.slot[(size_t)t * k + j];
+                        wv[j] = g.topk_w[(size_t)t * k + j];
+                        n += sl[j] >= 0 ? 1 : 0;
+                    }
+                }
+                bool fin = true;
+                if (n > 1) {
+                    uint32_t* cp = g.tcnt + (size_t)t * (g.N / BNO) + c.n0 / BNO;
+                    const uint32_t before =
+                        __hip_atomic_fetch_add(cp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                    fin = before == (uint32_t)(n - 1);
+                    if (fin) __hip_atomic_store(cp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                }
+                if (fin) {
+                    const int idx = atomicAdd(s_cnt, 1);
+                    s_tok[idx] = t;
+#pragma unroll
+                    for (int j = 0; j < KM; ++j) {
+                        if (j < k) {
+                            s_slot[idx * KM + j] = sl[j];
+                            s_w[idx * KM + j] = wv[j];
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            const int nf = *s_cnt;
+            const int c8 = tid % TPR, rsub = tid / TPR;
+            const int col = c.n0 + c8 * 8;
+            const i32x4_t rsY = make_rsrc(g.out, (uint32_t)((size_t)g.E * g.C * g.N * 4));
+            for (int b0 = 0; b0 < nf; b0 += RPP * U) {
+                f32x4_t a0[U], a1[U];
+                int tt[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int idx = b0 + u * RPP + rsub;
+                    tt[u] = idx < nf ? s_tok[idx] : -1;
+                    a0[u] = a1[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    if (tt[u] >= 0 && g.yadd) {
+                        const f32x4_t* ya =
+                            reinterpret_cast<const f32x4_t*>(g.yadd + (size_t)tt[u] * g.N + col);
+                        a0[u] = ya[0];
+                        a1[u] = ya[1];
+                    }
+                }
+                for (int j = 0; j < k; ++j) {
+                    f32x4_t q0[U], q1[U];
+                    float wj[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int idx = b0 + u * RPP + rsub;
+                        const int sj = tt[u] >= 0 ? s_slot[idx * KM + j] : -1;
+                        wj[u] = tt[u] >= 0 ? s_w[idx * KM + j] : 0.f;
+                        if (sj >= 0) {
+                            const uint32_t off = ((uint32_t)sj * (uint32_t)g.N + (uint32_t)col) * 4u;
+                            q0[u] = buffer_load_f32x4(rsY, (int)off, 0, kAuxSystem);
+                            q1[u] = buffer_load_f32x4(rsY, (int)(off + 16u), 0, kAuxSystem);
+                        } else {
+                            q0[u] = q1[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        a0[u].x = fmaf(wj[u], q0[u].x, a0[u].x);
+                        a0[u].y = fmaf(wj[u], q0[u].y, a0[u].y);
+                        a0[u].z = fmaf(wj[u], q0[u].z, a0[u].z);
+                        a0[u].w = fmaf(wj[u], q0[u].w, a0[u].w);
+                        a1[u].x = fmaf(wj[u], q1[u].x, a1[u].x);
+                        a1[u].y = fmaf(wj[u], q1[u].y, a1[u].y);
+                        a1[u].z = fmaf(wj[u], q1[u].z, a1[u].z);
+                        a1[u].w = fmaf(wj[u], q1[u].w, a1[u].w);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if (tt[u] < 0) continue;
+                    *reinterpret_cast<uint4*>(g.y + (size_t)tt[u] * g.N + col) =
+                        make_uint4(pack_bf2(a0[u].x, a0[u].y), pack_bf2(a0[u].z, a0[u].w),
+                                   pack_bf2(a1[u].x, a1[u].y), pack_bf2(a1[u].z, a1[u].w));
+                }
             }
         }
     };
@@ -760,7 +916,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
                             }
                         }
                         if (MB == MODE_DOWN)
-                            store_rows4_f32(v, rsO, voff, soff, lane);
+                            store_rows4_f32<AUX_OUT>(v, rsO, voff, soff, lane);
                         else
                             store_rows4_bf16(v, rsO, voff, soff, lane);
                         if (SAVE) {
@@ -771,6 +927,7 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
                 }
             }
         }
+        fused_finish(cur);
         if (!nxt.valid) break;
         p0 += cur.nks;
         // the next tile was computed at the top of this round (the prefetch
@@ -869,13 +1026,14 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
                             v[r] = (F8 ? av[r] * sc0 : av[r]) + bv;
                     }
                     if (MB == MODE_DOWN)
-                        store_rows4_f32(v, rsO, voff, soff, lane);
+                        store_rows4_f32<AUX_OUT>(v, rsO, voff, soff, lane);
                     else
                         store_rows4_bf16(v, rsO, voff, soff, lane);
                 }
             }
         }
     }
+    fused_finish(cur);
 }
 
 // ----------------------------------------------------------- fp32 path ----
@@ -1007,6 +1165,16 @@ extern "C" size_t moe_expert_ffn_ws_bytes(void) { return ffn_ws_bytes(); }
 
 namespace {
 
+// The combine's inputs and output when it is fused into the down product.
+struct FuseArgs {
+    const int32_t* slot;
+    const float* topk_w;
+    const float* yadd;
+    void* y;
+    uint32_t* tcnt;
+    int k;
+};
+
 // Every entry point: A is x_disp [E, C, H], or with slot_token the token
 // rows x [a_rows, H] gathered through slot_token [E, C].  With scales
 // (s1 non-null), w1 / w3 / w2 are e4m3 codes [E, N, K] with per-column fp32
@@ -1016,7 +1184,8 @@ moe_status_t ffn_impl(void* stream, moe_dtype_t dtype, moe_act_t act, const void
                       int64_t C, int64_t H, int64_t I, const void* w1, const void* w3,
                       const void* w2, const void* b1, const void* b2, void* h_ws, void* y_disp,
                       void* ws, size_t ws_bytes, const float* s1 = nullptr,
-                      const float* s3 = nullptr, const float* s2 = nullptr) {
+                      const float* s3 = nullptr, const float* s2 = nullptr,
+                      const FuseArgs* fz = nullptr) {
     const bool f8 = s1 != nullptr;
     if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_DTYPE;
     if (act != MOE_ACT_SWIGLU && act != MOE_ACT_GELU_BIAS) return MOE_ERR_DTYPE;
@@ -1071,7 +1240,7 @@ moe_status_t ffn_impl(void* stream, moe_dtype_t dtype, moe_act_t act, const void
     // soffset) and one expert's rows of x_disp, h and fp32 y_disp
     if ((int64_t)H * I * 2 >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
     if (C * (H > I ? H : I) * 4 >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
-    GemmArgs a1;
+    GemmArgs a1{};
     a1.A = static_cast<const uint16_t*>(A);
     a1.slot_token = slot_token;
     a1.a_rows = a_rows;
@@ -1125,6 +1294,20 @@ moe_status_t ffn_impl(void* stream, moe_dtype_t dtype, moe_act_t act, const void
     a2.Q1 = nullptr;
     a2.scale0 = f8 ? s2 : nullptr;
     a2.scale1 = nullptr;
+    if (fz) {
+        a2.row_token = slot_token;
+        a2.slot = fz->slot;
+        a2.topk_w = fz->topk_w;
+        a2.yadd = fz->yadd;
+        a2.y = static_cast<uint16_t*>(fz->y);
+        a2.tcnt = fz->tcnt;
+        a2.k = fz->k;
+        if (thin)
+            return f8 ? launch_single<MODE_DOWN_FUSED, false, true, true>(a2, st)
+                      : launch_single<MODE_DOWN_FUSED, false, false, true>(a2, st);
+        return f8 ? launch_single<MODE_DOWN_FUSED, false, true>(a2, st)
+                  : launch_single<MODE_DOWN_FUSED>(a2, st);
+    }
     if (thin)
         return f8 ? launch_single<MODE_DOWN, false, true, true>(a2, st)
                   : launch_single<MODE_DOWN, false, false, true>(a2, st);
@@ -1138,7 +1321,7 @@ moe_status_t ffn_impl(void* stream, moe_dtype_t dtype, moe_act_t act, const void
 moe_status_t moe_ffn1_save(hipStream_t st, moe_act_t act, const void* x_disp, const int32_t* kept,
                            int E, int64_t C, int64_t H, int64_t I, const void* w1, const void* w3,
                            const void* b1, void* h, void* save0, void* save1) {
-    GemmArgs a;
+    GemmArgs a{};
     a.A = static_cast<const uint16_t*>(x_disp);
     a.slot_token = nullptr;
     a.a_rows = 0;
@@ -1207,6 +1390,47 @@ extern "C" moe_status_t moe_expert_ffn_gather(void* stream, moe_dtype_t dtype, m
     if (T < 0) return MOE_ERR_SHAPE;
     return ffn_impl(stream, dtype, act, x, slot_token, T, kept, E, C, H, I, w1, w3, w2, b1, b2,
                     h_ws, y_disp, ws, ws_bytes);
+}
+
+// Counters of the fused combine: one per token and 128-column tile (the
+// narrowest output tile), after the split-tail workspace.
+static size_t fuse_cnt_bytes(int64_t T, int64_t H) {
+    return ((size_t)T * (size_t)(H / 128) * 4 + 255) / 256 * 256;
+}
+
+extern "C" size_t moe_expert_ffn_combine_ws_bytes(int64_t T, int64_t H) {
+    if (T < 0 || H <= 0) return 0;
+    return ffn_ws_bytes() + fuse_cnt_bytes(T, H);
+}
+
+extern "C" moe_status_t moe_expert_ffn_gather_combine(
+    void* stream, moe_act_t act, const void* x, const int32_t* slot_token, const int32_t* slot,
+    const float* topk_w, int64_t T, int k, const int32_t* kept, int E, int64_t C, int64_t H,
+    int64_t I, const void* w1, const void* w3, const void* w2, const void* b1, const void* b2,
+    const float* y_shared, void* h_ws, void* y_disp, void* ws, size_t ws_bytes, void* y) {
+    if (T < 0 || k < 1 || E < 1 || H <= 0 || I <= 0 || C < 0) return MOE_ERR_SHAPE;
+    if (k > MOE_MAX_TOPK || k > E || T * k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!slot || !topk_w || !y || !kept) return MOE_ERR_NULL;
+    if (C > 0 && !slot_token) return MOE_ERR_NULL;
+    if (!ws || ws_bytes < moe_expert_ffn_combine_ws_bytes(T, H)) return MOE_ERR_WORKSPACE;
+    if (!moe_aligned16(ws) || !moe_aligned16(y) || (y_shared && !moe_aligned16(y_shared)))
+        return MOE_ERR_ALIGN;
+    if (H % 8) return MOE_ERR_ALIGN;
+    // the finishing tiles read y_disp rows through one 32-bit buffer range
+    if ((int64_t)E * C * H * 4 >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+    FuseArgs fz;
+    fz.slot = slot;
+    fz.topk_w = topk_w;
+    fz.yadd = y_shared;
+    fz.y = y;
+    fz.tcnt = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(ws) + ffn_ws_bytes());
+    fz.k = k;
+    const moe_status_t s = ffn_impl(stream, MOE_BF16, act, x, slot_token, T, kept, E, C, H, I, w1,
+                                    w3, w2, b1, b2, h_ws, y_disp, ws, ffn_ws_bytes(), nullptr,
+                                    nullptr, nullptr, &fz);
+    if (s != MOE_OK) return s;
+    return moe_combine_empty(static_cast<hipStream_t>(stream), slot, topk_w, T, H, k, y_shared, y);
 }
 
 extern "C" moe_status_t moe_expert_ffn_fp8(void* stream, moe_act_t act, const void* x_disp,

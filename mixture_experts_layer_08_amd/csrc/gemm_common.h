@@ -176,6 +176,7 @@ __device__ __forceinline__ void quad_transpose_f32(float (&v)[4], int lane) {
     v[2] = __uint_as_float(w2);
     v[3] = __uint_as_float(w3);
 }
+template <int AUX = 0>
 __device__ __forceinline__ void store_rows4_f32(const float (&vin)[4], i32x4_t rs, int voff,
                                                 int soff, int lane) {
     float v[4] = {vin[0], vin[1], vin[2], vin[3]};
@@ -190,7 +191,7 @@ __device__ __forceinline__ void store_rows4_f32(const float (&vin)[4], i32x4_t r
     // registers at once, and the first dword of some lanes' stores then held
     // the new value (measured wrong outputs).  With soffset 0 it pads the
     // store with the wait state a 16-byte store needs.
-    buffer_store_f32x4(o, rs, voff + soff, 0, 0);
+    buffer_store_f32x4(o, rs, voff + soff, 0, AUX);
 }
 
 // LDS swizzles (16-byte chunk index XOR).  A rows are 128 bytes: XOR with

@@ -19,3 +19,10 @@ moe_status_t moe_ffn1_save(hipStream_t st, moe_act_t act, const void* x_disp, co
 moe_status_t moe_ffn2(hipStream_t st, const void* h, const int32_t* kept, int E, int64_t C,
                       int64_t H, int64_t I, const void* w2, const void* b2, void* y_disp,
                       void* part, size_t part_bytes);
+
+// The rows of the tokens none of whose copies was kept (slot[t, j] < 0 for
+// every j), as moe_combine computes them: bf16 y [T, H] from the optional
+// fp32 addend y_shared [T, H] and the weights; other rows are not touched.
+// Arguments as moe_combine's (already checked by the caller).
+moe_status_t moe_combine_empty(hipStream_t st, const int32_t* slot, const float* topk_w, int64_t T,
+                               int64_t H, int k, const float* y_shared, void* y);

@@ -67,20 +67,27 @@ class Buffers:
     sh_h: Optional[torch.Tensor] = None
     sh_y: Optional[torch.Tensor] = None
     sh_ws: Optional[torch.Tensor] = None
+    # the fused combine's counters and split workspace (None without it)
+    fc_ws: Optional[torch.Tensor] = None
 
 
 class MoELayerGPU:
     """Device-resident weights + buffers for one configuration."""
 
     def __init__(self, cfg: MoEConfig, inputs: Dict[str, np.ndarray], device="cuda:0",
-                 fused_gather: bool = True, weights: str = "bf16"):
+                 fused_gather: bool = True, weights: str = "bf16", fused_combine: bool = False):
         """weights="fp8": the routed experts run on 8-bit (e4m3) weights with
         per-expert, per-column scales, quantised here on the device from the
-        bf16 weights (moe_quantize_fp8)."""
+        bf16 weights (moe_quantize_fp8).  fused_combine: forward runs the
+        expert products and the combine as one call
+        (moe_expert_ffn_gather_combine; bf16 weights, fused gather)."""
         if weights not in ("bf16", "fp8"):
             raise ValueError("weights must be 'bf16' or 'fp8'")
+        if fused_combine and (not fused_gather or weights != "bf16" or cfg.dtype != "bf16"):
+            raise ValueError("the fused combine needs the fused gather and bf16 weights")
         self.cfg = cfg
         self.fused_gather = fused_gather
+        self.fused_combine = fused_combine
         self.weights = weights
         dev = torch.device(device)
         self.dev = dev
@@ -149,7 +156,8 @@ class MoELayerGPU:
             kept=e(E, dt=i32), dropped=e(1, dt=i32), h=e(E, C, I, dt=td),
             y_disp=e(E, C, H), y=e(T, H, dt=td),
             ws=z(max(16, ops.moe_workspace_bytes(T, E, k))),
-            ffn_ws=z(ops.moe_expert_ffn_ws_bytes()))
+            ffn_ws=z(ops.moe_expert_ffn_ws_bytes()),
+            fc_ws=z(ops.moe_expert_ffn_combine_ws_bytes(T, H)) if self.fused_combine else None)
 
     # the five steps, each one library call ---------------------------------
     def route(self, x: torch.Tensor, keys: bool = False):
@@ -210,6 +218,16 @@ class MoELayerGPU:
         return ops.moe_expert_ffn(x.view(1, T, H), b.sh_kept, self.sw1, self.sw3, self.sw2,
                                   self.sb1, self.sb2, act=self.cfg.act, h_ws=b.sh_h,
                                   y_disp=b.sh_y, ws=b.sh_ws)
+
+    def experts_combine(self, x: torch.Tensor):
+        """experts(x) and combine() as one call: the down product's tiles
+        write y (moe_expert_ffn_gather_combine)."""
+        b = self.buf
+        ysh = b.sh_y.view(self.cfg.T, self.cfg.H) if self.shared else None
+        return ops.moe_expert_ffn_gather_combine(
+            x, b.slot_token, b.slot, b.topk_w, b.kept, self.w1, self.w3, self.w2, self.b1,
+            self.b2, act=self.cfg.act, y_shared=ysh, h_ws=b.h, y_disp=b.y_disp, ws=b.fc_ws,
+            y=b.y)
 
     def combine(self):
         b = self.buf
@@ -293,8 +311,11 @@ class MoELayerGPU:
             self.shared_expert(x)
         self.route(x, keys=keys)
         self.dispatch_aux(x)
-        self.experts(x)
-        self.combine()
+        if self.fused_combine:
+            self.experts_combine(x)
+        else:
+            self.experts(x)
+            self.combine()
         return self.buf.y, self.buf.l_aux
 
 

@@ -240,6 +240,58 @@ def moe_expert_ffn_gather(x: torch.Tensor, slot_token: torch.Tensor, kept: torch
     return y_disp, h_ws
 
 
+def moe_expert_ffn_combine_ws_bytes(T: int, H: int) -> int:
+    return int(lib().moe_expert_ffn_combine_ws_bytes(T, H))
+
+
+def moe_expert_ffn_gather_combine(x: torch.Tensor, slot_token: torch.Tensor, slot: torch.Tensor,
+                                  topk_w: torch.Tensor, kept: torch.Tensor, w1: torch.Tensor,
+                                  w3: Optional[torch.Tensor], w2: torch.Tensor,
+                                  b1: Optional[torch.Tensor] = None,
+                                  b2: Optional[torch.Tensor] = None, *, act: str = "swiglu",
+                                  y_shared: Optional[torch.Tensor] = None,
+                                  h_ws: Optional[torch.Tensor] = None,
+                                  y_disp: Optional[torch.Tensor] = None,
+                                  ws: Optional[torch.Tensor] = None,
+                                  y: Optional[torch.Tensor] = None):
+    """moe_expert_ffn_gather and moe_combine in one call: the down product's
+    tiles write each token's bf16 output row once its last kept copy is in.
+    ws: zero-filled once, at least moe_expert_ffn_combine_ws_bytes(T, H)
+    bytes (every call leaves it zero).  Returns (y, y_disp, h_ws)."""
+    T, H = x.shape
+    E, C = slot_token.shape
+    k = slot.shape[1]
+    I = w1.shape[2]
+    dev = x.device
+    if x.dtype != torch.bfloat16:
+        raise ValueError("the fused combine runs on bf16 activations")
+    if tuple(w1.shape) != (E, H, I) or tuple(w2.shape) != (E, I, H):
+        raise ValueError("w1 must be [E, H, I] and w2 [E, I, H]")
+    if w3 is not None and tuple(w3.shape) != (E, H, I):
+        raise ValueError("w3 must be [E, H, I]")
+    for t in (w1, w3, w2, b1, b2):
+        if t is not None and t.dtype != x.dtype:
+            raise ValueError("weights and biases must have x's dtype")
+    if slot_token.dtype != torch.int32 or slot.dtype != torch.int32:
+        raise ValueError("slot_token and slot must be int32")
+    if tuple(slot.shape) != (T, k) or tuple(topk_w.shape) != (T, k) or topk_w.dtype != torch.float32:
+        raise ValueError("slot must be int32 [T, k] and topk_w fp32 [T, k]")
+    if y_shared is not None and (y_shared.dtype != torch.float32 or y_shared.numel() != T * H
+                                 or not y_shared.is_contiguous()):
+        raise ValueError("y_shared must be a contiguous fp32 [T, H] tensor")
+    h_ws = _want(h_ws, (E, C, I), x.dtype, dev)
+    y_disp = _want(y_disp, (E, C, H), torch.float32, dev)
+    y = _want(y, (T, H), torch.bfloat16, dev)
+    if ws is None:
+        ws = torch.zeros(moe_expert_ffn_combine_ws_bytes(T, H), dtype=torch.uint8, device=dev)
+    st = lib().moe_expert_ffn_gather_combine(
+        _stream(dev), ACTS[act], _ptr(x), _ptr(slot_token), _ptr(slot), _ptr(topk_w), T, k,
+        _ptr(kept), E, C, H, I, _ptr(w1), _ptr(w3), _ptr(w2), _ptr(b1), _ptr(b2), _ptr(y_shared),
+        _ptr(h_ws), _ptr(y_disp), _ptr(ws), ws.numel() * ws.element_size(), _ptr(y))
+    check("moe_expert_ffn_gather_combine", st)
+    return y, y_disp, h_ws
+
+
 def moe_quantize_fp8(w: torch.Tensor, *, q: Optional[torch.Tensor] = None,
                      scale: Optional[torch.Tensor] = None):
     """bf16 weights [E, K, N] -> (e4m3 codes [E, N, K] uint8, fp32 scales

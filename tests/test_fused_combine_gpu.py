@@ -1,0 +1,160 @@
+"""GPU parity of the combine fused into the down product
+(moe_expert_ffn_gather_combine) through the C ABI.
+
+The fused call computes each token's output row with the same operations,
+in the same order, as moe_combine after moe_expert_ffn_gather (the addend
+row or zero, then w_j * y_j added by fused multiply-add for j = 0 .. k-1,
+one bf16 rounding), so its y must be bitwise the unfused layer's, whichever
+of a token's copies finishes last.  The unfused layer is itself checked
+against the oracle on every row (test_parity_gpu.py); here the small
+workloads are also checked against the oracle directly, with the layer's
+output bound (max |err| <= 2e-2 RMS(row) + 2^-8 |y|).  Every call must leave
+the workspace's counters at zero, so a second call on the same workspace
+gives the same bits.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as M
+from mixture_experts_layer_08_amd import ops
+from mixture_experts_layer_08_amd._lib import MoEError
+from mixture_experts_layer_08_amd.layer import MoELayerGPU, x_to_device
+from mixture_experts_layer_08_amd.synth import CONFIGS, MoEConfig, drop_free, make_inputs
+
+from parity_util import assert_rows_close, log, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+SMALL = {
+    "swiglu-e8": MoEConfig("f-e8", "bf16", T=3001, H=512, I=384, E=8, k=2, cf=1.25, seed=11),
+    # k = 3 with drops: tokens with one, two or no kept copies
+    "swiglu-e5-k3-drops": MoEConfig("f-e5", "bf16", T=777, H=256, I=256, E=5, k=3, cf=0.8,
+                                    router_bias0=1.0, seed=12),
+    "gelu-e4": MoEConfig("f-gelu", "bf16", T=600, H=256, I=512, E=4, k=2, cf=1.25, act="gelu",
+                         seed=13),
+    "gumbel-e32": MoEConfig("f-gumbel", "bf16", T=900, H=512, I=256, E=32, k=2, cf=1.25,
+                            route="gumbel", seq=900, seed=14),
+    "e64-k8": MoEConfig("f-e64", "bf16", T=300, H=256, I=128, E=64, k=8, cf=1.0, seed=15),
+    "e1-dense": MoEConfig("f-e1", "bf16", T=257, H=256, I=128, E=1, k=1, cf=1.0, seed=17),
+    # heavy drops (every copy of many tokens dropped) with a shared expert
+    "swiglu-e8-shared-drops": MoEConfig("f-sh", "bf16", T=1001, H=256, I=256, E=8, k=2,
+                                        cf=0.5, router_bias0=2.0, shared_I=512, seed=18),
+    "gelu-e4-shared": MoEConfig("f-sh-gelu", "bf16", T=600, H=256, I=512, E=4, k=2, cf=1.25,
+                                act="gelu", shared_I=256, seed=19),
+    # several row tiles per expert and 256-column output tiles: whole tiles,
+    # a split tail round, rows of one token finishing in either order
+    "swiglu-e8-t8192-h2048": MoEConfig("f-big", "bf16", T=8192, H=2048, I=512, E=8, k=2,
+                                       cf=1.25, seed=21),
+}
+
+
+def _counters(ws: torch.Tensor) -> torch.Tensor:
+    """The workspace's counters: the split tail's tile counters (after one
+    fp32 partial tile per compute unit) and the per-token counters after them."""
+    ffn = ops.moe_expert_ffn_ws_bytes()
+    tile = 256 * 256 * 4
+    return ws[(ffn // tile) * tile:]
+
+
+def _run_pair(cfg, inp):
+    """The fused and the unfused layer on the same inputs: (fused, unfused)."""
+    x = x_to_device(inp, cfg, DEV)
+    fused = MoELayerGPU(cfg, inp, DEV, fused_combine=True)
+    plain = MoELayerGPU(cfg, inp, DEV)
+    y_f, _ = fused.forward(x)
+    y_p, _ = plain.forward(x)
+    torch.cuda.synchronize()
+    return fused, plain, x
+
+
+def _same_bits(a: torch.Tensor, b: torch.Tensor, what: str) -> None:
+    ai = a.view(torch.int16)
+    bi = b.view(torch.int16)
+    diff = int((ai != bi).sum())
+    assert diff == 0, f"{what}: {diff} elements differ from the unfused layer"
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_fused_combine_small(name):
+    cfg = SMALL[name]
+    log(f"[fused] {name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} cf={cfg.cf} "
+        f"{cfg.act} {cfg.route} shared={cfg.shared_I}")
+    inp = make_inputs(cfg)
+    fused, plain, x = _run_pair(cfg, inp)
+    bf, bp = fused.buf, plain.buf
+    for n in ("topk_idx", "slot", "slot_token", "kept"):
+        assert torch.equal(getattr(bf, n), getattr(bp, n)), n
+    _same_bits(bf.y, bp.y, name)
+    assert int(_counters(bf.fc_ws).count_nonzero()) == 0, "counters left non-zero"
+    # against the oracle on every token whose routing and dispatch agree
+    ref = M.forward(inp, cfg)
+    ok = np.all(to_np(bf.topk_idx) == ref.route.idx, axis=1)
+    ok &= np.all(to_np(bf.slot) == ref.disp.slot, axis=1)
+    worst = assert_rows_close(to_np(bf.y)[ok], ref.y[ok], 2e-2, f"{name}: y", stored_bf16=True)
+    none_kept = np.all(to_np(bf.slot) < 0, axis=1)
+    if not cfg.shared_I:
+        assert np.all(to_np(bf.y)[none_kept] == 0.0)
+    # a second call on the same workspace gives the same bits
+    y1 = bf.y.clone()
+    bf.y.fill_(1.0)
+    fused.forward(x)
+    torch.cuda.synchronize()
+    _same_bits(bf.y, y1, f"{name}: second call")
+    assert int(_counters(bf.fc_ws).count_nonzero()) == 0
+    log(f"[fused] {name}: bitwise equal to the unfused layer; {int(none_kept.sum())} tokens "
+        f"with no kept copy; oracle rows {int(ok.sum())}/{cfg.T}, worst err/rms {worst:.3e}")
+
+
+@pytest.mark.parametrize("T", [1, 16, 64])
+def test_fused_combine_decode(T):
+    """Drop-free decode steps (C = T <= 64): the 64-row tile variant."""
+    cfg = drop_free(MoEConfig("f-decode", "bf16", T=T, H=512, I=512, E=8, k=2, cf=1.0,
+                              batch=T, seq=1, seed=20 + T))
+    log(f"[fused decode] T={T}")
+    inp = make_inputs(cfg)
+    fused, plain, _ = _run_pair(cfg, inp)
+    _same_bits(fused.buf.y, plain.buf.y, f"decode T={T}")
+    assert int(_counters(fused.buf.fc_ws).count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("cid", [2, 3, 5, 6])
+def test_fused_combine_full_size(cid):
+    """Full-size workloads in the benchmark's launch configuration (4096
+    tokens; the skewed layer with drops; the 32768-token, 32-expert Gumbel
+    layer; the 64-token decode step): bitwise the unfused layer on every
+    element, counters zero after the call."""
+    cfg = CONFIGS[cid]
+    log(f"[fused full] config {cid} {cfg.name}")
+    inp = make_inputs(cfg)
+    fused, plain, x = _run_pair(cfg, inp)
+    _same_bits(fused.buf.y, plain.buf.y, f"config {cid}")
+    assert int(_counters(fused.buf.fc_ws).count_nonzero()) == 0
+    dropped = int(to_np(fused.buf.dropped)[0])
+    none_kept = int(np.all(to_np(fused.buf.slot) < 0, axis=1).sum())
+    log(f"[fused full] config {cid}: bitwise equal; dropped {dropped}, tokens with no kept "
+        f"copy {none_kept}")
+
+
+def test_fused_combine_argument_errors():
+    """Refusals before anything is enqueued: missing or small workspace,
+    fp32 activations, shapes past the limits."""
+    cfg = SMALL["gelu-e4"]
+    inp = make_inputs(cfg)
+    layer = MoELayerGPU(cfg, inp, DEV)
+    x = x_to_device(inp, cfg, DEV)
+    layer.forward(x)
+    torch.cuda.synchronize()
+    b = layer.buf
+    small = torch.zeros(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(MoEError, match="WORKSPACE"):
+        ops.moe_expert_ffn_gather_combine(x, b.slot_token, b.slot, b.topk_w, b.kept, layer.w1,
+                                          layer.w3, layer.w2, layer.b1, layer.b2, act="gelu",
+                                          ws=small)
+    with pytest.raises(ValueError):
+        ops.moe_expert_ffn_gather_combine(x.float(), b.slot_token, b.slot, b.topk_w, b.kept,
+                                          layer.w1, layer.w3, layer.w2, layer.b1, layer.b2,
+                                          act="gelu")
