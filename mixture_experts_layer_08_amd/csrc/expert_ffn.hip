@@ -133,6 +133,10 @@ struct GemmArgs {
 
 constexpr size_t kPartBytes = (size_t)kBM * kBNMax * 4;  // one fp32 tile
 constexpr int kSMax = 8;  // most pieces per split tile
+// rows each thread of the fused combine finishes at a time (k <= 2)
+#ifndef FUSE_ROWS
+#define FUSE_ROWS 2
+#endif
 
 // ---------------------------------------------------------- tile schedule --
 // Expert e has ceil(kept[e] / BM) row tiles times NT column tiles.  A last
@@ -526,18 +530,19 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
             constexpr int BNO = EP::BN_OUT;
             constexpr int TPR = BNO / 8;            // threads per row
             constexpr int RPP = kGThreads / TPR;    // rows per pass
-            constexpr int U = 2;                    // passes with loads in flight together
             constexpr int KM = MOE_MAX_TOPK;
             int* s_cnt = reinterpret_cast<int*>(smem + EP::SLOTS + 16);
             int* s_tok = s_cnt + 4;
             int* s_slot = s_tok + EP::BM;
             float* s_w = reinterpret_cast<float*>(s_slot + EP::BM * KM);
+            // the row's token is loaded while the stores drain
+            const bool live = tid < EP::BM && c.m0 + tid < c.kept;
+            const int t = live ? g.row_token[(size_t)c.e * g.C + c.m0 + tid] : -1;
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             if (tid == 0) *s_cnt = 0;
             __syncthreads();
             const int k = g.k;
-            if (tid < EP::BM && c.m0 + tid < c.kept) {
-                const int t = g.row_token[(size_t)c.e * g.C + c.m0 + tid];
+            if (live) {
                 int sl[KM];
                 float wv[KM];
                 int n = 0;
@@ -574,57 +579,77 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
             const int c8 = tid % TPR, rsub = tid / TPR;
             const int col = c.n0 + c8 * 8;
             const i32x4_t rsY = make_rsrc(g.out, (uint32_t)((size_t)g.E * g.C * g.N * 4));
-            for (int b0 = 0; b0 < nf; b0 += RPP * U) {
-                f32x4_t a0[U], a1[U];
-                int tt[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int idx = b0 + u * RPP + rsub;
-                    tt[u] = idx < nf ? s_tok[idx] : -1;
-                    a0[u] = a1[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                    if (tt[u] >= 0 && g.yadd) {
-                        const f32x4_t* ya =
-                            reinterpret_cast<const f32x4_t*>(g.yadd + (size_t)tt[u] * g.N + col);
-                        a0[u] = ya[0];
-                        a1[u] = ya[1];
-                    }
-                }
-                for (int j = 0; j < k; ++j) {
-                    f32x4_t q0[U], q1[U];
-                    float wj[U];
+            // U rows per thread at a time; the loads of JB copies of each are
+            // in flight together, then added in j order
+            auto finish_rows = [&](auto u_c, auto jb_c) {
+                constexpr int U = decltype(u_c)::value;
+                constexpr int JB = decltype(jb_c)::value;
+                for (int b0 = 0; b0 < nf; b0 += RPP * U) {
+                    f32x4_t a0[U], a1[U];
+                    int tt[U];
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const int idx = b0 + u * RPP + rsub;
-                        const int sj = tt[u] >= 0 ? s_slot[idx * KM + j] : -1;
-                        wj[u] = tt[u] >= 0 ? s_w[idx * KM + j] : 0.f;
-                        if (sj >= 0) {
-                            const uint32_t off = ((uint32_t)sj * (uint32_t)g.N + (uint32_t)col) * 4u;
-                            q0[u] = buffer_load_f32x4(rsY, (int)off, 0, kAuxSystem);
-                            q1[u] = buffer_load_f32x4(rsY, (int)(off + 16u), 0, kAuxSystem);
-                        } else {
-                            q0[u] = q1[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                        tt[u] = idx < nf ? s_tok[idx] : -1;
+                        a0[u] = a1[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                        if (tt[u] >= 0 && g.yadd) {
+                            const f32x4_t* ya =
+                                reinterpret_cast<const f32x4_t*>(g.yadd + (size_t)tt[u] * g.N + col);
+                            a0[u] = ya[0];
+                            a1[u] = ya[1];
+                        }
+                    }
+                    for (int j0 = 0; j0 < k; j0 += JB) {
+                        f32x4_t q0[U][JB], q1[U][JB];
+                        float wj[U][JB];
+#pragma unroll
+                        for (int u = 0; u < U; ++u) {
+                            const int idx = b0 + u * RPP + rsub;
+#pragma unroll
+                            for (int jj = 0; jj < JB; ++jj) {
+                                const bool on = tt[u] >= 0 && j0 + jj < k;
+                                const int sj = on ? s_slot[idx * KM + j0 + jj] : -1;
+                                wj[u][jj] = on ? s_w[idx * KM + j0 + jj] : 0.f;
+                                if (sj >= 0) {
+                                    const uint32_t off =
+                                        ((uint32_t)sj * (uint32_t)g.N + (uint32_t)col) * 4u;
+                                    q0[u][jj] = buffer_load_f32x4(rsY, (int)off, 0, kAuxSystem);
+                                    q1[u][jj] = buffer_load_f32x4(rsY, (int)(off + 16u), 0, kAuxSystem);
+                                } else {
+                                    q0[u][jj] = q1[u][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                                }
+                            }
+                        }
+#pragma unroll
+                        for (int jj = 0; jj < JB; ++jj) {
+                            if (j0 + jj >= k) break;
+#pragma unroll
+                            for (int u = 0; u < U; ++u) {
+                                const float w_ = wj[u][jj];
+                                a0[u].x = fmaf(w_, q0[u][jj].x, a0[u].x);
+                                a0[u].y = fmaf(w_, q0[u][jj].y, a0[u].y);
+                                a0[u].z = fmaf(w_, q0[u][jj].z, a0[u].z);
+                                a0[u].w = fmaf(w_, q0[u][jj].w, a0[u].w);
+                                a1[u].x = fmaf(w_, q1[u][jj].x, a1[u].x);
+                                a1[u].y = fmaf(w_, q1[u][jj].y, a1[u].y);
+                                a1[u].z = fmaf(w_, q1[u][jj].z, a1[u].z);
+                                a1[u].w = fmaf(w_, q1[u][jj].w, a1[u].w);
+                            }
                         }
                     }
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
-                        a0[u].x = fmaf(wj[u], q0[u].x, a0[u].x);
-                        a0[u].y = fmaf(wj[u], q0[u].y, a0[u].y);
-                        a0[u].z = fmaf(wj[u], q0[u].z, a0[u].z);
-                        a0[u].w = fmaf(wj[u], q0[u].w, a0[u].w);
-                        a1[u].x = fmaf(wj[u], q1[u].x, a1[u].x);
-                        a1[u].y = fmaf(wj[u], q1[u].y, a1[u].y);
-                        a1[u].z = fmaf(wj[u], q1[u].z, a1[u].z);
-                        a1[u].w = fmaf(wj[u], q1[u].w, a1[u].w);
+                        if (tt[u] < 0) continue;
+                        *reinterpret_cast<uint4*>(g.y + (size_t)tt[u] * g.N + col) =
+                            make_uint4(pack_bf2(a0[u].x, a0[u].y), pack_bf2(a0[u].z, a0[u].w),
+                                       pack_bf2(a1[u].x, a1[u].y), pack_bf2(a1[u].z, a1[u].w));
                     }
                 }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    if (tt[u] < 0) continue;
-                    *reinterpret_cast<uint4*>(g.y + (size_t)tt[u] * g.N + col) =
-                        make_uint4(pack_bf2(a0[u].x, a0[u].y), pack_bf2(a0[u].z, a0[u].w),
-                                   pack_bf2(a1[u].x, a1[u].y), pack_bf2(a1[u].z, a1[u].w));
-                }
-            }
+            };
+            if (k <= 2)
+                finish_rows(std::integral_constant<int, FUSE_ROWS>{}, std::integral_constant<int, 2>{});
+            else
+                finish_rows(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
         }
     };
 
