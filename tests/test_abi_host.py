@@ -188,6 +188,49 @@ def test_expert_ffn_gather_argument_errors(L):
     assert f(C=0, x=None, st=None, h=None, y=None) == OK
 
 
+def test_expert_ffn_gather_combine_argument_errors(L):
+    """The fused combine's own checks come first (its workspace is required),
+    then moe_expert_ffn_gather's; every case below is refused before anything
+    is enqueued."""
+    def f(**kw):
+        T, H = kw.get("T", 100), kw.get("H", 256)
+        need = L.moe_expert_ffn_combine_ws_bytes(T, H)
+        return L.moe_expert_ffn_gather_combine(
+            None, kw.get("act", 0), kw.get("x", P), kw.get("st", P), kw.get("slot", P),
+            kw.get("tw", P), T, kw.get("k", 2), kw.get("kept", P), kw.get("E", 8),
+            kw.get("C", 64), H, kw.get("I", 256), kw.get("w1", P), kw.get("w3", P),
+            kw.get("w2", P), None, None, kw.get("ysh", None), kw.get("h", P), kw.get("yd", P),
+            kw.get("ws", P), kw.get("ws_bytes", need), kw.get("y", P))
+    assert f(T=-1) == SHAPE
+    assert f(k=0) == SHAPE
+    assert f(k=9) == UNSUP
+    assert f(k=3, E=2) == UNSUP
+    assert f(T=0, x=None, st=None, slot=None, tw=None, y=None, ws=None) == OK
+    assert f(slot=None) == NULL
+    assert f(tw=None) == NULL
+    assert f(y=None) == NULL
+    assert f(kept=None) == NULL
+    assert f(st=None) == NULL
+    assert f(ws=None) == WS
+    assert f(ws_bytes=16) == WS
+    assert f(y=MIS) == ALIGN
+    assert f(ws=MIS) == ALIGN
+    assert f(ysh=MIS) == ALIGN
+    assert f(E=64, C=1 << 20) == UNSUP      # y_disp past one 32-bit buffer range
+    assert f(H=200) == ALIGN                # the products' tile width
+    assert f(x=None) == NULL                # moe_expert_ffn_gather's checks follow
+    assert f(T=1 << 22, H=1 << 10) == UNSUP
+
+
+def test_expert_ffn_combine_workspace_size(L):
+    # the split tail's workspace, then one 4-byte counter per token and
+    # 128-column output tile, rounded up to 256 bytes
+    base = L.moe_expert_ffn_ws_bytes()
+    assert L.moe_expert_ffn_combine_ws_bytes(32768, 2048) == base + 32768 * 16 * 4
+    assert L.moe_expert_ffn_combine_ws_bytes(3, 256) == base + 256
+    assert L.moe_expert_ffn_combine_ws_bytes(-1, 256) == 0
+
+
 def test_expert_ffn_workspace_size(L):
     # one 256 x 256 fp32 partial tile per compute unit, then a 4-byte tile
     # counter per compute unit, rounded up to 256 bytes
