@@ -291,8 +291,13 @@ moe_status_t moe_expert_ffn_gather(void* stream, moe_dtype_t dtype, moe_act_t ac
  *                tail's workspace).  Required (MOE_ERR_WORKSPACE).  Two
  *                calls that run at the same time must not share one ws.
  *   y            [T, H] bf16 out
- * bf16 activations and weights only; other arguments and limits as for
- * moe_expert_ffn_gather, and E * C * H * 4 below 2^32. */
+ * slot_token, slot and kept must come from one moe_dispatch (or
+ * moe_dispatch_aux) call: the kept copies of a token are counted from slot
+ * and must each appear in slot_token; with an inconsistent set the output
+ * rows are wrong and the counters may stay non-zero (a slot_token entry
+ * outside [0, T) is skipped).  bf16 activations and weights only; other
+ * arguments and limits as for moe_expert_ffn_gather, and E * C * H * 4
+ * below 2^32. */
 size_t moe_expert_ffn_combine_ws_bytes(int64_t T, int64_t H);
 moe_status_t moe_expert_ffn_gather_combine(void* stream, moe_act_t act, const void* x,
                                            const int32_t* slot_token, const int32_t* slot,

@@ -128,6 +128,7 @@ struct GemmArgs {
     uint16_t* y;               // [T, N] bf16 output
     uint32_t* tcnt;            // [T, N / 128] copies stored so far per token and column
                                // tile (zero between launches)
+    int64_t tokens;            // T
     int k;
 };
 
@@ -535,14 +536,15 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
             int* s_tok = s_cnt + 4;
             int* s_slot = s_tok + EP::BM;
             float* s_w = reinterpret_cast<float*>(s_slot + EP::BM * KM);
-            // the row's token is loaded while the stores drain
-            const bool live = tid < EP::BM && c.m0 + tid < c.kept;
-            const int t = live ? g.row_token[(size_t)c.e * g.C + c.m0 + tid] : -1;
+            // the row's token is loaded while the stores drain (a token out of
+            // range, from a slot_token that is not this dispatch's, is skipped)
+            const bool row = tid < EP::BM && c.m0 + tid < c.kept;
+            const int t = row ? g.row_token[(size_t)c.e * g.C + c.m0 + tid] : -1;
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             if (tid == 0) *s_cnt = 0;
             __syncthreads();
             const int k = g.k;
-            if (live) {
+            if (row && t >= 0 && t < g.tokens) {
                 int sl[KM];
                 float wv[KM];
                 int n = 0;
@@ -1197,6 +1199,7 @@ struct FuseArgs {
     const float* yadd;
     void* y;
     uint32_t* tcnt;
+    int64_t tokens;
     int k;
 };
 
@@ -1326,6 +1329,7 @@ moe_status_t ffn_impl(void* stream, moe_dtype_t dtype, moe_act_t act, const void
         a2.yadd = fz->yadd;
         a2.y = static_cast<uint16_t*>(fz->y);
         a2.tcnt = fz->tcnt;
+        a2.tokens = fz->tokens;
         a2.k = fz->k;
         if (thin)
             return f8 ? launch_single<MODE_DOWN_FUSED, false, true, true>(a2, st)
@@ -1450,6 +1454,7 @@ extern "C" moe_status_t moe_expert_ffn_gather_combine(
     fz.yadd = y_shared;
     fz.y = y;
     fz.tcnt = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(ws) + ffn_ws_bytes());
+    fz.tokens = T;
     fz.k = k;
     const moe_status_t s = ffn_impl(stream, MOE_BF16, act, x, slot_token, T, kept, E, C, H, I, w1,
                                     w3, w2, b1, b2, h_ws, y_disp, ws, ffn_ws_bytes(), nullptr,
