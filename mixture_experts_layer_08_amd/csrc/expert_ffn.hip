@@ -60,6 +60,10 @@
 // consecutive columns, stored with one 8- or 16-byte store through a
 // descriptor that ends at row kept[e], so the hardware drops the padding
 // rows' stores.
+//   Fused combine (moe_expert_ffn_gather_combine; [P3] section 2.1 reduces
+//   each token's k expert rows inside the expert kernel): the second
+//   product's tiles also finish the tokens whose last kept copy they hold,
+//   writing the bf16 layer output; see fused_finish.
 #include "moe_common.h"
 #include "gemm_common.h"
 #include "internal.h"
@@ -524,8 +528,10 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
     //      completed tokens are listed in LDS;
     //   3. the workgroup reads the listed tokens' rows (system scope: other
     //      XCDs wrote them), eight columns per thread, and writes y.
-    // The wait in step 1 also drains the next tile's first loads, so the
-    // next tile's partial waits hold trivially.
+    // This is the split tail's publication protocol: rows written through to
+    // memory and completed before the relaxed count, read at system scope
+    // after it.  The wait in step 1 also drains the next tile's first loads,
+    // so the next tile's partial waits hold trivially.
     auto fused_finish = [&](const TileCtx& c) {
         if constexpr (FUSE) {
             constexpr int BNO = EP::BN_OUT;
