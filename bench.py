@@ -36,7 +36,8 @@ Further measurements, each added to the same JSON line: --backward (a
 training step: forward keeping the dispatched rows, then the combine, expert,
 dispatch and router backward, per phase), --weights fp8 (the layer on 8-bit
 e4m3 expert weights), --shared I_S (the layer plus a shared expert of
-intermediate size I_S), --copy-calibration (three plain 256 MiB device
+intermediate size I_S), --graph (the forward captured into a HIP graph and
+replayed), --copy-calibration (three plain 256 MiB device
 copies, the reference for the HBM traffic counters).
 """
 from __future__ import annotations
@@ -69,6 +70,8 @@ def parse():
                     help="other workloads measured in the same run, comma-separated ids "
                          "('' for none); each becomes a sub-record of the JSON line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the layer forward captured into a HIP graph and replayed")
     ap.add_argument("--no-fused-combine", action="store_true",
                     help="skip the sub-record of the layer with the combine fused into the "
                          "down product")
@@ -396,6 +399,35 @@ def bench_fused_combine(cfg, inputs, dev, args, plain_ms):
                     "combine in the down product's epilogue (moe_expert_ffn_gather_combine)"}
 
 
+def bench_graph(cfg, inputs, dev, args, eager_ms):
+    """The same forward captured into a HIP graph (MoELayerGPU.graph) and
+    replayed: K replays between two synchronisations.  eager_ms: the eager
+    layer's ms per step without events."""
+    import torch
+    from mixture_experts_layer_08_amd.layer import MoELayerGPU, x_to_device
+
+    layer = MoELayerGPU(cfg, inputs, dev, weights=args.weights)
+    x = x_to_device(inputs, cfg, dev)
+    g = layer.graph(x)
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = time.perf_counter()
+    for _ in range(K):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / K
+    del g, layer, x
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    print(f"[bench] {cfg.name}: graph replay {ms:.4f} ms/step (eager {eager_ms:.4f})",
+          file=sys.stderr, flush=True)
+    return {"value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 5),
+            "eager_ms_per_step": round(eager_ms, 5),
+            "path": "the layer forward captured once into a HIP graph, replayed K times"}
+
+
 def workload_name(cfg, weights):
     return (f"{cfg.name}: one MoE FFN layer forward, T={cfg.T} ({cfg.batch}x{cfg.seq_len}), "
             f"H={cfg.H}, I={cfg.I}, E={cfg.E}, top-{cfg.k}, cf={cfg.cf}, {cfg.act}, "
@@ -564,6 +596,8 @@ def run_workload(cid, args, with_cpu: bool):
     if args.weights == "bf16" and not args.no_fused_combine:
         rec["fused_combine"] = bench_fused_combine(cfg, inputs, dev, args,
                                                    ph["expert_ffn"] + ph["combine"])
+    if args.graph:
+        rec["graph"] = bench_graph(cfg, inputs, dev, args, ms_plain)
     if args.backward:
         rec["backward"] = bench_backward(cfg, inputs, dev, args)
     if args.shared:

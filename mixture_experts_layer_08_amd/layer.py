@@ -304,6 +304,26 @@ class MoELayerGPU:
         self._saved = True
         return b.y, b.l_aux
 
+    def graph(self, x: torch.Tensor) -> "torch.cuda.CUDAGraph":
+        """forward(x) captured once into a HIP graph (torch.cuda.CUDAGraph):
+        replay() reruns every launch of the layer with one call, for loops
+        that are bound by launch overhead (decode steps).  x is the captured
+        input: copy the next tokens into it, replay, read self.buf.y.  The
+        layer's calls only enqueue kernels on the current stream (no
+        allocation, no memset, no host synchronisation) and every workspace
+        counter is left at zero, so each replay equals an eager forward."""
+        side = torch.cuda.Stream(device=self.dev)
+        side.wait_stream(torch.cuda.current_stream(self.dev))
+        with torch.cuda.stream(side):  # first launches outside the capture
+            self.forward(x)
+        torch.cuda.current_stream(self.dev).wait_stream(side)
+        torch.cuda.synchronize(self.dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.forward(x)
+        torch.cuda.synchronize(self.dev)
+        return g
+
     def forward(self, x: torch.Tensor, keys: bool = False):
         """y [T, H] and L_aux [1]; every intermediate stays in self.buf."""
         self._saved = False
