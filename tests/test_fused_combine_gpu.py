@@ -158,3 +158,31 @@ def test_fused_combine_argument_errors():
         ops.moe_expert_ffn_gather_combine(x.float(), b.slot_token, b.slot, b.topk_w, b.kept,
                                           layer.w1, layer.w3, layer.w2, layer.b1, layer.b2,
                                           act="gelu")
+
+
+def test_fused_combine_no_capacity():
+    """C = 0: every copy is dropped, the products have nothing to do and the
+    pass for tokens with no kept copy writes every row: zero, or the addend
+    row rounded once to bf16 (what moe_combine gives)."""
+    T, E, k, H, I = 300, 4, 2, 256, 256
+    log(f"[fused] C = 0: T={T} E={E} k={k}")
+    g = torch.Generator(device="cpu").manual_seed(7)
+    x = torch.randn((T, H), generator=g).to(torch.bfloat16).to(DEV)
+    w1 = (torch.randn((E, H, I), generator=g) * 0.05).to(torch.bfloat16).to(DEV)
+    w3 = (torch.randn((E, H, I), generator=g) * 0.05).to(torch.bfloat16).to(DEV)
+    w2 = (torch.randn((E, I, H), generator=g) * 0.05).to(torch.bfloat16).to(DEV)
+    slot_token = torch.empty((E, 0), dtype=torch.int32, device=DEV)
+    slot = torch.full((T, k), -1, dtype=torch.int32, device=DEV)
+    topk_w = torch.rand((T, k), generator=g).to(DEV)
+    kept = torch.zeros((E,), dtype=torch.int32, device=DEV)
+    ysh = torch.randn((T, H), generator=g).to(DEV)
+    for addend in (None, ysh):
+        y = torch.full((T, H), 3.0, dtype=torch.bfloat16, device=DEV)
+        ops.moe_expert_ffn_gather_combine(x, slot_token, slot, topk_w, kept, w1, w3, w2,
+                                          y_shared=addend, y=y)
+        want = ops.moe_combine(torch.zeros((E, 1, H), dtype=torch.float32, device=DEV), slot,
+                               topk_w, y_shared=addend)
+        torch.cuda.synchronize()
+        _same_bits(y, want, "C = 0" + (" with an addend" if addend is not None else ""))
+        if addend is None:
+            assert int(y.float().abs().sum()) == 0
