@@ -305,13 +305,15 @@ class MoELayerGPU:
         return b.y, b.l_aux
 
     def graph(self, x: torch.Tensor) -> "torch.cuda.CUDAGraph":
-        """forward(x) captured once into a HIP graph (torch.cuda.CUDAGraph):
-        replay() reruns every launch of the layer with one call, for loops
-        that are bound by launch overhead (decode steps).  x is the captured
-        input: copy the next tokens into it, replay, read self.buf.y.  The
-        layer's calls only enqueue kernels on the current stream (no
-        allocation, no memset, no host synchronisation) and every workspace
-        counter is left at zero, so each replay equals an eager forward."""
+        """forward(x) captured once into a HIP graph (torch.cuda.CUDAGraph),
+        for callers that must capture (a larger captured model, a serving
+        loop that replays): replay() reruns every launch of the layer with
+        one call.  x is the captured input: copy the next tokens into it,
+        replay, read self.buf.y.  The layer's calls only enqueue kernels on
+        the current stream (no allocation, no memset, no host
+        synchronisation) and every workspace counter is left at zero, so each
+        replay equals an eager forward.  (Replay measured slower than eager
+        launches on this stack, the decode step included.)"""
         side = torch.cuda.Stream(device=self.dev)
         side.wait_stream(torch.cuda.current_stream(self.dev))
         with torch.cuda.stream(side):  # first launches outside the capture
