@@ -358,6 +358,20 @@ moe_status_t moe_expert_ffn_gather_fp8(void* stream, moe_act_t act, const void* 
                                        const void* b2, void* h_ws, void* y_disp,
                                        void* ws, size_t ws_bytes);
 
+/* moe_expert_ffn_gather_combine on 8-bit weights: the codes and scales as for
+ * moe_expert_ffn_gather_fp8 in place of w1, w3, w2; every other argument,
+ * the workspace and the bitwise agreement with moe_combine as for
+ * moe_expert_ffn_gather_combine. */
+moe_status_t moe_expert_ffn_gather_combine_fp8(void* stream, moe_act_t act, const void* x,
+                                               const int32_t* slot_token, const int32_t* slot,
+                                               const float* topk_w, int64_t T, int k,
+                                               const int32_t* kept, int E, int64_t C, int64_t H,
+                                               int64_t I, const uint8_t* w1q, const uint8_t* w3q,
+                                               const uint8_t* w2q, const float* s1,
+                                               const float* s3, const float* s2, const void* b1,
+                                               const void* b2, const float* y_shared, void* h_ws,
+                                               void* y_disp, void* ws, size_t ws_bytes, void* y);
+
 /* Bytes of the optional moe_expert_ffn workspace on the current device:
  * one 256 KiB fp32 tile per compute unit, then one 4-byte tile counter per
  * compute unit (rounded up to 256 bytes). */

@@ -30,7 +30,7 @@ EXPORTS = ("moe_capacity", "moe_status_string", "moe_workspace_bytes", "moe_rout
            "moe_route_bwd_ws_bytes", "moe_quantize_fp8", "moe_dequantize_fp8",
            "moe_expert_ffn_fp8", "moe_expert_ffn_gather_fp8", "moe_expert_ffn_fwd_save",
            "moe_dispatch_aux", "moe_dispatch_aux_noalloc", "moe_expert_ffn_gather_combine",
-           "moe_expert_ffn_combine_ws_bytes")
+           "moe_expert_ffn_combine_ws_bytes", "moe_expert_ffn_gather_combine_fp8")
 
 _lock = threading.Lock()
 _lib = None
@@ -108,6 +108,10 @@ def _declare(L: ctypes.CDLL) -> None:
                                                 i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                 c.c_size_t, vp]
     L.moe_expert_ffn_gather_combine.restype = i32
+    L.moe_expert_ffn_gather_combine_fp8.argtypes = [vp, i32, vp, vp, vp, vp, i64, i32, vp, i32,
+                                                    i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                    vp, vp, vp, vp, c.c_size_t, vp]
+    L.moe_expert_ffn_gather_combine_fp8.restype = i32
     L.moe_expert_ffn_combine_ws_bytes.argtypes = [i64, i64]
     L.moe_expert_ffn_combine_ws_bytes.restype = c.c_size_t
 

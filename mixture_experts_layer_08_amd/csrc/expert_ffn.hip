@@ -1438,11 +1438,18 @@ extern "C" size_t moe_expert_ffn_combine_ws_bytes(int64_t T, int64_t H) {
     return ffn_ws_bytes() + fuse_cnt_bytes(T, H);
 }
 
-extern "C" moe_status_t moe_expert_ffn_gather_combine(
-    void* stream, moe_act_t act, const void* x, const int32_t* slot_token, const int32_t* slot,
-    const float* topk_w, int64_t T, int k, const int32_t* kept, int E, int64_t C, int64_t H,
-    int64_t I, const void* w1, const void* w3, const void* w2, const void* b1, const void* b2,
-    const float* y_shared, void* h_ws, void* y_disp, void* ws, size_t ws_bytes, void* y) {
+namespace {
+
+// The fused call's own checks, then ffn_impl (bf16 weights, or 8-bit codes
+// with scales s1 / s3 / s2), then the rows of tokens with no kept copy.
+moe_status_t gather_combine_impl(void* stream, moe_act_t act, const void* x,
+                                 const int32_t* slot_token, const int32_t* slot,
+                                 const float* topk_w, int64_t T, int k, const int32_t* kept, int E,
+                                 int64_t C, int64_t H, int64_t I, const void* w1, const void* w3,
+                                 const void* w2, const void* b1, const void* b2,
+                                 const float* y_shared, void* h_ws, void* y_disp, void* ws,
+                                 size_t ws_bytes, void* y, const float* s1, const float* s3,
+                                 const float* s2) {
     if (T < 0 || k < 1 || E < 1 || H <= 0 || I <= 0 || C < 0) return MOE_ERR_SHAPE;
     if (k > MOE_MAX_TOPK || k > E || T * k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
     if (T == 0) return MOE_OK;
@@ -1463,10 +1470,34 @@ extern "C" moe_status_t moe_expert_ffn_gather_combine(
     fz.tokens = T;
     fz.k = k;
     const moe_status_t s = ffn_impl(stream, MOE_BF16, act, x, slot_token, T, kept, E, C, H, I, w1,
-                                    w3, w2, b1, b2, h_ws, y_disp, ws, ffn_ws_bytes(), nullptr,
-                                    nullptr, nullptr, &fz);
+                                    w3, w2, b1, b2, h_ws, y_disp, ws, ffn_ws_bytes(), s1, s3, s2,
+                                    &fz);
     if (s != MOE_OK) return s;
     return moe_combine_empty(static_cast<hipStream_t>(stream), slot, topk_w, T, H, k, y_shared, y);
+}
+
+}  // namespace
+
+extern "C" moe_status_t moe_expert_ffn_gather_combine(
+    void* stream, moe_act_t act, const void* x, const int32_t* slot_token, const int32_t* slot,
+    const float* topk_w, int64_t T, int k, const int32_t* kept, int E, int64_t C, int64_t H,
+    int64_t I, const void* w1, const void* w3, const void* w2, const void* b1, const void* b2,
+    const float* y_shared, void* h_ws, void* y_disp, void* ws, size_t ws_bytes, void* y) {
+    return gather_combine_impl(stream, act, x, slot_token, slot, topk_w, T, k, kept, E, C, H, I, w1,
+                               w3, w2, b1, b2, y_shared, h_ws, y_disp, ws, ws_bytes, y, nullptr,
+                               nullptr, nullptr);
+}
+
+extern "C" moe_status_t moe_expert_ffn_gather_combine_fp8(
+    void* stream, moe_act_t act, const void* x, const int32_t* slot_token, const int32_t* slot,
+    const float* topk_w, int64_t T, int k, const int32_t* kept, int E, int64_t C, int64_t H,
+    int64_t I, const uint8_t* w1q, const uint8_t* w3q, const uint8_t* w2q, const float* s1,
+    const float* s3, const float* s2, const void* b1, const void* b2, const float* y_shared,
+    void* h_ws, void* y_disp, void* ws, size_t ws_bytes, void* y) {
+    if (!s1) return MOE_ERR_NULL;
+    return gather_combine_impl(stream, act, x, slot_token, slot, topk_w, T, k, kept, E, C, H, I, w1q,
+                               w3q, w2q, b1, b2, y_shared, h_ws, y_disp, ws, ws_bytes, y, s1, s3,
+                               s2);
 }
 
 extern "C" moe_status_t moe_expert_ffn_fp8(void* stream, moe_act_t act, const void* x_disp,

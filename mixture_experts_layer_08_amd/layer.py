@@ -80,11 +80,11 @@ class MoELayerGPU:
         per-expert, per-column scales, quantised here on the device from the
         bf16 weights (moe_quantize_fp8).  fused_combine: forward runs the
         expert products and the combine as one call
-        (moe_expert_ffn_gather_combine; bf16 weights, fused gather)."""
+        (moe_expert_ffn_gather_combine[_fp8]; fused gather, bf16 activations)."""
         if weights not in ("bf16", "fp8"):
             raise ValueError("weights must be 'bf16' or 'fp8'")
-        if fused_combine and (not fused_gather or weights != "bf16" or cfg.dtype != "bf16"):
-            raise ValueError("the fused combine needs the fused gather and bf16 weights")
+        if fused_combine and (not fused_gather or cfg.dtype != "bf16"):
+            raise ValueError("the fused combine needs the fused gather and bf16 activations")
         self.cfg = cfg
         self.fused_gather = fused_gather
         self.fused_combine = fused_combine
@@ -224,6 +224,12 @@ class MoELayerGPU:
         write y (moe_expert_ffn_gather_combine)."""
         b = self.buf
         ysh = b.sh_y.view(self.cfg.T, self.cfg.H) if self.shared else None
+        if self.q is not None:
+            q = self.q
+            return ops.moe_expert_ffn_gather_combine_fp8(
+                x, b.slot_token, b.slot, b.topk_w, b.kept, q["w1q"], q["w3q"], q["w2q"], q["s1"],
+                q["s3"], q["s2"], self.b1, self.b2, act=self.cfg.act, y_shared=ysh, h_ws=b.h,
+                y_disp=b.y_disp, ws=b.fc_ws, y=b.y)
         return ops.moe_expert_ffn_gather_combine(
             x, b.slot_token, b.slot, b.topk_w, b.kept, self.w1, self.w3, self.w2, self.b1,
             self.b2, act=self.cfg.act, y_shared=ysh, h_ws=b.h, y_disp=b.y_disp, ws=b.fc_ws,

@@ -292,6 +292,50 @@ def moe_expert_ffn_gather_combine(x: torch.Tensor, slot_token: torch.Tensor, slo
     return y, y_disp, h_ws
 
 
+def moe_expert_ffn_gather_combine_fp8(x: torch.Tensor, slot_token: torch.Tensor,
+                                      slot: torch.Tensor, topk_w: torch.Tensor, kept: torch.Tensor,
+                                      w1q: torch.Tensor, w3q: Optional[torch.Tensor],
+                                      w2q: torch.Tensor, s1: torch.Tensor,
+                                      s3: Optional[torch.Tensor], s2: torch.Tensor,
+                                      b1: Optional[torch.Tensor] = None,
+                                      b2: Optional[torch.Tensor] = None, *, act: str = "swiglu",
+                                      y_shared: Optional[torch.Tensor] = None,
+                                      h_ws: Optional[torch.Tensor] = None,
+                                      y_disp: Optional[torch.Tensor] = None,
+                                      ws: Optional[torch.Tensor] = None,
+                                      y: Optional[torch.Tensor] = None):
+    """moe_expert_ffn_gather_combine on 8-bit weights (codes [E, N, K] and
+    per-column scales as moe_quantize_fp8 returns them).  Returns
+    (y, y_disp, h_ws)."""
+    T, H = x.shape
+    E, C = slot_token.shape
+    k = slot.shape[1]
+    I = w1q.shape[1]
+    dev = x.device
+    if x.dtype != torch.bfloat16:
+        raise ValueError("the fused combine runs on bf16 activations")
+    _check_fp8_weights(E, H, I, w1q, w3q, w2q, s1, s3, s2)
+    if slot_token.dtype != torch.int32 or slot.dtype != torch.int32:
+        raise ValueError("slot_token and slot must be int32")
+    if tuple(slot.shape) != (T, k) or tuple(topk_w.shape) != (T, k) or topk_w.dtype != torch.float32:
+        raise ValueError("slot must be int32 [T, k] and topk_w fp32 [T, k]")
+    if y_shared is not None and (y_shared.dtype != torch.float32 or y_shared.numel() != T * H
+                                 or not y_shared.is_contiguous()):
+        raise ValueError("y_shared must be a contiguous fp32 [T, H] tensor")
+    h_ws = _want(h_ws, (E, C, I), x.dtype, dev)
+    y_disp = _want(y_disp, (E, C, H), torch.float32, dev)
+    y = _want(y, (T, H), torch.bfloat16, dev)
+    if ws is None:
+        ws = torch.zeros(moe_expert_ffn_combine_ws_bytes(T, H), dtype=torch.uint8, device=dev)
+    st = lib().moe_expert_ffn_gather_combine_fp8(
+        _stream(dev), ACTS[act], _ptr(x), _ptr(slot_token), _ptr(slot), _ptr(topk_w), T, k,
+        _ptr(kept), E, C, H, I, _ptr(w1q), _ptr(w3q), _ptr(w2q), _ptr(s1), _ptr(s3), _ptr(s2),
+        _ptr(b1), _ptr(b2), _ptr(y_shared), _ptr(h_ws), _ptr(y_disp), _ptr(ws),
+        ws.numel() * ws.element_size(), _ptr(y))
+    check("moe_expert_ffn_gather_combine_fp8", st)
+    return y, y_disp, h_ws
+
+
 def moe_quantize_fp8(w: torch.Tensor, *, q: Optional[torch.Tensor] = None,
                      scale: Optional[torch.Tensor] = None):
     """bf16 weights [E, K, N] -> (e4m3 codes [E, N, K] uint8, fp32 scales

@@ -222,6 +222,22 @@ def test_expert_ffn_gather_combine_argument_errors(L):
     assert f(T=1 << 22, H=1 << 10) == UNSUP
 
 
+def test_expert_ffn_gather_combine_fp8_argument_errors(L):
+    def f(**kw):
+        T, H = kw.get("T", 100), kw.get("H", 256)
+        need = L.moe_expert_ffn_combine_ws_bytes(T, H)
+        return L.moe_expert_ffn_gather_combine_fp8(
+            None, 0, P, P, P, P, T, 2, P, 8, 64, H, kw.get("I", 256), P, P, P,
+            kw.get("s1", P), kw.get("s3", P), kw.get("s2", P), None, None, None, P, P,
+            kw.get("ws", P), kw.get("ws_bytes", need), P)
+    assert f(s1=None) == NULL
+    assert f(s3=None) == NULL          # SwiGLU needs the up matrix's scales
+    assert f(s2=None) == NULL
+    assert f(ws_bytes=16) == WS
+    assert f(H=200) == ALIGN
+    assert f(T=-1) == SHAPE
+
+
 def test_expert_ffn_combine_workspace_size(L):
     # the split tail's workspace, then one 4-byte counter per token and
     # 128-column output tile, rounded up to 256 bytes

@@ -186,3 +186,23 @@ def test_fused_combine_no_capacity():
         _same_bits(y, want, "C = 0" + (" with an addend" if addend is not None else ""))
         if addend is None:
             assert int(y.float().abs().sum()) == 0
+
+
+@pytest.mark.parametrize("name", ["swiglu-e8", "gelu-e4", "swiglu-e8-shared-drops",
+                                  "swiglu-e8-t8192-h2048"])
+def test_fused_combine_fp8(name):
+    """8-bit expert weights (moe_expert_ffn_gather_combine_fp8): bitwise the
+    unfused layer on the same 8-bit weights, counters zero after the call."""
+    cfg = SMALL[name]
+    log(f"[fused fp8] {name}")
+    inp = make_inputs(cfg)
+    x = x_to_device(inp, cfg, DEV)
+    fused = MoELayerGPU(cfg, inp, DEV, weights="fp8", fused_combine=True)
+    plain = MoELayerGPU(cfg, inp, DEV, weights="fp8")
+    fused.forward(x)
+    plain.forward(x)
+    torch.cuda.synchronize()
+    for n in ("w1q", "w2q", "s1", "s2"):
+        assert torch.equal(fused.q[n], plain.q[n]), n
+    _same_bits(fused.buf.y, plain.buf.y, f"{name} (8-bit weights)")
+    assert int(_counters(fused.buf.fc_ws).count_nonzero()) == 0
