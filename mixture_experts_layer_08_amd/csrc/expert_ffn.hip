@@ -654,6 +654,8 @@ __global__ __launch_bounds__(kGThreads, 1) void grouped_gemm_kernel(GemmArgs g) 
                     }
                 }
             };
+            // FUSE_ROWS tunes the k <= 2 case alone (at 4 rows the 256-column
+            // tiles spill registers; at the default 2 both calls are the same)
             if (k <= 2)
                 finish_rows(std::integral_constant<int, FUSE_ROWS>{}, std::integral_constant<int, 2>{});
             else
