@@ -305,14 +305,16 @@ def test_backward_full_size_config2():
     log(f"[bwd] config 2: worst weight-grad err/rms {worst:.3e}")
 
 
-def test_backward_full_size_config4():
-    """The wide GELU layer (T 8192, H 4096, I 16384, E 8, both biases) at full
-    size, every gradient against the float64 backward oracle: the longest
-    products of the backward (dX with K = I = 16384, dh with K = H = 4096,
-    the weight gradients over about 2048 rows per expert)."""
+@pytest.mark.parametrize("cid", [4, 5])
+def test_backward_full_size(cid):
+    """Workload 4, the wide GELU layer (T 8192, H 4096, I 16384, E 8, both
+    biases: the longest products of the backward, dX with K = I = 16384), and
+    workload 5, the 32768-token Gumbel layer (E 32: the router backward
+    through the tempered soft path), at full size, every gradient against the
+    float64 backward oracle."""
     from mixture_experts_layer_08_amd.synth import CONFIGS
-    cfg = CONFIGS[4]
-    log("[bwd] config 4 full size (training forward, saved planes)")
+    cfg = CONFIGS[cid]
+    log(f"[bwd] config {cid} full size (training forward, saved planes)")
     inp, layer, x, dy, dy64, gg = _run(cfg, 0.5, train=True)
     r = M.route(inp, cfg)
     near = M.near_tie_tokens(r.keys, cfg.k)
@@ -321,12 +323,12 @@ def test_backward_full_size_config4():
     if not same.all():   # the oracle's backward follows its own routing
         pytest.skip(f"{int((~same).sum())} near-tie token(s) routed differently")
     ref = B.backward(inp, cfg, dy64, 0.5)
-    log("[bwd] config 4: oracle done")
-    _rows_close(to_np(gg["dx"]), ref.dx, 3e-2, "config 4: dx")
-    _check_router_grads(cfg, inp, layer, ref, dy64, gg, "config 4")
+    log(f"[bwd] config {cid}: oracle done")
+    _rows_close(to_np(gg["dx"]), ref.dx, 3e-2, f"config {cid}: dx")
+    _check_router_grads(cfg, inp, layer, ref, dy64, gg, f"config {cid}")
     worst = 0.0
     for key, want in ref.dweights.items():
         got = to_np(gg[key])
         for e in range(cfg.E):
-            worst = max(worst, _close(got[e], want[e], 1e-2, f"config 4: d{key}[{e}]"))
-    log(f"[bwd] config 4: worst weight-grad err/rms {worst:.3e}")
+            worst = max(worst, _close(got[e], want[e], 1e-2, f"config {cid}: d{key}[{e}]"))
+    log(f"[bwd] config {cid}: worst weight-grad err/rms {worst:.3e}")
