@@ -121,12 +121,13 @@ def test_fused_combine_decode(T):
     assert int(_counters(fused.buf.fc_ws).count_nonzero()) == 0
 
 
-@pytest.mark.parametrize("cid", [2, 3, 5, 6])
+@pytest.mark.parametrize("cid", [2, 3, 4, 5, 6])
 def test_fused_combine_full_size(cid):
     """Full-size workloads in the benchmark's launch configuration (4096
-    tokens; the skewed layer with drops; the 32768-token, 32-expert Gumbel
-    layer; the 64-token decode step): bitwise the unfused layer on every
-    element, counters zero after the call."""
+    tokens; the skewed layer with drops; the wide GELU layer with both
+    biases; the 32768-token, 32-expert Gumbel layer; the 64-token decode
+    step): bitwise the unfused layer on every element, counters zero after
+    the call."""
     cfg = CONFIGS[cid]
     log(f"[fused full] config {cid} {cfg.name}")
     inp = make_inputs(cfg)
